@@ -1,0 +1,204 @@
+"""CPU oracle for the MiniMax-H3 AdaLN-modulated projection stages.
+
+TEST INFRASTRUCTURE ONLY: tests, the package smoke check and the benchmark's CPU baseline
+are the only callers.  The HIP path never imports this package and this package never
+imports the HIP path.
+
+The arithmetic lives in dit_oracle.c (plain loops, fp64 between the rounding points that
+the FlashInfer MiniMax-H3 pages print).  This wrapper only marshals numpy arrays, resolves
+identity RoPE positions (None -> the row's own number, as the bf16 pre-attention page's
+rope_positions entry states) and fans rows out over threads (rows are independent and
+ctypes releases the GIL during each call).
+
+brute.py is a second, independent NumPy transcription used to cross-check this one on
+one- and two-row inputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+HIDDEN, HEADS, HEAD_DIM = 5376, 56, 128
+QKV_ROWS, ATTN_WIDTH, INTER = 21504, 7168, 14336
+
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_d = ctypes.c_double
+
+
+def lib():
+    global _LIB
+    if _LIB is None:
+        path = os.path.join(HERE, "liboracle.so")
+        if not os.path.exists(path):
+            from . import build as _b
+            _b.build()
+        L = ctypes.CDLL(path)
+        L.oracle_round_bf16.restype = ctypes.c_uint16
+        L.oracle_round_bf16.argtypes = [_d]
+        L.oracle_bf16_value.restype = _d
+        L.oracle_bf16_value.argtypes = [ctypes.c_uint16]
+        L.oracle_round_e4m3.restype = ctypes.c_uint8
+        L.oracle_round_e4m3.argtypes = [_d]
+        L.oracle_e4m3_value.restype = _d
+        L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_pre_attn.restype = None
+        L.oracle_pre_attn.argtypes = [_i64, _i64, _p, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p,
+                                      _d, _d, _p, _p]
+        L.oracle_out_proj.restype = None
+        L.oracle_out_proj.argtypes = [_i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p]
+        L.oracle_mlp.restype = None
+        L.oracle_mlp.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _d,
+                                 _p, _p, _p, _p, _p, _p]
+        _LIB = L
+    return _LIB
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _c(a, dt):
+    return np.ascontiguousarray(a, dtype=dt)
+
+
+def round_bf16(v: float) -> int:
+    return int(lib().oracle_round_bf16(float(v)))
+
+
+def bf16_value(b: int) -> float:
+    return float(lib().oracle_bf16_value(int(b)))
+
+
+def round_e4m3(v: float) -> int:
+    return int(lib().oracle_round_e4m3(float(v)))
+
+
+def e4m3_value(c: int) -> float:
+    return float(lib().oracle_e4m3_value(int(c)))
+
+
+def _default_threads():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _fan_out(fn, nrows, threads, min_rows=1):
+    threads = max(1, min(threads or _default_threads(), nrows))
+    if threads == 1 or nrows <= min_rows:
+        fn(0, nrows)
+        return 1
+    bounds = np.linspace(0, nrows, threads + 1).astype(np.int64)
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda t: fn(int(bounds[t]), int(bounds[t + 1])), range(threads)))
+    return threads
+
+
+def _table(t):
+    """(base array, element offset, rows, row stride) of a synth.Table-like object."""
+    return t.base, int(t.offset), int(t.rows), int(t.row_stride)
+
+
+def _table_ptr(base, offset):
+    return ctypes.c_void_p(base.ctypes.data + 2 * offset)
+
+
+def pre_attn(d, rows_sel=None, threads=None):
+    """Oracle of the bf16 pre-attention stage on the rows rows_sel (default all).
+
+    Returns (workspace [R,5376] uint16, out [R,56,3,128] uint16) for the selected rows.
+    """
+    M = d["M"]
+    sel = np.arange(M, dtype=np.int64) if rows_sel is None else np.asarray(rows_sel, np.int64)
+    R = sel.size
+    x = _c(d["x"].reshape(M, HIDDEN)[sel], np.uint16)
+    idx = _c(d["adaln_index"][sel], np.int64)
+    pos = sel.copy() if d.get("rope_positions") is None else _c(d["rope_positions"][sel], np.int64)
+    sc_b, sc_o, rows, ld = _table(d["adaln_scale"])
+    sh_b, sh_o, rows2, ld2 = _table(d["adaln_shift"])
+    assert rows == rows2 and ld == ld2
+    W = _c(d["qkv_weight"], np.uint16)
+    xw = _c(d["x_norm_weight"], np.uint16)
+    qw = _c(d["q_norm_weight"], np.uint16)
+    kw = _c(d["k_norm_weight"], np.uint16)
+    cs = _c(d["rope_cos_sin"], np.uint16)
+    S = int(d["S"])
+    ws = np.zeros((R, HIDDEN), np.uint16)
+    out = np.zeros((R, HEADS, 3, HEAD_DIM), np.uint16)
+    L = lib()
+    qk_eps = d["qk_eps"] if d.get("qk_eps") is not None else d["eps"]
+    eps32 = float(np.float32(d["eps"]))
+    qk32 = float(np.float32(qk_eps))
+
+    def run(r0, r1):
+        L.oracle_pre_attn(r0, r1, _ptr(x), _ptr(xw), _table_ptr(sc_b, sc_o), _table_ptr(sh_b, sh_o), rows, ld,
+                          _ptr(idx), _ptr(W), _ptr(qw), _ptr(kw), _ptr(cs), S, _ptr(pos), eps32, qk32,
+                          _ptr(ws), _ptr(out))
+
+    _fan_out(run, R, threads)
+    return ws, out
+
+
+def out_proj(d, rows_sel=None, threads=None):
+    """Oracle of the bf16 out-projection with gated residual; returns out [R,5376] uint16."""
+    M = d["M"]
+    sel = np.arange(M, dtype=np.int64) if rows_sel is None else np.asarray(rows_sel, np.int64)
+    R = sel.size
+    attn = _c(d["attn_out"].reshape(M, ATTN_WIDTH)[sel], np.uint16)
+    gi = _c(d["gate_index"][sel], np.int32)
+    res = _c(d["residual"].reshape(M, HIDDEN)[sel], np.uint16)
+    g_b, g_o, rows, ld = _table(d["gate"])
+    Wo = _c(d["o_weight"], np.uint16)
+    out = np.zeros((R, HIDDEN), np.uint16)
+    L = lib()
+
+    def run(r0, r1):
+        L.oracle_out_proj(r0, r1, _ptr(attn), _ptr(Wo), _table_ptr(g_b, g_o), rows, ld, _ptr(gi), _ptr(res),
+                          _ptr(out))
+
+    _fan_out(run, R, threads)
+    return out
+
+
+def mlp(d, rows_sel=None, threads=None):
+    """Oracle of the FP8 W8A8 MLP block on the selected rows.
+
+    Returns a dict with a_q [R,5376] u8, a_scale [R] f32, y [R,14336] u16, y_q [R,14336] u8,
+    y_scale [R] f32, out [R,5376] u16.
+    """
+    M = d["M"]
+    sel = np.arange(M, dtype=np.int64) if rows_sel is None else np.asarray(rows_sel, np.int64)
+    R = sel.size
+    x = _c(d["x"].reshape(M, HIDDEN)[sel], np.uint16)
+    idx = _c(d["adaln_index"][sel], np.int64)
+    res = _c(d["residual"].reshape(M, HIDDEN)[sel], np.uint16)
+    sc_b, sc_o, rows, ld = _table(d["adaln_scale"])
+    sh_b, sh_o, rows2, ld2 = _table(d["adaln_shift"])
+    g_b, g_o, rows3, ld3 = _table(d["gate"])
+    assert rows == rows2 == rows3 and ld == ld2 == ld3
+    xw = _c(d["x_norm_weight"], np.uint16)
+    W1 = _c(d["fc1_q"], np.uint8)
+    s1 = _c(d["fc1_scale"], np.float32)
+    W2 = _c(d["fc2_q"], np.uint8)
+    s2 = _c(d["fc2_scale"], np.float32)
+    o = {
+        "a_q": np.zeros((R, HIDDEN), np.uint8), "a_scale": np.zeros(R, np.float32),
+        "y": np.zeros((R, INTER), np.uint16), "y_q": np.zeros((R, INTER), np.uint8),
+        "y_scale": np.zeros(R, np.float32), "out": np.zeros((R, HIDDEN), np.uint16),
+    }
+    L = lib()
+    eps32 = float(np.float32(d["eps"]))
+
+    def run(r0, r1):
+        L.oracle_mlp(r0, r1, _ptr(x), _ptr(xw), _table_ptr(sc_b, sc_o), _table_ptr(sh_b, sh_o),
+                     _table_ptr(g_b, g_o), rows, ld, _ptr(idx), _ptr(res), _ptr(W1), _ptr(s1), _ptr(W2), _ptr(s2),
+                     eps32, _ptr(o["a_q"]), _ptr(o["a_scale"]), _ptr(o["y"]), _ptr(o["y_q"]), _ptr(o["y_scale"]),
+                     _ptr(o["out"]))
+
+    _fan_out(run, R, threads)
+    return o
