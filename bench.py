@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark of the MiniMax-H3 AdaLN projection stages on one MI355X.
+
+One step = one pass of the whole hot path over one batch of M = 32760 tokens:
+  pre-attention (RMSNorm + AdaLN -> workspace; QKV GEMM + Q/K norm + RoPE + pack),
+  gated-residual out-projection (bf16), and the FP8 W8A8 MLP block,
+with the seeded synthetic inputs of the three M = 32760 workloads already resident in HBM.
+
+The headline value is the pre-attention stage throughput: 2*M*21504*5376 flop over the wall
+time of its two launches, from HIP events on the stream the kernels run on.  Each kernel
+launch of the step is bracketed by events so the dominant kernel (the QKV GEMM) can be
+priced against the bf16 MFMA peak.  The CPU oracle is timed on a bounded row sample of the
+same pre-attention workload on the host's cores (cpu_baseline).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M_TOKENS = 32760
+QKV_FLOP = 2.0 * M_TOKENS * 21504 * 5376          # 7.5745e12
+OUTP_FLOP = 2.0 * M_TOKENS * 5376 * 7168           # 2.5248e12
+MLP_FLOP = 2.0 * M_TOKENS * 28672 * 5376 + 2.0 * M_TOKENS * 5376 * 14336   # 1.5149e13
+# Published MI355X dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
+PEAK_BF16 = 2500.0
+PEAK_FP8 = 5000.0
+PEAK_HBM = 8000.0
+# Minimum HBM bytes of the norm/AdaLN launch per row: read x (5376 bf16), write the workspace
+# (5376 bf16), read the int64 index; tables and the norm weight stay in cache.
+NORM_BYTES_PER_ROW = 5376 * 2 * 2 + 8
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hpp", "pre_attn.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "diffusion_transformer_adaln_rmsnorm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per QKV GEMM launch from the committed counter summary, if it still
+    describes the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "qkv_gemm_traffic_m32760.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(d, seconds_target=15.0):
+    import numpy as np
+    import oracle
+    threads = max(1, min(16, os.cpu_count() or 1))
+    # one warm call sizes the sample so that the timed call lasts about seconds_target
+    t0 = time.perf_counter()
+    oracle.pre_attn(d, rows_sel=np.arange(threads, dtype=np.int64), threads=threads)
+    per_round = time.perf_counter() - t0
+    rounds = max(1, int(seconds_target / max(per_round, 1e-3)))
+    g = np.random.Generator(np.random.PCG64(12345))
+    rows = np.sort(g.choice(d["M"], size=min(d["M"], rounds * threads), replace=False)).astype(np.int64)
+    t0 = time.perf_counter()
+    oracle.pre_attn(d, rows_sel=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * rows.size * 21504 * 5376
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"pre-attention oracle (fp64, C) on {rows.size} seeded random rows of the M=32760 workload, "
+                      f"{dt:.1f} s wall; value = QKV flops of those rows / wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stages", default="pre_attn,out_proj,mlp")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: every stage here is data-parallel over rows and runs on a "
+              f"single MI355X; --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    stages = [s for s in args.stages.split(",") if s]
+
+    import numpy as np
+    import torch
+    import synth
+    import diffusion_transformer_adaln_rmsnorm_amd as dit
+
+    dit.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t_gen = time.perf_counter()
+    log("generating seeded inputs (pre-attention M=32760)")
+    _, d_pre = synth.config(2)
+    tp = synth.to_torch("pre_attn", d_pre, dev)
+    ws = torch.empty((M_TOKENS, 5376), dtype=torch.bfloat16, device=dev)
+    out_qkv = torch.empty((1, M_TOKENS, 56, 3, 128), dtype=torch.bfloat16, device=dev)
+    if "out_proj" in stages:
+        log("generating seeded inputs (out-projection M=32760)")
+        _, d_op = synth.config(3)
+        to = synth.to_torch("out_proj", d_op, dev)
+        out_op = torch.empty((M_TOKENS, 5376), dtype=torch.bfloat16, device=dev)
+        del d_op
+    if "mlp" in stages:
+        log("generating seeded inputs (fp8 MLP M=32760)")
+        _, d_mlp = synth.config(4)
+        tm = synth.to_torch("mlp", d_mlp, dev)
+        del d_mlp
+        mws = {"workspace_a_q": torch.empty((M_TOKENS, 5376), dtype=torch.float8_e4m3fn, device=dev),
+               "workspace_a_scale": torch.empty((M_TOKENS,), dtype=torch.float32, device=dev),
+               "workspace_y": torch.empty((M_TOKENS, 14336), dtype=torch.bfloat16, device=dev),
+               "workspace_y_q": torch.empty((M_TOKENS, 14336), dtype=torch.float8_e4m3fn, device=dev),
+               "workspace_y_scale": torch.empty((M_TOKENS,), dtype=torch.float32, device=dev)}
+        out_mlp = torch.empty((M_TOKENS, 5376), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log(f"inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s)")
+
+    def step(ev):
+        ev[0].record()
+        dit.dit_norm_adaln_bf16(tp["x"], tp["x_norm_weight"], tp["adaln_scale"], tp["adaln_shift"],
+                                tp["adaln_index"], workspace=ws, eps=tp["eps"])
+        ev[1].record()
+        dit.dit_qkv_rope_pack_bf16(ws, tp["qkv_weight"], tp["q_norm_weight"], tp["k_norm_weight"],
+                                   tp["rope_cos_sin"], ulysses_degree=1, out=out_qkv, qk_eps=tp["qk_eps"],
+                                   rope_positions=tp["rope_positions"])
+        ev[2].record()
+        if "out_proj" in stages:
+            dit.dit_out_proj_gated_bf16(to["attn_out"], to["o_weight"], to["gate"], to["gate_index"],
+                                        to["residual"], out=out_op)
+        ev[3].record()
+        if "mlp" in stages:
+            dit.dit_mlp_fp8(tm["x"], tm["x_norm_weight"], tm["adaln_scale"], tm["adaln_shift"], tm["adaln_index"],
+                            tm["gate"], tm["residual"], tm["fc1_weight_q"], tm["fc1_weight_scale"],
+                            tm["fc2_weight_q"], tm["fc2_weight_scale"], out=out_mlp, eps=tm["eps"], **mws)
+        ev[4].record()
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
+    for i in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
+    evs = [mk() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])   # ms
+    norm_ms, gemm_ms, op_ms, mlp_ms = seg.mean(axis=0)
+    pre_ms = norm_ms + gemm_ms
+    ms_per_step = wall * 1e3 / args.steps
+    value = QKV_FLOP / (pre_ms * 1e-3) / 1e12
+    gemm_tflops = QKV_FLOP / (gemm_ms * 1e-3) / 1e12
+    log(f"pre-attn {pre_ms:.3f} ms (norm {norm_ms:.3f} + qkv gemm {gemm_ms:.3f}) = {value:.1f} TFLOP/s; "
+        f"out-proj {op_ms:.3f} ms; mlp {mlp_ms:.3f} ms; step {ms_per_step:.3f} ms")
+    traffic = load_traffic()
+    res = {
+        "metric": "pre-attn TFLOP/s at M=32760 bf16 and % of MI355X MFMA peak (1 GPU)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded PCG64, shapes of the MiniMax-H3 block)",
+        "config": {"workload": "bf16 pre-attention M=32760 (QKV 32760x21504x5376, rows=2 AdaLN tables, S=32760 "
+                               "identity positions); step also runs the M=32760 bf16 gated out-projection and "
+                               "fp8 W8A8 MLP", "tokens": M_TOKENS, "stages": stages},
+        "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16, 2),
+        "roofline": {"bound": "mfma", "kernel": "k_qkv_gemm", "achieved": round(gemm_tflops, 2),
+                     "peak": PEAK_BF16, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16, 4),
+                     "traffic": traffic, "avg_launch_ms": round(float(gemm_ms), 4)},
+        "stages_ms": {"norm_adaln": round(float(norm_ms), 4), "qkv_gemm": round(float(gemm_ms), 4),
+                      "out_proj": round(float(op_ms), 4), "mlp_fp8": round(float(mlp_ms), 4)},
+        "stage_rates": {
+            "norm_adaln_GBps": round(NORM_BYTES_PER_ROW * M_TOKENS / (norm_ms * 1e-3) / 1e9, 1),
+            "norm_adaln_frac_hbm": round(NORM_BYTES_PER_ROW * M_TOKENS / (norm_ms * 1e-3) / 1e9 / PEAK_HBM, 4),
+        },
+    }
+    if "out_proj" in stages:
+        r = OUTP_FLOP / (op_ms * 1e-3) / 1e12
+        res["stage_rates"]["out_proj_TFLOPs"] = round(r, 2)
+        res["stage_rates"]["out_proj_frac_bf16"] = round(r / PEAK_BF16, 4)
+    if "mlp" in stages:
+        r = MLP_FLOP / (mlp_ms * 1e-3) / 1e12
+        res["stage_rates"]["mlp_fp8_TFLOPs"] = round(r, 2)
+        res["stage_rates"]["mlp_fp8_frac_fp8"] = round(r / PEAK_FP8, 4)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a row sample")
+        res["cpu_baseline"] = cpu_baseline(d_pre)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,102 @@
+// Device helpers shared by the gfx950 kernels: vector types, bf16/e4m3 conversions,
+// wavefront reductions.  CDNA4 only (64-lane wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+constexpr int kHidden = 5376;
+constexpr int kHeads = 56;
+constexpr int kHeadDim = 128;
+constexpr int kQkvRows = 3 * kHeads * kHeadDim;   // 21504
+constexpr int kAttnWidth = kHeads * kHeadDim;     // 7168
+constexpr int kRopeCols = 96;
+constexpr int kNFreq = 48;
+constexpr int kInter = 14336;
+constexpr int kFc1Rows = 2 * kInter;              // 28672
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+// bf16 bit pattern -> float (exact)
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t f2bf(float f) {
+    __bf16 b = (__bf16)f;
+    return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+// round a float to the nearest bf16 value, returned as float
+__device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
+
+// Correctly rounded double -> bf16.  The double is first rounded to odd into fp32 (truncate,
+// then force the last bit to 1 when inexact); since fp32 keeps 24 >= 8 + 2 significant bits,
+// the round-to-nearest-even to bf16 that follows equals a single rounding of the double.
+__device__ __forceinline__ float f64_to_f32_odd(double d) {
+    float f = (float)d;
+    const double back = (double)f;
+    if (back != d) {
+        uint32_t b = __float_as_uint(f);
+        if (fabs(back) > fabs(d)) b -= 1u;   // RNE went away from zero: step back toward zero
+        f = __uint_as_float(b | 1u);
+    }
+    return f;
+}
+__device__ __forceinline__ uint32_t f2bf_d(double d) { return f2bf(f64_to_f32_odd(d)); }
+__device__ __forceinline__ float rbf_d(double d) { return bf2f(f2bf_d(d)); }
+
+// unpack 8 bf16 (one 16-byte vector) to floats
+__device__ __forceinline__ void unpack8(const u32x4& v, float (&f)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = bf_lo(v[i]);
+        f[2 * i + 1] = bf_hi(v[i]);
+    }
+}
+__device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = pack_bf2(f[2 * i], f[2 * i + 1]);
+    return v;
+}
+
+// Two floats -> two float8_e4m3fn codes in the low 16 bits (OCP format on gfx950),
+// round to nearest even; inputs are clamped to +-448 first so that magnitudes beyond the
+// largest code saturate.
+__device__ __forceinline__ uint32_t f2e4m3x2(float a, float b) {
+    a = fminf(fmaxf(a, -448.0f), 448.0f);
+    b = fminf(fmaxf(b, -448.0f), 448.0f);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Streaming (non-temporal) 16-byte load/store for data touched once.
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, const u32x4& v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+
+}  // namespace dit

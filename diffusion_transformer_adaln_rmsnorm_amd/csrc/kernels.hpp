@@ -1,0 +1,37 @@
+// Internal launchers (host side).  Each enqueues its kernel(s) on `stream` and returns the
+// launch status; argument validation happens in api.cpp before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+hipError_t launch_norm_adaln_bf16(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,
+                                  int64_t ld_scale, const uint16_t* shift, int64_t ld_shift, int64_t rows,
+                                  const int64_t* idx, float eps, uint16_t* ws, hipStream_t stream);
+
+hipError_t launch_norm_adaln_fp8q(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,
+                                  int64_t ld_scale, const uint16_t* shift, int64_t ld_shift, int64_t rows,
+                                  const int64_t* idx, float eps, uint8_t* a_q, float* a_scale, float* y_amax,
+                                  hipStream_t stream);
+
+hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
+                           const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos, float qk_eps,
+                           uint16_t* out, hipStream_t stream);
+
+hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t* Wo, const uint16_t* gate,
+                                int64_t gate_rows, int64_t gate_ld, const int32_t* gate_index,
+                                const uint16_t* residual, uint16_t* out, hipStream_t stream);
+
+hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M, const uint8_t* W1,
+                             const float* w1s, uint16_t* y, float* y_amax, hipStream_t stream);
+
+hipError_t launch_quant_rows(const uint16_t* y, int64_t M, float* y_scale_inout, uint8_t* y_q,
+                             hipStream_t stream);
+
+hipError_t launch_fc2_gated(const uint8_t* y_q, const float* y_scale, int64_t M, const uint8_t* W2,
+                            const float* w2s, const uint16_t* gate, int64_t gate_rows, int64_t gate_ld,
+                            const int64_t* idx, const uint16_t* residual, uint16_t* out, hipStream_t stream);
+
+}  // namespace dit

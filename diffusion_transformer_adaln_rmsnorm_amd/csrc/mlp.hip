@@ -1,0 +1,159 @@
+// FP8 (W8A8) MLP block: FC1 + SwiGLU, per-token y quantisation, FC2 + gated residual.
+//
+// FlashInfer "minimax_h3_mlp_fp8_sm120", per-row formula block:
+//   h = bf16(a_q @ fc1^T * s_a * fc1_scale)            FP32 accumulation, [M, 28672]
+//   y = bf16(bf16(silu(h_gate)) * h_up)                 [M, 14336]
+//   y_q = e4m3(y / s_y), s_y = RN(amax_row|y| / 448)
+//   o = bf16(y_q @ fc2^T * s_y * fc2_scale)
+//   out = bf16(residual + bf16(gate[i] * o)), gate 0 where i is outside [0, rows).
+//
+// FC1 tile: 256 rows x (128 gate columns j0.. and the 128 up columns 14336+j0..), so the
+// SwiGLU pair of every column is in the same tile.  Its epilogue writes y and folds |y| into
+// a per-row maximum with an atomic max on the float bits (|y| >= 0, so the unsigned order is
+// the float order and the result does not depend on tile order).  The quantisation kernel then
+// turns each row's maximum into s_y and writes y_q; FC2 consumes y_q.  Stream order separates
+// the three launches, so no tile-ready flags are needed.
+#include "common.hpp"
+#include "gemm.hpp"
+#include "kernels.hpp"
+
+namespace dit {
+
+using namespace gemm;
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale, int64_t M,
+                  const uint8_t* __restrict__ W1, const float* __restrict__ w1s, uint16_t* __restrict__ y,
+                  float* __restrict__ y_amax, int mt, int nt) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    int tm, tn;
+    tile_coords(blockIdx.x, mt, nt, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM;
+    const int j0 = tn * 128;
+    f32x16 acc[4][4];
+    mainloop<true>(a_q, kHidden, m0, M, W1, kHidden, j0, kInter + j0, kHidden / kBKB, smem, acc);
+    stage_tile_bf16(acc, smem, a_scale, m0, M, w1s + j0, w1s + kInter + j0);
+    __syncthreads();
+
+    const int t = threadIdx.x;
+    const int c8 = (t & 15) * 8;
+    const int rsub = t >> 4;            // 0..15
+    for (int it = 0; it < kBM / 16; ++it) {
+        const int row = it * 16 + rsub;
+        const int64_t m = m0 + row;
+        float hg[8], hu[8], yv[8];
+        unpack8(epi_ld(smem, row, c8), hg);
+        unpack8(epi_ld(smem, row, 128 + c8), hu);
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float sl = rbf(hg[e] / (1.0f + expf(-hg[e])));
+            yv[e] = rbf(sl * hu[e]);
+            amax = fmaxf(amax, fabsf(yv[e]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 1));
+        amax = fmaxf(amax, __shfl_xor(amax, 2));
+        amax = fmaxf(amax, __shfl_xor(amax, 4));
+        amax = fmaxf(amax, __shfl_xor(amax, 8));
+        if (m < M) {
+            st16(y + m * kInter + j0 + c8, pack8(yv));
+            if ((t & 15) == 0) atomicMax(reinterpret_cast<unsigned int*>(y_amax + m), __float_as_uint(amax));
+        }
+    }
+}
+
+// y quantisation: one wavefront per row; 14336 = 1792 chunks of 8, 28 per lane.
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ y, int64_t M,
+                                                    float* __restrict__ y_scale, uint8_t* __restrict__ y_q) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    const float amax = y_scale[m];
+    const float s = amax / 448.0f;            // RN(amax / 448)
+    const uint16_t* yr = y + m * kInter;
+    uint8_t* qr = y_q + m * kInter;
+    constexpr int kPerLane = kInter / 8 / 64;    // 28
+#pragma unroll 4
+    for (int j = 0; j < kPerLane; ++j) {
+        const int c = (j * 64 + lane) * 8;
+        float a[8];
+        unpack8(ld16(yr + c), a);
+        uint2 q;
+        if (s == 0.f) {
+            q = make_uint2(0u, 0u);
+        } else {
+            q.x = f2e4m3x2(a[0] / s, a[1] / s) | (f2e4m3x2(a[2] / s, a[3] / s) << 16);
+            q.y = f2e4m3x2(a[4] / s, a[5] / s) | (f2e4m3x2(a[6] / s, a[7] / s) << 16);
+        }
+        *reinterpret_cast<uint2*>(qr + c) = q;
+    }
+    // every lane has read y_scale[m] above; the store below follows a wave-wide barrier
+    __builtin_amdgcn_wave_barrier();
+    if (lane == 0) y_scale[m] = s;
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_scale, int64_t M,
+                 const uint8_t* __restrict__ W2, const float* __restrict__ w2s, const uint16_t* __restrict__ gate,
+                 int64_t gate_rows, int64_t gate_ld, const int64_t* __restrict__ idx, const uint16_t* residual,
+                 uint16_t* out, int mt, int nt) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    int tm, tn;
+    tile_coords(blockIdx.x, mt, nt, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM;
+    const int n0 = tn * kBN;
+    f32x16 acc[4][4];
+    mainloop<true>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kBKB, smem, acc);
+    stage_tile_bf16(acc, smem, y_scale, m0, M, w2s + n0, w2s + n0 + 128);
+    __syncthreads();
+
+    const int t = threadIdx.x;
+    const int c8 = (t & 31) * 8;
+    const int rsub = t >> 5;
+    for (int it = 0; it < kBM / 8; ++it) {
+        const int row = it * 8 + rsub;
+        const int64_t m = m0 + row;
+        if (m >= M) break;
+        float o[8], g[8], r[8];
+        unpack8(epi_ld(smem, row, c8), o);
+        const int64_t i = idx[m];
+        if (i >= 0 && i < gate_rows) {
+            unpack8(ld16(gate + i * gate_ld + n0 + c8), g);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) g[e] = 0.f;
+        }
+        const int64_t off = m * kHidden + n0 + c8;
+        unpack8(ld16(residual + off), r);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r[e] = rbf_d((double)r[e] + (double)rbf(g[e] * o[e]));
+        st16(out + off, pack8(r));
+    }
+}
+
+hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M, const uint8_t* W1,
+                             const float* w1s, uint16_t* y, float* y_amax, hipStream_t stream) {
+    const int mt = (int)((M + kBM - 1) / kBM);
+    const int nt = kInter / 128;
+    hipLaunchKernelGGL(k_fc1_swiglu, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, a_q, a_scale, M, W1, w1s,
+                       y, y_amax, mt, nt);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_rows(const uint16_t* y, int64_t M, float* y_scale_inout, uint8_t* y_q,
+                             hipStream_t stream) {
+    hipLaunchKernelGGL(k_quant_rows, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, y, M, y_scale_inout, y_q);
+    return hipGetLastError();
+}
+
+hipError_t launch_fc2_gated(const uint8_t* y_q, const float* y_scale, int64_t M, const uint8_t* W2,
+                            const float* w2s, const uint16_t* gate, int64_t gate_rows, int64_t gate_ld,
+                            const int64_t* idx, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
+    const int mt = (int)((M + kBM - 1) / kBM);
+    const int nt = kHidden / kBN;
+    hipLaunchKernelGGL(k_fc2_gated, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, y_q, y_scale, M, W2, w2s,
+                       gate, gate_rows, gate_ld, idx, residual, out, mt, nt);
+    return hipGetLastError();
+}
+
+}  // namespace dit

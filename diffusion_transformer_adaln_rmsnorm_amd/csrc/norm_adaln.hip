@@ -1,0 +1,176 @@
+// Row RMSNorm + indexed AdaLN kernels (launch 1 of the bf16 pre-attention stage, kernel A of
+// the fp8 MLP block).
+//
+// FlashInfer "minimax_h3_mlp_fp8_sm120", per-row formula block (its first three lines and the
+// per-token activation scale), applied to the pre-attention stage as the
+// "minimax_h3_bf16_pre_attention" description orders it (norm, AdaLN, then the workspace the
+// QKV GEMM streams).  The adaln_index entry of that page fixes the guard: any int64 outside
+// [0, rows) zeroes the row and the tables are never addressed with it.
+//
+// Mapping: one 64-lane wavefront per row, four rows per 256-thread workgroup.  A 5376-wide
+// row is 672 chunks of 8 bf16 (16 bytes); lane l owns chunks l, l+64, ... (11 for lanes
+// 0..31, 10 for lanes 32..63), so every load and store is a coalesced 16-byte access and the
+// row stays in registers between the sum of squares and the modulation.  HBM-bound: per row
+// it reads x (10.5 KiB) and writes the workspace (10.5 KiB, or 5.25 KiB of e4m3 codes); the
+// norm weight and the few table rows stay in L2.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace dit {
+
+namespace {
+
+constexpr int kChunks = kHidden / 8;          // 672
+constexpr int kMaxPerLane = (kChunks + 63) / 64;  // 11
+
+__device__ __forceinline__ bool chunk_ok(int j, int lane) { return j * 64 + lane < kChunks; }
+
+// Loads the row into registers and returns r = 1 / sqrt(mean(x^2) + eps) (FP32 sum).
+__device__ __forceinline__ float load_row_rms(const uint16_t* xr, int lane, float eps,
+                                              u32x4 (&xv)[kMaxPerLane]) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (chunk_ok(j, lane)) {
+            xv[j] = ld16(xr + (j * 64 + lane) * 8);
+            float f[8];
+            unpack8(xv[j], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+        }
+    }
+    ss = wave_sum(ss);
+    return 1.0f / sqrtf(ss / (float)kHidden + eps);
+}
+
+// a = bf16(shift + n * bf16(1 + scale)),  n = bf16(x * r * w), for one 8-wide chunk.
+// r is the FP32 reciprocal root; each bf16(...) is one rounding of a double value (the
+// products of bf16 values and the sums below are exact or nearly so in double).
+__device__ __forceinline__ void modulate_chunk(const u32x4& xv, const u32x4& wv, const u32x4& scv,
+                                               const u32x4& shv, float r, float (&a)[8]) {
+    float x[8], w[8], sc[8], sh[8];
+    unpack8(xv, x);
+    unpack8(wv, w);
+    unpack8(scv, sc);
+    unpack8(shv, sh);
+    const double rd = (double)r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const double n = (double)rbf_d((double)x[e] * rd * (double)w[e]);
+        const double s1 = (double)rbf_d(1.0 + (double)sc[e]);
+        a[e] = rbf_d((double)sh[e] + n * s1);
+    }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void k_norm_adaln_bf16(const uint16_t* __restrict__ x, int64_t M,
+                                                         const uint16_t* __restrict__ xw,
+                                                         const uint16_t* __restrict__ scale, int64_t ld_scale,
+                                                         const uint16_t* __restrict__ shift, int64_t ld_shift,
+                                                         int64_t rows, const int64_t* __restrict__ idx,
+                                                         float eps, uint16_t* __restrict__ ws) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    uint16_t* wr = ws + m * kHidden;
+    const int64_t i = idx[m];
+    if (!(i >= 0 && i < rows)) {               // full-width int64 guard
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < kMaxPerLane; ++j)
+            if (chunk_ok(j, lane)) st16(wr + (j * 64 + lane) * 8, z);
+        return;
+    }
+    u32x4 xv[kMaxPerLane];
+    const float r = load_row_rms(x + m * kHidden, lane, eps, xv);
+    const uint16_t* scr = scale + i * ld_scale;
+    const uint16_t* shr = shift + i * ld_shift;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (!chunk_ok(j, lane)) continue;
+        const int c = (j * 64 + lane) * 8;
+        float a[8];
+        modulate_chunk(xv[j], ld16(xw + c), ld16(scr + c), ld16(shr + c), r, a);
+        st16(wr + c, pack8(a));
+    }
+}
+
+// MLP kernel A: the same row steps, then s_a = RN(amax|a| / 448) and a_q = e4m3(a / s_a).
+// Also clears y_amax[m], the per-row |y| maximum that the FC1 epilogue accumulates.
+__global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restrict__ x, int64_t M,
+                                                         const uint16_t* __restrict__ xw,
+                                                         const uint16_t* __restrict__ scale, int64_t ld_scale,
+                                                         const uint16_t* __restrict__ shift, int64_t ld_shift,
+                                                         int64_t rows, const int64_t* __restrict__ idx,
+                                                         float eps, uint8_t* __restrict__ a_q,
+                                                         float* __restrict__ a_scale, float* __restrict__ y_amax) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    uint8_t* qr = a_q + m * kHidden;
+    const int64_t i = idx[m];
+    if (lane == 0) y_amax[m] = 0.f;
+    if (!(i >= 0 && i < rows)) {
+        const uint2 z = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < kMaxPerLane; ++j)
+            if (chunk_ok(j, lane)) *reinterpret_cast<uint2*>(qr + (j * 64 + lane) * 8) = z;
+        if (lane == 0) a_scale[m] = 0.f;
+        return;
+    }
+    u32x4 xv[kMaxPerLane];
+    const float r = load_row_rms(x + m * kHidden, lane, eps, xv);
+    const uint16_t* scr = scale + i * ld_scale;
+    const uint16_t* shr = shift + i * ld_shift;
+    u32x4 av[kMaxPerLane];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (!chunk_ok(j, lane)) continue;
+        const int c = (j * 64 + lane) * 8;
+        float a[8];
+        modulate_chunk(xv[j], ld16(xw + c), ld16(scr + c), ld16(shr + c), r, a);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(a[e]));
+        av[j] = pack8(a);
+    }
+    amax = wave_max(amax);
+    const float s = amax / 448.0f;             // IEEE division: RN(amax / 448)
+    if (lane == 0) a_scale[m] = s;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (!chunk_ok(j, lane)) continue;
+        float a[8];
+        unpack8(av[j], a);
+        uint2 q;
+        if (s == 0.f) {
+            q = make_uint2(0u, 0u);
+        } else {
+            q.x = f2e4m3x2(a[0] / s, a[1] / s) | (f2e4m3x2(a[2] / s, a[3] / s) << 16);
+            q.y = f2e4m3x2(a[4] / s, a[5] / s) | (f2e4m3x2(a[6] / s, a[7] / s) << 16);
+        }
+        *reinterpret_cast<uint2*>(qr + (j * 64 + lane) * 8) = q;
+    }
+}
+
+hipError_t launch_norm_adaln_bf16(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,
+                                  int64_t ld_scale, const uint16_t* shift, int64_t ld_shift, int64_t rows,
+                                  const int64_t* idx, float eps, uint16_t* ws, hipStream_t stream) {
+    const int64_t blocks = (M + 3) / 4;
+    hipLaunchKernelGGL(k_norm_adaln_bf16, dim3((unsigned)blocks), dim3(256), 0, stream, x, M, xw, scale, ld_scale,
+                       shift, ld_shift, rows, idx, eps, ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_adaln_fp8q(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,
+                                  int64_t ld_scale, const uint16_t* shift, int64_t ld_shift, int64_t rows,
+                                  const int64_t* idx, float eps, uint8_t* a_q, float* a_scale, float* y_amax,
+                                  hipStream_t stream) {
+    const int64_t blocks = (M + 3) / 4;
+    hipLaunchKernelGGL(k_norm_adaln_fp8q, dim3((unsigned)blocks), dim3(256), 0, stream, x, M, xw, scale, ld_scale,
+                       shift, ld_shift, rows, idx, eps, a_q, a_scale, y_amax);
+    return hipGetLastError();
+}
+
+}  // namespace dit

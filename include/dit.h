@@ -1,0 +1,194 @@
+/*
+ * dit.h - C ABI of the MI355X (gfx950) MiniMax-H3 AdaLN-modulated projection stages.
+ *
+ * Three operations, each following the tensor contract of one FlashInfer diffusion_ops page:
+ *   dit_pre_attn_bf16       "minimax_h3_bf16_pre_attention" (description, Parameters, Notes)
+ *   dit_out_proj_gated_bf16 "minimax_h3_nvfp4_out_proj" gated-residual epilogue, bf16 operands
+ *   dit_mlp_fp8             "minimax_h3_mlp_fp8_sm120" (per-row formula block, Parameters)
+ *
+ * Conventions shared by every entry point:
+ *  - Every tensor pointer is caller-owned DEVICE memory on the current HIP device.  The
+ *    library never allocates, frees, copies to or from the host, or synchronises.
+ *  - bf16 tensors are passed as raw 16-bit patterns (void*); e4m3 tensors as uint8 codes of
+ *    OCP float8_e4m3fn; indices as int64 or int32 as stated.  All matrices are row-major and
+ *    contiguous except the AdaLN/gate tables, which are dit_bf16_table views.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *    returns immediately.  Results are ready when the stream reaches them.
+ *  - Host-side contract checks run before anything is launched; a failed check returns its
+ *    status and launches nothing.  Malformed index or position VALUES are not errors: they
+ *    are guarded on the device (zero rows, zero gates, clamped positions) as the pages state.
+ *  - Calls that share output or workspace buffers must not overlap in time.
+ *  - Launch failures reported by the HIP runtime return DIT_ERR_LAUNCH.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIT_HIDDEN 5376       /* model width */
+#define DIT_HEADS 56          /* attention heads */
+#define DIT_HEAD_DIM 128      /* per-head dimension */
+#define DIT_QKV_ROWS 21504    /* 3 * 56 * 128 */
+#define DIT_ATTN_WIDTH 7168   /* 56 * 128 */
+#define DIT_ROPE_COLS 96      /* 48 cos + 48 sin per cache row */
+#define DIT_INTER 14336       /* MLP intermediate width */
+#define DIT_FC1_ROWS 28672    /* gate | up */
+#define DIT_MLP_MAX_M 149796  /* row limit of the fp8 MLP page */
+
+typedef enum {
+    DIT_OK = 0,
+    DIT_ERR_NULL = 1,        /* a required pointer is NULL */
+    DIT_ERR_SHAPE = 2,       /* a size is out of range (M, rows, S, S < M with identity positions) */
+    DIT_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned (8 for int64 vectors, 4 for int32/f32) */
+    DIT_ERR_STRIDE = 4,      /* table row stride < 5376 or not a multiple of 8 elements, or mismatched */
+    DIT_ERR_UNSUPPORTED = 5, /* a valid argument this build does not implement (ulysses_degree 2/4/8) */
+    DIT_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
+    DIT_ERR_VALUE = 7        /* a scalar is invalid (eps <= 0 or not finite, ulysses_degree not 1/2/4/8) */
+} dit_status;
+
+/*
+ * A bf16 [rows, 5376] table view with unit column stride, as the pre-attention page's
+ * adaln_scale/adaln_shift entries allow: row r starts at ptr + r * row_stride ELEMENTS.
+ * row_stride >= 5376 and a multiple of 8; ptr 16-byte aligned.  A column chunk of a wider
+ * [rows, 6 * 5376] modulation matrix is passed as-is (ptr = chunk start, row_stride = 32256).
+ */
+typedef struct {
+    const void* ptr;
+    int64_t rows;
+    int64_t row_stride;
+} dit_bf16_table;
+
+/* Human-readable name of a status code (static string). */
+const char* dit_status_string(int status);
+
+/* ABI version of this library (major * 100 + minor). */
+int dit_abi_version(void);
+
+/*
+ * BF16 pre-attention stage ("minimax_h3_bf16_pre_attention": description and Parameters).
+ *
+ * For each row m of x [M, 5376]:
+ *   i = adaln_index[m]; if i is outside [0, rows) the workspace row is all +0 (and so is the
+ *   output row), without reading the tables;
+ *   n = bf16(x[m] * rsqrt(mean(x[m]^2) + eps) * x_norm_weight)       (FP32 sum of squares)
+ *   a = bf16(adaln_shift[i] + n * bf16(1 + adaln_scale[i]))  -> workspace[m, :]
+ *   qkv = bf16(a @ qkv_weight^T)                       (qkv_weight [21504, 5376], rows in
+ *                                                       [q_all | k_all | v_all] x 56 x 128)
+ *   per q and k head: u = bf16(v * rsqrt(mean(v^2) + qk_eps) * {q,k}_norm_weight)
+ *   p = rope_positions ? clamp(rope_positions[m], 0, S-1) : m
+ *   dims j < 48: o_j = bf16(u_j c_j - u_{j+48} s_j), o_{j+48} = bf16(u_{j+48} c_j + u_j s_j)
+ *   with c_j = rope_cos_sin[p, j], s_j = rope_cos_sin[p, 48 + j]; dims [96, 128) pass through
+ *   v heads: bf16(acc) only
+ *   out[0, m, h, kind, :] = o   (kind 0 = q, 1 = k, 2 = v)
+ *
+ * Arguments:
+ *   x              bf16 [M, 5376], contiguous, 16-B aligned
+ *   M              rows; 0 is a no-op returning DIT_OK
+ *   x_norm_weight  bf16 [5376]
+ *   adaln_scale, adaln_shift  tables with equal rows (>= 1)
+ *   adaln_index    int64 [M]; any value is allowed (see the guard above)
+ *   qkv_weight     bf16 [21504, 5376]
+ *   q_norm_weight, k_norm_weight  bf16 [128]
+ *   rope_cos_sin   bf16 [S, 96], S >= 1
+ *   rope_positions int64 [M] or NULL for the identity (then S >= M is required)
+ *   ulysses_degree destination count P; only 1 is implemented (2, 4, 8 -> DIT_ERR_UNSUPPORTED)
+ *   eps, qk_eps    positive finite RMSNorm epsilons (the Python binding maps qk_eps=None to eps)
+ *   workspace      bf16 [M, 5376] scratch, overwritten with a
+ *   out            bf16 [P, M, 56/P, 3, 128]; must not overlap any input
+ *   stream         hipStream_t
+ * Two kernels are enqueued: the row norm/AdaLN kernel and the QKV GEMM with the fused
+ * Q/K-norm, RoPE and pack epilogue.
+ */
+dit_status dit_pre_attn_bf16(const void* x, int64_t M, const void* x_norm_weight,
+                             dit_bf16_table adaln_scale, dit_bf16_table adaln_shift,
+                             const int64_t* adaln_index, const void* qkv_weight,
+                             const void* q_norm_weight, const void* k_norm_weight,
+                             const void* rope_cos_sin, int64_t S, const int64_t* rope_positions,
+                             int ulysses_degree, float eps, float qk_eps, void* workspace, void* out,
+                             void* stream);
+
+/*
+ * The two launches of dit_pre_attn_bf16, callable one at a time (same kernels, same
+ * arguments and checks).  dit_norm_adaln_bf16 writes the modulated activation a into
+ * workspace [M, 5376] (launch 1: input RMSNorm + indexed AdaLN + guard);
+ * dit_qkv_rope_pack_bf16 reads such a workspace and writes out (launch 2: QKV GEMM with the
+ * Q/K RMSNorm, RoPE and pack epilogue).  dit_pre_attn_bf16 is exactly the first followed by
+ * the second on one stream.  For engines that keep the modulated activation, and for timing
+ * each launch.
+ */
+dit_status dit_norm_adaln_bf16(const void* x, int64_t M, const void* x_norm_weight,
+                               dit_bf16_table adaln_scale, dit_bf16_table adaln_shift,
+                               const int64_t* adaln_index, float eps, void* workspace, void* stream);
+
+dit_status dit_qkv_rope_pack_bf16(const void* workspace, int64_t M, const void* qkv_weight,
+                                  const void* q_norm_weight, const void* k_norm_weight,
+                                  const void* rope_cos_sin, int64_t S, const int64_t* rope_positions,
+                                  int ulysses_degree, float qk_eps, void* out, void* stream);
+
+/*
+ * BF16 attention output projection with the fused gated residual (the epilogue of
+ * "minimax_h3_nvfp4_out_proj", with bf16 operands instead of NVFP4 ones):
+ *   o = bf16(attn_out[m] @ o_weight^T)
+ *   g = gate[gate_index[m]] if 0 <= gate_index[m] < gate.rows else 0
+ *   out[m] = bf16(residual[m] + bf16(g * o))
+ * Arguments:
+ *   attn_out   bf16 [M, 7168];  M = 0 is a no-op
+ *   o_weight   bf16 [5376, 7168]
+ *   gate       table view [rows, 5376] (the page's gate_msa rows, rows = 9 there)
+ *   gate_index int32 [M], any value
+ *   residual   bf16 [M, 5376]
+ *   out        bf16 [M, 5376]; may be the same pointer as residual (each element is read
+ *              before it is written); must not overlap attn_out
+ * One kernel is enqueued.
+ */
+dit_status dit_out_proj_gated_bf16(const void* attn_out, int64_t M, const void* o_weight,
+                                   dit_bf16_table gate, const int32_t* gate_index,
+                                   const void* residual, void* out, void* stream);
+
+/*
+ * FP8 (W8A8) MLP block ("minimax_h3_mlp_fp8_sm120", per-row formula block):
+ *   n, a  as in dit_pre_attn_bf16 (a = 0 for rows whose index is outside [0, rows))
+ *   s_a = RN(amax|a| / 448)  (fp32),  a_q = e4m3(a / s_a)  (RNE, saturating; amax 0 -> 0)
+ *   h = bf16((a_q @ fc1^T) * s_a * fc1_scale)       FP32 accumulation, [M, 28672]
+ *   y = bf16(bf16(silu(h[:, :14336])) * h[:, 14336:])
+ *   s_y = RN(amax|y| / 448),  y_q = e4m3(y / s_y)
+ *   o = bf16((y_q @ fc2^T) * s_y * fc2_scale)
+ *   out = bf16(residual + bf16(gate[i] * o)),  gate 0 for guarded rows
+ * Arguments:
+ *   x            bf16 [M, 5376], 1 <= M <= 149796
+ *   x_norm_weight bf16 [5376]
+ *   adaln_scale, adaln_shift, gate  tables with equal rows; scale and shift share row_stride
+ *   adaln_index  int64 [M]
+ *   residual     bf16 [M, 5376]
+ *   fc1_q        e4m3 [28672, 5376], rows [0,14336) gate and [14336,28672) up; fc1_scale f32 [28672]
+ *   fc2_q        e4m3 [5376, 14336];  fc2_scale f32 [5376]
+ *   eps          positive finite
+ *   ws_a_q e4m3 [M,5376], ws_a_scale f32 [M], ws_y bf16 [M,14336], ws_y_q e4m3 [M,14336],
+ *   ws_y_scale f32 [M]: caller-owned workspaces, all overwritten with the values above
+ *   ws_flags     may be NULL; see dit_mlp_fp8_flags_elems
+ *   out          bf16 [M, 5376]; may be residual or x, must not overlap any workspace
+ * Four kernels are enqueued (norm/AdaLN/quant, FC1+SwiGLU, y quant, FC2+gated residual).
+ */
+dit_status dit_mlp_fp8(const void* x, int64_t M, const void* x_norm_weight,
+                       dit_bf16_table adaln_scale, dit_bf16_table adaln_shift, dit_bf16_table gate,
+                       const int64_t* adaln_index, const void* residual, const uint8_t* fc1_q,
+                       const float* fc1_scale, const uint8_t* fc2_q, const float* fc2_scale,
+                       float eps, uint8_t* ws_a_q, float* ws_a_scale, void* ws_y, uint8_t* ws_y_q,
+                       float* ws_y_scale, int32_t* ws_flags, void* out, void* stream);
+
+/*
+ * Number of int32 tile-ready flags dit_mlp_fp8 needs for M rows (the counterpart of the
+ * page's minimax_h3_mlp_fc2_flags_sm120).  This implementation orders FC1, the y quant and
+ * FC2 by stream order and needs none: it returns 0 for every M, and ws_flags is ignored.
+ */
+int64_t dit_mlp_fp8_flags_elems(int64_t M);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DIT_H */

@@ -269,3 +269,73 @@ def config(cid: int, M: int | None = None, **kw):
         M = 32760 if M is None else M
         return "mlp", mlp_inputs(M, seed=seed, **kw)
     raise ValueError(f"unknown config {cid}")
+
+
+# ---------------------------------------------------------------- device upload (no arithmetic)
+
+def _t_bf16(a, device):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+
+
+def _t_e4m3(a, device):
+    return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).view(torch.float8_e4m3fn).to(device)
+
+
+def _t_table(t: Table, device, cache):
+    key = id(t.base)
+    if key not in cache:
+        cache[key] = _t_bf16(t.base, device)
+    base = cache[key]
+    return base.as_strided((t.rows, t.cols), (t.row_stride, 1), t.offset)
+
+
+def to_torch(kind: str, d: dict, device="cuda"):
+    """The arrays of a synthetic input dict as torch tensors on `device` (bit copies)."""
+    cache = {}
+    M = d["M"]
+    o = {"M": M}
+    if kind == "pre_attn":
+        o["x"] = _t_bf16(d["x"].reshape(M, HIDDEN), device)
+        o["x_norm_weight"] = _t_bf16(d["x_norm_weight"], device)
+        o["adaln_scale"] = _t_table(d["adaln_scale"], device, cache)
+        o["adaln_shift"] = _t_table(d["adaln_shift"], device, cache)
+        o["adaln_index"] = torch.from_numpy(np.ascontiguousarray(d["adaln_index"], np.int64)).to(device)
+        o["qkv_weight"] = _t_bf16(d["qkv_weight"].reshape(QKV_ROWS, HIDDEN), device)
+        o["q_norm_weight"] = _t_bf16(d["q_norm_weight"], device)
+        o["k_norm_weight"] = _t_bf16(d["k_norm_weight"], device)
+        o["rope_cos_sin"] = _t_bf16(d["rope_cos_sin"].reshape(-1, ROT_DIMS), device)
+        pos = d.get("rope_positions")
+        o["rope_positions"] = None if pos is None else torch.from_numpy(np.ascontiguousarray(pos, np.int64)).to(device)
+        o["eps"] = d["eps"]
+        o["qk_eps"] = d.get("qk_eps")
+    elif kind == "out_proj":
+        o["attn_out"] = _t_bf16(d["attn_out"].reshape(M, ATTN_WIDTH), device)
+        o["o_weight"] = _t_bf16(d["o_weight"].reshape(HIDDEN, ATTN_WIDTH), device)
+        o["gate"] = _t_table(d["gate"], device, cache)
+        o["gate_index"] = torch.from_numpy(np.ascontiguousarray(d["gate_index"], np.int32)).to(device)
+        o["residual"] = _t_bf16(d["residual"].reshape(M, HIDDEN), device)
+    elif kind == "mlp":
+        o["x"] = _t_bf16(d["x"].reshape(M, HIDDEN), device)
+        o["x_norm_weight"] = _t_bf16(d["x_norm_weight"], device)
+        o["adaln_scale"] = _t_table(d["adaln_scale"], device, cache)
+        o["adaln_shift"] = _t_table(d["adaln_shift"], device, cache)
+        o["gate"] = _t_table(d["gate"], device, cache)
+        o["adaln_index"] = torch.from_numpy(np.ascontiguousarray(d["adaln_index"], np.int64)).to(device)
+        o["residual"] = _t_bf16(d["residual"].reshape(M, HIDDEN), device)
+        o["fc1_weight_q"] = _t_e4m3(d["fc1_q"], device)
+        o["fc1_weight_scale"] = torch.from_numpy(np.ascontiguousarray(d["fc1_scale"], np.float32)).to(device)
+        o["fc2_weight_q"] = _t_e4m3(d["fc2_q"], device)
+        o["fc2_weight_scale"] = torch.from_numpy(np.ascontiguousarray(d["fc2_scale"], np.float32)).to(device)
+        o["eps"] = d["eps"]
+    else:
+        raise ValueError(kind)
+    return o
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    """Raw bit patterns of a bf16 (uint16) or e4m3 (uint8) tensor, copied to the host."""
+    if t.dtype == torch.bfloat16:
+        return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.detach().view(torch.uint8).cpu().numpy()
+    return t.detach().cpu().numpy()

@@ -68,3 +68,29 @@ def bf16_tolerance_ok(got_bits, ref_bits, max_rel_l2=2e-3, elem=1e-2):
     rel_l2 = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
     ok_elem = np.all(err <= elem * (1.0 + np.abs(r)))
     return bool(rel_l2 <= max_rel_l2 and ok_elem), float(rel_l2), float(err.max() if err.size else 0.0)
+
+
+def ulp_bf16(v):
+    """Spacing of the bf16 grid at |v| (2^(e-7) for |v| in [2^e, 2^(e+1)); subnormal floor)."""
+    v = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.maximum(v, 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def workspace_ok(got_bits, ref_bits, shift_vals, max_mismatch=1e-3):
+    """The AdaLN workspace bar: 1 bf16 ulp at each rounding point of a = bf16(shift + n*s1).
+
+    The GPU's n may sit one bf16 ulp from the oracle's (its sum of squares is FP32, as the
+    pages fix); that step reaches a as |s1| * ulp(n) <= 2 ulp(a - shift), which dwarfs ulp(a)
+    when shift cancels n*s1.  So each element must satisfy
+        |a_gpu - a_ref| <= ulp(a_ref) + 2 ulp(a_ref - shift),
+    and at most `max_mismatch` of the elements may differ at all.
+    Returns (ok, mismatch fraction, worst ratio err / bound).
+    """
+    g = bf16_val(got_bits)
+    r = bf16_val(ref_bits)
+    err = np.abs(g - r)
+    bound = ulp_bf16(r) + 2.0 * ulp_bf16(r - shift_vals)
+    ratio = float((err / bound).max()) if err.size else 0.0
+    mism = float(np.mean(g != r)) if err.size else 0.0
+    return bool(np.all(err <= bound) and mism <= max_mismatch), mism, ratio

@@ -1,0 +1,359 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the same seeded
+inputs.
+
+Bars (bf16 pre-attention, out-projection and fp8 MLP):
+  - the AdaLN workspace within 1 bf16 ulp at each rounding point of a = bf16(shift + n*s1):
+    |a_gpu - a_ref| <= ulp(a_ref) + 2 ulp(a_ref - shift), at most 0.1% of elements differing
+    (n's own rounding may land on the other neighbour; shift can cancel n*s1);
+  - e4m3 codes within one code step, per-token activation scales within 1 bf16 ulp; the y
+    quantisation is checked at its own step (s_y = RN(amax|y_gpu|/448) exactly, y_q within one
+    code step of the library e4m3 conversion of y_gpu/s_y) and s_y within 2^-5 of the oracle's;
+  - every bf16 output: relative L2 error <= 2e-3 and |err| <= 1e-2 * (1 + |ref|) per element;
+  - the bf16 intermediate y (three roundings after a GEMM): relative L2 <= 2e-3 and
+    |err| <= 2^-5 |ref| + 1e-2;
+  - rows with a guarded index: workspace/codes exactly zero, outputs zero (pre-attention) or
+    equal to the residual (out-projection, MLP).
+At the full workload sizes the oracle runs on a sampled row set (rows are independent, so
+this is exact parity on those rows): the first 64 rows, the whole last 256-row tile, every
+guarded row, every clamped-position row and 256 seeded random rows.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import (bf16_tolerance_ok, bf16_val, ordered_e4m3, torch_e4m3, ulp_bf16, ulp_diff_bf16,
+                           workspace_ok)
+
+pytestmark = pytest.mark.gpu
+
+H = synth.HIDDEN
+INT64_MIN, INT64_MAX = -(1 << 63), (1 << 63) - 1
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import diffusion_transformer_adaln_rmsnorm_amd as dit
+    dit.load_library()
+
+
+def _say(msg):
+    print(f"[parity] {msg}", file=sys.stderr, flush=True)
+
+
+def _dit():
+    import diffusion_transformer_adaln_rmsnorm_amd as dit
+    return dit
+
+
+def sample_rows(M, d=None, n_random=256, seed=0):
+    rows = set(range(min(M, 64)))
+    rows |= set(range(((M - 1) // 256) * 256, M))
+    if d is not None:
+        idx = d.get("adaln_index")
+        if idx is not None:
+            rows |= set(np.nonzero((idx < 0) | (idx >= d.get("rows", 1 << 62)))[0].tolist())
+        gi = d.get("gate_index")
+        if gi is not None:
+            rows |= set(np.nonzero((gi < 0) | (gi >= d["gate"].rows))[0][:128].tolist())
+        pos = d.get("rope_positions")
+        if pos is not None:
+            rows |= set(np.nonzero((pos < 0) | (pos >= d["S"]))[0].tolist())
+    g = np.random.Generator(np.random.PCG64(seed))
+    rows |= set(g.choice(M, size=min(n_random, M), replace=False).tolist())
+    return np.array(sorted(rows), np.int64)
+
+
+# ---------------------------------------------------------------- runners
+
+def run_pre(d, out=None, workspace=None):
+    t = synth.to_torch("pre_attn", d)
+    M = d["M"]
+    if out is None:
+        out = torch.empty((1, M, 56, 3, 128), dtype=torch.bfloat16, device="cuda")
+    _dit().dit_pre_attn_bf16(t["x"], t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], t["adaln_index"],
+                             t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
+                             ulysses_degree=1, out=out, eps=t["eps"], qk_eps=t["qk_eps"],
+                             rope_positions=t["rope_positions"], workspace=workspace)
+    torch.cuda.synchronize()
+    return t, out
+
+
+def check_pre(d, ws_gpu, out_gpu, rows=None):
+    M = d["M"]
+    rows = np.arange(M) if rows is None else rows
+    ws_ref, out_ref = oracle.pre_attn(d, rows_sel=rows)
+    ws = synth.bits(ws_gpu)[rows]
+    out = synth.bits(out_gpu).reshape(M, 56, 3, 128)[rows]
+    idx = d["adaln_index"][rows]
+    bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
+    shift = bf16_val(d["adaln_shift"].dense())[np.where(bad, 0, idx)]
+    wok, wmis, wratio = workspace_ok(ws[~bad], ws_ref[~bad], shift[~bad])
+    du = ulp_diff_bf16(ws, ws_ref)
+    assert wok, f"workspace: mismatch {wmis:.2e}, worst err/bound {wratio:.2f}"
+    assert np.all(ws[bad] == 0), "guarded workspace rows must be +0"
+    assert np.all(bf16_val(out[bad]) == 0.0), "guarded output rows must be zero"
+    ok, rel, mx = bf16_tolerance_ok(out, out_ref)
+    _say(f"pre_attn M={M} rows={rows.size} ws max ulp={du.max()} ws mismatch={wmis:.2e} (err/bound {wratio:.2f}) "
+         f"out relL2={rel:.2e} max|err|={mx:.3e} guarded={bad.sum()}")
+    assert ok, (rel, mx)
+    return ws, out
+
+
+def run_out_proj(d, alias=False):
+    t = synth.to_torch("out_proj", d)
+    out = t["residual"] if alias else None
+    out = _dit().dit_out_proj_gated_bf16(t["attn_out"], t["o_weight"], t["gate"], t["gate_index"], t["residual"],
+                                         out=out)
+    torch.cuda.synchronize()
+    return out
+
+
+def check_out_proj(d, out_gpu, rows=None):
+    M = d["M"]
+    rows = np.arange(M) if rows is None else rows
+    ref = oracle.out_proj(d, rows_sel=rows)
+    got = synth.bits(out_gpu)[rows]
+    gi = d["gate_index"][rows]
+    bad = (gi < 0) | (gi >= d["gate"].rows)
+    assert np.array_equal(got[bad], d["residual"].reshape(M, H)[rows][bad]), "guarded rows must equal residual"
+    ok, rel, mx = bf16_tolerance_ok(got, ref)
+    _say(f"out_proj M={M} rows={rows.size} relL2={rel:.2e} max|err|={mx:.3e} mismatch={np.mean(got != ref):.2e}")
+    assert ok, (rel, mx)
+
+
+def run_mlp(d, alias=None):
+    t = synth.to_torch("mlp", d)
+    M = d["M"]
+    ws = {"workspace_a_q": torch.empty((M, H), dtype=torch.float8_e4m3fn, device="cuda"),
+          "workspace_a_scale": torch.empty((M,), dtype=torch.float32, device="cuda"),
+          "workspace_y": torch.empty((M, synth.INTER), dtype=torch.bfloat16, device="cuda"),
+          "workspace_y_q": torch.empty((M, synth.INTER), dtype=torch.float8_e4m3fn, device="cuda"),
+          "workspace_y_scale": torch.empty((M,), dtype=torch.float32, device="cuda")}
+    out = None if alias is None else t[alias]
+    out = _dit().dit_mlp_fp8(t["x"], t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], t["adaln_index"],
+                             t["gate"], t["residual"], t["fc1_weight_q"], t["fc1_weight_scale"], t["fc2_weight_q"],
+                             t["fc2_weight_scale"], out=out, eps=t["eps"], **ws)
+    torch.cuda.synchronize()
+    return out, ws
+
+
+def check_mlp(d, out_gpu, ws, rows=None):
+    M = d["M"]
+    rows = np.arange(M) if rows is None else rows
+    ref = oracle.mlp(d, rows_sel=rows)
+    a_q = synth.bits(ws["workspace_a_q"])[rows]
+    a_s = ws["workspace_a_scale"].cpu().numpy()[rows]
+    y = synth.bits(ws["workspace_y"])[rows]
+    y_q = synth.bits(ws["workspace_y_q"])[rows]
+    y_s = ws["workspace_y_scale"].cpu().numpy()[rows]
+    out = synth.bits(out_gpu)[rows]
+    da = np.abs(ordered_e4m3(a_q) - ordered_e4m3(ref["a_q"]))
+    assert da.max() <= 1, f"a_q off by {da.max()} code steps"
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rs = np.where(ref["a_scale"] > 0, np.abs(a_s / ref["a_scale"] - 1), np.abs(a_s))
+        ry = np.where(ref["y_scale"] > 0, np.abs(y_s / ref["y_scale"] - 1), np.abs(y_s))
+    assert np.all(np.abs(a_s - ref["a_scale"]) <= ulp_bf16(ref["a_scale"])), f"a_scale rel err {rs.max()}"
+    assert ry.max() <= 2 ** -5, f"y_scale rel err {ry.max()}"
+    yg, yr = bf16_val(y), bf16_val(ref["y"])
+    rely = np.linalg.norm(yg - yr) / max(np.linalg.norm(yr), 1e-30)
+    mxy = float(np.max(np.abs(yg - yr)))
+    assert rely <= 2e-3 and np.all(np.abs(yg - yr) <= 2.0 ** -5 * np.abs(yr) + 1e-2), ("y", rely, mxy)
+    # the y quantisation step itself, on the GPU's own y
+    amax = np.max(np.abs(yg), axis=1).astype(np.float32)
+    assert np.array_equal(y_s, (amax / np.float32(448.0)).astype(np.float32)), "s_y != RN(amax|y|/448)"
+    nz = y_s > 0
+    q_lib = np.zeros_like(y_q)
+    q_lib[nz] = torch_e4m3((yg[nz].astype(np.float32) / y_s[nz, None]).astype(np.float32))
+    dql = np.abs(ordered_e4m3(y_q) - ordered_e4m3(q_lib))
+    assert dql.max() <= 1, f"y_q off by {dql.max()} code steps from e4m3(y/s_y)"
+    dq = np.abs(ordered_e4m3(y_q) - ordered_e4m3(ref["y_q"]))
+    idx = d["adaln_index"][rows]
+    bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
+    assert np.all(a_q[bad] == 0) and np.all(a_s[bad] == 0) and np.all(y_s[bad] == 0)
+    res = d["residual"].reshape(M, H)[rows]
+    assert np.array_equal(out[bad], res[bad]), "guarded rows must equal the residual"
+    ok, rel, mx = bf16_tolerance_ok(out, ref["out"])
+    _say(f"mlp M={M} rows={rows.size} a_q mismatch={np.mean(a_q != ref['a_q']):.2e} "
+         f"a_s exact={np.mean(a_s == ref['a_scale']):.3f} y relL2={rely:.2e} y max|err|={mxy:.3e} y_q vs own "
+         f"e4m3 mismatch={np.mean(y_q != q_lib):.2e} y_q vs oracle max step={dq.max()} out relL2={rel:.2e} max|err|={mx:.3e} guarded={bad.sum()}")
+    assert ok, (rel, mx)
+
+
+# ---------------------------------------------------------------- pre-attention
+
+def test_pre_attn_config0_full():
+    _say("config 0: pre_attn M=16 (rows=4 tables, guard -1 and 4)")
+    kind, d = synth.config(0)
+    ws = torch.empty((16, H), dtype=torch.bfloat16, device="cuda")
+    t, out = run_pre(d, workspace=ws)
+    check_pre(d, ws, out)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 255, 256, 257])
+def test_pre_attn_small_M_random_positions(M):
+    _say(f"pre_attn small M={M}, random positions with clamps, rows=2 wide tables")
+    d = synth.pre_attn_inputs(M, seed=100 + M, rows=2, S=64, positions="random", n_bad_positions=min(8, M),
+                              bad_index_frac=0.05, weight=_shared_weight())
+    ws = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    _, out = run_pre(d, workspace=ws)
+    check_pre(d, ws, out)
+
+
+_W = {}
+
+
+def _shared_weight():
+    if "w" not in _W:
+        _W["w"] = synth.to_bf16_bits(synth.normal(1, "qkv_weight", (synth.QKV_ROWS, H), 1 / np.sqrt(H)))
+    return _W["w"]
+
+
+def test_pre_attn_identity_positions_ragged():
+    M = 300
+    _say(f"pre_attn identity positions M={M}")
+    d = synth.pre_attn_inputs(M, seed=7, rows=3, S=M, positions="identity", bad_index_frac=0.02,
+                              bad_index_values=(-1, 3, INT64_MIN, INT64_MAX, 1 << 32), weight=_shared_weight())
+    ws = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    _, out = run_pre(d, workspace=ws)
+    check_pre(d, ws, out)
+
+
+def test_pre_attn_one_hot_pack_bit_exact():
+    # one-hot W: qkv[n] = a[k(n)] exactly, so V heads are bit copies of workspace entries
+    M = 260
+    _say("pre_attn one-hot weight pack check")
+    W = np.zeros((synth.QKV_ROWS, H), np.uint16)
+    n = np.arange(synth.QKV_ROWS)
+    k = (n * 5 + 3) % H
+    W[n, k] = 0x3F80
+    d = synth.pre_attn_inputs(M, seed=8, rows=2, S=M, positions="identity", bad_index_frac=0.0, weight=W)
+    ws = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    _, out = run_pre(d, workspace=ws)
+    wsb = synth.bits(ws)
+    ob = synth.bits(out).reshape(M, 56, 3, 128)
+    v_expect = wsb[:, k[2 * 7168:]].reshape(M, 56, 128)
+    assert np.array_equal(ob[:, :, 2], v_expect)
+    check_pre(d, ws, out)
+
+
+def test_pre_attn_exact_rope_angles():
+    # with (cos, sin) in {(1,0),(0,1),(-1,0),(0,-1)} RoPE is a permutation/negation of u; the
+    # GPU's output must be exactly that transform of its own cos=1, sin=0 output
+    M = 64
+    _say("pre_attn exact RoPE angles")
+    d = synth.pre_attn_inputs(M, seed=9, rows=2, S=M, positions="identity", bad_index_frac=0.0,
+                              weight=_shared_weight())
+    d["rope_cos_sin"] = synth.to_bf16_bits(np.concatenate([np.ones((M, 48)), np.zeros((M, 48))], 1).astype(np.float32))
+    ws = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    _, out_u = run_pre(d, workspace=ws)
+    u = bf16_val(synth.bits(out_u).reshape(M, 56, 3, 128))
+    check_pre(d, ws, out_u)
+    pairs = np.array([[1, 0], [0, 1], [-1, 0], [0, -1]], np.float32)
+    sel = (np.arange(M)[:, None] + np.arange(48)[None, :]) % 4
+    c, s_ = pairs[sel, 0], pairs[sel, 1]
+    d["rope_cos_sin"] = synth.to_bf16_bits(np.concatenate([c, s_], axis=1).astype(np.float32))
+    _, out = run_pre(d, workspace=ws)
+    o = bf16_val(synth.bits(out).reshape(M, 56, 3, 128))
+    for kind in (0, 1):
+        lo, hi = u[:, :, kind, :48], u[:, :, kind, 48:96]
+        cc, ss = c[:, None, :], s_[:, None, :]
+        assert np.array_equal(o[:, :, kind, :48], lo * cc - hi * ss)
+        assert np.array_equal(o[:, :, kind, 48:96], hi * cc + lo * ss)
+        assert np.array_equal(o[:, :, kind, 96:], u[:, :, kind, 96:])
+    assert np.array_equal(o[:, :, 2], u[:, :, 2])
+    check_pre(d, ws, out)
+
+
+def test_pre_attn_config1_sampled():
+    _say("config 1: pre_attn M=4096, S=8192 random positions with 8 clamps, ~0.5% guarded")
+    kind, d = synth.config(1)
+    ws = torch.empty((d["M"], H), dtype=torch.bfloat16, device="cuda")
+    _, out = run_pre(d, workspace=ws)
+    check_pre(d, ws, out, sample_rows(d["M"], d))
+
+
+def test_pre_attn_config2_sampled_and_deterministic():
+    _say("config 2: pre_attn M=32760 identity positions (the measured workload)")
+    kind, d = synth.config(2)
+    ws = torch.empty((d["M"], H), dtype=torch.bfloat16, device="cuda")
+    _, out = run_pre(d, workspace=ws)
+    ws1, out1 = synth.bits(ws), synth.bits(out)
+    _, out2 = run_pre(d, workspace=ws)
+    assert np.array_equal(out1, synth.bits(out2)) and np.array_equal(ws1, synth.bits(ws)), "not deterministic"
+    check_pre(d, ws, out, sample_rows(d["M"], d, n_random=192))
+
+
+# ---------------------------------------------------------------- out-projection
+
+@pytest.mark.parametrize("M", [1, 3, 257])
+def test_out_proj_small_M(M):
+    _say(f"out_proj small M={M}")
+    d = synth.out_proj_inputs(M, seed=200 + M)
+    out = run_out_proj(d)
+    check_out_proj(d, out)
+
+
+def test_out_proj_alias_residual():
+    M = 300
+    _say("out_proj out is residual")
+    d = synth.out_proj_inputs(M, seed=5)
+    out = run_out_proj(d, alias=True)
+    check_out_proj(d, out)
+
+
+def test_out_proj_config3_sampled():
+    _say("config 3: out_proj M=32760")
+    kind, d = synth.config(3)
+    out = run_out_proj(d)
+    o1 = synth.bits(out)
+    out2 = run_out_proj(d)
+    assert np.array_equal(o1, synth.bits(out2)), "not deterministic"
+    check_out_proj(d, out, sample_rows(d["M"], d, n_random=256))
+
+
+# ---------------------------------------------------------------- FP8 MLP
+
+_MW = {}
+
+
+def _mlp_weights():
+    if "w" not in _MW:
+        _MW["w"] = synth.mlp_weights(33)
+    return _MW["w"]
+
+
+@pytest.mark.parametrize("M", [1, 2, 257])
+def test_mlp_small_M(M):
+    _say(f"mlp small M={M}")
+    d = synth.mlp_inputs(M, seed=300 + M, weights=_mlp_weights(), bad_index_frac=0.02,
+                         bad_index_values=(-1, 2, INT64_MIN, INT64_MAX))
+    out, ws = run_mlp(d)
+    check_mlp(d, out, ws)
+
+
+@pytest.mark.parametrize("alias", ["residual", "x"])
+def test_mlp_alias(alias):
+    M = 40
+    _say(f"mlp out is {alias}")
+    d = synth.mlp_inputs(M, seed=400, weights=_mlp_weights(), bad_index_frac=0.05)
+    out, ws = run_mlp(d, alias=alias)
+    check_mlp(d, out, ws)
+
+
+def test_mlp_config4_sampled_and_deterministic():
+    _say("config 4: fp8 MLP M=32760")
+    kind, d = synth.config(4)
+    out, ws = run_mlp(d)
+    o1 = synth.bits(out)
+    y1 = synth.bits(ws["workspace_y_q"])
+    out2, ws2 = run_mlp(d)
+    assert np.array_equal(o1, synth.bits(out2)) and np.array_equal(y1, synth.bits(ws2["workspace_y_q"]))
+    check_mlp(d, out, ws, sample_rows(d["M"], d, n_random=96))
