@@ -60,14 +60,31 @@ def ordered_e4m3(c):
     return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
 
 
-def bf16_tolerance_ok(got_bits, ref_bits, max_rel_l2=2e-3, elem=1e-2):
-    """The acceptance bar for bf16 outputs: relative L2 error and |err| <= elem*(1+|ref|)."""
+def bf16_tolerance_ok(got_bits, ref_bits, max_rel_l2=2e-3, elem=1e-2, mag=None):
+    """The acceptance bar for bf16 outputs: relative L2 error and |err| <= elem*(1+|ref|).
+
+    mag, when given, replaces |ref| as the element's magnitude (same shape as ref)."""
     g = bf16_val(got_bits).ravel()
     r = bf16_val(ref_bits).ravel()
+    m = np.abs(r) if mag is None else np.asarray(mag, np.float64).ravel()
     err = np.abs(g - r)
     rel_l2 = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
-    ok_elem = np.all(err <= elem * (1.0 + np.abs(r)))
+    ok_elem = np.all(err <= elem * (1.0 + m))
     return bool(rel_l2 <= max_rel_l2 and ok_elem), float(rel_l2), float(err.max() if err.size else 0.0)
+
+
+def qkv_magnitude(out_ref_bits):
+    """Per-element magnitude of packed q/k/v outputs [..., 3, 128] for the elementwise bar.
+
+    RoPE rotates each (j, j+48) pair of q and k (j < 48) and preserves the pair's norm, so a
+    rotated element is judged against that norm: a one-ulp difference in a large u_j may land
+    in an output that the rotation made small.  V and the pass-through dims use |ref|."""
+    r = bf16_val(out_ref_bits)
+    mag = np.abs(r).copy()
+    pair = np.hypot(r[..., :2, :48], r[..., :2, 48:96])
+    mag[..., :2, :48] = pair
+    mag[..., :2, 48:96] = pair
+    return mag
 
 
 def ulp_bf16(v):

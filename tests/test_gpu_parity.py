@@ -8,7 +8,10 @@ Bars (bf16 pre-attention, out-projection and fp8 MLP):
   - e4m3 codes within one code step, per-token activation scales within 1 bf16 ulp; the y
     quantisation is checked at its own step (s_y = RN(amax|y_gpu|/448) exactly, y_q within one
     code step of the library e4m3 conversion of y_gpu/s_y) and s_y within 2^-5 of the oracle's;
-  - every bf16 output: relative L2 error <= 2e-3 and |err| <= 1e-2 * (1 + |ref|) per element;
+  - every bf16 output: relative L2 error <= 2e-3 and |err| <= 1e-2 * (1 + |ref|) per element,
+    where for the RoPE-rotated q/k dims |ref| is the norm of the rotated (j, j+48) pair (the
+    rotation preserves it; an FP32-accumulated v may round to the other bf16 neighbour, and
+    the rotation can carry that ulp of a large u into a small output);
   - the bf16 intermediate y (three roundings after a GEMM): relative L2 <= 2e-3 and
     |err| <= 2^-5 |ref| + 1e-2;
   - rows with a guarded index: workspace/codes exactly zero, outputs zero (pre-attention) or
@@ -27,8 +30,8 @@ import torch
 
 import oracle
 import synth
-from tests.helpers import (bf16_tolerance_ok, bf16_val, ordered_e4m3, torch_e4m3, ulp_bf16, ulp_diff_bf16,
-                           workspace_ok)
+from tests.helpers import (bf16_tolerance_ok, bf16_val, ordered_e4m3, qkv_magnitude, torch_e4m3, ulp_bf16,
+                           ulp_diff_bf16, workspace_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -100,7 +103,14 @@ def check_pre(d, ws_gpu, out_gpu, rows=None):
     assert wok, f"workspace: mismatch {wmis:.2e}, worst err/bound {wratio:.2f}"
     assert np.all(ws[bad] == 0), "guarded workspace rows must be +0"
     assert np.all(bf16_val(out[bad]) == 0.0), "guarded output rows must be zero"
-    ok, rel, mx = bf16_tolerance_ok(out, out_ref)
+    mag = qkv_magnitude(out_ref)
+    ok, rel, mx = bf16_tolerance_ok(out, out_ref, mag=mag)
+    err = np.abs(bf16_val(out) - bf16_val(out_ref))
+    worst = np.unravel_index(np.argmax(err / (1.0 + mag)), err.shape)
+    _say(f"  worst element (row, head, kind, dim)={tuple(int(t) for t in worst)} ref={bf16_val(out_ref)[worst]:.5f} "
+         f"got={bf16_val(out)[worst]:.5f} pair-norm={mag[worst]:.4f} |ref|-bound violations="
+         f"{int(np.sum(err > 1e-2 * (1 + np.abs(bf16_val(out_ref)))))} v mismatch="
+         f"{np.mean(out[:, :, 2] != out_ref[:, :, 2]):.2e}")
     _say(f"pre_attn M={M} rows={rows.size} ws max ulp={du.max()} ws mismatch={wmis:.2e} (err/bound {wratio:.2f}) "
          f"out relL2={rel:.2e} max|err|={mx:.3e} guarded={bad.sum()}")
     assert ok, (rel, mx)
