@@ -4,20 +4,26 @@
 // [M, K], weights [N, K]), FP32 accumulation.
 //
 // Workgroup: 256 threads = 4 wavefronts (one per SIMD), output tile 256 x 256, wave tile
-// 128 x 128 held as 4 x 4 blocks of the 32x32 MFMA (256 FP32 accumulators per lane).  K is
-// consumed in tiles of 128 bytes (64 bf16 or 128 e4m3): per K tile every thread fetches
-// eight 16-byte chunks of A and eight of B of the next tile into registers, the waves run
-// the MFMAs on the current LDS stage, then the fetched chunks are written to the other stage
-// (double buffer, 2 x 64 KiB) and one barrier closes the step.  LDS rows are 128 bytes; the 16-byte chunk index is
-// XOR-swizzled with the row so that the MFMA operand reads of 8 consecutive rows hit 8
-// different bank groups.
+// 128 x 128 held as 4 x 4 blocks of the 32x32 MFMA (256 FP32 accumulators per lane, in
+// AGPRs).  K is consumed in stages of 64 bytes per row (32 bf16 or 64 e4m3).  Each stage
+// (A 256 x 64 B + B 256 x 64 B = 32 KiB) is filled straight from global memory into LDS by
+// buffer_load_dwordx4 ... lds (no register staging, no LDS store instructions); four stages
+// rotate in 128 KiB of LDS and the loads run three stages ahead of the MFMAs.
 //
-// bf16: v_mfma_f32_32x32x16_bf16, 4 k-steps per K tile.
-// e4m3: v_mfma_f32_32x32x64_f8f6f4 (both operands OCP e4m3), 2 k-steps per K tile.
+// Per stage (two halves of 16 bf16 MFMAs, or 8 e4m3 MFMAs, per wave):
+//   first half  : MFMAs on fragments already in registers, interleaved with the LDS reads of
+//                 the second half's fragments;
+//   wait for the next stage's loads (vmcnt), barrier;
+//   issue the loads of the stage three ahead into the buffer just released;
+//   second half : MFMAs, interleaved with the LDS reads of the next stage's first fragments.
+// So every LDS read is covered by MFMAs and global latency by three stages of them.
+//
+// bf16: v_mfma_f32_32x32x16_bf16 (two k-steps of 16 per stage).
+// e4m3: v_mfma_f32_32x32x64_f8f6f4 (one k-step of 64 per stage, split by A blocks).
 // A and B fragments take their k values from the same (lane half, byte) positions, so the
 // product is the same whatever order the instruction assigns to k inside a fragment.
 //
-// Rows of A past M are read from row M-1 (always in bounds) and never stored.
+// Rows of A past M read as zeros (buffer descriptor bound) and are never stored.
 #pragma once
 
 #include "common.hpp"
@@ -27,16 +33,22 @@ namespace gemm {
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBKB = 128;                       // K tile, bytes per row
+constexpr int kRowB = 64;                       // bytes of K per row per stage
 constexpr int kThreads = 256;
-constexpr int kTileBytes = 256 * kBKB;          // one operand tile: 32 KiB
-constexpr int kStageBytes = 2 * kTileBytes;     // A + B
-constexpr int kMainBytes = 2 * kStageBytes;     // double buffer: 128 KiB
+constexpr int kOpBytes = 256 * kRowB;           // one operand of one stage: 16 KiB
+constexpr int kStageBytes = 2 * kOpBytes;       // A then B: 32 KiB
+constexpr int kStages = 4;
+constexpr int kMainBytes = kStages * kStageBytes;   // 128 KiB
 constexpr int kEpiPitch = kBN * 2 + 16;         // bf16 epilogue tile, padded row pitch (bytes)
 constexpr int kEpiBytes = kBM * kEpiPitch;      // 132 KiB
 constexpr int kSmemBytes = kMainBytes > kEpiBytes ? kMainBytes : kEpiBytes;
+constexpr int kLoadsPerStage = 8;               // buffer loads per wave per stage (4 A + 4 B)
 
-__device__ __forceinline__ int lds_off(int row, int chunk) { return row * kBKB + ((chunk ^ (row & 7)) << 4); }
+// LDS layout of an operand within a stage: row r (0..255) holds 64 bytes = 4 chunks of 16;
+// chunk c of row r sits at r * 64 + ((c ^ ((r / 4) % 4)) * 16).  An MFMA operand read has 16
+// lanes on 16 consecutive rows and one chunk: (r % 4, swizzled chunk) then takes 16 distinct
+// values, i.e. 16 distinct 16-byte bank groups of the 64-bank LDS.  The fills are 64 lanes
+// writing 1 KiB contiguously, conflict-free.
 
 // Workgroup id -> (m tile, n tile).  Workgroups are dispatched round-robin over the 8 XCDs,
 // so id % 8 names the XCD: each XCD gets one contiguous range of the logical order, and the
@@ -56,74 +68,78 @@ __device__ __forceinline__ void tile_coords(int bid, int mt, int nt, int& tm, in
     tn = in / gsize;
 }
 
-// MFMA operand fragments of one k-step: 4 A blocks and 4 B blocks of 32 rows.
-template <bool kFp8>
-struct Frags;
-template <>
-struct Frags<false> {
-    bf16x8 a[4], b[4];
-};
-template <>
-struct Frags<true> {
-    i32x8 a[4], b[4];
-};
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-constexpr int ksteps(bool fp8) { return fp8 ? 2 : 4; }
-
-// Reads the fragments of k-step ks from an LDS stage.  bf16: lane l takes 8 consecutive k
-// (16 bytes) of row l%32 at k offset 8*(l/32) within the 16-wide step; e4m3: 32 bytes at
-// byte offset 32*(l/32) within the 64-wide step.
-template <bool kFp8>
-__device__ __forceinline__ void load_frags(const uint8_t* __restrict__ stage, int ks, Frags<kFp8>& f) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int r32 = lane & 31, hi = lane >> 5;
-    const uint8_t* As = stage;
-    const uint8_t* Bs = stage + kTileBytes;
-    if constexpr (!kFp8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            f.a[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(wm * 128 + i * 32 + r32, ks * 2 + hi));
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            f.b[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(wn * 128 + j * 32 + r32, ks * 2 + hi));
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wm * 128 + i * 32 + r32;
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(As + lds_off(row, ks * 4 + hi * 2));
-            const u32x4 up = *reinterpret_cast<const u32x4*>(As + lds_off(row, ks * 4 + hi * 2 + 1));
-            f.a[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = wn * 128 + j * 32 + r32;
-            const u32x4 lo = *reinterpret_cast<const u32x4*>(Bs + lds_off(row, ks * 4 + hi * 2));
-            const u32x4 up = *reinterpret_cast<const u32x4*>(Bs + lds_off(row, ks * 4 + hi * 2 + 1));
-            f.b[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
-        }
-    }
+// s_waitcnt with only a vmcnt limit (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <bool kFp8>
-__device__ __forceinline__ void mma_step(const Frags<kFp8>& f, f32x16 (&acc)[4][4]) {
+// Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Global -> LDS fill of one stage.  Wave w fills rows [64w, 64w + 64) of A and of B in four
+// 1 KiB pieces of 16 rows; lane l of piece j lands at byte 16 l of the piece, i.e. row
+// 64w + 16j + l/4, stored chunk l%4, so it loads logical chunk (l%4) ^ ((l/16)%4).
+struct StageFill {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t va[4];      // A: row offset of piece j + chunk offset (per lane; bounds-checked)
+    uint32_t vb;         // B: row-in-piece offset + chunk offset (per lane)
+    uint32_t sb[4];      // B: offset of piece j's first row (uniform)
+    uint32_t lds_w;      // this wave's 4 KiB slice within an operand
+    __device__ __forceinline__ void issue(uint8_t* smem, int stage, int kt) const {
+        lds_u8* S = (lds_u8*)smem + stage * kStageBytes + lds_w;
+        const int koff = kt * kRowB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, S + j * 1024, 16, (int)va[j], koff, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if constexpr (!kFp8)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-            else
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, 0,
-                                                                             0, 0);
+        for (int j = 0; j < 4; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + kOpBytes + j * 1024, 16, (int)vb, (int)sb[j] + koff, 0,
+                                                     0);
+    }
+};
+
+// Per-lane LDS offsets of the fragment reads (relative to a stage).  Lane l reads row
+// r = l % 32 of each 32-row block; the swizzle depends only on (r / 4) % 4, so block i is an
+// immediate i * 2048 and the stage an immediate too.  Slot q: bf16 k-step q reads chunk
+// 2q + l/32; e4m3 reads chunks 2(l/32) + q (the two halves of its 32 bytes).
+struct FragAddr {
+    uint32_t a[2], b[2];
+    __device__ __forceinline__ void init(bool fp8) {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave >> 1, wn = wave & 1;
+        const int r32 = lane & 31, hi = lane >> 5;
+        const int sw = (r32 >> 2) & 3;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int c = fp8 ? 2 * hi + q : 2 * q + hi;
+            a[q] = (uint32_t)((wm * 128 + r32) * kRowB + ((c ^ sw) << 4));
+            b[q] = (uint32_t)(kOpBytes + (wn * 128 + r32) * kRowB + ((c ^ sw) << 4));
         }
+    }
+};
+
+__device__ __forceinline__ u32x4 lds_ld16(const uint8_t* smem, uint32_t off) {
+    return *reinterpret_cast<const u32x4*>(smem + off);
+}
+__device__ __forceinline__ bf16x8 lds_bf16x8(const uint8_t* smem, uint32_t off) {
+    return *reinterpret_cast<const bf16x8*>(smem + off);
+}
+__device__ __forceinline__ i32x8 lds_i32x8(const uint8_t* smem, uint32_t off0, uint32_t off1) {
+    const u32x4 lo = lds_ld16(smem, off0), up = lds_ld16(smem, off1);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
 }
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008;
 constexpr int kSgDsRead = 0x100;
 
-// Orders the scheduling region as n x [mfma_per MFMAs, 1 LDS read].
+// Orders the scheduling region as N x [MfmaPer MFMAs, 1 LDS read].
 template <int N, int MfmaPer>
 __device__ __forceinline__ void interleave_mfma_ds() {
 #pragma unroll
@@ -132,41 +148,127 @@ __device__ __forceinline__ void interleave_mfma_ds() {
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
     }
 }
+// Orders the scheduling region as N x [1 LDS read, MfmaPer MFMAs] (the reads lead, so the
+// last one has MfmaPer MFMAs of time to land before the region ends).
+template <int N, int MfmaPer>
+__device__ __forceinline__ void interleave_ds_mfma() {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, MfmaPer, 0);
+    }
+}
 
-// Main loop over `ktiles` K tiles.  A rows m0.. (clamped to M-1), B local rows [0,128) are
-// global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a plain tile).
-//
-// One iteration, in this order (scheduling barriers keep the compiler from merging phases):
-//   1. issue the global loads of K tile kt+1 into registers;
-//   2. the MFMAs of every k-step but the last, each interleaved with the LDS reads of the
-//      next k-step's fragments (fragments are double-buffered in registers);
-//   3. write the registers of tile kt+1 to the other LDS stage; barrier;
-//   4. the MFMAs of the last k-step (its fragments are already in registers), interleaved
-//      with the LDS reads of the first fragments of tile kt+1.
-// The global latency is covered by a K tile of MFMAs and every LDS read by a k-step of them.
-// The body has no branches: on the last iteration the loads re-read the last K tile (in
-// bounds) and the stage written is never read.  Ends with a barrier, so the caller may reuse
-// the LDS.
+// Stage hand-over: this wave's LDS reads of the stage it is leaving have landed (lgkmcnt 0:
+// after the barrier other waves refill that stage by DMA), its loads of the next stage have
+// landed (vmcnt), then the workgroup barrier makes every wave's fill visible.
+__device__ __forceinline__ void stage_barrier() {
+    constexpr int kVm = kLoadsPerStage * (kStages - 2);
+    static_assert(kVm < 64, "vmcnt range");
+    // s_waitcnt vmcnt(kVm) expcnt(7) lgkmcnt(0)
+    __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (0 << 8));
+    __syncthreads();
+}
+
+// bf16 pipeline.  fA/fB[h]: fragments of k-step h (4 A blocks, 4 B blocks).
+struct PipeBf16 {
+    bf16x8 a[2][4], b[2][4];
+    __device__ __forceinline__ void read(const uint8_t* st, const FragAddr& fa, int h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[h][i] = lds_bf16x8(st, fa.a[h] + i * 2048);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[h][j] = lds_bf16x8(st, fa.b[h] + j * 2048);
+    }
+    __device__ __forceinline__ void mma(int h, f32x16 (&acc)[4][4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+    }
+    // first half: k-step 0, while reading k-step 1; second half: k-step 1, while reading the
+    // next stage's k-step 0
+    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+        read(st, fa, 1);
+        mma(0, acc);
+        interleave_ds_mfma<8, 2>();
+    }
+    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+        read(next, fa, 0);
+        mma(1, acc);
+        interleave_mfma_ds<8, 2>();
+    }
+    __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0); }
+};
+
+// e4m3 pipeline: one 32x32x64 k-step per stage; the first half runs A blocks 0-1, the
+// second A blocks 2-3, both against B blocks 0-3.  During the second half the next stage's
+// A blocks 0-1 are read first (free since the first half), then each B block is re-read for
+// the next stage right after its last two MFMAs, so no fragment needs a second buffer.
+struct PipeFp8 {
+    i32x8 a[4], b[4];
+    __device__ __forceinline__ void read_a(const uint8_t* st, const FragAddr& fa, int i) {
+        a[i] = lds_i32x8(st, fa.a[0] + i * 2048, fa.a[1] + i * 2048);
+    }
+    __device__ __forceinline__ void read_b(const uint8_t* st, const FragAddr& fa, int j) {
+        b[j] = lds_i32x8(st, fa.b[0] + j * 2048, fa.b[1] + j * 2048);
+    }
+    __device__ __forceinline__ void mma(int i, int j, f32x16 (&acc)[4][4]) {
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
+    }
+    __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) read_a(st, fa, i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) read_b(st, fa, j);
+    }
+    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+        read_a(st, fa, 2);
+        read_a(st, fa, 3);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mma(i, j, acc);
+        interleave_ds_mfma<4, 2>();
+    }
+    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+        read_a(next, fa, 0);
+        read_a(next, fa, 1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            mma(2, j, acc);
+            mma(3, j, acc);
+            read_b(next, fa, j);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
+        interleave_mfma_ds<8, 1>();
+    }
+};
+
+// Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
+// [0,128) are global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a
+// plain tile).  Ends with all loads drained and a barrier, so the caller may reuse the LDS.
 template <bool kFp8>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
                                          int ktiles, uint8_t* smem, f32x16 (&acc)[4][4]) {
-    constexpr int KS = ksteps(kFp8);
-    constexpr int kReadsPerStep = kFp8 ? 16 : 8;     // ds_read_b128 per k-step per lane
-    constexpr int kMfmaPerRead = 16 / kReadsPerStep;
-    const int t = threadIdx.x;
-    const int lrow = t >> 3, chunk = t & 7;
-    const uint8_t* pa[8];
-    const uint8_t* pb[8];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+    StageFill sf;
+    const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
+    sf.ra = make_rsrc(A + m0 * lda, (uint32_t)(arows * lda));
+    sf.rb = make_rsrc(B + nb0 * ldb, (uint32_t)((nb1 - nb0 + 128) * ldb));
+    const uint32_t cbyte = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int r = j * 32 + lrow;
-        int64_t gm = m0 + r;
-        gm = gm < M ? gm : M - 1;
-        pa[j] = A + gm * lda + chunk * 16;
-        const int64_t gn = r < 128 ? nb0 + r : nb1 + (r - 128);
-        pb[j] = B + gn * ldb + chunk * 16;
+    for (int j = 0; j < 4; ++j) {
+        sf.va[j] = (uint32_t)((64 * wave + 16 * j + (lane >> 2)) * lda) + cbyte;
+        const int64_t r0 = 64 * wave + 16 * j;
+        sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
     }
+    sf.vb = (uint32_t)((lane >> 2) * ldb) + cbyte;
+    sf.lds_w = (uint32_t)(wave * 4096);
+    FragAddr fa;
+    fa.init(kFp8);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -174,50 +276,57 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    u32x4 ra[8], rb[8];
+    // prologue: stages 0..3 in flight, wait for stage 0
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        ra[j] = ld16(pa[j]);
-        rb[j] = ld16(pb[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        *reinterpret_cast<u32x4*>(smem + lds_off(j * 32 + lrow, chunk)) = ra[j];
-        *reinterpret_cast<u32x4*>(smem + kTileBytes + lds_off(j * 32 + lrow, chunk)) = rb[j];
-    }
+    for (int s = 0; s < kStages; ++s) sf.issue(smem, s, s < ktiles ? s : ktiles - 1);
+    wait_vmcnt<kLoadsPerStage * (kStages - 1)>();
     __syncthreads();
-    Frags<kFp8> f[2];
-    load_frags<kFp8>(smem, 0, f[0]);
 
-    for (int kt = 0; kt < ktiles; ++kt) {
-        const uint8_t* cur = smem + (kt & 1) * kStageBytes;
-        uint8_t* nxt = smem + ((kt + 1) & 1) * kStageBytes;
-        const int64_t koff = (int64_t)(kt + 1 < ktiles ? kt + 1 : kt) * kBKB;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            ra[j] = ld16(pa[j] + koff);
-            rb[j] = ld16(pb[j] + koff);
+    if constexpr (!kFp8) {
+        PipeBf16 p;
+        p.prime(smem, fa);
+        for (int kt = 0; kt < ktiles; ++kt) {
+            const int s = kt & (kStages - 1);
+            const uint8_t* st = smem + s * kStageBytes;
+            const uint8_t* nx = smem + ((kt + 1) & (kStages - 1)) * kStageBytes;
+            __builtin_amdgcn_sched_barrier(0);
+            p.first(st, fa, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_barrier();
+            const int kl = kt + kStages < ktiles ? kt + kStages : ktiles - 1;
+            sf.issue(smem, s, kl);
+            __builtin_amdgcn_sched_barrier(0);
+            p.second(nx, fa, acc);
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ks = 0; ks + 1 < KS; ++ks) {
-            load_frags<kFp8>(cur, ks + 1, f[(ks + 1) & 1]);
-            mma_step<kFp8>(f[ks & 1], acc);
+    } else {
+        PipeFp8 p;
+        p.prime(smem, fa);
+        for (int kt = 0; kt < ktiles; ++kt) {
+            const int s = kt & (kStages - 1);
+            const uint8_t* st = smem + s * kStageBytes;
+            const uint8_t* nx = smem + ((kt + 1) & (kStages - 1)) * kStageBytes;
+            __builtin_amdgcn_sched_barrier(0);
+            p.first(st, fa, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            stage_barrier();
+            const int kl = kt + kStages < ktiles ? kt + kStages : ktiles - 1;
+            sf.issue(smem, s, kl);
+            __builtin_amdgcn_sched_barrier(0);
+            p.second(nx, fa, acc);
         }
-        interleave_mfma_ds<(KS - 1) * kReadsPerStep, kMfmaPerRead>();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            *reinterpret_cast<u32x4*>(nxt + lds_off(j * 32 + lrow, chunk)) = ra[j];
-            *reinterpret_cast<u32x4*>(nxt + kTileBytes + lds_off(j * 32 + lrow, chunk)) = rb[j];
-        }
-        __syncthreads();
-        load_frags<kFp8>(nxt, 0, f[KS & 1]);
-        mma_step<kFp8>(f[(KS - 1) & 1], acc);
-        interleave_mfma_ds<kReadsPerStep, kMfmaPerRead>();
-        __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<0>();
     __syncthreads();
+}
+
+// Reads one accumulator out of its AGPR where it is used.  Without this the compiler copies
+// all 256 accumulators into VGPRs at the loop exit (the conversions below cannot read AGPRs),
+// which does not fit next to the epilogue's own registers.
+__device__ __forceinline__ float acc_read(float a) {
+    float v;
+    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+    return v;
 }
 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS
@@ -238,29 +347,36 @@ __device__ __forceinline__ void stage_tile_bf16(const f32x16 (&acc)[4][4], uint8
 #pragma unroll
         for (int j = 0; j < 4; ++j) cscale[j] = cs[j * 32 + r32];
     }
+    // one 32x32 block at a time (the scheduling barrier keeps the compiler from pulling all
+    // 256 accumulators into VGPRs at once)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        float rs[16];
+        if (rowscale) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-            float rs = 1.f;
-            if (rowscale) {
-                int64_t gm = m0 + row;
+            for (int r = 0; r < 16; ++r) {
+                int64_t gm = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
                 gm = gm < M ? gm : M - 1;
-                rs = rowscale[gm];
+                rs[r] = rowscale[gm];
             }
+        }
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int col = wn * 128 + j * 32 + r32;
+        for (int j = 0; j < 4; ++j) {
+            const int col = wn * 128 + j * 32 + r32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+                const float a = acc_read(acc[i][j][r]);
                 uint32_t b;
                 if (rowscale) {
                     // (acc * s_row) * s_col in double, one rounding to bf16
-                    b = f2bf_d((double)acc[i][j][r] * (double)rs * (double)cscale[j]);
+                    b = f2bf_d((double)a * (double)rs[r] * (double)cscale[j]);
                 } else {
-                    b = f2bf(acc[i][j][r]);
+                    b = f2bf(a);
                 }
                 *reinterpret_cast<uint16_t*>(smem + row * kEpiPitch + col * 2) = (uint16_t)b;
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 }

@@ -33,7 +33,7 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     const int n0 = tn * kBN;
     f32x16 acc[4][4];
     mainloop<false>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M, reinterpret_cast<const uint8_t*>(W),
-                    kHidden * 2, n0, n0 + 128, kHidden * 2 / kBKB, smem, acc);
+                    kHidden * 2, n0, n0 + 128, kHidden * 2 / kRowB, smem, acc);
     stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
     __syncthreads();
 
