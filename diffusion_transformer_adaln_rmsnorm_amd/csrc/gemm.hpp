@@ -5,26 +5,30 @@
 //
 // Workgroup: 256 threads = 4 wavefronts (one per SIMD), output tile 256 x 256, wave tile
 // 128 x 128 held as 4 x 4 blocks of the 32x32 MFMA (256 FP32 accumulators per lane, in
-// AGPRs).  K is consumed in stages of 64 bytes per row (32 bf16 or 64 e4m3).  Each stage
-// (A 256 x 64 B + B 256 x 64 B = 32 KiB) is filled straight from global memory into LDS by
-// buffer_load_dwordx4 ... lds (no register staging, no LDS store instructions); four stages
-// rotate in 128 KiB of LDS and the loads run three stages ahead of the MFMAs.
+// AGPRs).  K is consumed in stages of kRowB bytes per row (128: 64 bf16 or 128 e4m3, one
+// full cache line per row).  Each stage (A 256 rows + B 256 rows) is filled straight from
+// global memory into LDS by buffer_load_dwordx4 ... lds (no register staging, no LDS store
+// instructions); kStages stages rotate in LDS and the loads of a stage are issued as soon as
+// its buffer is released.
 //
-// Per stage (two halves of 16 bf16 MFMAs, or 8 e4m3 MFMAs, per wave):
-//   first half  : MFMAs on fragments already in registers, interleaved with the LDS reads of
-//                 the second half's fragments;
-//   wait for the next stage's loads (vmcnt), barrier;
-//   issue the loads of the stage three ahead into the buffer just released;
-//   second half : MFMAs, interleaved with the LDS reads of the next stage's first fragments.
-// So every LDS read is covered by MFMAs and global latency by three stages of them.
+// Per stage:
+//   first : the MFMAs of all k-steps but the last, each interleaved with the LDS reads of
+//           the next k-step's fragments (fragments double-buffered in registers);
+//   wait for the next stage's loads (vmcnt) and this wave's LDS reads, barrier;
+//   issue the loads of the stage kStages ahead into the buffer just released;
+//   second: the MFMAs of the last k-step, interleaved with the LDS reads of the next stage's
+//           first fragments and with the loads just issued.
+// So every LDS read is covered by MFMAs and global latency by the stages in flight.
 //
-// bf16: v_mfma_f32_32x32x16_bf16 (two k-steps of 16 per stage).
-// e4m3: v_mfma_f32_32x32x64_f8f6f4 (one k-step of 64 per stage, split by A blocks).
+// bf16: v_mfma_f32_32x32x16_bf16 (k-steps of 16).
+// e4m3: v_mfma_f32_32x32x64_f8f6f4 (k-steps of 64).
 // A and B fragments take their k values from the same (lane half, byte) positions, so the
 // product is the same whatever order the instruction assigns to k inside a fragment.
 //
 // Rows of A past M read as zeros (buffer descriptor bound) and are never stored.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -33,22 +37,37 @@ namespace gemm {
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kRowB = 64;                       // bytes of K per row per stage
+#ifndef DIT_GEMM_ROW_BYTES
+#define DIT_GEMM_ROW_BYTES 128
+#endif
+constexpr int kRowB = DIT_GEMM_ROW_BYTES;       // bytes of K per row per stage (64 or 128)
+static_assert(kRowB == 64 || kRowB == 128, "stage row width");
 constexpr int kThreads = 256;
-constexpr int kOpBytes = 256 * kRowB;           // one operand of one stage: 16 KiB
-constexpr int kStageBytes = 2 * kOpBytes;       // A then B: 32 KiB
-constexpr int kStages = 4;
-constexpr int kMainBytes = kStages * kStageBytes;   // 128 KiB
+constexpr int kOpBytes = 256 * kRowB;           // one operand of one stage
+constexpr int kStageBytes = 2 * kOpBytes;       // A then B
+#ifndef DIT_GEMM_STAGES
+#define DIT_GEMM_STAGES (kRowB == 64 ? 4 : 2)
+#endif
+constexpr int kStages = DIT_GEMM_STAGES;        // LDS stages in the ring (loads run kStages-1 ahead)
+constexpr int kMainBytes = kStages * kStageBytes;
 constexpr int kEpiPitch = kBN * 2 + 16;         // bf16 epilogue tile, padded row pitch (bytes)
 constexpr int kEpiBytes = kBM * kEpiPitch;      // 132 KiB
 constexpr int kSmemBytes = kMainBytes > kEpiBytes ? kMainBytes : kEpiBytes;
-constexpr int kLoadsPerStage = 8;               // buffer loads per wave per stage (4 A + 4 B)
+#ifndef DIT_GEMM_LOAD_AUX
+#define DIT_GEMM_LOAD_AUX 0
+#endif
+constexpr int kLoadAux = DIT_GEMM_LOAD_AUX;     // cache-policy bits of the stage-fill loads
+constexpr int kSlots = kRowB / 16;              // 16-byte chunks per row
+constexpr int kRowsPerPiece = 1024 / kRowB;     // rows filled by one 1 KiB wave load
+constexpr int kPieces = 64 / kRowsPerPiece;     // wave loads per operand per stage
+constexpr int kLoadsPerStage = 2 * kPieces;     // buffer loads per wave per stage
 
-// LDS layout of an operand within a stage: row r (0..255) holds 64 bytes = 4 chunks of 16;
-// chunk c of row r sits at r * 64 + ((c ^ ((r / 4) % 4)) * 16).  An MFMA operand read has 16
-// lanes on 16 consecutive rows and one chunk: (r % 4, swizzled chunk) then takes 16 distinct
-// values, i.e. 16 distinct 16-byte bank groups of the 64-bank LDS.  The fills are 64 lanes
-// writing 1 KiB contiguously, conflict-free.
+// LDS layout of an operand within a stage: row r (0..255) holds kRowB bytes = kSlots chunks
+// of 16; chunk c of row r sits at r * kRowB + ((c ^ swz(r)) * 16), swz(r) = (r / 4) % 4 for
+// 64-byte rows and (r / 2) % 8 for 128-byte rows.  An MFMA operand read has 16 lanes on 16
+// consecutive rows and one chunk, which then land in 16 distinct 16-byte bank groups of the
+// 64-bank LDS.  Fills are 64 lanes writing 1 KiB contiguously, conflict-free.
+__host__ __device__ constexpr int swz(int r) { return kRowB == 64 ? (r >> 2) & 3 : (r >> 1) & 7; }
 
 // Workgroup id -> (m tile, n tile).  Workgroups are dispatched round-robin over the 8 XCDs,
 // so id % 8 names the XCD: each XCD gets one contiguous range of the logical order, and the
@@ -59,7 +78,10 @@ __device__ __forceinline__ void tile_coords(int bid, int mt, int nt, int& tm, in
     const int xcd = bid & 7, idx = bid >> 3;
     const int per = G >> 3, rem = G & 7;
     const int L = xcd * per + (xcd < rem ? xcd : rem) + idx;
-    constexpr int GM = 8;
+#ifndef DIT_GEMM_GROUP_M
+#define DIT_GEMM_GROUP_M 4
+#endif
+    constexpr int GM = DIT_GEMM_GROUP_M;
     const int group = L / (GM * nt);
     const int first_m = group * GM;
     const int gsize = (mt - first_m) < GM ? (mt - first_m) : GM;
@@ -82,42 +104,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Global -> LDS fill of one stage.  Wave w fills rows [64w, 64w + 64) of A and of B in four
-// 1 KiB pieces of 16 rows; lane l of piece j lands at byte 16 l of the piece, i.e. row
-// 64w + 16j + l/4, stored chunk l%4, so it loads logical chunk (l%4) ^ ((l/16)%4).
+// Global -> LDS fill of one stage.  Wave w fills rows [64w, 64w + 64) of A and of B in
+// kPieces 1 KiB pieces of kRowsPerPiece rows; lane l of piece j lands at byte 16 l of the
+// piece, i.e. row 64w + j*kRowsPerPiece + l/kSlots, stored chunk l%kSlots, so it loads the
+// logical chunk (l % kSlots) ^ swz(row).
 struct StageFill {
     __amdgpu_buffer_rsrc_t ra, rb;
-    uint32_t va[4];      // A: row offset of piece j + chunk offset (per lane; bounds-checked)
-    uint32_t vb;         // B: row-in-piece offset + chunk offset (per lane)
-    uint32_t sb[4];      // B: offset of piece j's first row (uniform)
-    uint32_t lds_w;      // this wave's 4 KiB slice within an operand
+    uint32_t va[kPieces];    // A: row + chunk offset of piece j (per lane; bounds-checked)
+    uint32_t vb[kPieces];    // B: row-in-piece + chunk offset of piece j (per lane)
+    uint32_t sb[kPieces];    // B: offset of piece j's first row (uniform)
+    uint32_t lds_w;          // this wave's slice within an operand
     __device__ __forceinline__ void issue(uint8_t* smem, int stage, int kt) const {
         lds_u8* S = (lds_u8*)smem + stage * kStageBytes + lds_w;
         const int koff = kt * kRowB;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, S + j * 1024, 16, (int)va[j], koff, 0, 0);
+        for (int j = 0; j < kPieces; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, S + j * 1024, 16, (int)va[j], koff, 0, kLoadAux);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + kOpBytes + j * 1024, 16, (int)vb, (int)sb[j] + koff, 0,
-                                                     0);
+        for (int j = 0; j < kPieces; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + kOpBytes + j * 1024, 16, (int)vb[j], (int)sb[j] + koff,
+                                                     0, kLoadAux);
     }
 };
 
 // Per-lane LDS offsets of the fragment reads (relative to a stage).  Lane l reads row
-// r = l % 32 of each 32-row block; the swizzle depends only on (r / 4) % 4, so block i is an
-// immediate i * 2048 and the stage an immediate too.  Slot q: bf16 k-step q reads chunk
-// 2q + l/32; e4m3 reads chunks 2(l/32) + q (the two halves of its 32 bytes).
+// r = l % 32 of each 32-row block; the swizzle of rows r and r + 32i is the same, so block i
+// is an immediate (32 * kRowB * i) and the stage an immediate too.  Slot q: bf16 k-step q
+// reads chunk 2q + l/32; e4m3 k-step q/2 reads chunks 4(q/2) + 2(l/32) + q%2.
+constexpr int kQ = kSlots / 2;                  // fragment slots per operand
+constexpr int kBlk = 32 * kRowB;                // bytes of one 32-row block
 struct FragAddr {
-    uint32_t a[2], b[2];
+    uint32_t a[kQ], b[kQ];
     __device__ __forceinline__ void init(bool fp8) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave >> 1, wn = wave & 1;
         const int r32 = lane & 31, hi = lane >> 5;
-        const int sw = (r32 >> 2) & 3;
+        const int sw = swz(r32);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int c = fp8 ? 2 * hi + q : 2 * q + hi;
+        for (int q = 0; q < kQ; ++q) {
+            const int c = fp8 ? 4 * (q >> 1) + 2 * hi + (q & 1) : 2 * q + hi;
             a[q] = (uint32_t)((wm * 128 + r32) * kRowB + ((c ^ sw) << 4));
             b[q] = (uint32_t)(kOpBytes + (wn * 128 + r32) * kRowB + ((c ^ sw) << 4));
         }
@@ -137,6 +162,7 @@ __device__ __forceinline__ i32x8 lds_i32x8(const uint8_t* smem, uint32_t off0, u
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008;
+constexpr int kSgVmemRead = 0x020;
 constexpr int kSgDsRead = 0x100;
 
 // Orders the scheduling region as N x [MfmaPer MFMAs, 1 LDS read].
@@ -170,14 +196,18 @@ __device__ __forceinline__ void stage_barrier() {
     __syncthreads();
 }
 
-// bf16 pipeline.  fA/fB[h]: fragments of k-step h (4 A blocks, 4 B blocks).
+// bf16 pipeline: kRowB/32 k-steps of 16 per stage, fragments double-buffered in registers.
+//   first : k-steps 0..KS-2, each while reading the next k-step's fragments;
+//   second: the last k-step, while reading the next stage's k-step 0 (the stage fill issued
+//           just before is spread over it).
 struct PipeBf16 {
+    static constexpr int KS = kRowB / 32;
     bf16x8 a[2][4], b[2][4];
-    __device__ __forceinline__ void read(const uint8_t* st, const FragAddr& fa, int h) {
+    __device__ __forceinline__ void read(const uint8_t* st, const FragAddr& fa, int ks, int h) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[h][i] = lds_bf16x8(st, fa.a[h] + i * 2048);
+        for (int i = 0; i < 4; ++i) a[h][i] = lds_bf16x8(st, fa.a[ks] + i * kBlk);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[h][j] = lds_bf16x8(st, fa.b[h] + j * 2048);
+        for (int j = 0; j < 4; ++j) b[h][j] = lds_bf16x8(st, fa.b[ks] + j * kBlk);
     }
     __device__ __forceinline__ void mma(int h, f32x16 (&acc)[4][4]) {
 #pragma unroll
@@ -186,32 +216,41 @@ struct PipeBf16 {
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
     }
-    // first half: k-step 0, while reading k-step 1; second half: k-step 1, while reading the
-    // next stage's k-step 0
+    __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0, 0); }
     __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][4]) {
-        read(st, fa, 1);
-        mma(0, acc);
-        interleave_ds_mfma<8, 2>();
+#pragma unroll
+        for (int ks = 0; ks + 1 < KS; ++ks) {
+            read(st, fa, ks + 1, (ks + 1) & 1);
+            mma(ks & 1, acc);
+        }
+        interleave_ds_mfma<8 * (KS - 1), 2>();
     }
     __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][4]) {
-        read(next, fa, 0);
-        mma(1, acc);
-        interleave_mfma_ds<8, 2>();
+        read(next, fa, 0, KS & 1);
+        mma((KS - 1) & 1, acc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int v = 0; v < kLoadsPerStage / 8; ++v) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        }
     }
-    __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0); }
 };
 
-// e4m3 pipeline: one 32x32x64 k-step per stage; the first half runs A blocks 0-1, the
-// second A blocks 2-3, both against B blocks 0-3.  During the second half the next stage's
-// A blocks 0-1 are read first (free since the first half), then each B block is re-read for
-// the next stage right after its last two MFMAs, so no fragment needs a second buffer.
+// e4m3 pipeline for 64-byte rows: one 32x32x64 k-step per stage; the first half runs A
+// blocks 0-1, the second A blocks 2-3, both against B blocks 0-3.  During the second half
+// the next stage's A blocks 0-1 are read first (free since the first half), then each B
+// block is re-read for the next stage right after its last two MFMAs, so no fragment needs a
+// second buffer.
 struct PipeFp8 {
     i32x8 a[4], b[4];
     __device__ __forceinline__ void read_a(const uint8_t* st, const FragAddr& fa, int i) {
-        a[i] = lds_i32x8(st, fa.a[0] + i * 2048, fa.a[1] + i * 2048);
+        a[i] = lds_i32x8(st, fa.a[0] + i * kBlk, fa.a[1] + i * kBlk);
     }
     __device__ __forceinline__ void read_b(const uint8_t* st, const FragAddr& fa, int j) {
-        b[j] = lds_i32x8(st, fa.b[0] + j * 2048, fa.b[1] + j * 2048);
+        b[j] = lds_i32x8(st, fa.b[0] + j * kBlk, fa.b[1] + j * kBlk);
     }
     __device__ __forceinline__ void mma(int i, int j, f32x16 (&acc)[4][4]) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
@@ -240,9 +279,60 @@ struct PipeFp8 {
             mma(3, j, acc);
             read_b(next, fa, j);
         }
+        // stage-fill loads, 12 LDS reads, 8 MFMAs
         __builtin_amdgcn_sched_group_barrier(kSgDsRead, 4, 0);
-        interleave_mfma_ds<8, 1>();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgVmemRead, kLoadsPerStage / 8, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        }
     }
+};
+
+// e4m3 pipeline for 128-byte rows: two 32x32x64 k-steps per stage, fragments
+// double-buffered like the bf16 pipeline.
+struct PipeFp8K2 {
+    i32x8 a[2][4], b[2][4];
+    __device__ __forceinline__ void read(const uint8_t* st, const FragAddr& fa, int ks, int h) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[h][i] = lds_i32x8(st, fa.a[2 * ks] + i * kBlk, fa.a[2 * ks + 1] + i * kBlk);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[h][j] = lds_i32x8(st, fa.b[2 * ks] + j * kBlk, fa.b[2 * ks + 1] + j * kBlk);
+    }
+    __device__ __forceinline__ void mma(int h, f32x16 (&acc)[4][4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[h][i], b[h][j], acc[i][j], 0, 0, 0, 0,
+                                                                             0, 0);
+    }
+    __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0, 0); }
+    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+        read(st, fa, 1, 1);
+        mma(0, acc);
+        interleave_ds_mfma<16, 1>();
+    }
+    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+        read(next, fa, 0, 0);
+        mma(1, acc);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSgVmemRead, kLoadsPerStage / 16, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        }
+    }
+};
+
+template <bool kFp8>
+struct PipeOf {
+    using type = PipeBf16;
+};
+template <>
+struct PipeOf<true> {
+    using type = typename std::conditional<kRowB == 64, PipeFp8, PipeFp8K2>::type;
 };
 
 // Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
@@ -258,15 +348,17 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
     const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
     sf.ra = make_rsrc(A + m0 * lda, (uint32_t)(arows * lda));
     sf.rb = make_rsrc(B + nb0 * ldb, (uint32_t)((nb1 - nb0 + 128) * ldb));
-    const uint32_t cbyte = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) << 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        sf.va[j] = (uint32_t)((64 * wave + 16 * j + (lane >> 2)) * lda) + cbyte;
-        const int64_t r0 = 64 * wave + 16 * j;
+    for (int j = 0; j < kPieces; ++j) {
+        const int rin = j * kRowsPerPiece + lane / kSlots;          // row within the wave's 64
+        const int row = 64 * wave + rin;
+        const uint32_t cbyte = (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
+        sf.va[j] = (uint32_t)(row * lda) + cbyte;
+        const int64_t r0 = 64 * wave + j * kRowsPerPiece;             // piece's first row (uniform)
         sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
+        sf.vb[j] = (uint32_t)((lane / kSlots) * ldb) + cbyte;
     }
-    sf.vb = (uint32_t)((lane >> 2) * ldb) + cbyte;
-    sf.lds_w = (uint32_t)(wave * 4096);
+    sf.lds_w = (uint32_t)(wave * 64 * kRowB);
     FragAddr fa;
     fa.init(kFp8);
 #pragma unroll
@@ -276,44 +368,25 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // prologue: stages 0..3 in flight, wait for stage 0
+    // prologue: every stage of the ring in flight, wait for stage 0
 #pragma unroll
     for (int s = 0; s < kStages; ++s) sf.issue(smem, s, s < ktiles ? s : ktiles - 1);
     wait_vmcnt<kLoadsPerStage * (kStages - 1)>();
     __syncthreads();
 
-    if constexpr (!kFp8) {
-        PipeBf16 p;
-        p.prime(smem, fa);
-        for (int kt = 0; kt < ktiles; ++kt) {
-            const int s = kt & (kStages - 1);
-            const uint8_t* st = smem + s * kStageBytes;
-            const uint8_t* nx = smem + ((kt + 1) & (kStages - 1)) * kStageBytes;
-            __builtin_amdgcn_sched_barrier(0);
-            p.first(st, fa, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            stage_barrier();
-            const int kl = kt + kStages < ktiles ? kt + kStages : ktiles - 1;
-            sf.issue(smem, s, kl);
-            __builtin_amdgcn_sched_barrier(0);
-            p.second(nx, fa, acc);
-        }
-    } else {
-        PipeFp8 p;
-        p.prime(smem, fa);
-        for (int kt = 0; kt < ktiles; ++kt) {
-            const int s = kt & (kStages - 1);
-            const uint8_t* st = smem + s * kStageBytes;
-            const uint8_t* nx = smem + ((kt + 1) & (kStages - 1)) * kStageBytes;
-            __builtin_amdgcn_sched_barrier(0);
-            p.first(st, fa, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            stage_barrier();
-            const int kl = kt + kStages < ktiles ? kt + kStages : ktiles - 1;
-            sf.issue(smem, s, kl);
-            __builtin_amdgcn_sched_barrier(0);
-            p.second(nx, fa, acc);
-        }
+    typename PipeOf<kFp8>::type p;
+    p.prime(smem, fa);
+    for (int kt = 0; kt < ktiles; ++kt) {
+        const int s = kt % kStages;
+        const uint8_t* st = smem + s * kStageBytes;
+        const uint8_t* nx = smem + ((kt + 1) % kStages) * kStageBytes;
+        __builtin_amdgcn_sched_barrier(0);
+        p.first(st, fa, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_barrier();
+        const int kl = kt + kStages < ktiles ? kt + kStages : ktiles - 1;
+        sf.issue(smem, s, kl);
+        p.second(nx, fa, acc);
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();
