@@ -3,10 +3,14 @@
 // C[m, n] = sum_k A[m, k] * B[n, k]: both operands are K-contiguous rows (activations
 // [M, K], weights [N, K]), FP32 accumulation.
 //
-// Workgroup: 256 threads = 4 wavefronts (one per SIMD), output tile 256 x 256, wave tile
-// 128 x 128 held as 4 x 4 blocks of the 32x32 MFMA (256 FP32 accumulators per lane, in
-// AGPRs).  K is consumed in stages of kRowB bytes per row (128: 64 bf16 or 128 e4m3, one
-// full cache line per row).  Each stage (A 256 rows + B 256 rows) is filled straight from
+// Workgroup: kWaves wavefronts and one 256 x 256 output tile.  Default 8 waves, two per SIMD,
+// each a 128 x 64 wave tile of 4 x 2 blocks of the 32x32 MFMA (128 FP32 accumulators per lane,
+// so a wave fits in 256 registers): while one wave of a SIMD waits on its stage-fill loads or
+// LDS reads the other issues MFMAs.  4 waves (one per SIMD, 128 x 128 wave tiles, 256
+// accumulators in AGPRs) remain selectable with -DDIT_GEMM_WAVES=4.
+//
+// K is consumed in stages of kRowB bytes per row (128: 64 bf16 or 128 e4m3, one full cache
+// line per row).  Each stage (A 256 rows + B 256 rows) is filled straight from
 // global memory into LDS by buffer_load_dwordx4 ... lds (no register staging, no LDS store
 // instructions); kStages stages rotate in LDS and the loads of a stage are issued as soon as
 // its buffer is released.
@@ -42,7 +46,15 @@ constexpr int kBN = 256;
 #endif
 constexpr int kRowB = DIT_GEMM_ROW_BYTES;       // bytes of K per row per stage (64 or 128)
 static_assert(kRowB == 64 || kRowB == 128, "stage row width");
-constexpr int kThreads = 256;
+#ifndef DIT_GEMM_WAVES
+#define DIT_GEMM_WAVES 8
+#endif
+constexpr int kWaves = DIT_GEMM_WAVES;          // wavefronts per workgroup: 4 (one per SIMD) or 8 (two)
+static_assert(kWaves == 4 || kWaves == 8, "wave count");
+constexpr int kThreads = 64 * kWaves;
+constexpr int kWN = kWaves / 2;                 // waves across n (two across m)
+constexpr int kNB = 8 / kWN;                    // 32-column MFMA blocks per wave (4 or 2)
+constexpr int kWaveN = 32 * kNB;                // wave tile: 128 rows x kWaveN columns
 constexpr int kOpBytes = 256 * kRowB;           // one operand of one stage
 constexpr int kStageBytes = 2 * kOpBytes;       // A then B
 #ifndef DIT_GEMM_STAGES
@@ -59,7 +71,8 @@ constexpr int kSmemBytes = kMainBytes > kEpiBytes ? kMainBytes : kEpiBytes;
 constexpr int kLoadAux = DIT_GEMM_LOAD_AUX;     // cache-policy bits of the stage-fill loads
 constexpr int kSlots = kRowB / 16;              // 16-byte chunks per row
 constexpr int kRowsPerPiece = 1024 / kRowB;     // rows filled by one 1 KiB wave load
-constexpr int kPieces = 64 / kRowsPerPiece;     // wave loads per operand per stage
+constexpr int kFillRows = 256 / kWaves;         // rows of each operand one wave fills per stage
+constexpr int kPieces = kFillRows / kRowsPerPiece;   // wave loads per operand per stage
 constexpr int kLoadsPerStage = 2 * kPieces;     // buffer loads per wave per stage
 
 // LDS layout of an operand within a stage: row r (0..255) holds kRowB bytes = kSlots chunks
@@ -104,10 +117,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Global -> LDS fill of one stage.  Wave w fills rows [64w, 64w + 64) of A and of B in
-// kPieces 1 KiB pieces of kRowsPerPiece rows; lane l of piece j lands at byte 16 l of the
-// piece, i.e. row 64w + j*kRowsPerPiece + l/kSlots, stored chunk l%kSlots, so it loads the
-// logical chunk (l % kSlots) ^ swz(row).
+// Global -> LDS fill of one stage.  Wave w fills rows [F w, F w + F) of A and of B
+// (F = kFillRows) in kPieces 1 KiB pieces of kRowsPerPiece rows; lane l of piece j lands at
+// byte 16 l of the piece, i.e. row F w + j*kRowsPerPiece + l/kSlots, stored chunk l%kSlots,
+// so it loads the logical chunk (l % kSlots) ^ swz(row).
 struct StageFill {
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t va[kPieces];    // A: row + chunk offset of piece j (per lane; bounds-checked)
@@ -137,14 +150,14 @@ struct FragAddr {
     uint32_t a[kQ], b[kQ];
     __device__ __forceinline__ void init(bool fp8) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const int wm = wave >> 1, wn = wave & 1;
+        const int wm = wave / kWN, wn = wave % kWN;
         const int r32 = lane & 31, hi = lane >> 5;
-        const int sw = swz(r32);
+        const int sw = swz(r32);    // swz has period 16 rows, so rows r32 + 32i share it
 #pragma unroll
         for (int q = 0; q < kQ; ++q) {
             const int c = fp8 ? 4 * (q >> 1) + 2 * hi + (q & 1) : 2 * q + hi;
             a[q] = (uint32_t)((wm * 128 + r32) * kRowB + ((c ^ sw) << 4));
-            b[q] = (uint32_t)(kOpBytes + (wn * 128 + r32) * kRowB + ((c ^ sw) << 4));
+            b[q] = (uint32_t)(kOpBytes + (wn * kWaveN + r32) * kRowB + ((c ^ sw) << 4));
         }
     }
 };
@@ -185,6 +198,37 @@ __device__ __forceinline__ void interleave_ds_mfma() {
     }
 }
 
+// Orders the scheduling region as N k-steps of R LDS reads spread over F MFMAs (each read
+// leads its share of the MFMAs).  The group sizes of sched_group_barrier must be constants,
+// hence the recursion over the group index.
+template <int R, int F, int I = 0>
+__device__ __forceinline__ void interleave_kstep() {
+    if constexpr (I < R) {
+        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, F * (I + 1) / R - F * I / R, 0);
+        interleave_kstep<R, F, I + 1>();
+    }
+}
+template <int N, int R, int F>
+__device__ __forceinline__ void interleave_ksteps() {
+    if constexpr (N > 0) {
+        interleave_kstep<R, F>();
+        interleave_ksteps<N - 1, R, F>();
+    }
+}
+// Orders the scheduling region as F x [its share of V stage loads, its share of R LDS reads,
+// 1 MFMA].
+template <int V, int R, int F, int I = 0>
+__device__ __forceinline__ void interleave_fill() {
+    if constexpr (I < F) {
+        constexpr int v = V * (I + 1) / F - V * I / F, r = R * (I + 1) / F - R * I / F;
+        if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, v, 0);
+        if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(kSgDsRead, r, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        interleave_fill<V, R, F, I + 1>();
+    }
+}
+
 // Stage hand-over: this wave's LDS reads of the stage it is leaving have landed (lgkmcnt 0:
 // after the barrier other waves refill that stage by DMA), its loads of the next stage have
 // landed (vmcnt), then the workgroup barrier makes every wave's fill visible.
@@ -202,39 +246,49 @@ __device__ __forceinline__ void stage_barrier() {
 //           just before is spread over it).
 struct PipeBf16 {
     static constexpr int KS = kRowB / 32;
-    bf16x8 a[2][4], b[2][4];
+    static constexpr int R = 4 + kNB;           // fragment reads per k-step
+    static constexpr int F = 4 * kNB;           // MFMAs per k-step
+    bf16x8 a[2][4], b[2][kNB];
     __device__ __forceinline__ void read(const uint8_t* st, const FragAddr& fa, int ks, int h) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[h][i] = lds_bf16x8(st, fa.a[ks] + i * kBlk);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[h][j] = lds_bf16x8(st, fa.b[ks] + j * kBlk);
+        for (int j = 0; j < kNB; ++j) b[h][j] = lds_bf16x8(st, fa.b[ks] + j * kBlk);
     }
-    __device__ __forceinline__ void mma(int h, f32x16 (&acc)[4][4]) {
+    __device__ __forceinline__ void mma(int h, f32x16 (&acc)[4][kNB]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < kNB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
     }
     __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0, 0); }
-    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read(st, fa, ks + 1, (ks + 1) & 1);
             mma(ks & 1, acc);
         }
-        interleave_ds_mfma<8 * (KS - 1), 2>();
+        if constexpr (kWaves == 4) {
+            interleave_ds_mfma<8 * (KS - 1), 2>();
+        } else {
+            interleave_ksteps<KS - 1, R, F>();
+        }
     }
-    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
         read(next, fa, 0, KS & 1);
         mma((KS - 1) & 1, acc);
+        if constexpr (kWaves == 4) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 8; ++i) {
 #pragma unroll
-            for (int v = 0; v < kLoadsPerStage / 8; ++v) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                for (int v = 0; v < kLoadsPerStage / 8; ++v) __builtin_amdgcn_sched_group_barrier(kSgVmemRead, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            }
+        } else {
+            interleave_fill<kLoadsPerStage, R, F>();
         }
     }
 };
@@ -245,6 +299,7 @@ struct PipeBf16 {
 // block is re-read for the next stage right after its last two MFMAs, so no fragment needs a
 // second buffer.
 struct PipeFp8 {
+    static_assert(kWaves == 4 || kRowB != 64, "the 64-byte-row e4m3 pipeline is written for 4 waves");
     i32x8 a[4], b[4];
     __device__ __forceinline__ void read_a(const uint8_t* st, const FragAddr& fa, int i) {
         a[i] = lds_i32x8(st, fa.a[0] + i * kBlk, fa.a[1] + i * kBlk);
@@ -293,35 +348,45 @@ struct PipeFp8 {
 // e4m3 pipeline for 128-byte rows: two 32x32x64 k-steps per stage, fragments
 // double-buffered like the bf16 pipeline.
 struct PipeFp8K2 {
-    i32x8 a[2][4], b[2][4];
+    static constexpr int R = 2 * (4 + kNB);     // 16-byte LDS reads per k-step
+    static constexpr int F = 4 * kNB;           // MFMAs per k-step
+    i32x8 a[2][4], b[2][kNB];
     __device__ __forceinline__ void read(const uint8_t* st, const FragAddr& fa, int ks, int h) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) a[h][i] = lds_i32x8(st, fa.a[2 * ks] + i * kBlk, fa.a[2 * ks + 1] + i * kBlk);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[h][j] = lds_i32x8(st, fa.b[2 * ks] + j * kBlk, fa.b[2 * ks + 1] + j * kBlk);
+        for (int j = 0; j < kNB; ++j) b[h][j] = lds_i32x8(st, fa.b[2 * ks] + j * kBlk, fa.b[2 * ks + 1] + j * kBlk);
     }
-    __device__ __forceinline__ void mma(int h, f32x16 (&acc)[4][4]) {
+    __device__ __forceinline__ void mma(int h, f32x16 (&acc)[4][kNB]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < kNB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[h][i], b[h][j], acc[i][j], 0, 0, 0, 0,
                                                                              0, 0);
     }
     __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0, 0); }
-    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
         read(st, fa, 1, 1);
         mma(0, acc);
-        interleave_ds_mfma<16, 1>();
+        if constexpr (kWaves == 4) {
+            interleave_ds_mfma<16, 1>();
+        } else {
+            interleave_ksteps<1, R, F>();
+        }
     }
-    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
         read(next, fa, 0, 0);
         mma(1, acc);
+        if constexpr (kWaves == 4) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            __builtin_amdgcn_sched_group_barrier(kSgVmemRead, kLoadsPerStage / 16, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            for (int i = 0; i < 16; ++i) {
+                __builtin_amdgcn_sched_group_barrier(kSgVmemRead, kLoadsPerStage / 16, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+            }
+        } else {
+            interleave_fill<kLoadsPerStage, R, F>();
         }
     }
 };
@@ -341,7 +406,7 @@ struct PipeOf<true> {
 template <bool kFp8>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                         int ktiles, uint8_t* smem, f32x16 (&acc)[4][4]) {
+                                         int ktiles, uint8_t* smem, f32x16 (&acc)[4][kNB]) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     StageFill sf;
@@ -350,21 +415,21 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
     sf.rb = make_rsrc(B + nb0 * ldb, (uint32_t)((nb1 - nb0 + 128) * ldb));
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) {
-        const int rin = j * kRowsPerPiece + lane / kSlots;          // row within the wave's 64
-        const int row = 64 * wave + rin;
+        const int rin = j * kRowsPerPiece + lane / kSlots;          // row within the wave's slice
+        const int row = kFillRows * wave + rin;
         const uint32_t cbyte = (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
         sf.va[j] = (uint32_t)(row * lda) + cbyte;
-        const int64_t r0 = 64 * wave + j * kRowsPerPiece;             // piece's first row (uniform)
+        const int64_t r0 = kFillRows * wave + j * kRowsPerPiece;      // piece's first row (uniform)
         sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
         sf.vb[j] = (uint32_t)((lane / kSlots) * ldb) + cbyte;
     }
-    sf.lds_w = (uint32_t)(wave * 64 * kRowB);
+    sf.lds_w = (uint32_t)(wave * kFillRows * kRowB);
     FragAddr fa;
     fa.init(kFp8);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kNB; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -393,13 +458,17 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
     __syncthreads();
 }
 
-// Reads one accumulator out of its AGPR where it is used.  Without this the compiler copies
-// all 256 accumulators into VGPRs at the loop exit (the conversions below cannot read AGPRs),
-// which does not fit next to the epilogue's own registers.
+// Reads one accumulator out of its AGPR where it is used (4 waves: 256 accumulators per lane,
+// in AGPRs).  Without this the compiler copies all of them into VGPRs at the loop exit (the
+// conversions below cannot read AGPRs), which does not fit next to the epilogue's registers.
 __device__ __forceinline__ float acc_read(float a) {
-    float v;
-    asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
-    return v;
+    if constexpr (kWaves == 4) {
+        float v;
+        asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+        return v;
+    } else {
+        return a;   // 128 accumulators per lane: they stay in VGPRs
+    }
 }
 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS
@@ -407,35 +476,41 @@ __device__ __forceinline__ float acc_read(float a) {
 // Accumulator layout of the 32x32 MFMA: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4
 // and column l%32 of its block.  rowscale and colscale are both given or both null (factor 1).
 // Must follow a barrier that ends all LDS reads of the main loop.
-__device__ __forceinline__ void stage_tile_bf16(const f32x16 (&acc)[4][4], uint8_t* smem, const float* rowscale,
+__device__ __forceinline__ void stage_tile_bf16(const f32x16 (&acc)[4][kNB], uint8_t* smem, const float* rowscale,
                                                 int64_t m0, int64_t M, const float* colscale_lo,
                                                 const float* colscale_hi) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave / kWN, wn = wave % kWN;
     const int r32 = lane & 31, hi = lane >> 5;
-    float cscale[4] = {1.f, 1.f, 1.f, 1.f};
+    float cscale[kNB];
+#pragma unroll
+    for (int j = 0; j < kNB; ++j) cscale[j] = 1.f;
     if (colscale_lo) {
         // local columns [0,128) come from colscale_lo, [128,256) from colscale_hi
-        const float* cs = wn == 0 ? colscale_lo : colscale_hi;
+        const int c0 = wn * kWaveN;
+        const float* cs = c0 < 128 ? colscale_lo + c0 : colscale_hi + (c0 - 128);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) cscale[j] = cs[j * 32 + r32];
+        for (int j = 0; j < kNB; ++j) cscale[j] = cs[j * 32 + r32];
     }
     // one 32x32 block at a time (the scheduling barrier keeps the compiler from pulling all
     // 256 accumulators into VGPRs at once)
+    // row scales of block row i + 1 are loaded while block row i converts
+    auto load_rs = [&](int i, float (&rs)[16]) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            int64_t gm = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
+            gm = gm < M ? gm : M - 1;
+            rs[r] = rowscale[gm];
+        }
+    };
+    float rs[16], rs_nx[16];
+    if (rowscale) load_rs(0, rs);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float rs[16];
-        if (rowscale) {
+        if (rowscale && i + 1 < 4) load_rs(i + 1, rs_nx);
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                int64_t gm = m0 + wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-                gm = gm < M ? gm : M - 1;
-                rs[r] = rowscale[gm];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = wn * 128 + j * 32 + r32;
+        for (int j = 0; j < kNB; ++j) {
+            const int col = wn * kWaveN + j * 32 + r32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
@@ -450,6 +525,10 @@ __device__ __forceinline__ void stage_tile_bf16(const f32x16 (&acc)[4][4], uint8
                 *reinterpret_cast<uint16_t*>(smem + row * kEpiPitch + col * 2) = (uint16_t)b;
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        if (rowscale) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) rs[r] = rs_nx[r];
         }
     }
 }

@@ -21,7 +21,7 @@ namespace dit {
 
 using namespace gemm;
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale, int64_t M,
                   const uint8_t* __restrict__ W1, const float* __restrict__ w1s, uint16_t* __restrict__ y,
                   float* __restrict__ y_amax, int mt, int nt) {
@@ -30,16 +30,17 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
     const int j0 = tn * 128;
-    f32x16 acc[4][4];
+    f32x16 acc[4][kNB];
     mainloop<true>(a_q, kHidden, m0, M, W1, kHidden, j0, kInter + j0, kHidden / kRowB, smem, acc);
     stage_tile_bf16(acc, smem, a_scale, m0, M, w1s + j0, w1s + kInter + j0);
     __syncthreads();
 
     const int t = threadIdx.x;
     const int c8 = (t & 15) * 8;
-    const int rsub = t >> 4;            // 0..15
-    for (int it = 0; it < kBM / 16; ++it) {
-        const int row = it * 16 + rsub;
+    const int rsub = t >> 4;            // 0..kThreads/16-1
+    constexpr int kRowsPerPass = kThreads / 16;
+    for (int it = 0; it < kBM / kRowsPerPass; ++it) {
+        const int row = it * kRowsPerPass + rsub;
         const int64_t m = m0 + row;
         float hg[8], hu[8], yv[8];
         unpack8(epi_ld(smem, row, c8), hg);
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
     if (lane == 0) y_scale[m] = s;
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_scale, int64_t M,
                  const uint8_t* __restrict__ W2, const float* __restrict__ w2s, const uint16_t* __restrict__ gate,
                  int64_t gate_rows, int64_t gate_ld, const int64_t* __restrict__ idx, const uint16_t* residual,
@@ -102,7 +103,7 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
     const int n0 = tn * kBN;
-    f32x16 acc[4][4];
+    f32x16 acc[4][kNB];
     mainloop<true>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc);
     stage_tile_bf16(acc, smem, y_scale, m0, M, w2s + n0, w2s + n0 + 128);
     __syncthreads();
@@ -110,24 +111,44 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
     const int t = threadIdx.x;
     const int c8 = (t & 31) * 8;
     const int rsub = t >> 5;
-    for (int it = 0; it < kBM / 8; ++it) {
-        const int row = it * 8 + rsub;
+    constexpr int kRowsPerPass = kThreads / 32;
+    constexpr int kIters = kBM / kRowsPerPass;
+    // residual and gate chunks of row it + 1 (and the index of row it + 2) load while row it
+    // computes; rows grow with it, so the first row past M ends the loop
+    auto index_of = [&](int it) -> int64_t {
+        const int64_t m = m0 + it * kRowsPerPass + rsub;
+        return it < kIters && m < M ? idx[m] : -1;
+    };
+    auto load_row = [&](int it, int64_t gi, u32x4& rr, u32x4& gg) {
+        const int64_t m = m0 + it * kRowsPerPass + rsub;
+        if (it < kIters && m < M) {
+            rr = ld16(residual + m * kHidden + n0 + c8);
+            if (gi >= 0 && gi < gate_rows) gg = ld16(gate + gi * gate_ld + n0 + c8);
+        }
+    };
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    u32x4 r_cur = zero, g_cur = zero;
+    load_row(0, index_of(0), r_cur, g_cur);
+    int64_t gi_nx = index_of(1);
+    for (int it = 0; it < kIters; ++it) {
+        const int row = it * kRowsPerPass + rsub;
         const int64_t m = m0 + row;
         if (m >= M) break;
+        u32x4 r_nx = zero, g_nx = zero;
+        load_row(it + 1, gi_nx, r_nx, g_nx);
+        const int64_t gi_nx2 = index_of(it + 2);
         float o[8], g[8], r[8];
         unpack8(epi_ld(smem, row, c8), o);
-        const int64_t i = idx[m];
-        if (i >= 0 && i < gate_rows) {
-            unpack8(ld16(gate + i * gate_ld + n0 + c8), g);
-        } else {
+        unpack8(g_cur, g);
+        unpack8(r_cur, r);
+        // two bf16 values add exactly in fp32 (or the smaller is below half a bf16 ulp of the
+        // larger), so this is one rounding of the exact sum
 #pragma unroll
-            for (int e = 0; e < 8; ++e) g[e] = 0.f;
-        }
-        const int64_t off = m * kHidden + n0 + c8;
-        unpack8(ld16(residual + off), r);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = rbf_d((double)r[e] + (double)rbf(g[e] * o[e]));
-        st16(out + off, pack8(r));
+        for (int e = 0; e < 8; ++e) r[e] = rbf(r[e] + rbf(g[e] * o[e]));
+        st16(out + m * kHidden + n0 + c8, pack8(r));
+        r_cur = r_nx;
+        g_cur = g_nx;
+        gi_nx = gi_nx2;
     }
 }
 
