@@ -112,31 +112,59 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zeros.
+// Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zeros and
+// stores there are dropped (the check covers the per-lane offset, not the scalar one).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Epilogue accesses through descriptors: out-of-range lanes need no branch, so every load of
+// an epilogue row is issued unconditionally and the compiler can count the loads in flight
+// instead of waiting for all of them where control flow merges.
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ int64_t buf_ld_i64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+    return (int64_t)(((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0]);
+}
+__device__ __forceinline__ int32_t buf_ld_i32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
+constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past every descriptor's bound
 
 // Global -> LDS fill of one stage.  Wave w fills rows [F w, F w + F) of A and of B
 // (F = kFillRows) in kPieces 1 KiB pieces of kRowsPerPiece rows; lane l of piece j lands at
 // byte 16 l of the piece, i.e. row F w + j*kRowsPerPiece + l/kSlots, stored chunk l%kSlots,
 // so it loads the logical chunk (l % kSlots) ^ swz(row).
+// Within a wave's slice the swizzle of a piece's rows depends only on the piece's parity
+// (128-byte rows) or not at all (64-byte rows), so B needs kVPat per-lane offsets; A keeps
+// the row in the per-lane offset because only that part is checked against the descriptor's
+// bound (rows past M).
+constexpr int kVPat = kRowB == 128 ? 2 : 1;
 struct StageFill {
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t va[kPieces];    // A: row + chunk offset of piece j (per lane; bounds-checked)
-    uint32_t vb[kPieces];    // B: row-in-piece + chunk offset of piece j (per lane)
+    uint32_t vb[kVPat];      // B: row-in-piece + chunk offset, by piece parity (per lane)
     uint32_t sb[kPieces];    // B: offset of piece j's first row (uniform)
     uint32_t lds_w;          // this wave's slice within an operand
-    __device__ __forceinline__ void issue(uint8_t* smem, int stage, int kt) const {
+    // load j of the stage: A piece j for j < kPieces, else B piece j - kPieces
+    __device__ __forceinline__ void one(uint8_t* smem, int stage, int kt, int j) const {
         lds_u8* S = (lds_u8*)smem + stage * kStageBytes + lds_w;
         const int koff = kt * kRowB;
-#pragma unroll
-        for (int j = 0; j < kPieces; ++j)
+        if (j < kPieces) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, S + j * 1024, 16, (int)va[j], koff, 0, kLoadAux);
+        } else {
+            const int b = j - kPieces;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + kOpBytes + b * 1024, 16, (int)vb[b % kVPat],
+                                                     (int)sb[b] + koff, 0, kLoadAux);
+        }
+    }
+    __device__ __forceinline__ void issue(uint8_t* smem, int stage, int kt) const {
 #pragma unroll
-        for (int j = 0; j < kPieces; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + kOpBytes + j * 1024, 16, (int)vb[j], (int)sb[j] + koff,
-                                                     0, kLoadAux);
+        for (int j = 0; j < kLoadsPerStage; ++j) one(smem, stage, kt, j);
     }
 };
 
@@ -175,7 +203,10 @@ __device__ __forceinline__ i32x8 lds_i32x8(const uint8_t* smem, uint32_t off0, u
 
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSgMfma = 0x008;
-constexpr int kSgVmemRead = 0x020;
+#ifndef DIT_SG_VMEM
+#define DIT_SG_VMEM 0x020
+#endif
+constexpr int kSgVmemRead = DIT_SG_VMEM;
 constexpr int kSgDsRead = 0x100;
 
 // Orders the scheduling region as N x [MfmaPer MFMAs, 1 LDS read].
@@ -201,11 +232,19 @@ __device__ __forceinline__ void interleave_ds_mfma() {
 // Orders the scheduling region as N k-steps of R LDS reads spread over F MFMAs (each read
 // leads its share of the MFMAs).  The group sizes of sched_group_barrier must be constants,
 // hence the recursion over the group index.
+#ifndef DIT_MFMA_FIRST
+#define DIT_MFMA_FIRST 0
+#endif
 template <int R, int F, int I = 0>
 __device__ __forceinline__ void interleave_kstep() {
     if constexpr (I < R) {
-        __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, F * (I + 1) / R - F * I / R, 0);
+        if constexpr (DIT_MFMA_FIRST) {
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, F * (I + 1) / R - F * I / R, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+        } else {
+            __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSgMfma, F * (I + 1) / R - F * I / R, 0);
+        }
         interleave_kstep<R, F, I + 1>();
     }
 }
@@ -262,6 +301,15 @@ struct PipeBf16 {
             for (int j = 0; j < kNB; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
     }
+    // fragment f of k-step ks into buffer h: A blocks 0..3, then B blocks 0..kNB-1
+    __device__ __forceinline__ void read_one(const uint8_t* st, const FragAddr& fa, int ks, int h, int f) {
+        if (f < 4) a[h][f] = lds_bf16x8(st, fa.a[ks] + f * kBlk);
+        else b[h][f - 4] = lds_bf16x8(st, fa.b[ks] + (f - 4) * kBlk);
+    }
+    __device__ __forceinline__ void mma_one(int h, int i, f32x16 (&acc)[4][kNB]) {
+        const int bi = i / kNB, bj = i % kNB;
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][bi], b[h][bj], acc[bi][bj], 0, 0, 0);
+    }
     __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0, 0); }
     __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
 #pragma unroll
@@ -273,6 +321,19 @@ struct PipeBf16 {
             interleave_ds_mfma<8 * (KS - 1), 2>();
         } else {
             interleave_ksteps<KS - 1, R, F>();
+        }
+    }
+    // The last k-step in F slots, fenced so the order is exactly: stage-fill load i, the next
+    // stage's k-step-0 fragment read i (first R slots), MFMA i.
+    __device__ __forceinline__ void second_fenced(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][kNB],
+                                                  const StageFill& sf, uint8_t* smem, int stage, int kl) {
+        static_assert(kLoadsPerStage <= F && R <= F, "slots");
+#pragma unroll
+        for (int i = 0; i < F; ++i) {
+            if (i < kLoadsPerStage) sf.one(smem, stage, kl, i);
+            if (i < R) read_one(next, fa, 0, KS & 1, i);
+            mma_one((KS - 1) & 1, i, acc);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
@@ -365,6 +426,27 @@ struct PipeFp8K2 {
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[h][i], b[h][j], acc[i][j], 0, 0, 0, 0,
                                                                              0, 0);
     }
+    __device__ __forceinline__ void read_one(const uint8_t* st, const FragAddr& fa, int ks, int h, int f) {
+        if (f < 4) a[h][f] = lds_i32x8(st, fa.a[2 * ks] + f * kBlk, fa.a[2 * ks + 1] + f * kBlk);
+        else b[h][f - 4] = lds_i32x8(st, fa.b[2 * ks] + (f - 4) * kBlk, fa.b[2 * ks + 1] + (f - 4) * kBlk);
+    }
+    __device__ __forceinline__ void mma_one(int h, int i, f32x16 (&acc)[4][kNB]) {
+        const int bi = i / kNB, bj = i % kNB;
+        acc[bi][bj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[h][bi], b[h][bj], acc[bi][bj], 0, 0, 0, 0,
+                                                                       0, 0);
+    }
+    // as in the bf16 pipeline: fill load i, fragment i of the next stage's k-step 0, MFMA i
+    __device__ __forceinline__ void second_fenced(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][kNB],
+                                                  const StageFill& sf, uint8_t* smem, int stage, int kl) {
+        static_assert(kLoadsPerStage <= F && 4 + kNB <= F, "slots");
+#pragma unroll
+        for (int i = 0; i < F; ++i) {
+            if (i < kLoadsPerStage) sf.one(smem, stage, kl, i);
+            if (i < 4 + kNB) read_one(next, fa, 0, 0, i);
+            mma_one(1, i, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
     __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0, 0); }
     __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
         read(st, fa, 1, 1);
@@ -421,7 +503,7 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
         sf.va[j] = (uint32_t)(row * lda) + cbyte;
         const int64_t r0 = kFillRows * wave + j * kRowsPerPiece;      // piece's first row (uniform)
         sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
-        sf.vb[j] = (uint32_t)((lane / kSlots) * ldb) + cbyte;
+        if (j < kVPat) sf.vb[j] = (uint32_t)((lane / kSlots) * ldb) + cbyte;
     }
     sf.lds_w = (uint32_t)(wave * kFillRows * kRowB);
     FragAddr fa;
@@ -450,8 +532,13 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
         __builtin_amdgcn_sched_barrier(0);
         stage_barrier();
         const int kl = kt + kStages < ktiles ? kt + kStages : ktiles - 1;
-        sf.issue(smem, s, kl);
-        p.second(nx, fa, acc);
+        if constexpr (kWaves == 8) {
+            __builtin_amdgcn_sched_barrier(0);
+            p.second_fenced(nx, fa, acc, sf, smem, s, kl);
+        } else {
+            sf.issue(smem, s, kl);
+            p.second(nx, fa, acc);
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<0>();

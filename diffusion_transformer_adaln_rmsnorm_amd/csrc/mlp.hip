@@ -130,6 +130,10 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
     u32x4 r_cur = zero, g_cur = zero;
     load_row(0, index_of(0), r_cur, g_cur);
     int64_t gi_nx = index_of(1);
+#ifndef DIT_EPI_UNROLL
+#define DIT_EPI_UNROLL 1
+#endif
+#pragma unroll DIT_EPI_UNROLL
     for (int it = 0; it < kIters; ++it) {
         const int row = it * kRowsPerPass + rsub;
         const int64_t m = m0 + row;

@@ -56,6 +56,10 @@ void k_out_proj_gemm(const uint16_t* __restrict__ attn, int64_t M, const uint16_
     u32x4 r_cur = zero, g_cur = zero;
     load_row(0, gate_of(0), r_cur, g_cur);
     int64_t gi_nx = gate_of(1);
+#ifndef DIT_EPI_UNROLL
+#define DIT_EPI_UNROLL 1
+#endif
+#pragma unroll DIT_EPI_UNROLL
     for (int it = 0; it < kIters; ++it) {
         const int row = it * kRowsPerPass + rsub;
         const int64_t m = m0 + row;

@@ -9,10 +9,14 @@
 //
 // A 256-wide n tile is exactly two heads of one kind (7168 = 28 x 256), so each tile owns
 // whole heads and needs nothing from its neighbours.  After the main loop the tile is
-// rounded to bf16 into LDS; then 16 consecutive lanes own one (row, head): 8 dims each, a
-// 4-step xor reduction gives the head's sum of squares, and the RoPE partner of dims
-// [8q, 8q+8) (q < 12) sits 6 lanes away (pairs (j, j+48)).  Each lane writes 16 contiguous
-// bytes of out, so the 16 lanes of a head store its 256 bytes in one piece.
+// rounded to bf16 into LDS; then the 16 lanes of one DPP row own one (row, head), 8 dims
+// each, and a 4-step DPP reduction gives the head's sum of squares.  The chunks are placed
+// so that the RoPE partner (pairs (j, j+48), i.e. chunk c and c + 6 for c < 6) is always 8
+// lanes away: lanes 0-5 hold chunks 0-5, lanes 8-13 chunks 6-11, and lanes 6, 7, 14, 15 the
+// pass-through chunks 12-15.  One row rotation by 8 then fetches every partner, with no
+// lane-dependent choice (a DPP move must run with its source lanes active, which a select
+// lowered to a branch would break).  Each lane writes 16 contiguous bytes of out, so the 16
+// lanes of a head store its 256 bytes in one piece.
 #include "common.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
@@ -20,6 +24,30 @@
 namespace dit {
 
 using namespace gemm;
+
+// Cross-lane moves inside a 16-lane DPP row (VALU, no LDS round trip).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;         // quad_perm(1,0,3,2): lane i <- i ^ 1
+constexpr int kDppXor2 = 0x4E;         // quad_perm(2,3,0,1): lane i <- i ^ 2
+constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within each 16 lanes
+constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- (i + 8) mod 16
+
+// Sum over the 16 lanes of a DPP row, left in every lane of it.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<kDppXor1>(x);
+    x += dpp_f<kDppXor2>(x);
+    x += dpp_f<kDppHalfMirror>(x);    // pairs the two quads of each 8
+    x += dpp_f<kDppMirror>(x);        // pairs the two 8s of the row
+    return x;
+}
 
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __restrict__ W,
@@ -38,14 +66,14 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     __syncthreads();
 
     const int t = threadIdx.x;
-    const int q = t & 15;               // 8-dim chunk of the head
+    const int li = t & 15;              // lane within the (row, head) group
+    // 8-dim chunk of the head held by this lane (partner chunk q +/- 6 sits at lane li ^ 8)
+    const int q = li < 6 ? li : (li < 8 ? 12 + (li - 6) : (li < 14 ? li - 2 : li));
     const int hh = (t >> 4) & 1;        // which of the tile's two heads
     const int rsub = t >> 5;            // 0..kThreads/32-1
     const int kind = n0 / kAttnWidth;   // 0 q, 1 k, 2 v
     const int head = (n0 % kAttnWidth) / kHeadDim + hh;
     const int d0 = q * 8;
-    const int lane = t & 63;
-    const int partner = (lane & ~15) | (q < 6 ? q + 6 : (q < 12 ? q - 6 : q));
     const int j0 = (q % 6) * 8;         // frequency index of this chunk (q < 12)
 
     float nw[8];
@@ -54,36 +82,45 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
         unpack8(w, nw);
     }
 
-    // The cos/sin rows of iteration it + 1 (and the position of it + 2) are loaded while
-    // iteration it computes, so the global-load latency is not paid once per row.
+    // The cos/sin rows of iteration it + 1 and the position of it + 2 are loaded while
+    // iteration it computes.  All epilogue loads and stores go through buffer descriptors and
+    // are issued unconditionally (out-of-range lanes read zeros, stores past M are dropped),
+    // so no branch sits between a load and its use and no full wait is forced per row.
     constexpr int kRowsPerPass = kThreads / 32;
     constexpr int kIters = kBM / kRowsPerPass;
     const bool need_cs = kind < 2 && q < 12;
-    auto row_pos = [&](int it) -> int64_t {
+    const __amdgpu_buffer_rsrc_t rcs = make_rsrc(cs, kind < 2 ? (uint32_t)(S * kRopeCols * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t rpos = make_rsrc(pos, pos ? (uint32_t)(M * 8) : 0u);
+    const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
+    constexpr int64_t kOutRow = (int64_t)kHeads * 3 * kHeadDim;        // elements per token
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + m0 * kOutRow, (uint32_t)(tile_rows * kOutRow * 2));
+    // raw position of iteration it's row (its own number when pos is null), clamped where used
+    auto raw_pos = [&](int it) -> int64_t {
         const int64_t m = m0 + it * kRowsPerPass + rsub;
-        if (it >= kIters || m >= M) return 0;
-        const int64_t p = pos ? pos[m] : m;
-        return p < 0 ? 0 : (p > S - 1 ? S - 1 : p);
+        const int64_t p = buf_ld_i64(rpos, (uint32_t)(m * 8));
+        return pos ? p : m;
     };
-    u32x4 c_cur = {0u, 0u, 0u, 0u}, s_cur = {0u, 0u, 0u, 0u};
-    int64_t p_nx = 0;
-    if (need_cs) {
-        const int64_t p0 = row_pos(0);
-        c_cur = ld16(cs + p0 * kRopeCols + j0);
-        s_cur = ld16(cs + p0 * kRopeCols + kNFreq + j0);
-        p_nx = row_pos(1);
+    auto cs_off = [&](int64_t p, int col) -> uint32_t {
+        const int64_t pc = p < 0 ? 0 : (p > S - 1 ? S - 1 : p);
+        return need_cs ? (uint32_t)((pc * kRopeCols + col) * 2) : kOffNone;
+    };
+    u32x4 c_cur, s_cur;
+    {
+        const int64_t p0 = raw_pos(0);
+        c_cur = buf_ld16(rcs, cs_off(p0, j0));
+        s_cur = buf_ld16(rcs, cs_off(p0, kNFreq + j0));
     }
+    int64_t p_nx = raw_pos(1);
 
+#ifndef DIT_EPI_UNROLL
+#define DIT_EPI_UNROLL 1
+#endif
+#pragma unroll DIT_EPI_UNROLL
     for (int it = 0; it < kIters; ++it) {
         const int row = it * kRowsPerPass + rsub;
-        const int64_t m = m0 + row;
-        u32x4 c_nx = {0u, 0u, 0u, 0u}, s_nx = {0u, 0u, 0u, 0u};
-        int64_t p_nx2 = 0;
-        if (need_cs && it + 1 < kIters) {
-            c_nx = ld16(cs + p_nx * kRopeCols + j0);
-            s_nx = ld16(cs + p_nx * kRopeCols + kNFreq + j0);
-            p_nx2 = row_pos(it + 2);
-        }
+        const u32x4 c_nx = buf_ld16(rcs, cs_off(p_nx, j0));
+        const u32x4 s_nx = buf_ld16(rcs, cs_off(p_nx, kNFreq + j0));
+        const int64_t p_nx2 = raw_pos(it + 2);
         float v[8];
         unpack8(epi_ld(smem, row, hh * 128 + d0), v);
         u32x4 o;
@@ -93,33 +130,28 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-            ss += __shfl_xor(ss, 1);
-            ss += __shfl_xor(ss, 2);
-            ss += __shfl_xor(ss, 4);
-            ss += __shfl_xor(ss, 8);
+            ss = row16_sum(ss);       // the 16 lanes of a (row, head) are one DPP row
             const float r2 = rsqrtf(ss * (1.0f / kHeadDim) + qk_eps);
             float u[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) u[e] = rbf(v[e] * r2 * nw[e]);
             const u32x4 up = pack8(u);
+            // RoPE partner chunk q + 6 (q < 6) or q - 6 (6 <= q < 12), 8 lanes away
             u32x4 pv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = (uint32_t)__shfl((int)up[e], partner);
-            if (q < 12 && m < M) {
+            for (int e = 0; e < 4; ++e) pv[e] = dpp_u<kDppRor8>(up[e]);
+            if (q < 12) {
                 float c[8], s[8], w2[8];
                 unpack8(c_cur, c);
                 unpack8(s_cur, s);
                 unpack8(pv, w2);
+                // o_j = u_j c - u_{j+48} s (first half), o_{j+48} = u_{j+48} c + u_j s (second);
                 // bf16 x bf16 products are exact in fp32, so each fma is one rounding of
                 // u c -/+ w s, then one rounding to bf16
+                const float sg = q < 6 ? -1.f : 1.f;
                 float r[8];
-                if (q < 6) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) r[e] = rbf(fmaf(u[e], c[e], -(w2[e] * s[e])));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) r[e] = rbf(fmaf(u[e], c[e], w2[e] * s[e]));
-                }
+                for (int e = 0; e < 8; ++e) r[e] = rbf(fmaf(u[e], c[e], sg * (w2[e] * s[e])));
                 o = pack8(r);
             } else {
                 o = up;
@@ -127,7 +159,8 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
         } else {
             o = pack8(v);
         }
-        if (m < M) st16(out + ((m * kHeads + head) * 3 + kind) * kHeadDim + d0, o);
+        // rows past M fall outside rout and are dropped
+        buf_st16(rout, (uint32_t)((((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0) * 2, o);
         c_cur = c_nx;
         s_cur = s_nx;
         p_nx = p_nx2;
