@@ -12,14 +12,14 @@
 // K is consumed in stages of kRowB bytes per row (128: 64 bf16 or 128 e4m3, one full cache
 // line per row).  Each stage (A 256 rows + B 256 rows) is filled straight from
 // global memory into LDS by buffer_load_dwordx4 ... lds (no register staging, no LDS store
-// instructions); kStages stages rotate in LDS and the loads of a stage are issued as soon as
-// its buffer is released.
+// instructions); A and B each rotate through a ring of LDS slots, and the loads of a stage
+// are issued as soon as its slots are released.
 //
 // Per stage:
 //   first : the MFMAs of all k-steps but the last, each interleaved with the LDS reads of
 //           the next k-step's fragments (fragments double-buffered in registers);
 //   wait for the next stage's loads (vmcnt) and this wave's LDS reads, barrier;
-//   issue the loads of the stage kStages ahead into the buffer just released;
+//   issue the loads of the stages one ring depth ahead into the slots just released;
 //   second: the MFMAs of the last k-step, interleaved with the LDS reads of the next stage's
 //           first fragments and with the loads just issued.
 // So every LDS read is covered by MFMAs and global latency by the stages in flight.
@@ -55,13 +55,23 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWN = kWaves / 2;                 // waves across n (two across m)
 constexpr int kNB = 8 / kWN;                    // 32-column MFMA blocks per wave (4 or 2)
 constexpr int kWaveN = 32 * kNB;                // wave tile: 128 rows x kWaveN columns
-constexpr int kOpBytes = 256 * kRowB;           // one operand of one stage
-constexpr int kStageBytes = 2 * kOpBytes;       // A then B
+constexpr int kOpBytes = 256 * kRowB;           // one operand of one stage (an LDS slot)
 #ifndef DIT_GEMM_STAGES
 #define DIT_GEMM_STAGES (kRowB == 64 ? 4 : 2)
 #endif
-constexpr int kStages = DIT_GEMM_STAGES;        // LDS stages in the ring (loads run kStages-1 ahead)
-constexpr int kMainBytes = kStages * kStageBytes;
+// A and B each rotate through their own ring of LDS slots; a ring of depth S keeps S - 1
+// stages of that operand in flight.
+#ifndef DIT_GEMM_STAGES_A
+#define DIT_GEMM_STAGES_A DIT_GEMM_STAGES
+#endif
+#ifndef DIT_GEMM_STAGES_B
+#define DIT_GEMM_STAGES_B DIT_GEMM_STAGES
+#endif
+constexpr int kStagesA = DIT_GEMM_STAGES_A;
+constexpr int kStagesB = DIT_GEMM_STAGES_B;
+static_assert(kStagesA >= 2 && kStagesB >= 2, "ring depth");
+constexpr int kBRing = kStagesA * kOpBytes;     // LDS offset of the B ring
+constexpr int kMainBytes = (kStagesA + kStagesB) * kOpBytes;
 constexpr int kEpiPitch = kBN * 2 + 16;         // bf16 epilogue tile, padded row pitch (bytes)
 constexpr int kEpiBytes = kBM * kEpiPitch;      // 132 KiB
 constexpr int kSmemBytes = kMainBytes > kEpiBytes ? kMainBytes : kEpiBytes;
@@ -144,31 +154,55 @@ constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past every descriptor'
 // the row in the per-lane offset because only that part is checked against the descriptor's
 // bound (rows past M).
 constexpr int kVPat = kRowB == 128 ? 2 : 1;
+// Within a stage's loads, the operand with the shallower ring goes first: the stage barrier
+// then waits for it while the deeper ring's newest stage may still be in flight.
+constexpr bool kBFirst = kStagesB < kStagesA;
 struct StageFill {
     __amdgpu_buffer_rsrc_t ra, rb;
     uint32_t va[kPieces];    // A: row + chunk offset of piece j (per lane; bounds-checked)
     uint32_t vb[kVPat];      // B: row-in-piece + chunk offset, by piece parity (per lane)
     uint32_t sb[kPieces];    // B: offset of piece j's first row (uniform)
     uint32_t lds_w;          // this wave's slice within an operand
-    // load j of the stage: A piece j for j < kPieces, else B piece j - kPieces
-    __device__ __forceinline__ void one(uint8_t* smem, int stage, int kt, int j) const {
-        lds_u8* S = (lds_u8*)smem + stage * kStageBytes + lds_w;
-        const int koff = kt * kRowB;
-        if (j < kPieces) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, S + j * 1024, 16, (int)va[j], koff, 0, kLoadAux);
+    __device__ __forceinline__ void a_piece(uint8_t* smem, int slot, int kt, int j) const {
+        lds_u8* S = (lds_u8*)smem + slot * kOpBytes + lds_w;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, S + j * 1024, 16, (int)va[j], kt * kRowB, 0, kLoadAux);
+    }
+    __device__ __forceinline__ void b_piece(uint8_t* smem, int slot, int kt, int j) const {
+        lds_u8* S = (lds_u8*)smem + kBRing + slot * kOpBytes + lds_w;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + j * 1024, 16, (int)vb[j % kVPat], (int)sb[j] + kt * kRowB,
+                                                 0, kLoadAux);
+    }
+    // load j of one step of the fill: stage kta of A into A slot `as`, stage ktb of B into
+    // B slot `bs` (with kSkip, a negative kta / ktb skips that operand: prologue only, where
+    // the step is a compile-time constant)
+    template <bool kSkip = false>
+    __device__ __forceinline__ void one(uint8_t* smem, int as, int kta, int bs, int ktb, int j) const {
+        const bool first = j < kPieces;
+        const int jj = first ? j : j - kPieces;
+        if (first != kBFirst) {
+            if (!kSkip || kta >= 0) a_piece(smem, as, kta, jj);
         } else {
-            const int b = j - kPieces;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + kOpBytes + b * 1024, 16, (int)vb[b % kVPat],
-                                                     (int)sb[b] + koff, 0, kLoadAux);
+            if (!kSkip || ktb >= 0) b_piece(smem, bs, ktb, jj);
         }
     }
-    __device__ __forceinline__ void issue(uint8_t* smem, int stage, int kt) const {
+    template <bool kSkip = false>
+    __device__ __forceinline__ void issue(uint8_t* smem, int as, int kta, int bs, int ktb) const {
 #pragma unroll
-        for (int j = 0; j < kLoadsPerStage; ++j) one(smem, stage, kt, j);
+        for (int j = 0; j < kLoadsPerStage; ++j) one<kSkip>(smem, as, kta, bs, ktb, j);
     }
 };
 
-// Per-lane LDS offsets of the fragment reads (relative to a stage).  Lane l reads row
+// The LDS slots holding one stage of A and of B.
+struct Stage {
+    const uint8_t* a;
+    const uint8_t* b;
+};
+// One step of the fill: stage kta of A into A slot `as`, stage ktb of B into B slot `bs`.
+struct FillStep {
+    int as, kta, bs, ktb;
+};
+
+// Per-lane LDS offsets of the fragment reads (relative to an operand slot).  Lane l reads row
 // r = l % 32 of each 32-row block; the swizzle of rows r and r + 32i is the same, so block i
 // is an immediate (32 * kRowB * i) and the stage an immediate too.  Slot q: bf16 k-step q
 // reads chunk 2q + l/32; e4m3 k-step q/2 reads chunks 4(q/2) + 2(l/32) + q%2.
@@ -185,7 +219,7 @@ struct FragAddr {
         for (int q = 0; q < kQ; ++q) {
             const int c = fp8 ? 4 * (q >> 1) + 2 * hi + (q & 1) : 2 * q + hi;
             a[q] = (uint32_t)((wm * 128 + r32) * kRowB + ((c ^ sw) << 4));
-            b[q] = (uint32_t)(kOpBytes + (wn * kWaveN + r32) * kRowB + ((c ^ sw) << 4));
+            b[q] = (uint32_t)((wn * kWaveN + r32) * kRowB + ((c ^ sw) << 4));
         }
     }
 };
@@ -268,12 +302,32 @@ __device__ __forceinline__ void interleave_fill() {
     }
 }
 
+// Load accounting.  Fill step i (issued at the hand-over of main-loop iteration i, or as a
+// virtual step i < 0 in the prologue) loads stage i + S_A of A and i + S_B of B, the
+// shallower ring's operand first (F, ring depth S_F; the other is G, depth S_G >= S_F).  The
+// hand-over of iteration kt needs stage kt + 1 of both, issued in steps kt + 1 - S_F and
+// kt + 1 - S_G; loads complete in issue order, so the vmcnt limit is the number of loads
+// issued after the younger of the two: the G half of step kt + 1 - S_F and steps
+// kt + 2 - S_F .. kt - 1 in full (or, for G, steps kt + 2 - S_G .. kt - 1).
+constexpr int kSF = kStagesA < kStagesB ? kStagesA : kStagesB;
+constexpr int kSG = kStagesA < kStagesB ? kStagesB : kStagesA;
+constexpr int kVmF = kPieces + (kSF - 2) * kLoadsPerStage;
+constexpr int kVmG = (kSG - 2) * kLoadsPerStage;
+constexpr int kVmSteady = kVmF < kVmG ? kVmF : kVmG;
+// Before iteration 0 the prologue (steps -S_G .. -1, each with the loads whose stage is
+// >= 0) has to have landed stage 0: after F's stage 0 come the G half of step -S_F and
+// steps -S_F + 1 .. -1 in full; after G's stage 0 come, in steps -S_G + 1 .. -1, every G
+// load and the F loads of the steps >= -S_F.
+constexpr int kVmPrologueF = kPieces + (kSF - 1) * kLoadsPerStage;
+constexpr int kVmPrologueG = (kSG - 1) * kPieces + (kSF < kSG - 1 ? kSF : kSG - 1) * kPieces;
+constexpr int kVmPrologue = kVmPrologueF < kVmPrologueG ? kVmPrologueF : kVmPrologueG;
+static_assert(kVmSteady < 64 && kVmPrologue < 64, "vmcnt range");
+
 // Stage hand-over: this wave's LDS reads of the stage it is leaving have landed (lgkmcnt 0:
-// after the barrier other waves refill that stage by DMA), its loads of the next stage have
+// after the barrier other waves refill those slots by DMA), its loads of the next stage have
 // landed (vmcnt), then the workgroup barrier makes every wave's fill visible.
 __device__ __forceinline__ void stage_barrier() {
-    constexpr int kVm = kLoadsPerStage * (kStages - 2);
-    static_assert(kVm < 64, "vmcnt range");
+    constexpr int kVm = kVmSteady;
     // s_waitcnt vmcnt(kVm) expcnt(7) lgkmcnt(0)
     __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (0 << 8));
     __syncthreads();
@@ -288,11 +342,11 @@ struct PipeBf16 {
     static constexpr int R = 4 + kNB;           // fragment reads per k-step
     static constexpr int F = 4 * kNB;           // MFMAs per k-step
     bf16x8 a[2][4], b[2][kNB];
-    __device__ __forceinline__ void read(const uint8_t* st, const FragAddr& fa, int ks, int h) {
+    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa, int ks, int h) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[h][i] = lds_bf16x8(st, fa.a[ks] + i * kBlk);
+        for (int i = 0; i < 4; ++i) a[h][i] = lds_bf16x8(st.a, fa.a[ks] + i * kBlk);
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) b[h][j] = lds_bf16x8(st, fa.b[ks] + j * kBlk);
+        for (int j = 0; j < kNB; ++j) b[h][j] = lds_bf16x8(st.b, fa.b[ks] + j * kBlk);
     }
     __device__ __forceinline__ void mma(int h, f32x16 (&acc)[4][kNB]) {
 #pragma unroll
@@ -302,16 +356,16 @@ struct PipeBf16 {
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
     }
     // fragment f of k-step ks into buffer h: A blocks 0..3, then B blocks 0..kNB-1
-    __device__ __forceinline__ void read_one(const uint8_t* st, const FragAddr& fa, int ks, int h, int f) {
-        if (f < 4) a[h][f] = lds_bf16x8(st, fa.a[ks] + f * kBlk);
-        else b[h][f - 4] = lds_bf16x8(st, fa.b[ks] + (f - 4) * kBlk);
+    __device__ __forceinline__ void read_one(const Stage& st, const FragAddr& fa, int ks, int h, int f) {
+        if (f < 4) a[h][f] = lds_bf16x8(st.a, fa.a[ks] + f * kBlk);
+        else b[h][f - 4] = lds_bf16x8(st.b, fa.b[ks] + (f - 4) * kBlk);
     }
     __device__ __forceinline__ void mma_one(int h, int i, f32x16 (&acc)[4][kNB]) {
         const int bi = i / kNB, bj = i % kNB;
         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][bi], b[h][bj], acc[bi][bj], 0, 0, 0);
     }
-    __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0, 0); }
-    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
+    __device__ __forceinline__ void prime(const Stage& st, const FragAddr& fa) { read(st, fa, 0, 0); }
+    __device__ __forceinline__ void first(const Stage& st, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
 #pragma unroll
         for (int ks = 0; ks + 1 < KS; ++ks) {
             read(st, fa, ks + 1, (ks + 1) & 1);
@@ -325,18 +379,18 @@ struct PipeBf16 {
     }
     // The last k-step in F slots, fenced so the order is exactly: stage-fill load i, the next
     // stage's k-step-0 fragment read i (first R slots), MFMA i.
-    __device__ __forceinline__ void second_fenced(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][kNB],
-                                                  const StageFill& sf, uint8_t* smem, int stage, int kl) {
+    __device__ __forceinline__ void second_fenced(const Stage& next, const FragAddr& fa, f32x16 (&acc)[4][kNB],
+                                                  const StageFill& sf, uint8_t* smem, const FillStep& fs) {
         static_assert(kLoadsPerStage <= F && R <= F, "slots");
 #pragma unroll
         for (int i = 0; i < F; ++i) {
-            if (i < kLoadsPerStage) sf.one(smem, stage, kl, i);
+            if (i < kLoadsPerStage) sf.one(smem, fs.as, fs.kta, fs.bs, fs.ktb, i);
             if (i < R) read_one(next, fa, 0, KS & 1, i);
             mma_one((KS - 1) & 1, i, acc);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
+    __device__ __forceinline__ void second(const Stage& next, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
         read(next, fa, 0, KS & 1);
         mma((KS - 1) & 1, acc);
         if constexpr (kWaves == 4) {
@@ -359,25 +413,26 @@ struct PipeBf16 {
 // the next stage's A blocks 0-1 are read first (free since the first half), then each B
 // block is re-read for the next stage right after its last two MFMAs, so no fragment needs a
 // second buffer.
-struct PipeFp8 {
-    static_assert(kWaves == 4 || kRowB != 64, "the 64-byte-row e4m3 pipeline is written for 4 waves");
+template <int kW = kWaves>
+struct PipeFp8Impl {
+    static_assert(kW == 4, "the 64-byte-row e4m3 pipeline is written for 4 waves");
     i32x8 a[4], b[4];
-    __device__ __forceinline__ void read_a(const uint8_t* st, const FragAddr& fa, int i) {
-        a[i] = lds_i32x8(st, fa.a[0] + i * kBlk, fa.a[1] + i * kBlk);
+    __device__ __forceinline__ void read_a(const Stage& st, const FragAddr& fa, int i) {
+        a[i] = lds_i32x8(st.a, fa.a[0] + i * kBlk, fa.a[1] + i * kBlk);
     }
-    __device__ __forceinline__ void read_b(const uint8_t* st, const FragAddr& fa, int j) {
-        b[j] = lds_i32x8(st, fa.b[0] + j * kBlk, fa.b[1] + j * kBlk);
+    __device__ __forceinline__ void read_b(const Stage& st, const FragAddr& fa, int j) {
+        b[j] = lds_i32x8(st.b, fa.b[0] + j * kBlk, fa.b[1] + j * kBlk);
     }
     __device__ __forceinline__ void mma(int i, int j, f32x16 (&acc)[4][4]) {
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], 0, 0, 0, 0, 0, 0);
     }
-    __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) {
+    __device__ __forceinline__ void prime(const Stage& st, const FragAddr& fa) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) read_a(st, fa, i);
 #pragma unroll
         for (int j = 0; j < 4; ++j) read_b(st, fa, j);
     }
-    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+    __device__ __forceinline__ void first(const Stage& st, const FragAddr& fa, f32x16 (&acc)[4][4]) {
         read_a(st, fa, 2);
         read_a(st, fa, 3);
 #pragma unroll
@@ -386,7 +441,7 @@ struct PipeFp8 {
             for (int j = 0; j < 4; ++j) mma(i, j, acc);
         interleave_ds_mfma<4, 2>();
     }
-    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][4]) {
+    __device__ __forceinline__ void second(const Stage& next, const FragAddr& fa, f32x16 (&acc)[4][4]) {
         read_a(next, fa, 0);
         read_a(next, fa, 1);
 #pragma unroll
@@ -412,11 +467,11 @@ struct PipeFp8K2 {
     static constexpr int R = 2 * (4 + kNB);     // 16-byte LDS reads per k-step
     static constexpr int F = 4 * kNB;           // MFMAs per k-step
     i32x8 a[2][4], b[2][kNB];
-    __device__ __forceinline__ void read(const uint8_t* st, const FragAddr& fa, int ks, int h) {
+    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa, int ks, int h) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[h][i] = lds_i32x8(st, fa.a[2 * ks] + i * kBlk, fa.a[2 * ks + 1] + i * kBlk);
+        for (int i = 0; i < 4; ++i) a[h][i] = lds_i32x8(st.a, fa.a[2 * ks] + i * kBlk, fa.a[2 * ks + 1] + i * kBlk);
 #pragma unroll
-        for (int j = 0; j < kNB; ++j) b[h][j] = lds_i32x8(st, fa.b[2 * ks] + j * kBlk, fa.b[2 * ks + 1] + j * kBlk);
+        for (int j = 0; j < kNB; ++j) b[h][j] = lds_i32x8(st.b, fa.b[2 * ks] + j * kBlk, fa.b[2 * ks + 1] + j * kBlk);
     }
     __device__ __forceinline__ void mma(int h, f32x16 (&acc)[4][kNB]) {
 #pragma unroll
@@ -426,9 +481,9 @@ struct PipeFp8K2 {
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[h][i], b[h][j], acc[i][j], 0, 0, 0, 0,
                                                                              0, 0);
     }
-    __device__ __forceinline__ void read_one(const uint8_t* st, const FragAddr& fa, int ks, int h, int f) {
-        if (f < 4) a[h][f] = lds_i32x8(st, fa.a[2 * ks] + f * kBlk, fa.a[2 * ks + 1] + f * kBlk);
-        else b[h][f - 4] = lds_i32x8(st, fa.b[2 * ks] + (f - 4) * kBlk, fa.b[2 * ks + 1] + (f - 4) * kBlk);
+    __device__ __forceinline__ void read_one(const Stage& st, const FragAddr& fa, int ks, int h, int f) {
+        if (f < 4) a[h][f] = lds_i32x8(st.a, fa.a[2 * ks] + f * kBlk, fa.a[2 * ks + 1] + f * kBlk);
+        else b[h][f - 4] = lds_i32x8(st.b, fa.b[2 * ks] + (f - 4) * kBlk, fa.b[2 * ks + 1] + (f - 4) * kBlk);
     }
     __device__ __forceinline__ void mma_one(int h, int i, f32x16 (&acc)[4][kNB]) {
         const int bi = i / kNB, bj = i % kNB;
@@ -436,19 +491,19 @@ struct PipeFp8K2 {
                                                                        0, 0);
     }
     // as in the bf16 pipeline: fill load i, fragment i of the next stage's k-step 0, MFMA i
-    __device__ __forceinline__ void second_fenced(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][kNB],
-                                                  const StageFill& sf, uint8_t* smem, int stage, int kl) {
+    __device__ __forceinline__ void second_fenced(const Stage& next, const FragAddr& fa, f32x16 (&acc)[4][kNB],
+                                                  const StageFill& sf, uint8_t* smem, const FillStep& fs) {
         static_assert(kLoadsPerStage <= F && 4 + kNB <= F, "slots");
 #pragma unroll
         for (int i = 0; i < F; ++i) {
-            if (i < kLoadsPerStage) sf.one(smem, stage, kl, i);
+            if (i < kLoadsPerStage) sf.one(smem, fs.as, fs.kta, fs.bs, fs.ktb, i);
             if (i < 4 + kNB) read_one(next, fa, 0, 0, i);
             mma_one(1, i, acc);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    __device__ __forceinline__ void prime(const uint8_t* st, const FragAddr& fa) { read(st, fa, 0, 0); }
-    __device__ __forceinline__ void first(const uint8_t* st, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
+    __device__ __forceinline__ void prime(const Stage& st, const FragAddr& fa) { read(st, fa, 0, 0); }
+    __device__ __forceinline__ void first(const Stage& st, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
         read(st, fa, 1, 1);
         mma(0, acc);
         if constexpr (kWaves == 4) {
@@ -457,7 +512,7 @@ struct PipeFp8K2 {
             interleave_ksteps<1, R, F>();
         }
     }
-    __device__ __forceinline__ void second(const uint8_t* next, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
+    __device__ __forceinline__ void second(const Stage& next, const FragAddr& fa, f32x16 (&acc)[4][kNB]) {
         read(next, fa, 0, 0);
         mma(1, acc);
         if constexpr (kWaves == 4) {
@@ -473,6 +528,8 @@ struct PipeFp8K2 {
     }
 };
 
+using PipeFp8 = PipeFp8Impl<>;
+
 template <bool kFp8>
 struct PipeOf {
     using type = PipeBf16;
@@ -482,11 +539,10 @@ struct PipeOf<true> {
     using type = typename std::conditional<kRowB == 64, PipeFp8, PipeFp8K2>::type;
 };
 
-// Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
-// [0,128) are global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a
-// plain tile).  Ends with all loads drained and a barrier, so the caller may reuse the LDS.
+// Interleaved main loop (every wave fills, reads and multiplies within each stage); the
+// 4-wave layout and 64-byte stage rows use it.
 template <bool kFp8>
-__device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
+__device__ __forceinline__ void mainloop_interleaved(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
                                          int ktiles, uint8_t* smem, f32x16 (&acc)[4][kNB]) {
     const int lane = threadIdx.x & 63;
@@ -515,28 +571,42 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    // prologue: every stage of the ring in flight, wait for stage 0
+    // prologue: fill steps -S_G .. -1 (every slot of both rings in flight), wait for stage 0
+    auto step = [&](int i) -> FillStep {
+        const int ka = i + kStagesA, kb = i + kStagesB;
+        FillStep f;
+        f.as = (i + kStagesA) % kStagesA;
+        f.bs = (i + kStagesB) % kStagesB;
+        f.kta = ka < 0 ? -1 : (ka < ktiles ? ka : ktiles - 1);
+        f.ktb = kb < 0 ? -1 : (kb < ktiles ? kb : ktiles - 1);
+        return f;
+    };
 #pragma unroll
-    for (int s = 0; s < kStages; ++s) sf.issue(smem, s, s < ktiles ? s : ktiles - 1);
-    wait_vmcnt<kLoadsPerStage * (kStages - 1)>();
+    for (int i = -kSG; i < 0; ++i) {
+        const FillStep f = step(i);
+        sf.issue<true>(smem, f.as, f.kta, f.bs, f.ktb);
+    }
+    wait_vmcnt<kVmPrologue>();
     __syncthreads();
 
+    auto slots = [&](int kt) -> Stage {
+        return Stage{smem + (kt % kStagesA) * kOpBytes, smem + kBRing + (kt % kStagesB) * kOpBytes};
+    };
     typename PipeOf<kFp8>::type p;
-    p.prime(smem, fa);
+    p.prime(slots(0), fa);
     for (int kt = 0; kt < ktiles; ++kt) {
-        const int s = kt % kStages;
-        const uint8_t* st = smem + s * kStageBytes;
-        const uint8_t* nx = smem + ((kt + 1) % kStages) * kStageBytes;
+        const Stage st = slots(kt);
+        const Stage nx = slots(kt + 1);
         __builtin_amdgcn_sched_barrier(0);
         p.first(st, fa, acc);
         __builtin_amdgcn_sched_barrier(0);
         stage_barrier();
-        const int kl = kt + kStages < ktiles ? kt + kStages : ktiles - 1;
+        const FillStep f = step(kt);
         if constexpr (kWaves == 8) {
             __builtin_amdgcn_sched_barrier(0);
-            p.second_fenced(nx, fa, acc, sf, smem, s, kl);
+            p.second_fenced(nx, fa, acc, sf, smem, f);
         } else {
-            sf.issue(smem, s, kl);
+            sf.issue(smem, f.as, f.kta, f.bs, f.ktb);
             p.second(nx, fa, acc);
         }
     }
@@ -544,6 +614,224 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
     wait_vmcnt<0>();
     __syncthreads();
 }
+
+// ---------------------------------------------------------------------------------------
+// Ping-pong main loop (8 waves, 128-byte stage rows, two slots per operand).
+//
+// Group G0 = waves 0-3 (tile rows 0-127) and group G1 = waves 4-7 (rows 128-255); waves w
+// and w + 4 share a SIMD.  Each wave alternates a memory phase (read every fragment of one
+// stage from LDS into registers) and a compute phase (that stage's MFMAs, from registers
+// only).  G1 runs one phase behind G0, so on every SIMD one wave issues MFMAs back to back
+// while the other waits on LDS; a workgroup barrier ends every phase.  G1 enters one extra
+// barrier before its first phase and G0 one after its last, so both groups pass the same
+// number of barriers.
+//
+// Phase 2s: G0 memory(s), G1 compute(s-1).  Phase 2s+1: G0 compute(s), G1 memory(s).
+// Stage s sits in slot s % 2, and every wave refills only rows whose readers are done:
+//   A rows 0-127 are read by G0 alone (phase 2s): G0 wave w refills rows 32w.. with stage
+//     s+2 during its compute phase 2s+1;
+//   A rows 128-255 are read by G1 alone (phase 2s+1): G1 wave w refills rows 32w.. during
+//     its compute phase 2s+2;
+//   B rows 64c.. are read by waves c and 4+c only (phases 2s, 2s+1): G1 wave 4+c refills
+//     them at the end of its memory phase 2s+1, once its own reads have landed.
+// Every load of stage s+2 has landed before the barrier that ends phase 2s+3 (A rows 0-127,
+// B) or 2s+4 (A rows 128-255), the last barriers before their first reads.  Loads for
+// stages past the end re-load the stage a slot already holds (same bytes), so every phase
+// issues the same loads and the vmcnt limits below hold throughout.
+constexpr int kPPAPieces = 32 / kRowsPerPiece;      // A: 32 rows per wave
+constexpr int kPPBPieces = 64 / kRowsPerPiece;      // B: 64 rows per G1 wave
+
+struct PPFill {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    uint32_t va[kPPAPieces];  // A: row + chunk offset of piece j (per lane; bounds-checked)
+    uint32_t vb[kVPat];       // B: row-in-piece + chunk offset, by piece parity (per lane)
+    uint32_t sb[kPPBPieces];  // B: offset of piece j's first row (uniform)
+    uint32_t lds_a, lds_b;    // this wave's rows within an A slot / a B slot
+    __device__ __forceinline__ void a_rows(uint8_t* smem, int slot, int kt) const {
+        lds_u8* S = (lds_u8*)smem + slot * kOpBytes + lds_a;
+#pragma unroll
+        for (int j = 0; j < kPPAPieces; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, S + j * 1024, 16, (int)va[j], kt * kRowB, 0, kLoadAux);
+    }
+    __device__ __forceinline__ void b_rows(uint8_t* smem, int slot, int kt) const {
+        lds_u8* S = (lds_u8*)smem + 2 * kOpBytes + slot * kOpBytes + lds_b;
+#pragma unroll
+        for (int j = 0; j < kPPBPieces; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + j * 1024, 16, (int)vb[j % kVPat], (int)sb[j] + kt * kRowB,
+                                                     0, kLoadAux);
+    }
+};
+
+// Every fragment of one stage in registers: bf16 has kRowB/32 k-steps of 16, e4m3 kRowB/64
+// k-steps of 64 (each fragment then two 16-byte reads).
+template <bool kFp8>
+struct PPFrags;
+template <>
+struct PPFrags<false> {
+    static constexpr int KS = kRowB / 32;
+    bf16x8 a[KS][4], b[KS][kNB];
+    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[ks][i] = lds_bf16x8(st.a, fa.a[ks] + i * kBlk);
+#pragma unroll
+            for (int j = 0; j < kNB; ++j) b[ks][j] = lds_bf16x8(st.b, fa.b[ks] + j * kBlk);
+        }
+    }
+    __device__ __forceinline__ void mma(f32x16 (&acc)[4][kNB]) const {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < kNB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+    }
+};
+template <>
+struct PPFrags<true> {
+    static constexpr int KS = kRowB / 64;
+    i32x8 a[KS][4], b[KS][kNB];
+    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[ks][i] = lds_i32x8(st.a, fa.a[2 * ks] + i * kBlk, fa.a[2 * ks + 1] + i * kBlk);
+#pragma unroll
+            for (int j = 0; j < kNB; ++j)
+                b[ks][j] = lds_i32x8(st.b, fa.b[2 * ks] + j * kBlk, fa.b[2 * ks + 1] + j * kBlk);
+        }
+    }
+    __device__ __forceinline__ void mma(f32x16 (&acc)[4][kNB]) const {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < kNB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0,
+                                                                                 0, 0, 0);
+    }
+};
+
+// Phase-ending barrier: wait for vmcnt(kVm) and lgkmcnt(0), then a bare s_barrier.  These
+// waits are all the hand-over needs, so younger fill loads stay in flight across it (the
+// __syncthreads() fence would drain them).  The asm's memory clobber keeps the compiler from
+// moving memory accesses across the barrier.
+template <int kVm>
+__device__ __forceinline__ void pp_barrier() {
+    static_assert(kVm >= 0 && kVm < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (0 << 8));
+    asm volatile("s_barrier" ::: "memory");
+}
+
+template <bool kFp8>
+__device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
+                                            const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
+                                            int ktiles, uint8_t* smem, f32x16 (&acc)[4][kNB]) {
+    static_assert(kWaves == 8 && kRowB == 128, "ping-pong layout");
+    static_assert(4 * kOpBytes <= kSmemBytes, "two slots per operand");
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+    const bool g0 = wave < 4;
+    const int c = wave & 3;                          // B rows 64c.. (G1 fills them)
+    PPFill sf;
+    const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
+    sf.ra = make_rsrc(A + m0 * lda, (uint32_t)(arows * lda));
+    sf.rb = make_rsrc(B + nb0 * ldb, (uint32_t)((nb1 - nb0 + 128) * ldb));
+#pragma unroll
+    for (int j = 0; j < kPPAPieces; ++j) {
+        const int row = 32 * wave + j * kRowsPerPiece + lane / kSlots;
+        sf.va[j] = (uint32_t)(row * lda) + (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < kPPBPieces; ++j) {
+        const int64_t r0 = 64 * c + j * kRowsPerPiece;               // piece's first row (uniform)
+        sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
+        if (j < kVPat) {
+            const int row = (int)r0 + lane / kSlots;
+            sf.vb[j] = (uint32_t)((lane / kSlots) * ldb) + (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
+        }
+    }
+    sf.lds_a = (uint32_t)(32 * wave * kRowB);
+    sf.lds_b = (uint32_t)(64 * c * kRowB);
+    FragAddr fa;
+    fa.init(kFp8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < kNB; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    auto slot = [&](int kt) -> Stage {
+        const int s = kt & 1;
+        return Stage{smem + s * kOpBytes, smem + 2 * kOpBytes + s * kOpBytes};
+    };
+    auto ahead = [&](int kt) -> int { return kt + 2 < ktiles ? kt + 2 : kt; };   // stage loaded in kt's slot
+    PPFrags<kFp8> fr;
+
+    // prologue: stages 0 and 1 (each wave its A rows; G1 the B rows)
+#pragma unroll
+    for (int s0 = 0; s0 < 2; ++s0) {
+        const int kt = s0 < ktiles ? s0 : 0;
+        sf.a_rows(smem, s0, kt);
+        if (!g0) sf.b_rows(smem, s0, kt);
+    }
+    pp_barrier<0>();
+    if (!g0) pp_barrier<63>();       // G1 starts one phase behind
+    for (int kt = 0; kt < ktiles; ++kt) {
+        const int s = kt & 1;
+        // memory phase
+        __builtin_amdgcn_sched_barrier(0);
+        fr.read(slot(kt), fa);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g0) {
+            pp_barrier<63>();
+        } else {
+            // B rows 64c.. of this slot: the partner G0 wave read them in the last phase,
+            // this wave's reads land here
+            __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));    // lgkmcnt(0)
+            sf.b_rows(smem, s, ahead(kt));
+            // landed: B of stage kt+1 (issued before this phase's loads and the A rows of
+            // the last compute phase)
+            pp_barrier<kPPBPieces + kPPAPieces>();
+        }
+        // compute phase: this wave's A rows of the slot are free (its group's reads landed
+        // before the last barrier)
+        __builtin_amdgcn_sched_barrier(0);
+        sf.a_rows(smem, s, ahead(kt));
+        __builtin_amdgcn_sched_barrier(0);
+        fr.mma(acc);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g0) {
+            pp_barrier<kPPAPieces>();        // G0: A rows of stage kt+1 landed
+        } else {
+            pp_barrier<kPPBPieces + kPPAPieces>();   // G1: A rows of stage kt+1 landed
+        }
+    }
+    if (g0) pp_barrier<63>();        // G1's last compute phase
+    __syncthreads();
+}
+
+// Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
+// [0,128) are global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a
+// plain tile).  Ends with all loads drained and a barrier, so the caller may reuse the LDS.
+#ifndef DIT_GEMM_PINGPONG
+#define DIT_GEMM_PINGPONG (kWaves == 8 && kRowB == 128)
+#endif
+template <bool kFp8>
+__device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
+                                         const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
+                                         int ktiles, uint8_t* smem, f32x16 (&acc)[4][kNB]) {
+    if constexpr (DIT_GEMM_PINGPONG) {
+        mainloop_pp<kFp8>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc);
+    } else {
+        mainloop_interleaved<kFp8>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc);
+    }
+}
+
 
 // Reads one accumulator out of its AGPR where it is used (4 waves: 256 accumulators per lane,
 // in AGPRs).  Without this the compiler copies all of them into VGPRs at the loop exit (the

@@ -62,8 +62,6 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     f32x16 acc[4][kNB];
     mainloop<false>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M, reinterpret_cast<const uint8_t*>(W),
                     kHidden * 2, n0, n0 + 128, kHidden * 2 / kRowB, smem, acc);
-    stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
-    __syncthreads();
 
     const int t = threadIdx.x;
     const int li = t & 15;              // lane within the (row, head) group
@@ -76,16 +74,11 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     const int d0 = q * 8;
     const int j0 = (q % 6) * 8;         // frequency index of this chunk (q < 12)
 
-    float nw[8];
-    if (kind < 2) {
-        const u32x4 w = ld16((kind == 0 ? qw : kw) + d0);
-        unpack8(w, nw);
-    }
-
-    // The cos/sin rows of iteration it + 1 and the position of it + 2 are loaded while
-    // iteration it computes.  All epilogue loads and stores go through buffer descriptors and
-    // are issued unconditionally (out-of-range lanes read zeros, stores past M are dropped),
-    // so no branch sits between a load and its use and no full wait is forced per row.
+    // Every global operand of the epilogue is requested before it is needed, so the loop
+    // below pays one memory latency per tile rather than one per row: the positions of this
+    // thread's kIters rows now (they land while the accumulators are staged), the cos/sin
+    // rows right after.  All epilogue loads and stores go through buffer descriptors and are
+    // issued unconditionally (out-of-range lanes read zeros, stores past M are dropped).
     constexpr int kRowsPerPass = kThreads / 32;
     constexpr int kIters = kBM / kRowsPerPass;
     const bool need_cs = kind < 2 && q < 12;
@@ -94,33 +87,34 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
     constexpr int64_t kOutRow = (int64_t)kHeads * 3 * kHeadDim;        // elements per token
     const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + m0 * kOutRow, (uint32_t)(tile_rows * kOutRow * 2));
-    // raw position of iteration it's row (its own number when pos is null), clamped where used
-    auto raw_pos = [&](int it) -> int64_t {
-        const int64_t m = m0 + it * kRowsPerPass + rsub;
-        const int64_t p = buf_ld_i64(rpos, (uint32_t)(m * 8));
-        return pos ? p : m;
-    };
-    auto cs_off = [&](int64_t p, int col) -> uint32_t {
-        const int64_t pc = p < 0 ? 0 : (p > S - 1 ? S - 1 : p);
-        return need_cs ? (uint32_t)((pc * kRopeCols + col) * 2) : kOffNone;
-    };
-    u32x4 c_cur, s_cur;
-    {
-        const int64_t p0 = raw_pos(0);
-        c_cur = buf_ld16(rcs, cs_off(p0, j0));
-        s_cur = buf_ld16(rcs, cs_off(p0, kNFreq + j0));
+    u32x4 nwv = {0u, 0u, 0u, 0u};       // this lane's 8 q/k norm weights
+    if (kind < 2) nwv = ld16((kind == 0 ? qw : kw) + d0);
+    int64_t praw[kIters];               // raw positions (read only when pos is given)
+    if (pos != nullptr && kind < 2) {
+#pragma unroll
+        for (int it = 0; it < kIters; ++it)
+            praw[it] = buf_ld_i64(rpos, (uint32_t)((m0 + it * kRowsPerPass + rsub) * 8));
     }
-    int64_t p_nx = raw_pos(1);
 
-#ifndef DIT_EPI_UNROLL
-#define DIT_EPI_UNROLL 1
-#endif
-#pragma unroll DIT_EPI_UNROLL
+    stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
+    __syncthreads();
+
+    float nw[8];
+    unpack8(nwv, nw);
+    u32x4 cv[kIters], sv[kIters];
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+        const int64_t m = m0 + it * kRowsPerPass + rsub;
+        const int64_t p = pos != nullptr ? praw[it] : m;      // identity positions: the row
+        const int64_t pc = p < 0 ? 0 : (p > S - 1 ? S - 1 : p);
+        const uint32_t off = need_cs ? (uint32_t)((pc * kRopeCols + j0) * 2) : kOffNone;
+        cv[it] = buf_ld16(rcs, off);
+        sv[it] = buf_ld16(rcs, off + (need_cs ? kNFreq * 2 : 0u));
+    }
+
+#pragma unroll
     for (int it = 0; it < kIters; ++it) {
         const int row = it * kRowsPerPass + rsub;
-        const u32x4 c_nx = buf_ld16(rcs, cs_off(p_nx, j0));
-        const u32x4 s_nx = buf_ld16(rcs, cs_off(p_nx, kNFreq + j0));
-        const int64_t p_nx2 = raw_pos(it + 2);
         float v[8];
         unpack8(epi_ld(smem, row, hh * 128 + d0), v);
         u32x4 o;
@@ -141,9 +135,9 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
 #pragma unroll
             for (int e = 0; e < 4; ++e) pv[e] = dpp_u<kDppRor8>(up[e]);
             if (q < 12) {
-                float c[8], s[8], w2[8];
-                unpack8(c_cur, c);
-                unpack8(s_cur, s);
+                float c[8], sn[8], w2[8];
+                unpack8(cv[it], c);
+                unpack8(sv[it], sn);
                 unpack8(pv, w2);
                 // o_j = u_j c - u_{j+48} s (first half), o_{j+48} = u_{j+48} c + u_j s (second);
                 // bf16 x bf16 products are exact in fp32, so each fma is one rounding of
@@ -151,7 +145,7 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
                 const float sg = q < 6 ? -1.f : 1.f;
                 float r[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) r[e] = rbf(fmaf(u[e], c[e], sg * (w2[e] * s[e])));
+                for (int e = 0; e < 8; ++e) r[e] = rbf(fmaf(u[e], c[e], sg * (w2[e] * sn[e])));
                 o = pack8(r);
             } else {
                 o = up;
@@ -161,9 +155,6 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
         }
         // rows past M fall outside rout and are dropped
         buf_st16(rout, (uint32_t)((((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0) * 2, o);
-        c_cur = c_nx;
-        s_cur = s_nx;
-        p_nx = p_nx2;
     }
 }
 
