@@ -33,7 +33,14 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
     __bf16 b = (__bf16)f;
     return (uint32_t)__builtin_bit_cast(uint16_t, b);
 }
-__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+// two floats -> two bf16 (lo in bits 0-15), both rounded to nearest even by one
+// v_cvt_pk_bf16_f32
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    const bf16x2 b = __builtin_convertvector((f32x2){lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
 // round a float to the nearest bf16 value, returned as float
 __device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
 

@@ -887,17 +887,20 @@ __device__ __forceinline__ void stage_tile_bf16(const f32x16 (&acc)[4][kNB], uin
         for (int j = 0; j < kNB; ++j) {
             const int col = wn * kWaveN + j * 32 + r32;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
+            for (int r = 0; r < 16; r += 2) {
+                // registers r and r + 1 hold rows R and R + 1 of the column
                 const int row = wm * 128 + i * 32 + (r >> 2) * 8 + hi * 4 + (r & 3);
-                const float a = acc_read(acc[i][j][r]);
+                const float a0 = acc_read(acc[i][j][r]), a1 = acc_read(acc[i][j][r + 1]);
                 uint32_t b;
                 if (rowscale) {
                     // (acc * s_row) * s_col in double, one rounding to bf16
-                    b = f2bf_d((double)a * (double)rs[r] * (double)cscale[j]);
+                    b = f2bf_d((double)a0 * (double)rs[r] * (double)cscale[j]) |
+                        (f2bf_d((double)a1 * (double)rs[r + 1] * (double)cscale[j]) << 16);
                 } else {
-                    b = f2bf(a);
+                    b = pack_bf2(a0, a1);
                 }
                 *reinterpret_cast<uint16_t*>(smem + row * kEpiPitch + col * 2) = (uint16_t)b;
+                *reinterpret_cast<uint16_t*>(smem + (row + 1) * kEpiPitch + col * 2) = (uint16_t)(b >> 16);
             }
             __builtin_amdgcn_sched_barrier(0);
         }

@@ -30,9 +30,10 @@ template <int kCtrl>
 __device__ __forceinline__ float dpp_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
+// (for moves whose source lane always exists, e.g. row rotations: the old value is unused)
 template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kCtrl, 0xF, 0xF, false);
 }
 constexpr int kDppXor1 = 0xB1;         // quad_perm(1,0,3,2): lane i <- i ^ 1
 constexpr int kDppXor2 = 0x4E;         // quad_perm(2,3,0,1): lane i <- i ^ 2
@@ -101,6 +102,7 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
 
     float nw[8];
     unpack8(nwv, nw);
+    const uint32_t sgn = q < 6 ? 0x80008000u : 0u;   // negates both bf16 halves of a word
     u32x4 cv[kIters], sv[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
@@ -115,8 +117,9 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
         const int row = it * kRowsPerPass + rsub;
+        const u32x4 vp = epi_ld(smem, row, hh * 128 + d0);
         float v[8];
-        unpack8(epi_ld(smem, row, hh * 128 + d0), v);
+        unpack8(vp, v);
         u32x4 o;
         if (kind < 2) {
             // per-head RMSNorm in fp32: bf16 squares are exact, the sum carries fp32 rounding
@@ -128,30 +131,31 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
             const float r2 = rsqrtf(ss * (1.0f / kHeadDim) + qk_eps);
             float u[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) u[e] = rbf(v[e] * r2 * nw[e]);
-            const u32x4 up = pack8(u);
-            // RoPE partner chunk q + 6 (q < 6) or q - 6 (6 <= q < 12), 8 lanes away
+            for (int e = 0; e < 8; ++e) u[e] = v[e] * r2 * nw[e];
+            const u32x4 up = pack8(u);          // the bf16 u, packed
+            // RoPE partner chunk q + 6 (q < 6) or q - 6 (6 <= q < 12), 8 lanes away; its sign
+            // flipped for the first half, so both halves take o = u c + w s:
+            // o_j = u_j c - u_{j+48} s, o_{j+48} = u_{j+48} c + u_j s
             u32x4 pv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = dpp_u<kDppRor8>(up[e]);
+            for (int e = 0; e < 4; ++e) pv[e] = dpp_u<kDppRor8>(up[e]) ^ sgn;
             if (q < 12) {
-                float c[8], sn[8], w2[8];
+                float uu[8], c[8], sn[8], w2[8];
+                unpack8(up, uu);
                 unpack8(cv[it], c);
                 unpack8(sv[it], sn);
                 unpack8(pv, w2);
-                // o_j = u_j c - u_{j+48} s (first half), o_{j+48} = u_{j+48} c + u_j s (second);
                 // bf16 x bf16 products are exact in fp32, so each fma is one rounding of
-                // u c -/+ w s, then one rounding to bf16
-                const float sg = q < 6 ? -1.f : 1.f;
+                // u c +/- w s, then one rounding to bf16
                 float r[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) r[e] = rbf(fmaf(u[e], c[e], sg * (w2[e] * sn[e])));
+                for (int e = 0; e < 8; ++e) r[e] = fmaf(uu[e], c[e], w2[e] * sn[e]);
                 o = pack8(r);
             } else {
                 o = up;
             }
         } else {
-            o = pack8(v);
+            o = vp;
         }
         // rows past M fall outside rout and are dropped
         buf_st16(rout, (uint32_t)((((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0) * 2, o);
