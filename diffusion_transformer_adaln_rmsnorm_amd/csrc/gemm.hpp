@@ -638,6 +638,12 @@ __device__ __forceinline__ void mainloop_interleaved(const uint8_t* __restrict__
 // B) or 2s+4 (A rows 128-255), the last barriers before their first reads.  Loads for
 // stages past the end re-load the stage a slot already holds (same bytes), so every phase
 // issues the same loads and the vmcnt limits below hold throughout.
+#ifndef DIT_PP_PRIO
+#define DIT_PP_PRIO 0
+#endif
+#ifndef DIT_PP_LOADPOS
+#define DIT_PP_LOADPOS 1
+#endif
 constexpr int kPPAPieces = 32 / kRowsPerPiece;      // A: 32 rows per wave
 constexpr int kPPBPieces = 64 / kRowsPerPiece;      // B: 64 rows per G1 wave
 
@@ -679,14 +685,12 @@ struct PPFrags<false> {
             for (int j = 0; j < kNB; ++j) b[ks][j] = lds_bf16x8(st.b, fa.b[ks] + j * kBlk);
         }
     }
-    __device__ __forceinline__ void mma(f32x16 (&acc)[4][kNB]) const {
+    __device__ __forceinline__ void mma_ks(f32x16 (&acc)[4][kNB], int ks) const {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < kNB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < kNB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
     }
 };
 template <>
@@ -703,15 +707,13 @@ struct PPFrags<true> {
                 b[ks][j] = lds_i32x8(st.b, fa.b[2 * ks] + j * kBlk, fa.b[2 * ks + 1] + j * kBlk);
         }
     }
-    __device__ __forceinline__ void mma(f32x16 (&acc)[4][kNB]) const {
+    __device__ __forceinline__ void mma_ks(f32x16 (&acc)[4][kNB], int ks) const {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < kNB; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0,
-                                                                                 0, 0, 0);
+            for (int j = 0; j < kNB; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0, 0,
+                                                                             0, 0);
     }
 };
 
@@ -801,10 +803,23 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         // compute phase: this wave's A rows of the slot are free (its group's reads landed
         // before the last barrier)
         __builtin_amdgcn_sched_barrier(0);
-        sf.a_rows(smem, s, ahead(kt));
+#if DIT_PP_PRIO
+        __builtin_amdgcn_s_setprio(1);
+#endif
+        // the MFMAs of the first k-step go out before this wave's fill loads
+#pragma unroll
+        for (int ks = 0; ks < PPFrags<kFp8>::KS; ++ks) {
+            if (ks == DIT_PP_LOADPOS) {
+                __builtin_amdgcn_sched_barrier(0);
+                sf.a_rows(smem, s, ahead(kt));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            fr.mma_ks(acc, ks);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        fr.mma(acc);
-        __builtin_amdgcn_sched_barrier(0);
+#if DIT_PP_PRIO
+        __builtin_amdgcn_s_setprio(0);
+#endif
         if (g0) {
             pp_barrier<kPPAPieces>();        // G0: A rows of stage kt+1 landed
         } else {
