@@ -43,23 +43,47 @@ __device__ __forceinline__ float load_row_rms(const uint16_t* xr, int lane, floa
     return 1.0f / sqrtf(ss / (float)kHidden + eps);
 }
 
-// a = bf16(shift + n * bf16(1 + scale)),  n = bf16(x * r * w), for one 8-wide chunk.
-// r is the FP32 reciprocal root; each bf16(...) is one rounding of a double value (the
-// products of bf16 values and the sums below are exact or nearly so in double).
+// p = RN32(v) with error e = v - p (exact): the fp32 value rounded to odd from v (truncate
+// toward zero, then force the last bit to 1 when inexact).  fp32 keeps 24 >= 8 + 2 significant
+// bits, so the RNE to bf16 that follows equals one rounding of v.  p == 0 only when v rounds
+// to zero in bf16 anyway.
+__device__ __forceinline__ float odd32(float p, float e) {
+    uint32_t u = __float_as_uint(p);
+    const bool inexact = (e != 0.f) & (p != 0.f);
+    const bool toward_zero = ((__float_as_uint(e) ^ u) & 0x80000000u) != 0u;   // |p| > |v|
+    u -= (inexact && toward_zero) ? 1u : 0u;
+    u |= inexact ? 1u : 0u;
+    return __uint_as_float(u);
+}
+
+// a = bf16(shift + n * bf16(1 + scale)),  n = bf16(x * r * w), for one 8-wide chunk, each
+// bf16(...) one rounding of the exact value, in fp32 with error-free transforms:
+//   x w is exact (two 8-bit significands); (x w) r = p + e with e = fma(x w, r, -p);
+//   1 + scale is exact in fp32 unless |scale| < 2^-16, where both roundings give 1;
+//   n s1 is exact; shift + n s1 = s + e by TwoSum.
+// r is the FP32 reciprocal root.
 __device__ __forceinline__ void modulate_chunk(const u32x4& xv, const u32x4& wv, const u32x4& scv,
-                                               const u32x4& shv, float r, float (&a)[8]) {
+                                               const u32x4& shv, float r, uint32_t (&out)[4]) {
     float x[8], w[8], sc[8], sh[8];
     unpack8(xv, x);
     unpack8(wv, w);
     unpack8(scv, sc);
     unpack8(shv, sh);
-    const double rd = (double)r;
+    float a[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const double n = (double)rbf_d((double)x[e] * rd * (double)w[e]);
-        const double s1 = (double)rbf_d(1.0 + (double)sc[e]);
-        a[e] = rbf_d((double)sh[e] + n * s1);
+        const float xw = x[e] * w[e];
+        const float p = xw * r;
+        const float n = rbf(odd32(p, fmaf(xw, r, -p)));
+        const float s1 = rbf(1.0f + sc[e]);
+        const float prod = n * s1;
+        const float s = sh[e] + prod;
+        const float z = s - sh[e];
+        const float err = (sh[e] - (s - z)) + (prod - z);
+        a[e] = odd32(s, err);
     }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) out[k] = pack_bf2(a[2 * k], a[2 * k + 1]);
 }
 
 }  // namespace
@@ -90,9 +114,9 @@ __global__ __launch_bounds__(256) void k_norm_adaln_bf16(const uint16_t* __restr
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (!chunk_ok(j, lane)) continue;
         const int c = (j * 64 + lane) * 8;
-        float a[8];
+        uint32_t a[4];
         modulate_chunk(xv[j], ld16(xw + c), ld16(scr + c), ld16(shr + c), r, a);
-        st16(wr + c, pack8(a));
+        st16(wr + c, u32x4{a[0], a[1], a[2], a[3]});
     }
 }
 
@@ -129,11 +153,13 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (!chunk_ok(j, lane)) continue;
         const int c = (j * 64 + lane) * 8;
+        uint32_t ap[4];
+        modulate_chunk(xv[j], ld16(xw + c), ld16(scr + c), ld16(shr + c), r, ap);
+        av[j] = u32x4{ap[0], ap[1], ap[2], ap[3]};
         float a[8];
-        modulate_chunk(xv[j], ld16(xw + c), ld16(scr + c), ld16(shr + c), r, a);
+        unpack8(av[j], a);
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(a[e]));
-        av[j] = pack8(a);
     }
     amax = wave_max(amax);
     const float s = amax / 448.0f;             // IEEE division: RN(amax / 448)
