@@ -627,23 +627,22 @@ __device__ __forceinline__ void mainloop_interleaved(const uint8_t* __restrict__
 // number of barriers.
 //
 // Phase 2s: G0 memory(s), G1 compute(s-1).  Phase 2s+1: G0 compute(s), G1 memory(s).
-// Stage s sits in slot s % 2, and every wave refills only rows whose readers are done:
-//   A rows 0-127 are read by G0 alone (phase 2s): G0 wave w refills rows 32w.. with stage
-//     s+2 during its compute phase 2s+1;
-//   A rows 128-255 are read by G1 alone (phase 2s+1): G1 wave w refills rows 32w.. during
-//     its compute phase 2s+2;
-//   B rows 64c.. are read by waves c and 4+c only (phases 2s, 2s+1): G1 wave 4+c refills
-//     them at the end of its memory phase 2s+1, once its own reads have landed.
-// Every load of stage s+2 has landed before the barrier that ends phase 2s+3 (A rows 0-127,
-// B) or 2s+4 (A rows 128-255), the last barriers before their first reads.  Loads for
-// stages past the end re-load the stage a slot already holds (same bytes), so every phase
-// issues the same loads and the vmcnt limits below hold throughout.
-#ifndef DIT_PP_PRIO
-#define DIT_PP_PRIO 0
-#endif
-#ifndef DIT_PP_LOADPOS
-#define DIT_PP_LOADPOS 1
-#endif
+// Stage s sits in slot s % 2.  All fill loads are issued in memory phases (a compute phase
+// is MFMAs only: a wave issues in order, so a fill load that waits for the memory pipeline
+// would hold back the MFMAs behind it), and every wave refills only rows whose readers are
+// done:
+//   A rows 0-127 are read by G0 alone: at the start of its memory phase for stage s, G0 wave
+//     w refills rows 32w.. of the other slot (stage s-1, read in its previous memory phase)
+//     with stage s+1;
+//   A rows 128-255 likewise by G1, at the start of its memory phase for stage s;
+//   B rows 64c.. are read by waves c and 4+c only: G1 wave 4+c refills them in its slot of
+//     stage s with stage s+2 at the end of its memory phase for s, once its own reads have
+//     landed (wave c read them a phase earlier).
+// Each group waits for its A rows of stage s+1 before the barrier that ends its compute phase
+// for s, and G1 for the B rows of stage s+1 before the barrier that ends its memory phase for
+// s; those are the last barriers before the first reads.  Loads for stages past the end
+// re-load a stage whose slot has no reader left, so every phase issues the same loads and
+// the vmcnt limits hold throughout.
 constexpr int kPPAPieces = 32 / kRowsPerPiece;      // A: 32 rows per wave
 constexpr int kPPBPieces = 64 / kRowsPerPiece;      // B: 64 rows per G1 wave
 
@@ -685,12 +684,14 @@ struct PPFrags<false> {
             for (int j = 0; j < kNB; ++j) b[ks][j] = lds_bf16x8(st.b, fa.b[ks] + j * kBlk);
         }
     }
-    __device__ __forceinline__ void mma_ks(f32x16 (&acc)[4][kNB], int ks) const {
+    __device__ __forceinline__ void mma(f32x16 (&acc)[4][kNB]) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int j = 0; j < kNB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < kNB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0);
     }
 };
 template <>
@@ -707,13 +708,15 @@ struct PPFrags<true> {
                 b[ks][j] = lds_i32x8(st.b, fa.b[2 * ks] + j * kBlk, fa.b[2 * ks + 1] + j * kBlk);
         }
     }
-    __device__ __forceinline__ void mma_ks(f32x16 (&acc)[4][kNB], int ks) const {
+    __device__ __forceinline__ void mma(f32x16 (&acc)[4][kNB]) const {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int j = 0; j < kNB; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0, 0,
-                                                                             0, 0);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < kNB; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks][i], b[ks][j], acc[i][j], 0, 0, 0,
+                                                                                 0, 0, 0);
     }
 };
 
@@ -771,59 +774,50 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         const int s = kt & 1;
         return Stage{smem + s * kOpBytes, smem + 2 * kOpBytes + s * kOpBytes};
     };
-    auto ahead = [&](int kt) -> int { return kt + 2 < ktiles ? kt + 2 : kt; };   // stage loaded in kt's slot
     PPFrags<kFp8> fr;
 
-    // prologue: stages 0 and 1 (each wave its A rows; G1 the B rows)
-#pragma unroll
-    for (int s0 = 0; s0 < 2; ++s0) {
-        const int kt = s0 < ktiles ? s0 : 0;
-        sf.a_rows(smem, s0, kt);
-        if (!g0) sf.b_rows(smem, s0, kt);
+    // prologue: A of stage 0 (each wave its rows), B of stages 0 and 1 (G1)
+    sf.a_rows(smem, 0, 0);
+    if (!g0) {
+        sf.b_rows(smem, 0, 0);
+        sf.b_rows(smem, 1, ktiles > 1 ? 1 : 0);
     }
     pp_barrier<0>();
     if (!g0) pp_barrier<63>();       // G1 starts one phase behind
     for (int kt = 0; kt < ktiles; ++kt) {
         const int s = kt & 1;
-        // memory phase
+        // memory phase.  First this wave's A rows of stage kt+1 into the other slot: its
+        // group read them (stage kt-1) in its last memory phase.  Past the end, the stage a
+        // slot would be refilled with is replaced by kt (no reader is left for that slot).
+        __builtin_amdgcn_sched_barrier(0);
+        sf.a_rows(smem, s ^ 1, kt + 1 < ktiles ? kt + 1 : kt);
         __builtin_amdgcn_sched_barrier(0);
         fr.read(slot(kt), fa);
         __builtin_amdgcn_sched_barrier(0);
         if (g0) {
             pp_barrier<63>();
         } else {
-            // B rows 64c.. of this slot: the partner G0 wave read them in the last phase,
-            // this wave's reads land here
+            // B rows 64c.. of this slot, stage kt+2: the partner G0 wave read them in the
+            // last phase, this wave's reads land here
             __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));    // lgkmcnt(0)
-            sf.b_rows(smem, s, ahead(kt));
-            // landed: B of stage kt+1 (issued before this phase's loads and the A rows of
-            // the last compute phase)
-            pp_barrier<kPPBPieces + kPPAPieces>();
+            sf.b_rows(smem, s, kt + 2 < ktiles ? kt + 2 : kt);
+            // landed: B of stage kt+1 (issued before the A rows and B rows of this phase)
+            pp_barrier<kPPAPieces + kPPBPieces>();
         }
-        // compute phase: this wave's A rows of the slot are free (its group's reads landed
-        // before the last barrier)
+        // compute phase: MFMAs only
         __builtin_amdgcn_sched_barrier(0);
 #if DIT_PP_PRIO
         __builtin_amdgcn_s_setprio(1);
 #endif
-        // the MFMAs of the first k-step go out before this wave's fill loads
-#pragma unroll
-        for (int ks = 0; ks < PPFrags<kFp8>::KS; ++ks) {
-            if (ks == DIT_PP_LOADPOS) {
-                __builtin_amdgcn_sched_barrier(0);
-                sf.a_rows(smem, s, ahead(kt));
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            fr.mma_ks(acc, ks);
-        }
+        fr.mma(acc);
         __builtin_amdgcn_sched_barrier(0);
 #if DIT_PP_PRIO
         __builtin_amdgcn_s_setprio(0);
 #endif
         if (g0) {
-            pp_barrier<kPPAPieces>();        // G0: A rows of stage kt+1 landed
+            pp_barrier<0>();                 // G0: A rows of stage kt+1 landed
         } else {
-            pp_barrier<kPPBPieces + kPPAPieces>();   // G1: A rows of stage kt+1 landed
+            pp_barrier<kPPBPieces>();        // G1: A rows of stage kt+1 landed (B of kt+2 may fly)
         }
     }
     if (g0) pp_barrier<63>();        // G1's last compute phase
