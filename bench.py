@@ -87,8 +87,9 @@ def cpu_baseline(d, seconds_target=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    # the first launches run at a lower shader clock while power management ramps up
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stages", default="pre_attn,out_proj,mlp")
     ap.add_argument("--calibrate-copy", action="store_true",
