@@ -86,14 +86,14 @@ dit_status dit_qkv_rope_pack_bf16(const void* workspace, int64_t M, const void* 
         return DIT_ERR_ALIGN;
     if (S < 1) return DIT_ERR_SHAPE;
     if (!rope_positions && S < M) return DIT_ERR_SHAPE;
-    if (ulysses_degree != 1) return DIT_ERR_UNSUPPORTED;
     if (M == 0) return DIT_OK;
     return launched(dit::launch_qkv_gemm(static_cast<const uint16_t*>(workspace), M,
                                          static_cast<const uint16_t*>(qkv_weight),
                                          static_cast<const uint16_t*>(q_norm_weight),
                                          static_cast<const uint16_t*>(k_norm_weight),
                                          static_cast<const uint16_t*>(rope_cos_sin), S, rope_positions, qk_eps,
-                                         static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
+                                         ulysses_degree, static_cast<uint16_t*>(out),
+                                         static_cast<hipStream_t>(stream)));
 }
 
 dit_status dit_pre_attn_bf16(const void* x, int64_t M, const void* x_norm_weight, dit_bf16_table adaln_scale,
@@ -120,7 +120,6 @@ dit_status dit_pre_attn_bf16(const void* x, int64_t M, const void* x_norm_weight
         return DIT_ERR_ALIGN;
     if (S < 1) return DIT_ERR_SHAPE;
     if (!rope_positions && S < M) return DIT_ERR_SHAPE;
-    if (ulysses_degree != 1) return DIT_ERR_UNSUPPORTED;
     if (M == 0) return DIT_OK;
     st = dit_norm_adaln_bf16(x, M, x_norm_weight, adaln_scale, adaln_shift, adaln_index, eps, workspace, stream);
     if (st != DIT_OK) return st;

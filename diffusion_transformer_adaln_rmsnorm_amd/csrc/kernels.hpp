@@ -16,9 +16,10 @@ hipError_t launch_norm_adaln_fp8q(const uint16_t* x, int64_t M, const uint16_t* 
                                   const int64_t* idx, float eps, uint8_t* a_q, float* a_scale, float* y_amax,
                                   hipStream_t stream);
 
+// P: Ulysses destination count (1, 2, 4 or 8); out is [P, M, 56 / P, 3, 128]
 hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
                            const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos, float qk_eps,
-                           uint16_t* out, hipStream_t stream);
+                           int P, uint16_t* out, hipStream_t stream);
 
 hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t* Wo, const uint16_t* gate,
                                 int64_t gate_rows, int64_t gate_ld, const int32_t* gate_index,

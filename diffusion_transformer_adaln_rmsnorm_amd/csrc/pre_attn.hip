@@ -5,7 +5,8 @@
 // epilogue applies the per-head Q/K RMSNorm, partial split-half NeoX RoPE and the
 // destination-major pack) and Parameters (qkv_weight row order [q_all | k_all | v_all] x 56
 // heads x 128, q/k_norm_weight [128], rope_cos_sin [S, 96] with cos in columns [0,48) and sin
-// in [48,96), rope_positions clamped to [0, S) or the identity, out [1, M, 56, 3, 128]).
+// in [48,96), rope_positions clamped to [0, S) or the identity, out [P, M, 56 / P, 3, 128] for
+// P = ulysses_degree destinations, destination p holding heads [p 56/P, (p+1) 56/P)).
 //
 // A 256-wide n tile is exactly two heads of one kind (7168 = 28 x 256), so each tile owns
 // whole heads and needs nothing from its neighbours.  After the main loop the tile is
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __restrict__ W,
                 const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
                 const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
-                uint16_t* __restrict__ out, int mt, int nt) {
+                int hpd, uint16_t* __restrict__ out, int mt, int nt) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
@@ -72,6 +73,9 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     const int rsub = t >> 5;            // 0..kThreads/32-1
     const int kind = n0 / kAttnWidth;   // 0 q, 1 k, 2 v
     const int head = (n0 % kAttnWidth) / kHeadDim + hh;
+    // destination-major pack: destination dst takes heads [dst * hpd, (dst + 1) * hpd) of every
+    // token (hpd = 56 / P), out[dst, m, hl, kind, :]
+    const int dst = head / hpd, hl = head - dst * hpd;
     const int d0 = q * 8;
     const int j0 = (q % 6) * 8;         // frequency index of this chunk (q < 12)
 
@@ -157,18 +161,23 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
         } else {
             o = vp;
         }
-        // rows past M fall outside rout and are dropped
-        buf_st16(rout, (uint32_t)((((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0) * 2, o);
+        if (hpd == kHeads) {
+            // one destination: rows past M fall outside rout and are dropped
+            buf_st16(rout, (uint32_t)((((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0) * 2, o);
+        } else {
+            const int64_t m = m0 + row;
+            if (m < M) st16(out + (((dst * M + m) * hpd + hl) * 3 + kind) * kHeadDim + d0, o);
+        }
     }
 }
 
 hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
                            const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos, float qk_eps,
-                           uint16_t* out, hipStream_t stream) {
+                           int P, uint16_t* out, hipStream_t stream) {
     const int mt = (int)((M + kBM - 1) / kBM);
     const int nt = kQkvRows / kBN;
     hipLaunchKernelGGL(k_qkv_gemm, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs, S,
-                       pos, qk_eps, out, mt, nt);
+                       pos, qk_eps, kHeads / P, out, mt, nt);
     return hipGetLastError();
 }
 

@@ -45,7 +45,7 @@ typedef enum {
     DIT_ERR_SHAPE = 2,       /* a size is out of range (M, rows, S, S < M with identity positions) */
     DIT_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned (8 for int64 vectors, 4 for int32/f32) */
     DIT_ERR_STRIDE = 4,      /* table row stride < 5376 or not a multiple of 8 elements, or mismatched */
-    DIT_ERR_UNSUPPORTED = 5, /* a valid argument this build does not implement (ulysses_degree 2/4/8) */
+    DIT_ERR_UNSUPPORTED = 5, /* a valid argument this build does not implement (none at present) */
     DIT_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
     DIT_ERR_VALUE = 7        /* a scalar is invalid (eps <= 0 or not finite, ulysses_degree not 1/2/4/8) */
 } dit_status;
@@ -83,7 +83,8 @@ int dit_abi_version(void);
  *   dims j < 48: o_j = bf16(u_j c_j - u_{j+48} s_j), o_{j+48} = bf16(u_{j+48} c_j + u_j s_j)
  *   with c_j = rope_cos_sin[p, j], s_j = rope_cos_sin[p, 48 + j]; dims [96, 128) pass through
  *   v heads: bf16(acc) only
- *   out[0, m, h, kind, :] = o   (kind 0 = q, 1 = k, 2 = v)
+ *   out[h / (56/P), m, h % (56/P), kind, :] = o   (kind 0 = q, 1 = k, 2 = v): the
+ *   destination-major pack, destination p taking the contiguous heads [p 56/P, (p+1) 56/P)
  *
  * Arguments:
  *   x              bf16 [M, 5376], contiguous, 16-B aligned
@@ -95,7 +96,7 @@ int dit_abi_version(void);
  *   q_norm_weight, k_norm_weight  bf16 [128]
  *   rope_cos_sin   bf16 [S, 96], S >= 1
  *   rope_positions int64 [M] or NULL for the identity (then S >= M is required)
- *   ulysses_degree destination count P; only 1 is implemented (2, 4, 8 -> DIT_ERR_UNSUPPORTED)
+ *   ulysses_degree destination count P: 1, 2, 4 or 8 (else DIT_ERR_VALUE)
  *   eps, qk_eps    positive finite RMSNorm epsilons (the Python binding maps qk_eps=None to eps)
  *   workspace      bf16 [M, 5376] scratch, overwritten with a
  *   out            bf16 [P, M, 56/P, 3, 128]; must not overlap any input

@@ -144,6 +144,26 @@ def pre_attn(d, rows_sel=None, threads=None):
     return ws, out
 
 
+def ulysses_pack(out_rows, P):
+    """Destination-major pack of pre-attention outputs for P Ulysses destinations.
+
+    out_rows is [M, 56, 3, 128] (one row per token, heads in q/k/v weight order, as pre_attn
+    returns it).  The bf16 pre-attention page gives out the shape [P, M, 56 // P, 3, 128] with
+    P in {1, 2, 4, 8}; destination p takes the contiguous head block [p * 56 // P, (p + 1) *
+    56 // P) of every token (reading: the all-to-all that consumes out sends block p to rank p).
+    Returns that [P, M, 56 // P, 3, 128] array.
+    """
+    if P not in (1, 2, 4, 8):
+        raise ValueError(f"ulysses degree {P} is not one of 1, 2, 4, 8")
+    a = np.asarray(out_rows)
+    M = a.shape[0]
+    hl = HEADS // P
+    packed = np.empty((P, M, hl, 3, HEAD_DIM), a.dtype)
+    for p in range(P):
+        packed[p] = a[:, p * hl:(p + 1) * hl]
+    return packed
+
+
 def out_proj(d, rows_sel=None, threads=None):
     """Oracle of the bf16 out-projection with gated residual; returns out [R,5376] uint16."""
     M = d["M"]

@@ -67,7 +67,7 @@ def pre(**kw):
     (dict(sc=_T(stride=5375 + 1 + 4)), STRIDE), (dict(sh=_T(stride=5368)), STRIDE),
     (dict(sc=_T(rows=0)), SHAPE), (dict(sc=_T(rows=3)), SHAPE),
     (dict(M=-1), SHAPE), (dict(M=1 << 40), SHAPE), (dict(S=0), SHAPE), (dict(S=15), SHAPE),
-    (dict(P=2), UNSUP), (dict(P=8), UNSUP), (dict(P=3), VALUE), (dict(P=0), VALUE),
+    (dict(P=2, M=0), OK), (dict(P=8, M=0), OK), (dict(P=3), VALUE), (dict(P=0), VALUE), (dict(P=16), VALUE),
     (dict(eps=0.0), VALUE), (dict(eps=-1e-5), VALUE), (dict(qk_eps=float("nan")), VALUE),
     (dict(eps=float("inf")), VALUE),
     (dict(M=0), OK),

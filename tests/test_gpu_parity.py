@@ -76,14 +76,14 @@ def sample_rows(M, d=None, n_random=256, seed=0):
 
 # ---------------------------------------------------------------- runners
 
-def run_pre(d, out=None, workspace=None):
+def run_pre(d, out=None, workspace=None, P=1):
     t = synth.to_torch("pre_attn", d)
     M = d["M"]
     if out is None:
-        out = torch.empty((1, M, 56, 3, 128), dtype=torch.bfloat16, device="cuda")
+        out = torch.empty((P, M, 56 // P, 3, 128), dtype=torch.bfloat16, device="cuda")
     _dit().dit_pre_attn_bf16(t["x"], t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], t["adaln_index"],
                              t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
-                             ulysses_degree=1, out=out, eps=t["eps"], qk_eps=t["qk_eps"],
+                             ulysses_degree=P, out=out, eps=t["eps"], qk_eps=t["qk_eps"],
                              rope_positions=t["rope_positions"], workspace=workspace)
     torch.cuda.synchronize()
     return t, out
@@ -215,6 +215,41 @@ def test_pre_attn_small_M_random_positions(M):
     ws = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
     _, out = run_pre(d, workspace=ws)
     check_pre(d, ws, out)
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_pre_attn_ulysses_pack_is_the_degree_one_output_repacked(P):
+    """P destinations: the same values as P = 1, bit for bit, in the destination-major layout
+    [P, M, 56 // P, 3, 128] (two m-tiles with a ragged tail, random positions, guarded rows)."""
+    M = 300
+    _say(f"pre_attn ulysses P={P}, M={M}")
+    d = synth.pre_attn_inputs(M, seed=400 + P, rows=2, S=512, positions="random", n_bad_positions=4,
+                              bad_index_frac=0.02, weight=_shared_weight())
+    _, out1 = run_pre(d, P=1)
+    _, outp = run_pre(d, P=P)
+    one = synth.bits(out1).reshape(M, 56, 3, 128)
+    got = synth.bits(outp)
+    assert got.shape == (P, M, 56 // P, 3, 128)
+    assert np.array_equal(got, oracle.ulysses_pack(one, P))
+
+
+def test_pre_attn_ulysses_degree8_against_oracle():
+    """P = 8 on the M = 16 workload (guarded rows, rows=4 tables), checked against the oracle's
+    output after the oracle's destination-major pack."""
+    _say("config 0 with ulysses_degree 8")
+    kind, d = synth.config(0)
+    ws = torch.empty((16, H), dtype=torch.bfloat16, device="cuda")
+    _, outp = run_pre(d, workspace=ws, P=8)
+    got = synth.bits(outp)
+    ws_ref, out_ref = oracle.pre_attn(d)
+    ref = oracle.ulysses_pack(out_ref, 8)
+    mag = oracle.ulysses_pack(qkv_magnitude(out_ref), 8)
+    ok, rel, mx = bf16_tolerance_ok(got, ref, mag=mag)
+    _say(f"  P=8 relL2={rel:.2e} max|err|={mx:.3e}")
+    assert ok, (rel, mx)
+    idx = d["adaln_index"]
+    bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
+    assert np.all(bf16_val(got[:, bad]) == 0.0), "guarded rows must be zero in every destination"
 
 
 _W = {}

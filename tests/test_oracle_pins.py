@@ -528,3 +528,31 @@ def test_brute_force_mlp(M):
         assert np.abs(ordered_e4m3(o[k]) - ordered_e4m3(b[k])).max() <= 1 and np.mean(o[k] != b[k]) < 1e-3, k
     for k in ("a_scale", "y_scale"):
         assert np.array_equal(o[k], b[k]), k
+
+
+# --- Ulysses destination-major pack (bf16 pre-attention page: out [P, M, 56 // P, 3, 128]) ---
+
+@pytest.mark.parametrize("P", [1, 2, 4, 8])
+def test_ulysses_pack_index_definition(P):
+    """Element by element: packed[p, m, j, kind, d] is head p * (56 // P) + j of token m."""
+    g = np.random.default_rng(50 + P)
+    a = g.integers(0, 1 << 16, size=(3, 56, 3, 128), dtype=np.uint16)
+    packed = oracle.ulysses_pack(a, P)
+    assert packed.shape == (P, 3, 56 // P, 3, 128)
+    for p in range(P):
+        for m in range(3):
+            for j in range(56 // P):
+                for kind in range(3):
+                    assert np.array_equal(packed[p, m, j, kind], a[m, p * (56 // P) + j, kind])
+
+
+def test_ulysses_pack_degree_one_is_identity_and_blocks_partition_heads():
+    g = np.random.default_rng(60)
+    a = g.integers(0, 1 << 16, size=(5, 56, 3, 128), dtype=np.uint16)
+    assert np.array_equal(oracle.ulysses_pack(a, 1)[0], a)
+    for P in (2, 4, 8):
+        packed = oracle.ulysses_pack(a, P)
+        # the destinations' head blocks, in order, are exactly the 56 heads once each
+        assert np.array_equal(np.concatenate(list(packed), axis=1), a)
+    with pytest.raises(ValueError):
+        oracle.ulysses_pack(a, 3)
