@@ -806,14 +806,8 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         }
         // compute phase: MFMAs only
         __builtin_amdgcn_sched_barrier(0);
-#if DIT_PP_PRIO
-        __builtin_amdgcn_s_setprio(1);
-#endif
         fr.mma(acc);
         __builtin_amdgcn_sched_barrier(0);
-#if DIT_PP_PRIO
-        __builtin_amdgcn_s_setprio(0);
-#endif
         if (g0) {
             pp_barrier<0>();                 // G0: A rows of stage kt+1 landed
         } else {
