@@ -776,14 +776,18 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     };
     PPFrags<kFp8> fr;
 
-    // prologue: A of stage 0 (each wave its rows), B of stages 0 and 1 (G1)
+    // prologue: A of stage 0 (each wave its rows), B of stages 0 and 1 (G1).  Only stage 0 must
+    // have landed here; B of stage 1 is first read in phase 2, after G1's memory-phase barrier
+    // (whose vmcnt limit counts only younger loads).
     sf.a_rows(smem, 0, 0);
     if (!g0) {
         sf.b_rows(smem, 0, 0);
         sf.b_rows(smem, 1, ktiles > 1 ? 1 : 0);
+        pp_barrier<kPPBPieces>();
+        pp_barrier<63>();            // G1 starts one phase behind
+    } else {
+        pp_barrier<0>();
     }
-    pp_barrier<0>();
-    if (!g0) pp_barrier<63>();       // G1 starts one phase behind
     for (int kt = 0; kt < ktiles; ++kt) {
         const int s = kt & 1;
         // memory phase.  First this wave's A rows of stage kt+1 into the other slot: its
