@@ -31,16 +31,27 @@ template <int kCtrl>
 __device__ __forceinline__ float dpp_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
 }
-// (for moves whose source lane always exists, e.g. row rotations: the old value is unused)
+// (for moves whose source lane always exists, e.g. row rotations)
 template <int kCtrl>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, kCtrl, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kCtrl, 0xF, 0xF, true);
 }
 constexpr int kDppXor1 = 0xB1;         // quad_perm(1,0,3,2): lane i <- i ^ 1
 constexpr int kDppXor2 = 0x4E;         // quad_perm(2,3,0,1): lane i <- i ^ 2
 constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
 constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within each 16 lanes
 constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- (i + 8) mod 16
+
+// v_perm_b32 selectors on (src0, src1): low halves (src1.lo | src0.lo << 16) and high halves
+// (src1.hi | src0.hi << 16).
+constexpr uint32_t kPermLo = 0x05040100u;
+constexpr uint32_t kPermHi = 0x07060302u;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// a.lo b.lo + a.hi b.hi for two packed bf16 pairs (v_dot2_f32_bf16, fp32 result)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), 0.0f,
+                                           false);
+}
 
 // Sum over the 16 lanes of a DPP row, left in every lane of it.
 __device__ __forceinline__ float row16_sum(float x) {
@@ -128,11 +139,17 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
         if (kind < 2) {
             // per-head RMSNorm in fp32: bf16 squares are exact, the sum carries fp32 rounding
             // only, and u = bf16((v * r2) * w)
-            float ss = 0.f;
+            // two partial sums halve the dependent chain
+            float s0 = v[0] * v[0], s1 = v[1] * v[1];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
-            ss = row16_sum(ss);       // the 16 lanes of a (row, head) are one DPP row
-            const float r2 = rsqrtf(ss * (1.0f / kHeadDim) + qk_eps);
+            for (int e = 2; e < 8; e += 2) {
+                s0 = fmaf(v[e], v[e], s0);
+                s1 = fmaf(v[e + 1], v[e + 1], s1);
+            }
+            const float ss = row16_sum(s0 + s1);   // the 16 lanes of a (row, head) are one DPP row
+            // v_rsq_f32 directly: its argument is at least qk_eps, a normal float, where the
+            // library rsqrtf adds only a denormal-range rescaling around the same instruction
+            const float r2 = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + qk_eps);
             float u[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) u[e] = v[e] * r2 * nw[e];
@@ -144,17 +161,19 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
 #pragma unroll
             for (int e = 0; e < 4; ++e) pv[e] = dpp_u<kDppRor8>(up[e]) ^ sgn;
             if (q < 12) {
-                float uu[8], c[8], sn[8], w2[8];
-                unpack8(up, uu);
-                unpack8(cv[it], c);
-                unpack8(sv[it], sn);
-                unpack8(pv, w2);
-                // bf16 x bf16 products are exact in fp32, so each fma is one rounding of
-                // u c +/- w s, then one rounding to bf16
-                float r[8];
+                // o = u c + w s per element as one v_dot2 of the bf16 pairs (u, w) and (c, s):
+                // the two products are exact in fp32 and their sum is rounded once, as the
+                // fma form u c + (w s) is
+                u32x4 r;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) r[e] = fmaf(uu[e], c[e], w2[e] * sn[e]);
-                o = pack8(r);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t uw0 = __builtin_amdgcn_perm(pv[e], up[e], kPermLo);   // (u_2e, w_2e)
+                    const uint32_t uw1 = __builtin_amdgcn_perm(pv[e], up[e], kPermHi);   // (u_2e+1, w_2e+1)
+                    const uint32_t cs0 = __builtin_amdgcn_perm(sv[it][e], cv[it][e], kPermLo);
+                    const uint32_t cs1 = __builtin_amdgcn_perm(sv[it][e], cv[it][e], kPermHi);
+                    r[e] = pack_bf2(dot2_bf16(uw0, cs0), dot2_bf16(uw1, cs1));
+                }
+                o = r;
             } else {
                 o = up;
             }
