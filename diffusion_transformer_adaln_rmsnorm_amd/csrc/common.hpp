@@ -60,6 +60,39 @@ __device__ __forceinline__ float f64_to_f32_odd(double d) {
 __device__ __forceinline__ uint32_t f2bf_d(double d) { return f2bf(f64_to_f32_odd(d)); }
 __device__ __forceinline__ float rbf_d(double d) { return bf2f(f2bf_d(d)); }
 
+// p = RN32(v) with error e = v - p (exact): the fp32 value rounded to odd from v (truncate
+// toward zero, then force the last bit to 1 when inexact).  fp32 keeps 24 >= 8 + 2 significant
+// bits, so the RNE to bf16 that follows equals one rounding of v.  p == 0 only when v rounds
+// to zero in bf16 anyway.
+__device__ __forceinline__ float odd32(float p, float e) {
+    uint32_t u = __float_as_uint(p);
+    const bool inexact = (e != 0.f) & (p != 0.f);
+    const bool toward_zero = ((__float_as_uint(e) ^ u) & 0x80000000u) != 0u;   // |p| > |v|
+    u -= (inexact && toward_zero) ? 1u : 0u;
+    u |= inexact ? 1u : 0u;
+    return __uint_as_float(u);
+}
+
+// (a * b) * c of three fp32 values, rounded to odd into fp32 (then one RNE to bf16 rounds the
+// product once).  a b = p1 + e1 and p1 c = p2 + e2 exactly (fma error terms), so the product
+// is p2 + (e2 + e1 c); fma(e1, c, e2) gives that tail to within 2^-24 of itself, enough for
+// its sign and zero-ness, which are all the rounding to odd uses (short of a tail that
+// cancels to within 2^-24 of itself while p2 also sits exactly on a bf16 midpoint).
+__device__ __forceinline__ float mul3_odd32(float a, float b, float c) {
+    const float p1 = a * b;
+    const float e1 = fmaf(a, b, -p1);
+    const float p2 = p1 * c;
+    const float e2 = fmaf(p1, c, -p2);
+    return odd32(p2, fmaf(e1, c, e2));
+}
+
+// silu(t) = t / (1 + e^-t) from the hardware exp2 and reciprocal (each ~1 ulp); e^-t -> inf
+// gives 0 and e^-t -> 0 gives t, the limits
+__device__ __forceinline__ float silu_fast(float t) {
+    const float ex = __builtin_amdgcn_exp2f(-t * 1.4426950408889634f);
+    return t * __builtin_amdgcn_rcpf(1.0f + ex);
+}
+
 // unpack 8 bf16 (one 16-byte vector) to floats
 __device__ __forceinline__ void unpack8(const u32x4& v, float (&f)[8]) {
 #pragma unroll

@@ -854,7 +854,7 @@ __device__ __forceinline__ float acc_read(float a) {
 }
 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS
-// (row pitch kEpiPitch); with scales the products are formed in double and rounded once.
+// (row pitch kEpiPitch); with scales the product of the three fp32 values is rounded once.
 // Accumulator layout of the 32x32 MFMA: lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4
 // and column l%32 of its block.  rowscale and colscale are both given or both null (factor 1).
 // Must follow a barrier that ends all LDS reads of the main loop.
@@ -900,9 +900,8 @@ __device__ __forceinline__ void stage_tile_bf16(const f32x16 (&acc)[4][kNB], uin
                 const float a0 = acc_read(acc[i][j][r]), a1 = acc_read(acc[i][j][r + 1]);
                 uint32_t b;
                 if (rowscale) {
-                    // (acc * s_row) * s_col in double, one rounding to bf16
-                    b = f2bf_d((double)a0 * (double)rs[r] * (double)cscale[j]) |
-                        (f2bf_d((double)a1 * (double)rs[r + 1] * (double)cscale[j]) << 16);
+                    // (acc * s_row) * s_col, one rounding to bf16
+                    b = pack_bf2(mul3_odd32(a0, rs[r], cscale[j]), mul3_odd32(a1, rs[r + 1], cscale[j]));
                 } else {
                     b = pack_bf2(a0, a1);
                 }

@@ -48,7 +48,7 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
         float amax = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float sl = rbf(hg[e] / (1.0f + expf(-hg[e])));
+            const float sl = rbf(silu_fast(hg[e]));
             yv[e] = rbf(sl * hu[e]);
             amax = fmaxf(amax, fabsf(yv[e]));
         }

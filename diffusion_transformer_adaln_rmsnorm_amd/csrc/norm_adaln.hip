@@ -43,19 +43,6 @@ __device__ __forceinline__ float load_row_rms(const uint16_t* xr, int lane, floa
     return 1.0f / sqrtf(ss / (float)kHidden + eps);
 }
 
-// p = RN32(v) with error e = v - p (exact): the fp32 value rounded to odd from v (truncate
-// toward zero, then force the last bit to 1 when inexact).  fp32 keeps 24 >= 8 + 2 significant
-// bits, so the RNE to bf16 that follows equals one rounding of v.  p == 0 only when v rounds
-// to zero in bf16 anyway.
-__device__ __forceinline__ float odd32(float p, float e) {
-    uint32_t u = __float_as_uint(p);
-    const bool inexact = (e != 0.f) & (p != 0.f);
-    const bool toward_zero = ((__float_as_uint(e) ^ u) & 0x80000000u) != 0u;   // |p| > |v|
-    u -= (inexact && toward_zero) ? 1u : 0u;
-    u |= inexact ? 1u : 0u;
-    return __uint_as_float(u);
-}
-
 // a = bf16(shift + n * bf16(1 + scale)),  n = bf16(x * r * w), for one 8-wide chunk, each
 // bf16(...) one rounding of the exact value, in fp32 with error-free transforms:
 //   x w is exact (two 8-bit significands); (x w) r = p + e with e = fma(x w, r, -p);
