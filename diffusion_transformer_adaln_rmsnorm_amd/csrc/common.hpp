@@ -86,6 +86,14 @@ __device__ __forceinline__ float mul3_odd32(float a, float b, float c) {
     return odd32(p2, fmaf(e1, c, e2));
 }
 
+// a / s rounded to nearest, given y = RN(1 / s) (one division per row instead of one per
+// element): q0 = RN(a y), the remainder a - q0 s by fma, and one fma correction (Markstein's
+// final step for a correctly rounded reciprocal).
+__device__ __forceinline__ float div_by(float a, float s, float y) {
+    const float q0 = a * y;
+    return fmaf(fmaf(-q0, s, a), y, q0);
+}
+
 // silu(t) = t / (1 + e^-t) from the hardware exp2 and reciprocal (each ~1 ulp); e^-t -> inf
 // gives 0 and e^-t -> 0 gives t, the limits
 __device__ __forceinline__ float silu_fast(float t) {
