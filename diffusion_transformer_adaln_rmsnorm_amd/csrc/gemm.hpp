@@ -640,29 +640,35 @@ __device__ __forceinline__ void mainloop_interleaved(const uint8_t* __restrict__
 //     landed (wave c read them a phase earlier).
 // Each group waits for its A rows of stage s+1 before the barrier that ends its compute phase
 // for s, and G1 for the B rows of stage s+1 before the barrier that ends its memory phase for
-// s; those are the last barriers before the first reads.  Loads for stages past the end
-// re-load a stage whose slot has no reader left, so every phase issues the same loads and
-// the vmcnt limits hold throughout.
+// s; those are the last barriers before the first reads.  Loads for stages past the end go
+// through a zero-length descriptor (no memory read, zeros into a slot with no reader left),
+// so every phase issues the same loads and the vmcnt limits hold throughout.
 constexpr int kPPAPieces = 32 / kRowsPerPiece;      // A: 32 rows per wave
 constexpr int kPPBPieces = 64 / kRowsPerPiece;      // B: 64 rows per G1 wave
 
 struct PPFill {
     __amdgpu_buffer_rsrc_t ra, rb;
+    __amdgpu_buffer_rsrc_t rnull;   // zero records: every load through it is out of range
     uint32_t va[kPPAPieces];  // A: row + chunk offset of piece j (per lane; bounds-checked)
     uint32_t vb[kVPat];       // B: row-in-piece + chunk offset, by piece parity (per lane)
     uint32_t sb[kPPBPieces];  // B: offset of piece j's first row (uniform)
     uint32_t lds_a, lds_b;    // this wave's rows within an A slot / a B slot
-    __device__ __forceinline__ void a_rows(uint8_t* smem, int slot, int kt) const {
+    // Stage kt of this wave's rows into `slot`.  A load past the last stage (live false) goes
+    // through rnull: it reads no memory and writes zeros into a slot that has no reader left,
+    // but still counts in vmcnt, so every phase issues the same number of loads.
+    __device__ __forceinline__ void a_rows(uint8_t* smem, int slot, int kt, bool live) const {
         lds_u8* S = (lds_u8*)smem + slot * kOpBytes + lds_a;
+        const __amdgpu_buffer_rsrc_t r = live ? ra : rnull;
 #pragma unroll
         for (int j = 0; j < kPPAPieces; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, S + j * 1024, 16, (int)va[j], kt * kRowB, 0, kLoadAux);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + j * 1024, 16, (int)va[j], kt * kRowB, 0, kLoadAux);
     }
-    __device__ __forceinline__ void b_rows(uint8_t* smem, int slot, int kt) const {
+    __device__ __forceinline__ void b_rows(uint8_t* smem, int slot, int kt, bool live) const {
         lds_u8* S = (lds_u8*)smem + 2 * kOpBytes + slot * kOpBytes + lds_b;
+        const __amdgpu_buffer_rsrc_t r = live ? rb : rnull;
 #pragma unroll
         for (int j = 0; j < kPPBPieces; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + j * 1024, 16, (int)vb[j % kVPat], (int)sb[j] + kt * kRowB,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + j * 1024, 16, (int)vb[j % kVPat], (int)sb[j] + kt * kRowB,
                                                      0, kLoadAux);
     }
 };
@@ -745,6 +751,7 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
     sf.ra = make_rsrc(A + m0 * lda, (uint32_t)(arows * lda));
     sf.rb = make_rsrc(B + nb0 * ldb, (uint32_t)((nb1 - nb0 + 128) * ldb));
+    sf.rnull = make_rsrc(B, 0u);
 #pragma unroll
     for (int j = 0; j < kPPAPieces; ++j) {
         const int row = 32 * wave + j * kRowsPerPiece + lane / kSlots;
@@ -779,10 +786,10 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     // prologue: A of stage 0 (each wave its rows), B of stages 0 and 1 (G1).  Only stage 0 must
     // have landed here; B of stage 1 is first read in phase 2, after G1's memory-phase barrier
     // (whose vmcnt limit counts only younger loads).
-    sf.a_rows(smem, 0, 0);
+    sf.a_rows(smem, 0, 0, true);
     if (!g0) {
-        sf.b_rows(smem, 0, 0);
-        sf.b_rows(smem, 1, ktiles > 1 ? 1 : 0);
+        sf.b_rows(smem, 0, 0, true);
+        sf.b_rows(smem, 1, 1, ktiles > 1);
         pp_barrier<kPPBPieces>();
         pp_barrier<63>();            // G1 starts one phase behind
     } else {
@@ -791,10 +798,9 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     for (int kt = 0; kt < ktiles; ++kt) {
         const int s = kt & 1;
         // memory phase.  First this wave's A rows of stage kt+1 into the other slot: its
-        // group read them (stage kt-1) in its last memory phase.  Past the end, the stage a
-        // slot would be refilled with is replaced by kt (no reader is left for that slot).
+        // group read them (stage kt-1) in its last memory phase.
         __builtin_amdgcn_sched_barrier(0);
-        sf.a_rows(smem, s ^ 1, kt + 1 < ktiles ? kt + 1 : kt);
+        sf.a_rows(smem, s ^ 1, kt + 1, kt + 1 < ktiles);
         __builtin_amdgcn_sched_barrier(0);
         fr.read(slot(kt), fa);
         __builtin_amdgcn_sched_barrier(0);
@@ -804,7 +810,7 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
             // B rows 64c.. of this slot, stage kt+2: the partner G0 wave read them in the
             // last phase, this wave's reads land here
             __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));    // lgkmcnt(0)
-            sf.b_rows(smem, s, kt + 2 < ktiles ? kt + 2 : kt);
+            sf.b_rows(smem, s, kt + 2, kt + 2 < ktiles);
             // landed: B of stage kt+1 (issued before the A rows and B rows of this phase)
             pp_barrier<kPPAPieces + kPPBPieces>();
         }
