@@ -62,6 +62,58 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Q/K output of one (row, head) for the 16 lanes of a DPP row: vp holds this lane's 8 dims
+// (chunk q) of the head as bf16, nw its 8 norm weights; cv / sv the cos and sin of frequencies
+// 8 (q mod 6) .. + 7 for the row's position (q < 12).  All 16 lanes of the row must be active.
+__device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const float (&nw)[8], float qk_eps, int q,
+                                              const u32x4& cv, const u32x4& sv) {
+    float v[8];
+    unpack8(vp, v);
+    // per-head RMSNorm in fp32: bf16 squares are exact, the sum carries fp32 rounding only,
+    // and u = bf16((v * r2) * w); two partial sums halve the dependent chain
+    float s0 = v[0] * v[0], s1 = v[1] * v[1];
+#pragma unroll
+    for (int e = 2; e < 8; e += 2) {
+        s0 = fmaf(v[e], v[e], s0);
+        s1 = fmaf(v[e + 1], v[e + 1], s1);
+    }
+    const float ss = row16_sum(s0 + s1);   // the 16 lanes of a (row, head) are one DPP row
+    // v_rsq_f32 directly: its argument is at least qk_eps, a normal float, where the library
+    // rsqrtf adds only a denormal-range rescaling around the same instruction
+    const float r2 = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + qk_eps);
+    float u[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) u[e] = v[e] * r2 * nw[e];
+    const u32x4 up = pack8(u);          // the bf16 u, packed
+    // RoPE partner chunk q + 6 (q < 6) or q - 6 (6 <= q < 12), 8 lanes away; its sign flipped
+    // for the first half, so both halves take o = u c + w s:
+    // o_j = u_j c - u_{j+48} s, o_{j+48} = u_{j+48} c + u_j s
+    const uint32_t sgn = q < 6 ? 0x80008000u : 0u;   // negates both bf16 halves of a word
+    u32x4 pv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pv[e] = dpp_u<kDppRor8>(up[e]) ^ sgn;
+    if (q >= 12) return up;
+    // o = u c + w s per element as one v_dot2 of the bf16 pairs (u, w) and (c, s): the two
+    // products are exact in fp32 and their sum is rounded once, as the fma form u c + (w s) is
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t uw0 = __builtin_amdgcn_perm(pv[e], up[e], kPermLo);   // (u_2e, w_2e)
+        const uint32_t uw1 = __builtin_amdgcn_perm(pv[e], up[e], kPermHi);   // (u_2e+1, w_2e+1)
+        const uint32_t cs0 = __builtin_amdgcn_perm(sv[e], cv[e], kPermLo);
+        const uint32_t cs1 = __builtin_amdgcn_perm(sv[e], cv[e], kPermHi);
+        r[e] = pack_bf2(dot2_bf16(uw0, cs0), dot2_bf16(uw1, cs1));
+    }
+    return r;
+}
+
+// 8-dim chunk of a head held by lane li of its DPP row (the partner chunk q +/- 6 sits at
+// lane li ^ 8): lanes 0-5 hold chunks 0-5, lanes 8-13 chunks 6-11, lanes 6, 7, 14, 15 the
+// pass-through chunks 12-15.
+__device__ __forceinline__ int chunk_of_lane(int li) {
+    return li < 6 ? li : (li < 8 ? 12 + (li - 6) : (li < 14 ? li - 2 : li));
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __restrict__ W,
                 const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
@@ -72,14 +124,14 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
     const int n0 = tn * kBN;
-    f32x16 acc[4][kNB];
+    Acc<false> acc;
     mainloop<false>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M, reinterpret_cast<const uint8_t*>(W),
                     kHidden * 2, n0, n0 + 128, kHidden * 2 / kRowB, smem, acc);
 
     const int t = threadIdx.x;
     const int li = t & 15;              // lane within the (row, head) group
     // 8-dim chunk of the head held by this lane (partner chunk q +/- 6 sits at lane li ^ 8)
-    const int q = li < 6 ? li : (li < 8 ? 12 + (li - 6) : (li < 14 ? li - 2 : li));
+    const int q = chunk_of_lane(li);
     const int hh = (t >> 4) & 1;        // which of the tile's two heads
     const int rsub = t >> 5;            // 0..kThreads/32-1
     const int kind = n0 / kAttnWidth;   // 0 q, 1 k, 2 v
@@ -117,7 +169,6 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
 
     float nw[8];
     unpack8(nwv, nw);
-    const uint32_t sgn = q < 6 ? 0x80008000u : 0u;   // negates both bf16 halves of a word
     u32x4 cv[kIters], sv[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
@@ -133,53 +184,8 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     for (int it = 0; it < kIters; ++it) {
         const int row = it * kRowsPerPass + rsub;
         const u32x4 vp = epi_ld(smem, row, hh * 128 + d0);
-        float v[8];
-        unpack8(vp, v);
-        u32x4 o;
-        if (kind < 2) {
-            // per-head RMSNorm in fp32: bf16 squares are exact, the sum carries fp32 rounding
-            // only, and u = bf16((v * r2) * w)
-            // two partial sums halve the dependent chain
-            float s0 = v[0] * v[0], s1 = v[1] * v[1];
-#pragma unroll
-            for (int e = 2; e < 8; e += 2) {
-                s0 = fmaf(v[e], v[e], s0);
-                s1 = fmaf(v[e + 1], v[e + 1], s1);
-            }
-            const float ss = row16_sum(s0 + s1);   // the 16 lanes of a (row, head) are one DPP row
-            // v_rsq_f32 directly: its argument is at least qk_eps, a normal float, where the
-            // library rsqrtf adds only a denormal-range rescaling around the same instruction
-            const float r2 = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + qk_eps);
-            float u[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) u[e] = v[e] * r2 * nw[e];
-            const u32x4 up = pack8(u);          // the bf16 u, packed
-            // RoPE partner chunk q + 6 (q < 6) or q - 6 (6 <= q < 12), 8 lanes away; its sign
-            // flipped for the first half, so both halves take o = u c + w s:
-            // o_j = u_j c - u_{j+48} s, o_{j+48} = u_{j+48} c + u_j s
-            u32x4 pv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) pv[e] = dpp_u<kDppRor8>(up[e]) ^ sgn;
-            if (q < 12) {
-                // o = u c + w s per element as one v_dot2 of the bf16 pairs (u, w) and (c, s):
-                // the two products are exact in fp32 and their sum is rounded once, as the
-                // fma form u c + (w s) is
-                u32x4 r;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t uw0 = __builtin_amdgcn_perm(pv[e], up[e], kPermLo);   // (u_2e, w_2e)
-                    const uint32_t uw1 = __builtin_amdgcn_perm(pv[e], up[e], kPermHi);   // (u_2e+1, w_2e+1)
-                    const uint32_t cs0 = __builtin_amdgcn_perm(sv[it][e], cv[it][e], kPermLo);
-                    const uint32_t cs1 = __builtin_amdgcn_perm(sv[it][e], cv[it][e], kPermHi);
-                    r[e] = pack_bf2(dot2_bf16(uw0, cs0), dot2_bf16(uw1, cs1));
-                }
-                o = r;
-            } else {
-                o = up;
-            }
-        } else {
-            o = vp;
-        }
+        u32x4 o = vp;
+        if (kind < 2) o = qk_norm_rope(vp, nw, qk_eps, q, cv[it], sv[it]);
         if (hpd == kHeads) {
             // one destination: rows past M fall outside rout and are dropped
             buf_st16(rout, (uint32_t)((((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0) * 2, o);
