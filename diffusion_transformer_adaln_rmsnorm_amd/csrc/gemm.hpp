@@ -4,12 +4,14 @@
 // [M, K], weights [N, K]), FP32 accumulation.
 //
 // Workgroup: 8 waves, two per SIMD, and one 256 x 256 output tile; each wave owns a 128 x 64
-// wave tile (128 FP32 accumulators per lane, so a wave fits in 256 registers).
-//   bf16: 8 x 4 blocks of v_mfma_f32_16x16x32_bf16.  Under a full-chip load the shader clock
-//         is set by power, and for the same MACs the 16x16x32 form moves fewer register bytes
-//         than 32x32x16 (operands plus accumulator read and write: 0.5 against 0.625 bytes
-//         per MAC); a register-only MFMA loop sustains about 12% more FLOP/s with it.
-//   e4m3: 4 x 2 blocks of v_mfma_scale_f32_32x32x64_f8f6f4 (unit scales).
+// wave tile of 8 x 4 blocks of 16 x 16 (128 FP32 accumulators per lane, so a wave fits in 256
+// registers):
+//   bf16: v_mfma_f32_16x16x32_bf16, two k-steps per stage;
+//   e4m3: v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), one k-step per stage.
+// Under a full-chip load the shader clock is set by power.  For the same MACs the 16x16 forms
+// move fewer register bytes than the 32x32 ones (bf16: operands plus accumulator read and
+// write, 0.5 against 0.625 bytes per MAC), and a register-only MFMA loop sustains about 12%
+// (bf16) and 7% (e4m3) more FLOP/s with them.
 // A and B fragments take their k values from the same (lane group, byte) positions, so the
 // product is the same whatever order the instruction assigns to k inside a fragment.
 //
@@ -32,7 +34,6 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kWN = 4;                          // waves across n (two across m)
 constexpr int kWaveN = kBN / kWN;               // wave tile: 128 rows x 64 columns
-constexpr int kNB = kWaveN / 32;                // 32-column blocks per wave (e4m3)
 constexpr int kOpBytes = 256 * kRowB;           // one operand of one stage (an LDS slot)
 constexpr int kMainBytes = 4 * kOpBytes;        // two slots per operand
 constexpr int kEpiPitch = kBN * 2 + 16;         // bf16 epilogue tile, padded row pitch (bytes)
@@ -102,40 +103,29 @@ struct Stage {
     const uint8_t* b;
 };
 
-// Accumulators of one wave: 16x16 blocks for bf16, 32x32 blocks for e4m3.
-template <bool kFp8>
-struct Acc;
-template <>
-struct Acc<false> {
-    static constexpr int MB = 8, NB = 4;        // 16-row x 16-column blocks
+// Accumulators of one wave: 8 x 4 blocks of 16 x 16.  Lane l, register r of a block holds
+// row 4 (l / 16) + r and column l % 16.
+struct Acc {
+    static constexpr int MB = 8, NB = 4;
     f32x4 v[MB][NB];
 };
-template <>
-struct Acc<true> {
-    static constexpr int MB = 4, NB = kNB;      // 32-row x 32-column blocks
-    f32x16 v[MB][NB];
-};
 
-// Per-lane LDS offsets of the fragment reads (relative to an operand slot), one per k-step.
-//   bf16, 16x16x32: lane l reads row l % 16 of each 16-row block and chunk 4 ks + l / 16
-//         (8 bf16 of k); two k-steps of 32 per stage.
-//   e4m3, 32x32x64: lane l reads row l % 32 of each 32-row block and chunks
-//         4 ks + 2 (l / 32) + {0, 1} (32 bytes of k); two k-steps of 64 per stage.
+// Per-lane LDS offsets of the fragment reads (relative to an operand slot).  Lane l reads row
+// l % 16 of each 16-row block; in lane group g = l / 16 it reads
+//   bf16, 16x16x32:  chunk 4 ks + g (8 bf16 of k) for k-steps ks = 0, 1;
+//   e4m3, 16x16x128: chunks 2 g and 2 g + 1 (32 bytes of k), one k-step.
 // swz has period 16 rows, so one offset serves every block of a wave (blocks are immediates).
-template <bool kFp8>
+constexpr int kBlk = 16 * kRowB;                // bytes between 16-row blocks
 struct FragAddr {
-    static constexpr int KS = 2;
-    static constexpr int kBlkRows = kFp8 ? 32 : 16;
-    static constexpr int kBlk = kBlkRows * kRowB;   // bytes between blocks
-    uint32_t a[kFp8 ? 2 * KS : KS], b[kFp8 ? 2 * KS : KS];
-    __device__ __forceinline__ void init() {
+    uint32_t a[2], b[2];
+    __device__ __forceinline__ void init(bool fp8) {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / kWN, wn = wave % kWN;
-        const int r = lane % kBlkRows, g = lane / kBlkRows;
+        const int r = lane % 16, g = lane / 16;
         const int sw = swz(r);
 #pragma unroll
-        for (int q = 0; q < (kFp8 ? 2 * KS : KS); ++q) {
-            const int c = kFp8 ? 4 * (q >> 1) + 2 * g + (q & 1) : 4 * q + g;
+        for (int q = 0; q < 2; ++q) {
+            const int c = fp8 ? 2 * g + q : 4 * q + g;
             a[q] = (uint32_t)((wm * 128 + r) * kRowB + ((c ^ sw) << 4));
             b[q] = (uint32_t)((wn * kWaveN + r) * kRowB + ((c ^ sw) << 4));
         }
@@ -216,21 +206,20 @@ template <bool kFp8>
 struct PPFrags;
 template <>
 struct PPFrags<false> {
-    using FA = FragAddr<false>;
-    static constexpr int KS = FA::KS, MB = Acc<false>::MB, NB = Acc<false>::NB;
-    bf16x8 a[KS][MB], b[KS][NB];
-    __device__ __forceinline__ void read(const Stage& st, const FA& fa) {
+    static constexpr int MB = Acc::MB, NB = Acc::NB;
+    bf16x8 a[2][MB], b[2][NB];
+    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) a[ks][i] = lds_bf16x8(st.a, fa.a[ks] + i * FA::kBlk);
+            for (int i = 0; i < MB; ++i) a[ks][i] = lds_bf16x8(st.a, fa.a[ks] + i * kBlk);
 #pragma unroll
-            for (int j = 0; j < NB; ++j) b[ks][j] = lds_bf16x8(st.b, fa.b[ks] + j * FA::kBlk);
+            for (int j = 0; j < NB; ++j) b[ks][j] = lds_bf16x8(st.b, fa.b[ks] + j * kBlk);
         }
     }
-    __device__ __forceinline__ void mma(Acc<false>& acc) const {
+    __device__ __forceinline__ void mma(Acc& acc) const {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -240,29 +229,20 @@ struct PPFrags<false> {
 };
 template <>
 struct PPFrags<true> {
-    using FA = FragAddr<true>;
-    static constexpr int KS = FA::KS, MB = Acc<true>::MB, NB = Acc<true>::NB;
-    i32x8 a[KS][MB], b[KS][NB];
-    __device__ __forceinline__ void read(const Stage& st, const FA& fa) {
+    static constexpr int MB = Acc::MB, NB = Acc::NB;
+    i32x8 a[MB], b[NB];
+    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int i = 0; i < MB; ++i) a[i] = lds_i32x8(st.a, fa.a[0] + i * kBlk, fa.a[1] + i * kBlk);
 #pragma unroll
-            for (int i = 0; i < MB; ++i)
-                a[ks][i] = lds_i32x8(st.a, fa.a[2 * ks] + i * FA::kBlk, fa.a[2 * ks + 1] + i * FA::kBlk);
+        for (int j = 0; j < NB; ++j) b[j] = lds_i32x8(st.b, fa.b[0] + j * kBlk, fa.b[1] + j * kBlk);
+    }
+    __device__ __forceinline__ void mma(Acc& acc) const {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
             for (int j = 0; j < NB; ++j)
-                b[ks][j] = lds_i32x8(st.b, fa.b[2 * ks] + j * FA::kBlk, fa.b[2 * ks + 1] + j * FA::kBlk);
-        }
-    }
-    __device__ __forceinline__ void mma(Acc<true>& acc) const {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    acc.v[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[ks][i], b[ks][j], acc.v[i][j], 0,
-                                                                                   0, 0, 0, 0, 0);
+                acc.v[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc.v[i][j], 0, 0, 0, 0, 0, 0);
     }
 };
 
@@ -280,7 +260,7 @@ __device__ __forceinline__ void pp_barrier() {
 template <bool kFp8>
 __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                             const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                            int ktiles, uint8_t* smem, Acc<kFp8>& acc) {
+                                            int ktiles, uint8_t* smem, Acc& acc) {
     static_assert(kWaves == 8 && kRowB == 128, "ping-pong layout");
     static_assert(4 * kOpBytes <= kSmemBytes, "two slots per operand");
     const int lane = threadIdx.x & 63;
@@ -308,12 +288,12 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     }
     sf.lds_a = (uint32_t)(32 * wave * kRowB);
     sf.lds_b = (uint32_t)(64 * c * kRowB);
-    FragAddr<kFp8> fa;
-    fa.init();
+    FragAddr fa;
+    fa.init(kFp8);
 #pragma unroll
-    for (int i = 0; i < Acc<kFp8>::MB; ++i)
+    for (int i = 0; i < Acc::MB; ++i)
 #pragma unroll
-        for (int j = 0; j < Acc<kFp8>::NB; ++j) acc.v[i][j] = 0.f;
+        for (int j = 0; j < Acc::NB; ++j) acc.v[i][j] = 0.f;
 
     auto slot = [&](int kt) -> Stage {
         const int s = kt & 1;
@@ -372,59 +352,50 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
 template <bool kFp8>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                         int ktiles, uint8_t* smem, Acc<kFp8>& acc) {
+                                         int ktiles, uint8_t* smem, Acc& acc) {
     mainloop_pp<kFp8>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc);
 }
 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS
 // (row pitch kEpiPitch); with scales the product of the three fp32 values is rounded once.
-// rowscale and colscale are both given or both null (factor 1).  Accumulator layouts, lane l,
-// register r of a block:
-//   16x16: row 4 (l / 16) + r, column l % 16;
-//   32x32: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
-// Registers r and r + 1 (r even) hold rows R and R + 1 of one column in both.  Must follow a
-// barrier that ends all LDS reads of the main loop.
-template <bool kFp8>
-__device__ __forceinline__ void stage_tile_bf16(const Acc<kFp8>& acc, uint8_t* smem, const float* rowscale,
-                                                int64_t m0, int64_t M, const float* colscale_lo,
-                                                const float* colscale_hi) {
-    constexpr int MB = Acc<kFp8>::MB, NB = Acc<kFp8>::NB;
-    constexpr int BR = kFp8 ? 32 : 16;              // block rows (= block columns)
-    constexpr int NR = kFp8 ? 16 : 4;               // registers per block
+// rowscale and colscale are both given or both null (factor 1).  Registers r and r + 1 of a
+// block hold rows R and R + 1 of one column.  Must follow a barrier that ends all LDS reads
+// of the main loop.
+__device__ __forceinline__ void stage_tile_bf16(const Acc& acc, uint8_t* smem, const float* rowscale, int64_t m0,
+                                                int64_t M, const float* colscale_lo, const float* colscale_hi) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / kWN, wn = wave % kWN;
-    const int col_in = lane % BR;
-    auto row_in = [&](int r) { return kFp8 ? (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3) : (lane >> 4) * 4 + r; };
-    float cscale[NB];
+    const int col_in = lane % 16, row_in = (lane / 16) * 4;
+    float cscale[Acc::NB];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) cscale[j] = 1.f;
+    for (int j = 0; j < Acc::NB; ++j) cscale[j] = 1.f;
     if (colscale_lo) {
         // local columns [0,128) come from colscale_lo, [128,256) from colscale_hi
         const int c0 = wn * kWaveN;
         const float* cs = c0 < 128 ? colscale_lo + c0 : colscale_hi + (c0 - 128);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) cscale[j] = cs[j * BR + col_in];
+        for (int j = 0; j < Acc::NB; ++j) cscale[j] = cs[j * 16 + col_in];
     }
     // row scales of block row i + 1 are loaded while block row i converts
-    auto load_rs = [&](int i, float (&rs)[NR]) {
+    auto load_rs = [&](int i, float (&rs)[4]) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            int64_t gm = m0 + wm * 128 + i * BR + row_in(r);
+        for (int r = 0; r < 4; ++r) {
+            int64_t gm = m0 + wm * 128 + i * 16 + row_in + r;
             gm = gm < M ? gm : M - 1;
             rs[r] = rowscale[gm];
         }
     };
-    float rs[NR], rs_nx[NR];
+    float rs[4], rs_nx[4];
     if (rowscale) load_rs(0, rs);
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-        if (rowscale && i + 1 < MB) load_rs(i + 1, rs_nx);
+    for (int i = 0; i < Acc::MB; ++i) {
+        if (rowscale && i + 1 < Acc::MB) load_rs(i + 1, rs_nx);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int col = wn * kWaveN + j * BR + col_in;
+        for (int j = 0; j < Acc::NB; ++j) {
+            const int col = wn * kWaveN + j * 16 + col_in;
 #pragma unroll
-            for (int r = 0; r < NR; r += 2) {
-                const int row = wm * 128 + i * BR + row_in(r);
+            for (int r = 0; r < 4; r += 2) {
+                const int row = wm * 128 + i * 16 + row_in + r;
                 const float a0 = acc.v[i][j][r], a1 = acc.v[i][j][r + 1];
                 uint32_t b;
                 if (rowscale) {
@@ -439,7 +410,7 @@ __device__ __forceinline__ void stage_tile_bf16(const Acc<kFp8>& acc, uint8_t* s
         }
         if (rowscale) {
 #pragma unroll
-            for (int r = 0; r < NR; ++r) rs[r] = rs_nx[r];
+            for (int r = 0; r < 4; ++r) rs[r] = rs_nx[r];
         }
     }
 }
