@@ -111,21 +111,25 @@ struct Acc {
 };
 
 // Per-lane LDS offsets of the fragment reads (relative to an operand slot).  Lane l reads row
-// l % 16 of each 16-row block; in lane group g = l / 16 it reads
-//   bf16, 16x16x32:  chunk 4 ks + g (8 bf16 of k) for k-steps ks = 0, 1;
-//   e4m3, 16x16x128: chunks 2 g and 2 g + 1 (32 bytes of k), one k-step.
+// l % 16 of each 16-row block and, in lane group g = l / 16, chunks g and g + 4 of it:
+//   bf16, 16x16x32:  chunk 4 q + g (8 bf16 of k) is the fragment of k-step q = 0, 1;
+//   e4m3, 16x16x128: chunks g and g + 4 together (32 bytes of k) are the fragment of the one
+//         k-step.  Any assignment of a stage's 128 bytes to (lane group, byte) serves, as long
+//         as A and B use the same one; this one reads like the bf16 path, and in both the 16
+//         lanes of a group hit 16 distinct bank groups (contiguous chunks 2 g, 2 g + 1 would
+//         put two lane groups of a read on the same banks).
 // swz has period 16 rows, so one offset serves every block of a wave (blocks are immediates).
 constexpr int kBlk = 16 * kRowB;                // bytes between 16-row blocks
 struct FragAddr {
     uint32_t a[2], b[2];
-    __device__ __forceinline__ void init(bool fp8) {
+    __device__ __forceinline__ void init() {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / kWN, wn = wave % kWN;
         const int r = lane % 16, g = lane / 16;
         const int sw = swz(r);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            const int c = fp8 ? 2 * g + q : 4 * q + g;
+            const int c = 4 * q + g;
             a[q] = (uint32_t)((wm * 128 + r) * kRowB + ((c ^ sw) << 4));
             b[q] = (uint32_t)((wn * kWaveN + r) * kRowB + ((c ^ sw) << 4));
         }
@@ -289,7 +293,7 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     sf.lds_a = (uint32_t)(32 * wave * kRowB);
     sf.lds_b = (uint32_t)(64 * c * kRowB);
     FragAddr fa;
-    fa.init(kFp8);
+    fa.init();
 #pragma unroll
     for (int i = 0; i < Acc::MB; ++i)
 #pragma unroll
@@ -313,6 +317,9 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     } else {
         pp_barrier<0>();
     }
+    // Not unrolled or peeled: in a peeled copy the scheduler reorders the MFMAs of the two
+    // k-steps and the register allocator then spills accumulators to scratch.
+#pragma nounroll
     for (int kt = 0; kt < ktiles; ++kt) {
         const int s = kt & 1;
         // memory phase.  First this wave's A rows of stage kt+1 into the other slot: its
