@@ -366,13 +366,19 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS
 // (row pitch kEpiPitch); with scales the product of the three fp32 values is rounded once.
 // rowscale and colscale are both given or both null (factor 1).  Registers r and r + 1 of a
-// block hold rows R and R + 1 of one column.  Must follow a barrier that ends all LDS reads
-// of the main loop.
+// block hold rows R and R + 1 of one column c = l % 16, packed as one bf16 pair; lanes l and
+// l ^ 1 (columns c and c ^ 1) swap halves with one DPP move, so that the even lane holds row R,
+// columns c, c + 1 and the odd lane row R + 1, columns c - 1, c: one 32-bit LDS write each.
+// Must follow a barrier that ends all LDS reads of the main loop.
 __device__ __forceinline__ void stage_tile_bf16(const Acc& acc, uint8_t* smem, const float* rowscale, int64_t m0,
                                                 int64_t M, const float* colscale_lo, const float* colscale_hi) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / kWN, wn = wave % kWN;
     const int col_in = lane % 16, row_in = (lane / 16) * 4;
+    const int odd = lane & 1;
+    // v_perm selector on (neighbour pair, own pair): even lane (own.lo, nb.lo), odd lane
+    // (nb.hi, own.hi)
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
     float cscale[Acc::NB];
 #pragma unroll
     for (int j = 0; j < Acc::NB; ++j) cscale[j] = 1.f;
@@ -399,10 +405,10 @@ __device__ __forceinline__ void stage_tile_bf16(const Acc& acc, uint8_t* smem, c
         if (rowscale && i + 1 < Acc::MB) load_rs(i + 1, rs_nx);
 #pragma unroll
         for (int j = 0; j < Acc::NB; ++j) {
-            const int col = wn * kWaveN + j * 16 + col_in;
+            const int col = wn * kWaveN + j * 16 + col_in - odd;
 #pragma unroll
             for (int r = 0; r < 4; r += 2) {
-                const int row = wm * 128 + i * 16 + row_in + r;
+                const int row = wm * 128 + i * 16 + row_in + r + odd;
                 const float a0 = acc.v[i][j][r], a1 = acc.v[i][j][r + 1];
                 uint32_t b;
                 if (rowscale) {
@@ -411,8 +417,9 @@ __device__ __forceinline__ void stage_tile_bf16(const Acc& acc, uint8_t* smem, c
                 } else {
                     b = pack_bf2(a0, a1);
                 }
-                *reinterpret_cast<uint16_t*>(smem + row * kEpiPitch + col * 2) = (uint16_t)b;
-                *reinterpret_cast<uint16_t*>(smem + (row + 1) * kEpiPitch + col * 2) = (uint16_t)(b >> 16);
+                // quad_perm(1,0,3,2): lane l <- l ^ 1 (every lane active, the source always exists)
+                const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0xB1, 0xF, 0xF, true);
+                *reinterpret_cast<uint32_t*>(smem + row * kEpiPitch + col * 2) = __builtin_amdgcn_perm(nb, b, sel);
             }
         }
         if (rowscale) {
