@@ -47,10 +47,10 @@ constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- (i + 8) mod 16
 constexpr uint32_t kPermLo = 0x05040100u;
 constexpr uint32_t kPermHi = 0x07060302u;
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-// a.lo b.lo + a.hi b.hi for two packed bf16 pairs (v_dot2_f32_bf16, fp32 result)
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), 0.0f,
-                                           false);
+// a.lo b.lo + a.hi b.hi (+ c) for two packed bf16 pairs (v_dot2_f32_bf16, fp32 result; the
+// bf16 products are exact)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c = 0.0f) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
 // Sum over the 16 lanes of a DPP row, left in every lane of it.
@@ -63,27 +63,26 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // Q/K output of one (row, head) for the 16 lanes of a DPP row: vp holds this lane's 8 dims
-// (chunk q) of the head as bf16, nw its 8 norm weights; cv / sv the cos and sin of frequencies
-// 8 (q mod 6) .. + 7 for the row's position (q < 12).  All 16 lanes of the row must be active.
-__device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const float (&nw)[8], float qk_eps, int q,
-                                              const u32x4& cv, const u32x4& sv) {
-    float v[8];
-    unpack8(vp, v);
-    // per-head RMSNorm in fp32: bf16 squares are exact, the sum carries fp32 rounding only,
-    // and u = bf16((v * r2) * w); two partial sums halve the dependent chain
-    float s0 = v[0] * v[0], s1 = v[1] * v[1];
-#pragma unroll
-    for (int e = 2; e < 8; e += 2) {
-        s0 = fmaf(v[e], v[e], s0);
-        s1 = fmaf(v[e + 1], v[e + 1], s1);
-    }
+// (chunk q) of the head as bf16; nwlo / nwhi its 8 norm weights as bf16 pairs with the high /
+// low half zeroed; cv / sv the cos and sin of frequencies 8 (q mod 6) .. + 7 for the row's
+// position (q < 12).  All 16 lanes of the row must be active.
+__device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const u32x4& nwlo, const u32x4& nwhi, float qk_eps,
+                                              int q, const u32x4& cv, const u32x4& sv) {
+    // per-head RMSNorm in fp32 on the packed bf16 values: the squares and v w are exact
+    // bf16 products (v_dot2; a zero half picks one product), the sum of squares carries fp32
+    // rounding only, and u = bf16((v w) r2); two partial sums halve the dependent chain
+    const float s0 = dot2_bf16(vp[1], vp[1], dot2_bf16(vp[0], vp[0]));
+    const float s1 = dot2_bf16(vp[3], vp[3], dot2_bf16(vp[2], vp[2]));
     const float ss = row16_sum(s0 + s1);   // the 16 lanes of a (row, head) are one DPP row
     // v_rsq_f32 directly: its argument is at least qk_eps, a normal float, where the library
     // rsqrtf adds only a denormal-range rescaling around the same instruction
     const float r2 = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + qk_eps);
     float u[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) u[e] = v[e] * r2 * nw[e];
+    for (int e = 0; e < 4; ++e) {
+        u[2 * e] = dot2_bf16(vp[e], nwlo[e]) * r2;
+        u[2 * e + 1] = dot2_bf16(vp[e], nwhi[e]) * r2;
+    }
     const u32x4 up = pack8(u);          // the bf16 u, packed
     // RoPE partner chunk q + 6 (q < 6) or q - 6 (6 <= q < 12), 8 lanes away; its sign flipped
     // for the first half, so both halves take o = u c + w s:
@@ -167,8 +166,12 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
     __syncthreads();
 
-    float nw[8];
-    unpack8(nwv, nw);
+    u32x4 nwlo, nwhi;                   // the norm weights, one bf16 of each pair kept
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        nwlo[e] = nwv[e] & 0xFFFFu;
+        nwhi[e] = nwv[e] & 0xFFFF0000u;
+    }
     u32x4 cv[kIters], sv[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
@@ -185,7 +188,7 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
         const int row = it * kRowsPerPass + rsub;
         const u32x4 vp = epi_ld(smem, row, hh * 128 + d0);
         u32x4 o = vp;
-        if (kind < 2) o = qk_norm_rope(vp, nw, qk_eps, q, cv[it], sv[it]);
+        if (kind < 2) o = qk_norm_rope(vp, nwlo, nwhi, qk_eps, q, cv[it], sv[it]);
         if (hpd == kHeads) {
             // one destination: rows past M fall outside rout and are dropped
             buf_st16(rout, (uint32_t)((((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0) * 2, o);
