@@ -73,19 +73,6 @@ __device__ __forceinline__ float odd32(float p, float e) {
     return __uint_as_float(u);
 }
 
-// (a * b) * c of three fp32 values, rounded to odd into fp32 (then one RNE to bf16 rounds the
-// product once).  a b = p1 + e1 and p1 c = p2 + e2 exactly (fma error terms), so the product
-// is p2 + (e2 + e1 c); fma(e1, c, e2) gives that tail to within 2^-24 of itself, enough for
-// its sign and zero-ness, which are all the rounding to odd uses (short of a tail that
-// cancels to within 2^-24 of itself while p2 also sits exactly on a bf16 midpoint).
-__device__ __forceinline__ float mul3_odd32(float a, float b, float c) {
-    const float p1 = a * b;
-    const float e1 = fmaf(a, b, -p1);
-    const float p2 = p1 * c;
-    const float e2 = fmaf(p1, c, -p2);
-    return odd32(p2, fmaf(e1, c, e2));
-}
-
 // a / s rounded to nearest, given y = RN(1 / s) (one division per row instead of one per
 // element): q0 = RN(a y), the remainder a - q0 s by fma, and one fma correction (Markstein's
 // final step for a correctly rounded reciprocal).

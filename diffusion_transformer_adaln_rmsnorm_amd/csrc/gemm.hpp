@@ -364,7 +364,7 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
 }
 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS
-// (row pitch kEpiPitch); with scales the product of the three fp32 values is rounded once.
+// (row pitch kEpiPitch), the products in fp32 as printed, then RNE to bf16.
 // rowscale and colscale are both given or both null (factor 1).  Registers r and r + 1 of a
 // block hold rows R and R + 1 of one column c = l % 16, packed as one bf16 pair; lanes l and
 // l ^ 1 (columns c and c ^ 1) swap halves with one DPP move, so that the even lane holds row R,
@@ -412,8 +412,7 @@ __device__ __forceinline__ void stage_tile_bf16(const Acc& acc, uint8_t* smem, c
                 const float a0 = acc.v[i][j][r], a1 = acc.v[i][j][r + 1];
                 uint32_t b;
                 if (rowscale) {
-                    // (acc * s_row) * s_col, one rounding to bf16
-                    b = pack_bf2(mul3_odd32(a0, rs[r], cscale[j]), mul3_odd32(a1, rs[r + 1], cscale[j]));
+                    b = pack_bf2((a0 * rs[r]) * cscale[j], (a1 * rs[r + 1]) * cscale[j]);
                 } else {
                     b = pack_bf2(a0, a1);
                 }
