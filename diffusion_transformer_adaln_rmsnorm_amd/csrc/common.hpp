@@ -44,22 +44,6 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 // round a float to the nearest bf16 value, returned as float
 __device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
 
-// Correctly rounded double -> bf16.  The double is first rounded to odd into fp32 (truncate,
-// then force the last bit to 1 when inexact); since fp32 keeps 24 >= 8 + 2 significant bits,
-// the round-to-nearest-even to bf16 that follows equals a single rounding of the double.
-__device__ __forceinline__ float f64_to_f32_odd(double d) {
-    float f = (float)d;
-    const double back = (double)f;
-    if (back != d) {
-        uint32_t b = __float_as_uint(f);
-        if (fabs(back) > fabs(d)) b -= 1u;   // RNE went away from zero: step back toward zero
-        f = __uint_as_float(b | 1u);
-    }
-    return f;
-}
-__device__ __forceinline__ uint32_t f2bf_d(double d) { return f2bf(f64_to_f32_odd(d)); }
-__device__ __forceinline__ float rbf_d(double d) { return bf2f(f2bf_d(d)); }
-
 // p = RN32(v) with error e = v - p (exact): the fp32 value rounded to odd from v (truncate
 // toward zero, then force the last bit to 1 when inexact).  fp32 keeps 24 >= 8 + 2 significant
 // bits, so the RNE to bf16 that follows equals one rounding of v.  p == 0 only when v rounds
@@ -126,12 +110,9 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Streaming (non-temporal) 16-byte load/store for data touched once.
+// Streaming (non-temporal) 16-byte load for data touched once.
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ void st16_nt(void* p, const u32x4& v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 }  // namespace dit

@@ -84,9 +84,6 @@ __device__ __forceinline__ int64_t buf_ld_i64(__amdgpu_buffer_rsrc_t r, uint32_t
     const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
     return (int64_t)(((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0]);
 }
-__device__ __forceinline__ int32_t buf_ld_i32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-}
 __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }

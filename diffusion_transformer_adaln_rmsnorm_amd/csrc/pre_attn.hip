@@ -46,7 +46,6 @@ constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- (i + 8) mod 16
 // (src1.hi | src0.hi << 16).
 constexpr uint32_t kPermLo = 0x05040100u;
 constexpr uint32_t kPermHi = 0x07060302u;
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // a.lo b.lo + a.hi b.hi (+ c) for two packed bf16 pairs (v_dot2_f32_bf16, fp32 result; the
 // bf16 products are exact)
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c = 0.0f) {
