@@ -48,6 +48,8 @@ def lib():
         L.oracle_round_e4m3.argtypes = [_d]
         L.oracle_e4m3_value.restype = _d
         L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_quant_out_e4m3.restype = None
+        L.oracle_quant_out_e4m3.argtypes = [_p, _i64, _d, _d, _d, _p]
         L.oracle_pre_attn.restype = None
         L.oracle_pre_attn.argtypes = [_i64, _i64, _p, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _i64, _p,
                                       _d, _d, _p, _p]
@@ -162,6 +164,19 @@ def ulysses_pack(out_rows, P):
     for p in range(P):
         packed[p] = a[:, p * hl:(p + 1) * hl]
     return packed
+
+
+def quant_out_e4m3(out_bits, q_descale, k_descale, v_descale):
+    """e4m3 output mode: codes of the packed bf16 pre-attention output (uint16 bit patterns,
+    trailing axes [3, 128]), code = e4m3(fl32(v / descale)) with the descale of the element's
+    kind, saturating at 448 ("minimax_h3_nvfp4_pre_attention", Parameters: out_mode and
+    q/k/v_descale).  The descales are fp32 values."""
+    a = np.ascontiguousarray(out_bits, dtype=np.uint16)
+    assert a.shape[-2:] == (3, HEAD_DIM), a.shape
+    code = np.empty(a.shape, dtype=np.uint8)
+    lib().oracle_quant_out_e4m3(_ptr(a), a.size, float(np.float32(q_descale)), float(np.float32(k_descale)),
+                                float(np.float32(v_descale)), _ptr(code))
+    return code
 
 
 def out_proj(d, rows_sel=None, threads=None):

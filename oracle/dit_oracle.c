@@ -237,6 +237,21 @@ static float quant_row(const uint16_t* v, int n, uint8_t* code) {
     return (float)s;
 }
 
+/* ---- e4m3 output mode of the pre-attention ------------------------------------------------
+ * "minimax_h3_nvfp4_pre_attention", Parameters (out_mode "e4m3" with per-tensor q/k/v
+ * dequantization scales; its quantisation page is missing, so the plainest reading): each
+ * element v of the bf16 output becomes code = e4m3(fl32(v / descale)), saturating at 448, with
+ * descale the scale of the element's kind.  In the packed output [..., 3, 128] the kind of
+ * element e is (e / 128) mod 3.  fl32 of the fp64 quotient is the correctly rounded fp32
+ * quotient (53 >= 2 * 24 + 2 bits). */
+void oracle_quant_out_e4m3(const uint16_t* v, int64_t n, double dq, double dk, double dv, uint8_t* code) {
+    for (int64_t e = 0; e < n; e++) {
+        const int kind = (int)((e / HDIM) % 3);
+        const double d = kind == 0 ? dq : (kind == 1 ? dk : dv);
+        code[e] = oracle_round_e4m3(fl32(bf(v[e]) / d));
+    }
+}
+
 /* ---- FP8 W8A8 MLP ------------------------------------------------------------------------ */
 
 /* value of every e4m3 code, filled from oracle_e4m3_value (a lookup, not a second decoder) */

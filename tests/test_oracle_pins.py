@@ -556,3 +556,50 @@ def test_ulysses_pack_degree_one_is_identity_and_blocks_partition_heads():
         assert np.array_equal(np.concatenate(list(packed), axis=1), a)
     with pytest.raises(ValueError):
         oracle.ulysses_pack(a, 3)
+
+
+# ---------------------------------------------------------------- e4m3 output mode
+
+def _random_out_bits(g, shape):
+    """bf16 bit patterns of a packed pre-attention output, |v| spanning the e4m3 range and
+    beyond (saturation), with some exact zeros of both signs."""
+    v = (g.standard_normal(shape) * np.exp2(g.integers(-12, 11, size=shape))).astype(np.float32)
+    v.flat[::97] = 0.0
+    v.flat[1::97] = -0.0
+    return torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_quant_out_e4m3_matches_library_conversion_per_kind():
+    # torch's float8_e4m3fn conversion (a library routine) of the fp32 quotient, after clamping
+    # to the largest code; each kind sliced from the [.., 3, 128] axes with its own descale
+    g = np.random.Generator(np.random.PCG64(41))
+    bits = _random_out_bits(g, (2, 5, 7, 3, HD))
+    descale = (np.float32(0.37), np.float32(2.5), np.float32(0.0625))
+    got = oracle.quant_out_e4m3(bits, *descale)
+    v = bf16_val(bits)
+    for kind in range(3):
+        q = (v[..., kind, :].astype(np.float32) / descale[kind]).astype(np.float32)
+        ref = torch_e4m3(np.clip(q, -448.0, 448.0))
+        assert np.array_equal(got[..., kind, :], ref), kind
+
+
+def test_quant_out_e4m3_unit_descale_inverts_the_code_table():
+    # every finite e4m3 value is a bf16 value; with descale 1 it must come back as its own code
+    rows = _golden("e4m3fn_codes.txt")
+    bits = np.zeros((len(rows), 3, HD), np.uint16)
+    for i, (v, _) in enumerate(rows):
+        bits[i] = oracle.round_bf16(v)
+    got = oracle.quant_out_e4m3(bits, 1.0, 1.0, 1.0)
+    for i, (v, c) in enumerate(rows):
+        assert np.all(got[i] == c), (v, hex(c))
+
+
+def test_quant_out_e4m3_divides_and_saturates():
+    bits = np.full((1, 3, HD), oracle.round_bf16(1.0), np.uint16)
+    got = oracle.quant_out_e4m3(bits, 0.5, 0.25, 2.0)          # 1/0.5, 1/0.25, 1/2
+    assert np.all(got[0, 0] == 0x40) and np.all(got[0, 1] == 0x48) and np.all(got[0, 2] == 0x30)
+    big = np.full((1, 3, HD), oracle.round_bf16(1000.0), np.uint16)
+    assert np.all(oracle.quant_out_e4m3(big, 1.0, 1.0, 1.0) == 0x7E)
+    assert np.all(oracle.quant_out_e4m3(big | 0x8000, 1.0, 1.0, 1.0) == 0xFE)
+    tie = np.full((1, 3, HD), oracle.round_bf16(1.0625), np.uint16)   # midway 1 and 1.125
+    assert np.all(oracle.quant_out_e4m3(tie, 1.0, 1.0, 1.0) == 0x38)  # ties to even
