@@ -178,6 +178,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     seg = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])   # ms
+    # the e4m3 output mode of the QKV launch (same workspace and weights; not part of the step)
+    out_e4m3 = torch.empty((1, M_TOKENS, 56, 3, 128), dtype=torch.uint8, device=dev)
+    def qkv_e4m3():
+        dit.dit_qkv_rope_pack_e4m3(ws, tp["qkv_weight"], tp["q_norm_weight"], tp["k_norm_weight"],
+                                   tp["rope_cos_sin"], ulysses_degree=1, out=out_e4m3, q_descale=1.0 / 96.0,
+                                   k_descale=0.015, v_descale=0.0075, qk_eps=tp["qk_eps"],
+                                   rope_positions=tp["rope_positions"])
+    for _ in range(3):
+        qkv_e4m3()
+    e8 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    n8 = max(3, min(args.steps, 10))
+    e8[0].record()
+    for _ in range(n8):
+        qkv_e4m3()
+    e8[1].record()
+    torch.cuda.synchronize()
+    e4m3_ms = e8[0].elapsed_time(e8[1]) / n8
+    del out_e4m3
     norm_ms, gemm_ms, op_ms, mlp_ms = seg.mean(axis=0)
     pre_ms = norm_ms + gemm_ms
     ms_per_step = wall * 1e3 / args.steps
@@ -199,10 +217,13 @@ def main():
                      "peak": PEAK_BF16, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16, 4),
                      "traffic": traffic, "avg_launch_ms": round(float(gemm_ms), 4)},
         "stages_ms": {"norm_adaln": round(float(norm_ms), 4), "qkv_gemm": round(float(gemm_ms), 4),
-                      "out_proj": round(float(op_ms), 4), "mlp_fp8": round(float(mlp_ms), 4)},
+                      "out_proj": round(float(op_ms), 4), "mlp_fp8": round(float(mlp_ms), 4),
+                      "qkv_gemm_e4m3_out": round(float(e4m3_ms), 4)},
         "stage_rates": {
             "norm_adaln_GBps": round(NORM_BYTES_PER_ROW * M_TOKENS / (norm_ms * 1e-3) / 1e9, 1),
             "norm_adaln_frac_hbm": round(NORM_BYTES_PER_ROW * M_TOKENS / (norm_ms * 1e-3) / 1e9 / PEAK_HBM, 4),
+            "qkv_gemm_e4m3_out_TFLOPs": round(QKV_FLOP / (e4m3_ms * 1e-3) / 1e12, 2),
+            "qkv_gemm_e4m3_out_frac_bf16": round(QKV_FLOP / (e4m3_ms * 1e-3) / 1e12 / PEAK_BF16, 4),
         },
     }
     if "out_proj" in stages:

@@ -15,7 +15,8 @@ import os
 
 import torch
 
-__all__ = ["dit_pre_attn_bf16", "dit_norm_adaln_bf16", "dit_qkv_rope_pack_bf16", "dit_out_proj_gated_bf16", "dit_mlp_fp8", "dit_mlp_fp8_flags_elems",
+__all__ = ["dit_pre_attn_bf16", "dit_pre_attn_e4m3", "dit_norm_adaln_bf16", "dit_qkv_rope_pack_bf16",
+           "dit_qkv_rope_pack_e4m3", "dit_out_proj_gated_bf16", "dit_mlp_fp8", "dit_mlp_fp8_flags_elems",
            "DitError", "load_library", "LIB_PATH", "HIDDEN", "HEADS", "HEAD_DIM", "QKV_ROWS", "ATTN_WIDTH",
            "INTER", "FC1_ROWS", "MLP_MAX_M"]
 
@@ -69,6 +70,11 @@ def load_library(path: str = LIB_PATH):
     L.dit_norm_adaln_bf16.argtypes = [_p, _i64, _p, Table, Table, _p, _f, _p, _p]
     L.dit_qkv_rope_pack_bf16.restype = _i32
     L.dit_qkv_rope_pack_bf16.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _p, _i32, _f, _p, _p]
+    L.dit_pre_attn_e4m3.restype = _i32
+    L.dit_pre_attn_e4m3.argtypes = [_p, _i64, _p, Table, Table, _p, _p, _p, _p, _p, _i64, _p, _i32, _f, _f, _f, _f, _f,
+                                    _p, _p, _p]
+    L.dit_qkv_rope_pack_e4m3.restype = _i32
+    L.dit_qkv_rope_pack_e4m3.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _p, _i32, _f, _f, _f, _f, _p, _p]
     L.dit_out_proj_gated_bf16.restype = _i32
     L.dit_out_proj_gated_bf16.argtypes = [_p, _i64, _p, Table, _p, _p, _p, _p]
     L.dit_mlp_fp8.restype = _i32
@@ -114,10 +120,43 @@ def _check(fn, st):
         raise DitError(fn, st)
 
 
+_E4M3_DTYPES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _need_out(out, e4m3: bool, P: int, M: int):
+    """out [P, M, 56 // P, 3, 128]: bf16, or one byte per element (uint8 or float8_e4m3fn codes)."""
+    if P not in (1, 2, 4, 8):
+        return                       # the library rejects the degree (DIT_ERR_VALUE)
+    shape = (P, M, HEADS // P, 3, HEAD_DIM)
+    if not e4m3:
+        _need(out, "out", torch.bfloat16, shape)
+    elif out.dtype not in _E4M3_DTYPES:
+        raise ValueError(f"out must be uint8 or float8_e4m3fn, got {out.dtype}")
+    else:
+        _need(out, "out", out.dtype, shape)
+
+
 def dit_pre_attn_bf16(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight,
                       k_norm_weight, rope_cos_sin, *, ulysses_degree: int, out, eps: float = 1e-5,
                       qk_eps: float | None = None, rope_positions=None, workspace=None):
     """BF16 pre-attention stage; writes `out` [P, M, 56 // P, 3, 128] and returns it."""
+    return _pre_attn(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight,
+                     k_norm_weight, rope_cos_sin, ulysses_degree, out, eps, qk_eps, rope_positions, workspace, None)
+
+
+def dit_pre_attn_e4m3(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight,
+                      k_norm_weight, rope_cos_sin, *, ulysses_degree: int, out, q_descale: float, k_descale: float,
+                      v_descale: float, eps: float = 1e-5, qk_eps: float | None = None, rope_positions=None,
+                      workspace=None):
+    """Pre-attention stage with e4m3 output codes: out [P, M, 56 // P, 3, 128] (uint8 or
+    float8_e4m3fn) = e4m3(bf16 result / descale of its kind); returns out."""
+    return _pre_attn(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight,
+                     k_norm_weight, rope_cos_sin, ulysses_degree, out, eps, qk_eps, rope_positions, workspace,
+                     (q_descale, k_descale, v_descale))
+
+
+def _pre_attn(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight, k_norm_weight,
+              rope_cos_sin, ulysses_degree, out, eps, qk_eps, rope_positions, workspace, descale):
     L = load_library()
     M = x.shape[0] if x.dim() == 2 else -1
     _need(x, "x", torch.bfloat16, (M, HIDDEN))
@@ -134,16 +173,19 @@ def dit_pre_attn_bf16(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, q
     if rope_positions is not None:
         _need(rope_positions, "rope_positions", torch.int64, (M,))
     P = int(ulysses_degree)
-    if P in (1, 2, 4, 8):
-        _need(out, "out", torch.bfloat16, (P, M, HEADS // P, 3, HEAD_DIM))
+    _need_out(out, descale is not None, P, M)
     if workspace is None:
         workspace = torch.empty((M, HIDDEN), dtype=torch.bfloat16, device=x.device)
     _need(workspace, "workspace", torch.bfloat16, (M, HIDDEN))
     qk = eps if qk_eps is None else qk_eps
-    st = L.dit_pre_attn_bf16(_ptr(x), M, _ptr(x_norm_weight), ts, th, _ptr(adaln_index), _ptr(qkv_weight),
-                             _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(rope_cos_sin), S, _ptr(rope_positions),
-                             P, float(eps), float(qk), _ptr(workspace), _ptr(out), _stream())
-    _check("dit_pre_attn_bf16", st)
+    args = (_ptr(x), M, _ptr(x_norm_weight), ts, th, _ptr(adaln_index), _ptr(qkv_weight), _ptr(q_norm_weight),
+            _ptr(k_norm_weight), _ptr(rope_cos_sin), S, _ptr(rope_positions), P, float(eps), float(qk))
+    if descale is None:
+        st = L.dit_pre_attn_bf16(*args, _ptr(workspace), _ptr(out), _stream())
+        _check("dit_pre_attn_bf16", st)
+    else:
+        st = L.dit_pre_attn_e4m3(*args, *(float(d) for d in descale), _ptr(workspace), _ptr(out), _stream())
+        _check("dit_pre_attn_e4m3", st)
     return out
 
 
@@ -165,6 +207,20 @@ def dit_norm_adaln_bf16(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index,
 def dit_qkv_rope_pack_bf16(workspace, qkv_weight, q_norm_weight, k_norm_weight, rope_cos_sin, *,
                            ulysses_degree: int, out, qk_eps: float = 1e-5, rope_positions=None):
     """Launch 2 of the pre-attention stage: QKV GEMM + Q/K RMSNorm + RoPE + pack into out."""
+    return _qkv_rope_pack(workspace, qkv_weight, q_norm_weight, k_norm_weight, rope_cos_sin, ulysses_degree, out,
+                          qk_eps, rope_positions, None)
+
+
+def dit_qkv_rope_pack_e4m3(workspace, qkv_weight, q_norm_weight, k_norm_weight, rope_cos_sin, *,
+                           ulysses_degree: int, out, q_descale: float, k_descale: float, v_descale: float,
+                           qk_eps: float = 1e-5, rope_positions=None):
+    """Launch 2 with e4m3 output codes (see dit_pre_attn_e4m3)."""
+    return _qkv_rope_pack(workspace, qkv_weight, q_norm_weight, k_norm_weight, rope_cos_sin, ulysses_degree, out,
+                          qk_eps, rope_positions, (q_descale, k_descale, v_descale))
+
+
+def _qkv_rope_pack(workspace, qkv_weight, q_norm_weight, k_norm_weight, rope_cos_sin, ulysses_degree, out, qk_eps,
+                   rope_positions, descale):
     L = load_library()
     M = workspace.shape[0] if workspace.dim() == 2 else -1
     _need(workspace, "workspace", torch.bfloat16, (M, HIDDEN))
@@ -178,12 +234,15 @@ def dit_qkv_rope_pack_bf16(workspace, qkv_weight, q_norm_weight, k_norm_weight, 
     if rope_positions is not None:
         _need(rope_positions, "rope_positions", torch.int64, (M,))
     P = int(ulysses_degree)
-    if P in (1, 2, 4, 8):
-        _need(out, "out", torch.bfloat16, (P, M, HEADS // P, 3, HEAD_DIM))
-    st = L.dit_qkv_rope_pack_bf16(_ptr(workspace), M, _ptr(qkv_weight), _ptr(q_norm_weight), _ptr(k_norm_weight),
-                                  _ptr(rope_cos_sin), S, _ptr(rope_positions), P, float(qk_eps), _ptr(out),
-                                  _stream())
-    _check("dit_qkv_rope_pack_bf16", st)
+    _need_out(out, descale is not None, P, M)
+    args = (_ptr(workspace), M, _ptr(qkv_weight), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(rope_cos_sin), S,
+            _ptr(rope_positions), P, float(qk_eps))
+    if descale is None:
+        st = L.dit_qkv_rope_pack_bf16(*args, _ptr(out), _stream())
+        _check("dit_qkv_rope_pack_bf16", st)
+    else:
+        st = L.dit_qkv_rope_pack_e4m3(*args, *(float(d) for d in descale), _ptr(out), _stream())
+        _check("dit_qkv_rope_pack_e4m3", st)
     return out
 
 

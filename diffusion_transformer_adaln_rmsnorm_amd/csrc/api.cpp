@@ -71,13 +71,15 @@ dit_status dit_norm_adaln_bf16(const void* x, int64_t M, const void* x_norm_weig
         static_cast<uint16_t*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
-dit_status dit_qkv_rope_pack_bf16(const void* workspace, int64_t M, const void* qkv_weight,
-                                  const void* q_norm_weight, const void* k_norm_weight, const void* rope_cos_sin,
-                                  int64_t S, const int64_t* rope_positions, int ulysses_degree, float qk_eps,
-                                  void* out, void* stream) {
+// Checks and launch of the QKV GEMM (launch 2), bf16 output (descales null) or e4m3 codes.
+static dit_status qkv_rope_pack(const void* workspace, int64_t M, const void* qkv_weight, const void* q_norm_weight,
+                                const void* k_norm_weight, const void* rope_cos_sin, int64_t S,
+                                const int64_t* rope_positions, int ulysses_degree, float qk_eps, const float* descale,
+                                void* out, void* stream) {
     if (ulysses_degree != 1 && ulysses_degree != 2 && ulysses_degree != 4 && ulysses_degree != 8)
         return DIT_ERR_VALUE;
     if (!eps_ok(qk_eps)) return DIT_ERR_VALUE;
+    if (descale && (!eps_ok(descale[0]) || !eps_ok(descale[1]) || !eps_ok(descale[2]))) return DIT_ERR_VALUE;
     if (M < 0 || M > kMaxRows) return DIT_ERR_SHAPE;
     if (!workspace || !qkv_weight || !q_norm_weight || !k_norm_weight || !rope_cos_sin || !out) return DIT_ERR_NULL;
     if (!aligned(workspace, 16) || !aligned(qkv_weight, 16) || !aligned(q_norm_weight, 16) ||
@@ -87,24 +89,30 @@ dit_status dit_qkv_rope_pack_bf16(const void* workspace, int64_t M, const void* 
     if (S < 1) return DIT_ERR_SHAPE;
     if (!rope_positions && S < M) return DIT_ERR_SHAPE;
     if (M == 0) return DIT_OK;
-    return launched(dit::launch_qkv_gemm(static_cast<const uint16_t*>(workspace), M,
-                                         static_cast<const uint16_t*>(qkv_weight),
-                                         static_cast<const uint16_t*>(q_norm_weight),
-                                         static_cast<const uint16_t*>(k_norm_weight),
-                                         static_cast<const uint16_t*>(rope_cos_sin), S, rope_positions, qk_eps,
-                                         ulysses_degree, static_cast<uint16_t*>(out),
-                                         static_cast<hipStream_t>(stream)));
+    const uint16_t* ws = static_cast<const uint16_t*>(workspace);
+    const uint16_t* W = static_cast<const uint16_t*>(qkv_weight);
+    const uint16_t* qw = static_cast<const uint16_t*>(q_norm_weight);
+    const uint16_t* kw = static_cast<const uint16_t*>(k_norm_weight);
+    const uint16_t* cs = static_cast<const uint16_t*>(rope_cos_sin);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (descale)
+        return launched(dit::launch_qkv_gemm_e4m3(ws, M, W, qw, kw, cs, S, rope_positions, qk_eps, ulysses_degree,
+                                                  descale[0], descale[1], descale[2], static_cast<uint8_t*>(out),
+                                                  st));
+    return launched(dit::launch_qkv_gemm(ws, M, W, qw, kw, cs, S, rope_positions, qk_eps, ulysses_degree,
+                                         static_cast<uint16_t*>(out), st));
 }
 
-dit_status dit_pre_attn_bf16(const void* x, int64_t M, const void* x_norm_weight, dit_bf16_table adaln_scale,
-                             dit_bf16_table adaln_shift, const int64_t* adaln_index, const void* qkv_weight,
-                             const void* q_norm_weight, const void* k_norm_weight, const void* rope_cos_sin,
-                             int64_t S, const int64_t* rope_positions, int ulysses_degree, float eps, float qk_eps,
-                             void* workspace, void* out, void* stream) {
-    // check both halves before launching either, so a bad argument launches nothing
+// Both launches; every argument is checked before either is enqueued.
+static dit_status pre_attn(const void* x, int64_t M, const void* x_norm_weight, dit_bf16_table adaln_scale,
+                           dit_bf16_table adaln_shift, const int64_t* adaln_index, const void* qkv_weight,
+                           const void* q_norm_weight, const void* k_norm_weight, const void* rope_cos_sin, int64_t S,
+                           const int64_t* rope_positions, int ulysses_degree, float eps, float qk_eps,
+                           const float* descale, void* workspace, void* out, void* stream) {
     if (ulysses_degree != 1 && ulysses_degree != 2 && ulysses_degree != 4 && ulysses_degree != 8)
         return DIT_ERR_VALUE;
     if (!eps_ok(eps) || !eps_ok(qk_eps)) return DIT_ERR_VALUE;
+    if (descale && (!eps_ok(descale[0]) || !eps_ok(descale[1]) || !eps_ok(descale[2]))) return DIT_ERR_VALUE;
     if (M < 0 || M > kMaxRows) return DIT_ERR_SHAPE;
     if (!x || !x_norm_weight || !adaln_index || !qkv_weight || !q_norm_weight || !k_norm_weight ||
         !rope_cos_sin || !workspace || !out)
@@ -123,8 +131,47 @@ dit_status dit_pre_attn_bf16(const void* x, int64_t M, const void* x_norm_weight
     if (M == 0) return DIT_OK;
     st = dit_norm_adaln_bf16(x, M, x_norm_weight, adaln_scale, adaln_shift, adaln_index, eps, workspace, stream);
     if (st != DIT_OK) return st;
-    return dit_qkv_rope_pack_bf16(workspace, M, qkv_weight, q_norm_weight, k_norm_weight, rope_cos_sin, S,
-                                  rope_positions, ulysses_degree, qk_eps, out, stream);
+    return qkv_rope_pack(workspace, M, qkv_weight, q_norm_weight, k_norm_weight, rope_cos_sin, S, rope_positions,
+                         ulysses_degree, qk_eps, descale, out, stream);
+}
+
+dit_status dit_qkv_rope_pack_bf16(const void* workspace, int64_t M, const void* qkv_weight,
+                                  const void* q_norm_weight, const void* k_norm_weight, const void* rope_cos_sin,
+                                  int64_t S, const int64_t* rope_positions, int ulysses_degree, float qk_eps,
+                                  void* out, void* stream) {
+    return qkv_rope_pack(workspace, M, qkv_weight, q_norm_weight, k_norm_weight, rope_cos_sin, S, rope_positions,
+                         ulysses_degree, qk_eps, nullptr, out, stream);
+}
+
+dit_status dit_qkv_rope_pack_e4m3(const void* workspace, int64_t M, const void* qkv_weight,
+                                  const void* q_norm_weight, const void* k_norm_weight, const void* rope_cos_sin,
+                                  int64_t S, const int64_t* rope_positions, int ulysses_degree, float qk_eps,
+                                  float q_descale, float k_descale, float v_descale, void* out, void* stream) {
+    const float d[3] = {q_descale, k_descale, v_descale};
+    return qkv_rope_pack(workspace, M, qkv_weight, q_norm_weight, k_norm_weight, rope_cos_sin, S, rope_positions,
+                         ulysses_degree, qk_eps, d, out, stream);
+}
+
+dit_status dit_pre_attn_bf16(const void* x, int64_t M, const void* x_norm_weight, dit_bf16_table adaln_scale,
+                             dit_bf16_table adaln_shift, const int64_t* adaln_index, const void* qkv_weight,
+                             const void* q_norm_weight, const void* k_norm_weight, const void* rope_cos_sin,
+                             int64_t S, const int64_t* rope_positions, int ulysses_degree, float eps, float qk_eps,
+                             void* workspace, void* out, void* stream) {
+    return pre_attn(x, M, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight,
+                    k_norm_weight, rope_cos_sin, S, rope_positions, ulysses_degree, eps, qk_eps, nullptr, workspace, out,
+                    stream);
+}
+
+dit_status dit_pre_attn_e4m3(const void* x, int64_t M, const void* x_norm_weight, dit_bf16_table adaln_scale,
+                             dit_bf16_table adaln_shift, const int64_t* adaln_index, const void* qkv_weight,
+                             const void* q_norm_weight, const void* k_norm_weight, const void* rope_cos_sin,
+                             int64_t S, const int64_t* rope_positions, int ulysses_degree, float eps, float qk_eps,
+                             float q_descale, float k_descale, float v_descale, void* workspace, void* out,
+                             void* stream) {
+    const float d[3] = {q_descale, k_descale, v_descale};
+    return pre_attn(x, M, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight,
+                    k_norm_weight, rope_cos_sin, S, rope_positions, ulysses_degree, eps, qk_eps, d, workspace, out,
+                    stream);
 }
 
 dit_status dit_out_proj_gated_bf16(const void* attn_out, int64_t M, const void* o_weight, dit_bf16_table gate,

@@ -60,9 +60,12 @@ __device__ __forceinline__ float odd32(float p, float e) {
 // a / s rounded to nearest, given y = RN(1 / s) (one division per row instead of one per
 // element): q0 = RN(a y), the remainder a - q0 s by fma, and one fma correction (Markstein's
 // final step for a correctly rounded reciprocal).
+// A zero remainder means q0 is exact and is returned as is, which also keeps the sign of a
+// zero a (the correction would turn -0 into +0).
 __device__ __forceinline__ float div_by(float a, float s, float y) {
     const float q0 = a * y;
-    return fmaf(fmaf(-q0, s, a), y, q0);
+    const float r = fmaf(-q0, s, a);
+    return r == 0.0f ? q0 : fmaf(r, y, q0);
 }
 
 // silu(t) = t / (1 + e^-t) from the hardware exp2 and reciprocal (each ~1 ulp); e^-t -> inf

@@ -20,6 +20,10 @@ hipError_t launch_norm_adaln_fp8q(const uint16_t* x, int64_t M, const uint16_t* 
 hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
                            const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos, float qk_eps,
                            int P, uint16_t* out, hipStream_t stream);
+// the same with e4m3 output codes: out[...] = e4m3(bf16 result / descale of its kind)
+hipError_t launch_qkv_gemm_e4m3(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
+                                const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos,
+                                float qk_eps, int P, float dq, float dk, float dv, uint8_t* out, hipStream_t stream);
 
 hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t* Wo, const uint16_t* gate,
                                 int64_t gate_rows, int64_t gate_ld, const int32_t* gate_index,

@@ -112,11 +112,35 @@ __device__ __forceinline__ int chunk_of_lane(int li) {
     return li < 6 ? li : (li < 8 ? 12 + (li - 6) : (li < 14 ? li - 2 : li));
 }
 
+// a / s rounded to nearest (div_by), except that quotients far beyond the largest e4m3 value
+// (which saturate either way) skip the correction, which an infinite first guess would turn
+// into NaN
+__device__ __forceinline__ float div_sat(float a, float s, float y) {
+    const float q0 = a * y;
+    return fabsf(q0) > 1024.0f ? q0 : div_by(a, s, y);
+}
+
+// e4m3 output mode ("minimax_h3_nvfp4_pre_attention", Parameters: out_mode "e4m3" with
+// per-tensor q/k/v dequantization scales): the 8 bf16 values of o become e4m3(fl32(v / ds)),
+// saturating at 448, packed little-endian into 8 bytes.  y = RN(1 / ds).
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2 e4m3_codes8(const u32x4& o, float ds, float y) {
+    float v[8];
+    unpack8(o, v);
+    u32x2 q;
+    q.x = f2e4m3x2(div_sat(v[0], ds, y), div_sat(v[1], ds, y)) | (f2e4m3x2(div_sat(v[2], ds, y), div_sat(v[3], ds, y)) << 16);
+    q.y = f2e4m3x2(div_sat(v[4], ds, y), div_sat(v[5], ds, y)) | (f2e4m3x2(div_sat(v[6], ds, y), div_sat(v[7], ds, y)) << 16);
+    return q;
+}
+
+// kE4m3: out holds e4m3 codes (one byte per element) of the bf16 results divided by the
+// descale of their kind (dq, dk, dv); else bf16 values (the descales are unused).
+template <bool kE4m3>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __restrict__ W,
                 const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
                 const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
-                int hpd, uint16_t* __restrict__ out, int mt, int nt) {
+                int hpd, float dq, float dk, float dv, void* __restrict__ out, int mt, int nt) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
@@ -152,7 +176,12 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     const __amdgpu_buffer_rsrc_t rpos = make_rsrc(pos, pos ? (uint32_t)(M * 8) : 0u);
     const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
     constexpr int64_t kOutRow = (int64_t)kHeads * 3 * kHeadDim;        // elements per token
-    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + m0 * kOutRow, (uint32_t)(tile_rows * kOutRow * 2));
+    constexpr int64_t kElemB = kE4m3 ? 1 : 2;                         // bytes per output element
+    uint8_t* const out8 = static_cast<uint8_t*>(out);
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out8 + m0 * kOutRow * kElemB,
+                                                  (uint32_t)(tile_rows * kOutRow * kElemB));
+    const float ds = kind == 0 ? dq : (kind == 1 ? dk : dv);          // this tile's descale
+    const float ds_inv = kE4m3 ? 1.0f / ds : 0.0f;                     // RN(1 / ds)
     u32x4 nwv = {0u, 0u, 0u, 0u};       // this lane's 8 q/k norm weights
     if (kind < 2) nwv = ld16((kind == 0 ? qw : kw) + d0);
     int64_t praw[kIters];               // raw positions (read only when pos is given)
@@ -188,12 +217,23 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
         const u32x4 vp = epi_ld(smem, row, hh * 128 + d0);
         u32x4 o = vp;
         if (kind < 2) o = qk_norm_rope(vp, nwlo, nwhi, qk_eps, q, cv[it], sv[it]);
-        if (hpd == kHeads) {
-            // one destination: rows past M fall outside rout and are dropped
-            buf_st16(rout, (uint32_t)((((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0) * 2, o);
+        // one destination: rows past M fall outside rout and are dropped; else out[dst, m, hl, ...]
+        const int64_t e1 = (((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0;
+        const int64_t m = m0 + row;
+        const int64_t eP = (((dst * M + m) * hpd + hl) * 3 + kind) * kHeadDim + d0;
+        if constexpr (kE4m3) {
+            const u32x2 q = e4m3_codes8(o, ds, ds_inv);
+            if (hpd == kHeads) {
+                __builtin_amdgcn_raw_buffer_store_b64(q, rout, (int)(uint32_t)e1, 0, 0);
+            } else if (m < M) {
+                *reinterpret_cast<u32x2*>(out8 + eP) = q;
+            }
         } else {
-            const int64_t m = m0 + row;
-            if (m < M) st16(out + (((dst * M + m) * hpd + hl) * 3 + kind) * kHeadDim + d0, o);
+            if (hpd == kHeads) {
+                buf_st16(rout, (uint32_t)(e1 * 2), o);
+            } else if (m < M) {
+                st16(out8 + eP * 2, o);
+            }
         }
     }
 }
@@ -203,8 +243,18 @@ hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, con
                            int P, uint16_t* out, hipStream_t stream) {
     const int mt = (int)((M + kBM - 1) / kBM);
     const int nt = kQkvRows / kBN;
-    hipLaunchKernelGGL(k_qkv_gemm, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs, S,
-                       pos, qk_eps, kHeads / P, out, mt, nt);
+    hipLaunchKernelGGL(k_qkv_gemm<false>, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs,
+                       S, pos, qk_eps, kHeads / P, 1.0f, 1.0f, 1.0f, out, mt, nt);
+    return hipGetLastError();
+}
+
+hipError_t launch_qkv_gemm_e4m3(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
+                                const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos,
+                                float qk_eps, int P, float dq, float dk, float dv, uint8_t* out, hipStream_t stream) {
+    const int mt = (int)((M + kBM - 1) / kBM);
+    const int nt = kQkvRows / kBN;
+    hipLaunchKernelGGL(k_qkv_gemm<true>, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs,
+                       S, pos, qk_eps, kHeads / P, dq, dk, dv, out, mt, nt);
     return hipGetLastError();
 }
 

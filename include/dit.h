@@ -2,7 +2,9 @@
  * dit.h - C ABI of the MI355X (gfx950) MiniMax-H3 AdaLN-modulated projection stages.
  *
  * Three operations, each following the tensor contract of one FlashInfer diffusion_ops page:
- *   dit_pre_attn_bf16       "minimax_h3_bf16_pre_attention" (description, Parameters, Notes)
+ *   dit_pre_attn_bf16       "minimax_h3_bf16_pre_attention" (description, Parameters, Notes),
+ *                           and its e4m3 output mode dit_pre_attn_e4m3 ("minimax_h3_nvfp4_pre_attention",
+ *                           Parameters: out_mode, q/k/v_descale)
  *   dit_out_proj_gated_bf16 "minimax_h3_nvfp4_out_proj" gated-residual epilogue, bf16 operands
  *   dit_mlp_fp8             "minimax_h3_mlp_fp8_sm120" (per-row formula block, Parameters)
  *
@@ -129,6 +131,33 @@ dit_status dit_qkv_rope_pack_bf16(const void* workspace, int64_t M, const void* 
                                   const void* q_norm_weight, const void* k_norm_weight,
                                   const void* rope_cos_sin, int64_t S, const int64_t* rope_positions,
                                   int ulysses_degree, float qk_eps, void* out, void* stream);
+
+/*
+ * E4M3 output mode of the pre-attention ("minimax_h3_nvfp4_pre_attention", Parameters:
+ * out_mode "e4m3" with per-tensor q_descale / k_descale / v_descale dequantization scales;
+ * the page defers their conventions to a page that is missing, and this is the plainest
+ * reading).  The same computation as dit_pre_attn_bf16 / dit_qkv_rope_pack_bf16; each bf16
+ * result o of the pack is then stored as one byte
+ *   out[h / (56/P), m, h % (56/P), kind, d] = e4m3(fl32(o / descale_kind))
+ * (float8_e4m3fn, round to nearest even, saturating at +-448; descale_kind = q_descale,
+ * k_descale or v_descale), so that code * descale approximates o.
+ * Arguments as the bf16 calls, plus:
+ *   q_descale, k_descale, v_descale  positive finite fp32 scales (else DIT_ERR_VALUE)
+ *   out            uint8 e4m3 codes [P, M, 56/P, 3, 128], 16-B aligned; must not overlap any input
+ */
+dit_status dit_pre_attn_e4m3(const void* x, int64_t M, const void* x_norm_weight,
+                             dit_bf16_table adaln_scale, dit_bf16_table adaln_shift,
+                             const int64_t* adaln_index, const void* qkv_weight,
+                             const void* q_norm_weight, const void* k_norm_weight,
+                             const void* rope_cos_sin, int64_t S, const int64_t* rope_positions,
+                             int ulysses_degree, float eps, float qk_eps, float q_descale,
+                             float k_descale, float v_descale, void* workspace, void* out, void* stream);
+
+dit_status dit_qkv_rope_pack_e4m3(const void* workspace, int64_t M, const void* qkv_weight,
+                                  const void* q_norm_weight, const void* k_norm_weight,
+                                  const void* rope_cos_sin, int64_t S, const int64_t* rope_positions,
+                                  int ulysses_degree, float qk_eps, float q_descale, float k_descale,
+                                  float v_descale, void* out, void* stream);
 
 /*
  * BF16 attention output projection with the fused gated residual (the epilogue of

@@ -27,8 +27,8 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("dit_pre_attn_bf16", "dit_out_proj_gated_bf16", "dit_mlp_fp8", "dit_mlp_fp8_flags_elems",
-              "dit_status_string", "dit_abi_version"):
+    for n in ("dit_pre_attn_bf16", "dit_pre_attn_e4m3", "dit_qkv_rope_pack_e4m3", "dit_out_proj_gated_bf16",
+              "dit_mlp_fp8", "dit_mlp_fp8_flags_elems", "dit_status_string", "dit_abi_version"):
         assert n in names
 
 
@@ -74,6 +74,43 @@ def pre(**kw):
 ])
 def test_pre_attn_contract_checks(kw, status):
     assert pre(**kw) == status
+
+
+def pre8(**kw):
+    a = dict(x=_p(1), M=16, xw=_p(2), sc=_T(), sh=_T(A + 0x200000), idx=_p(3), W=_p(4), qw=_p(5), kw=_p(6),
+             cs=_p(7), S=16, pos=None, P=1, eps=1e-5, qk_eps=1e-5, dq=0.5, dk=0.25, dv=2.0, ws=_p(8), out=_p(9))
+    a.update(kw)
+    return dit.load_library().dit_pre_attn_e4m3(a["x"], a["M"], a["xw"], a["sc"], a["sh"], a["idx"], a["W"],
+                                                  a["qw"], a["kw"], a["cs"], a["S"], a["pos"], a["P"], a["eps"],
+                                                  a["qk_eps"], a["dq"], a["dk"], a["dv"], a["ws"], a["out"], None)
+
+
+def pack8(**kw):
+    a = dict(ws=_p(8), M=16, W=_p(4), qw=_p(5), kw=_p(6), cs=_p(7), S=16, pos=None, P=1, qk_eps=1e-5, dq=0.5,
+             dk=0.25, dv=2.0, out=_p(9))
+    a.update(kw)
+    return dit.load_library().dit_qkv_rope_pack_e4m3(a["ws"], a["M"], a["W"], a["qw"], a["kw"], a["cs"], a["S"],
+                                                       a["pos"], a["P"], a["qk_eps"], a["dq"], a["dk"], a["dv"],
+                                                       a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=0.0), VALUE), (dict(dk=-1.0), VALUE), (dict(dv=float("nan")), VALUE), (dict(dq=float("inf")), VALUE),
+    (dict(out=None), NULL), (dict(x=None), NULL), (dict(out=ctypes.c_void_p(A + 8)), ALIGN),
+    (dict(P=3), VALUE), (dict(S=15), SHAPE), (dict(M=-1), SHAPE),
+    (dict(M=0), OK), (dict(M=0, P=4), OK),
+])
+def test_pre_attn_e4m3_contract_checks(kw, status):
+    assert pre8(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dq=0.0), VALUE), (dict(dv=-2.0), VALUE), (dict(dk=float("nan")), VALUE),
+    (dict(out=None), NULL), (dict(ws=None), NULL), (dict(out=ctypes.c_void_p(A + 4)), ALIGN),
+    (dict(P=5), VALUE), (dict(qk_eps=0.0), VALUE), (dict(M=0), OK),
+])
+def test_qkv_rope_pack_e4m3_contract_checks(kw, status):
+    assert pack8(**kw) == status
 
 
 def test_pre_attn_positions_lift_the_S_ge_M_rule():

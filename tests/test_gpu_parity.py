@@ -89,6 +89,30 @@ def run_pre(d, out=None, workspace=None, P=1):
     return t, out
 
 
+def run_pre_e4m3(d, descale, P=1):
+    t = synth.to_torch("pre_attn", d)
+    M = d["M"]
+    out = torch.empty((P, M, 56 // P, 3, 128), dtype=torch.uint8, device="cuda")
+    _dit().dit_pre_attn_e4m3(t["x"], t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], t["adaln_index"],
+                             t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
+                             ulysses_degree=P, out=out, q_descale=descale[0], k_descale=descale[1],
+                             v_descale=descale[2], eps=t["eps"], qk_eps=t["qk_eps"],
+                             rope_positions=t["rope_positions"])
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def e4m3_of_bf16(bits, descale):
+    """e4m3(fl32(v / descale_kind)) of bf16 bit patterns [..., 3, 128], saturating, by torch's
+    float8_e4m3fn conversion (a library routine)."""
+    v = bf16_val(bits).astype(np.float32)
+    out = np.empty(bits.shape, np.uint8)
+    for kind in range(3):
+        q = (v[..., kind, :] / np.float32(descale[kind])).astype(np.float32)
+        out[..., kind, :] = torch_e4m3(np.clip(q, -448.0, 448.0))
+    return out
+
+
 def check_pre(d, ws_gpu, out_gpu, rows=None):
     M = d["M"]
     rows = np.arange(M) if rows is None else rows
@@ -231,6 +255,46 @@ def test_pre_attn_ulysses_pack_is_the_degree_one_output_repacked(P):
     got = synth.bits(outp)
     assert got.shape == (P, M, 56 // P, 3, 128)
     assert np.array_equal(got, oracle.ulysses_pack(one, P))
+
+
+# descales that put the q/k outputs (RMS ~1 after the norm) and the v outputs (~N(0,1)) over
+# most of the e4m3 range, with some saturation
+E4M3_DESCALE = (1.0 / 96.0, 0.015, 0.0075)
+
+
+@pytest.mark.parametrize("P", [1, 2])
+def test_pre_attn_e4m3_codes_are_the_bf16_output_quantised(P):
+    """e4m3 output mode: every code is e4m3(fl32(o / descale)) of the bf16 mode's own output o
+    (the same fp32 quotient decides the code on both sides), in the same layout; two m-tiles
+    with a ragged tail, random positions, guarded rows."""
+    M = 300
+    _say(f"pre_attn e4m3 output, P={P}, M={M}")
+    d = synth.pre_attn_inputs(M, seed=500 + P, rows=2, S=512, positions="random", n_bad_positions=4,
+                              bad_index_frac=0.02, weight=_shared_weight())
+    _, outb = run_pre(d, P=P)
+    codes = run_pre_e4m3(d, E4M3_DESCALE, P=P)
+    ref = e4m3_of_bf16(synth.bits(outb), E4M3_DESCALE)
+    assert codes.shape == ref.shape == (P, M, 56 // P, 3, 128)
+    mism = np.mean(codes != ref)
+    _say(f"  codes != e4m3(bf16 out / descale): {mism:.2e}; saturated {np.mean((codes & 0x7F) == 0x7E):.2e}")
+    assert np.array_equal(codes, ref)
+
+
+def test_pre_attn_e4m3_against_oracle():
+    """config 0 (M = 16, guarded rows, rows=4 tables) in e4m3 mode against the oracle's codes of
+    its own bf16 output: within one code step (the bf16 values may differ by an ulp), guarded
+    rows exactly zero."""
+    _say("config 0, e4m3 output")
+    kind, d = synth.config(0)
+    codes = run_pre_e4m3(d, E4M3_DESCALE).reshape(16, 56, 3, 128)
+    _, out_ref = oracle.pre_attn(d)
+    ref = oracle.quant_out_e4m3(out_ref, *E4M3_DESCALE)
+    step = np.abs(ordered_e4m3(codes) - ordered_e4m3(ref))
+    idx = d["adaln_index"]
+    bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
+    _say(f"  code mismatch {np.mean(codes != ref):.2e}, max step {step.max()}, guarded rows {bad.sum()}")
+    assert step.max() <= 1
+    assert np.all(codes[bad] == 0)
 
 
 def test_pre_attn_ulysses_degree8_against_oracle():
