@@ -457,6 +457,17 @@ def test_mlp_alias(alias):
     check_mlp(d, out, ws)
 
 
+def test_mlp_maximum_M():
+    """M = 149796, the largest M the MLP page allows: 586 m-tiles, the last one ragged
+    (36 rows).  Sampled rows (the first 64, the last m-tile, every guarded row, 32 random)
+    against the oracle."""
+    M = 149796
+    _say(f"fp8 MLP at the maximum M={M}")
+    d = synth.mlp_inputs(M, seed=900, bad_index_frac=0.0002)
+    out, ws = run_mlp(d)
+    check_mlp(d, out, ws, sample_rows(M, d, n_random=32))
+
+
 def test_mlp_config4_sampled_and_deterministic():
     _say("config 4: fp8 MLP M=32760")
     kind, d = synth.config(4)
