@@ -44,19 +44,6 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 // round a float to the nearest bf16 value, returned as float
 __device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
 
-// p = RN32(v) with error e = v - p (exact): the fp32 value rounded to odd from v (truncate
-// toward zero, then force the last bit to 1 when inexact).  fp32 keeps 24 >= 8 + 2 significant
-// bits, so the RNE to bf16 that follows equals one rounding of v.  p == 0 only when v rounds
-// to zero in bf16 anyway.
-__device__ __forceinline__ float odd32(float p, float e) {
-    uint32_t u = __float_as_uint(p);
-    const bool inexact = (e != 0.f) & (p != 0.f);
-    const bool toward_zero = ((__float_as_uint(e) ^ u) & 0x80000000u) != 0u;   // |p| > |v|
-    u -= (inexact && toward_zero) ? 1u : 0u;
-    u |= inexact ? 1u : 0u;
-    return __uint_as_float(u);
-}
-
 // a / s rounded to nearest, given y = RN(1 / s) (one division per row instead of one per
 // element): q0 = RN(a y), the remainder a - q0 s by fma, and one fma correction (Markstein's
 // final step for a correctly rounded reciprocal).

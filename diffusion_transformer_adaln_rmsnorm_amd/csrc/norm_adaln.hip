@@ -45,12 +45,11 @@ __device__ __forceinline__ float load_row_rms(const uint16_t* xr, int lane, floa
     return 1.0f / sqrtf(ss / (float)kHidden + eps);
 }
 
-// a = bf16(shift + n * bf16(1 + scale)),  n = bf16(x * r * w), for one 8-wide chunk, each
-// bf16(...) one rounding of the exact value, in fp32 with error-free transforms:
-//   x w is exact (two 8-bit significands); (x w) r = p + e with e = fma(x w, r, -p);
-//   1 + scale is exact in fp32 unless |scale| < 2^-16, where both roundings give 1;
-//   n s1 is exact; shift + n s1 = s + e by TwoSum.
-// r is the FP32 reciprocal root.
+// a = bf16(shift + n * bf16(1 + scale)),  n = bf16((x * r) * w), for one 8-wide chunk, in FP32
+// in the formula block's order: x * r and its product with w each rounded to FP32, then RNE to
+// bf16.  1 + scale is exact in FP32 unless |scale| < 2^-16, where both roundings give 1;
+// n * bf16(1 + scale) is a product of two bf16 values, exact in FP32, so the fma rounds
+// shift + n s1 once to FP32 before the RNE to bf16.  r is the FP32 reciprocal root.
 __device__ __forceinline__ void modulate_chunk(const u32x4& xv, const u32x4& wv, const u32x4& scv,
                                                const u32x4& shv, float r, uint32_t (&out)[4]) {
     float x[8], w[8], sc[8], sh[8];
@@ -58,21 +57,13 @@ __device__ __forceinline__ void modulate_chunk(const u32x4& xv, const u32x4& wv,
     unpack8(wv, w);
     unpack8(scv, sc);
     unpack8(shv, sh);
-    float a[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float xw = x[e] * w[e];
-        const float p = xw * r;
-        const float n = rbf(odd32(p, fmaf(xw, r, -p)));
-        const float s1 = rbf(1.0f + sc[e]);
-        const float prod = n * s1;
-        const float s = sh[e] + prod;
-        const float z = s - sh[e];
-        const float err = (sh[e] - (s - z)) + (prod - z);
-        a[e] = odd32(s, err);
+    for (int k = 0; k < 4; ++k) {
+        // two elements per packed bf16 conversion
+        const uint32_t n = pack_bf2((x[2 * k] * r) * w[2 * k], (x[2 * k + 1] * r) * w[2 * k + 1]);
+        const uint32_t s1 = pack_bf2(1.0f + sc[2 * k], 1.0f + sc[2 * k + 1]);
+        out[k] = pack_bf2(fmaf(bf_lo(n), bf_lo(s1), sh[2 * k]), fmaf(bf_hi(n), bf_hi(s1), sh[2 * k + 1]));
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) out[k] = pack_bf2(a[2 * k], a[2 * k + 1]);
 }
 
 }  // namespace

@@ -180,6 +180,10 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     uint8_t* const out8 = static_cast<uint8_t*>(out);
     const __amdgpu_buffer_rsrc_t rout = make_rsrc(out8 + m0 * kOutRow * kElemB,
                                                   (uint32_t)(tile_rows * kOutRow * kElemB));
+    // P = 1: byte offset (within the tile's rows) of this lane's 8 elements in the first pass;
+    // each pass moves kRowsPerPass rows on
+    const uint32_t o1 = (uint32_t)((((rsub * kHeads + head) * 3 + kind) * kHeadDim + d0) * kElemB);
+    constexpr uint32_t kPassB = (uint32_t)(kRowsPerPass * kOutRow * kElemB);
     const float ds = kind == 0 ? dq : (kind == 1 ? dk : dv);          // this tile's descale
     const float ds_inv = kE4m3 ? 1.0f / ds : 0.0f;                     // RN(1 / ds)
     u32x4 nwv = {0u, 0u, 0u, 0u};       // this lane's 8 q/k norm weights
@@ -218,19 +222,19 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
         u32x4 o = vp;
         if (kind < 2) o = qk_norm_rope(vp, nwlo, nwhi, qk_eps, q, cv[it], sv[it]);
         // one destination: rows past M fall outside rout and are dropped; else out[dst, m, hl, ...]
-        const int64_t e1 = (((int64_t)row * kHeads + head) * 3 + kind) * kHeadDim + d0;
+        const uint32_t e1 = o1 + (uint32_t)it * kPassB;
         const int64_t m = m0 + row;
         const int64_t eP = (((dst * M + m) * hpd + hl) * 3 + kind) * kHeadDim + d0;
         if constexpr (kE4m3) {
             const u32x2 q = e4m3_codes8(o, ds, ds_inv);
             if (hpd == kHeads) {
-                __builtin_amdgcn_raw_buffer_store_b64(q, rout, (int)(uint32_t)e1, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(q, rout, (int)e1, 0, 0);
             } else if (m < M) {
                 *reinterpret_cast<u32x2*>(out8 + eP) = q;
             }
         } else {
             if (hpd == kHeads) {
-                buf_st16(rout, (uint32_t)(e1 * 2), o);
+                buf_st16(rout, e1, o);
             } else if (m < M) {
                 st16(out8 + eP * 2, o);
             }
