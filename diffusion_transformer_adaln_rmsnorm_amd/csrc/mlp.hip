@@ -14,6 +14,7 @@
 // turns each row's maximum into s_y and writes y_q; FC2 consumes y_q.  Stream order separates
 // the three launches, so no tile-ready flags are needed.
 #include "common.hpp"
+#include "gated.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
 
@@ -108,55 +109,11 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
     const int n0 = tn * kBN;
     Acc acc;
     mainloop<true>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc);
+    GatedResidual<int64_t> gr;
+    gr.load_index(idx, m0, M);
     stage_tile_bf16(acc, smem, y_scale, m0, M, w2s + n0, w2s + n0 + 128);
     __syncthreads();
-
-    const int t = threadIdx.x;
-    const int c8 = (t & 31) * 8;
-    const int rsub = t >> 5;
-    constexpr int kRowsPerPass = kThreads / 32;
-    constexpr int kIters = kBM / kRowsPerPass;
-    // residual and gate chunks of row it + 1 (and the index of row it + 2) load while row it
-    // computes; rows grow with it, so the first row past M ends the loop
-    auto index_of = [&](int it) -> int64_t {
-        const int64_t m = m0 + it * kRowsPerPass + rsub;
-        return it < kIters && m < M ? idx[m] : -1;
-    };
-    auto load_row = [&](int it, int64_t gi, u32x4& rr, u32x4& gg) {
-        const int64_t m = m0 + it * kRowsPerPass + rsub;
-        if (it < kIters && m < M) {
-            rr = ld16(residual + m * kHidden + n0 + c8);
-            if (gi >= 0 && gi < gate_rows) gg = ld16(gate + gi * gate_ld + n0 + c8);
-        }
-    };
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 r_cur = zero, g_cur = zero;
-    load_row(0, index_of(0), r_cur, g_cur);
-    int64_t gi_nx = index_of(1);
-#ifndef DIT_EPI_UNROLL
-#define DIT_EPI_UNROLL 1
-#endif
-#pragma unroll DIT_EPI_UNROLL
-    for (int it = 0; it < kIters; ++it) {
-        const int row = it * kRowsPerPass + rsub;
-        const int64_t m = m0 + row;
-        if (m >= M) break;
-        u32x4 r_nx = zero, g_nx = zero;
-        load_row(it + 1, gi_nx, r_nx, g_nx);
-        const int64_t gi_nx2 = index_of(it + 2);
-        float o[8], g[8], r[8];
-        unpack8(epi_ld(smem, row, c8), o);
-        unpack8(g_cur, g);
-        unpack8(r_cur, r);
-        // two bf16 values add exactly in fp32 (or the smaller is below half a bf16 ulp of the
-        // larger), so this is one rounding of the exact sum
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = rbf(r[e] + rbf(g[e] * o[e]));
-        st16(out + m * kHidden + n0 + c8, pack8(r));
-        r_cur = r_nx;
-        g_cur = g_nx;
-        gi_nx = gi_nx2;
-    }
+    gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);
 }
 
 hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M, const uint8_t* W1,

@@ -5,11 +5,10 @@
 // [0, rows) get gate 0 (out = residual).  Here the operands are bf16 and o = bf16(acc), the
 // rounding the fp8 MLP page prints for its own o.
 //
-// After the main loop the tile holds bf16(o) in LDS; each thread then owns 8 consecutive
-// columns of a row: it reads the residual and the gate row with 16-byte loads, and writes
-// out with one 16-byte store.  The residual is read before out is written by the same
-// thread, so out may be the residual buffer.
+// After the main loop the tile holds bf16(o) in LDS, and the gated-residual epilogue
+// (gated.hpp) writes out; out may be the residual buffer.
 #include "common.hpp"
+#include "gated.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
 
@@ -31,55 +30,11 @@ void k_out_proj_gemm(const uint16_t* __restrict__ attn, int64_t M, const uint16_
     mainloop<false>(reinterpret_cast<const uint8_t*>(attn), kAttnWidth * 2, m0, M,
                     reinterpret_cast<const uint8_t*>(Wo), kAttnWidth * 2, n0, n0 + 128, kAttnWidth * 2 / kRowB, smem,
                     acc);
+    GatedResidual<int32_t> gr;
+    gr.load_index(gate_index, m0, M);
     stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
     __syncthreads();
-
-    const int t = threadIdx.x;
-    const int c8 = (t & 31) * 8;
-    const int rsub = t >> 5;
-    constexpr int kRowsPerPass = kThreads / 32;
-    constexpr int kIters = kBM / kRowsPerPass;
-    // The residual and gate chunks of row it + 1 (and the gate index of row it + 2) are loaded
-    // while row it computes.  Rows grow with it, so the first row past M ends the loop.
-    auto gate_of = [&](int it) -> int64_t {
-        const int64_t m = m0 + it * kRowsPerPass + rsub;
-        return it < kIters && m < M ? (int64_t)gate_index[m] : -1;
-    };
-    auto load_row = [&](int it, int64_t gi, u32x4& rr, u32x4& gg) {
-        const int64_t m = m0 + it * kRowsPerPass + rsub;
-        if (it < kIters && m < M) {
-            rr = ld16(residual + m * kHidden + n0 + c8);
-            if (gi >= 0 && gi < gate_rows) gg = ld16(gate + gi * gate_ld + n0 + c8);
-        }
-    };
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    u32x4 r_cur = zero, g_cur = zero;
-    load_row(0, gate_of(0), r_cur, g_cur);
-    int64_t gi_nx = gate_of(1);
-#ifndef DIT_EPI_UNROLL
-#define DIT_EPI_UNROLL 1
-#endif
-#pragma unroll DIT_EPI_UNROLL
-    for (int it = 0; it < kIters; ++it) {
-        const int row = it * kRowsPerPass + rsub;
-        const int64_t m = m0 + row;
-        if (m >= M) break;
-        u32x4 r_nx = zero, g_nx = zero;
-        load_row(it + 1, gi_nx, r_nx, g_nx);
-        const int64_t gi_nx2 = gate_of(it + 2);
-        float o[8], g[8], r[8];
-        unpack8(epi_ld(smem, row, c8), o);
-        unpack8(g_cur, g);
-        unpack8(r_cur, r);
-        // two bf16 values add exactly in fp32 (or the smaller is below half a bf16 ulp of the
-        // larger), so this is one rounding of the exact sum
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r[e] = rbf(r[e] + rbf(g[e] * o[e]));
-        st16(out + m * kHidden + n0 + c8, pack8(r));
-        r_cur = r_nx;
-        g_cur = g_nx;
-        gi_nx = gi_nx2;
-    }
+    gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);
 }
 
 hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t* Wo, const uint16_t* gate,
