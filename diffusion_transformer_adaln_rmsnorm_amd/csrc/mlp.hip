@@ -40,27 +40,32 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
     const int c8 = (t & 15) * 8;
     const int rsub = t >> 4;            // 0..kThreads/16-1
     constexpr int kRowsPerPass = kThreads / 16;
+    // y rows of this tile through a descriptor: stores of rows past M are dropped by its bound
+    const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(y + m0 * kInter, (uint32_t)(tile_rows * kInter * 2));
+    const uint32_t o1 = (uint32_t)((rsub * kInter + j0 + c8) * 2);
+    constexpr uint32_t kPassB = (uint32_t)(kRowsPerPass * kInter * 2);
+#pragma unroll
     for (int it = 0; it < kBM / kRowsPerPass; ++it) {
         const int row = it * kRowsPerPass + rsub;
-        const int64_t m = m0 + row;
-        float hg[8], hu[8], yv[8];
-        unpack8(epi_ld(smem, row, c8), hg);
-        unpack8(epi_ld(smem, row, 128 + c8), hu);
+        const u32x4 hg = epi_ld(smem, row, c8), hu = epi_ld(smem, row, 128 + c8);
+        u32x4 yv;
         float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float sl = rbf(silu_fast(hg[e]));
-            yv[e] = rbf(sl * hu[e]);
-            amax = fmaxf(amax, fabsf(yv[e]));
+        for (int k = 0; k < 4; ++k) {
+            // two columns at a time: bf16(silu(h_gate)), then y = bf16(that * h_up)
+            const uint32_t sl = pack_bf2(silu_fast(bf_lo(hg[k])), silu_fast(bf_hi(hg[k])));
+            yv[k] = pack_bf2(bf_lo(sl) * bf_lo(hu[k]), bf_hi(sl) * bf_hi(hu[k]));
+            amax = fmaxf(amax, fabsf(bf_lo(yv[k])));
+            amax = fmaxf(amax, fabsf(bf_hi(yv[k])));
         }
         amax = fmaxf(amax, __shfl_xor(amax, 1));
         amax = fmaxf(amax, __shfl_xor(amax, 2));
         amax = fmaxf(amax, __shfl_xor(amax, 4));
         amax = fmaxf(amax, __shfl_xor(amax, 8));
-        if (m < M) {
-            st16(y + m * kInter + j0 + c8, pack8(yv));
-            if ((t & 15) == 0) atomicMax(reinterpret_cast<unsigned int*>(y_amax + m), __float_as_uint(amax));
-        }
+        buf_st16(ry, o1 + it * kPassB, yv);
+        if ((t & 15) == 0 && row < (int)tile_rows)
+            atomicMax(reinterpret_cast<unsigned int*>(y_amax + m0 + row), __float_as_uint(amax));
     }
 }
 
