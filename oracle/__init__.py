@@ -55,6 +55,16 @@ def lib():
                                       _d, _d, _p, _p]
         L.oracle_out_proj.restype = None
         L.oracle_out_proj.argtypes = [_i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p]
+        L.oracle_e2m1_value.restype = _d
+        L.oracle_e2m1_value.argtypes = [ctypes.c_uint8]
+        L.oracle_round_e2m1.restype = ctypes.c_uint8
+        L.oracle_round_e2m1.argtypes = [_d]
+        L.oracle_mx_scale_exp.restype = ctypes.c_int
+        L.oracle_mx_scale_exp.argtypes = [_d]
+        L.oracle_mx_quant_fp4.restype = None
+        L.oracle_mx_quant_fp4.argtypes = [_p, _i64, _i64, _p, _p]
+        L.oracle_out_proj_mxfp4.restype = None
+        L.oracle_out_proj_mxfp4.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p]
         L.oracle_mlp.restype = None
         L.oracle_mlp.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _d,
                                  _p, _p, _p, _p, _p, _p]
@@ -195,6 +205,74 @@ def out_proj(d, rows_sel=None, threads=None):
     def run(r0, r1):
         L.oracle_out_proj(r0, r1, _ptr(attn), _ptr(Wo), _table_ptr(g_b, g_o), rows, ld, _ptr(gi), _ptr(res),
                           _ptr(out))
+
+    _fan_out(run, R, threads)
+    return out
+
+
+def e2m1_value(c: int) -> float:
+    return lib().oracle_e2m1_value(c)
+
+
+def round_e2m1(v: float) -> int:
+    return lib().oracle_round_e2m1(v)
+
+
+def mx_scale_exp(amax: float) -> int:
+    return lib().oracle_mx_scale_exp(amax)
+
+
+def mx_quant_fp4(x_bits, threads=None):
+    """MXFP4 of bf16 rows x [R, K] (uint16 bits, K % 32 == 0): (codes [R, K/2] uint8 with element
+    2j in the low nibble of byte j, scales [R, K/32] uint8 E8M0, row-major)."""
+    x = _c(x_bits, np.uint16)
+    R, K = x.shape
+    codes = np.zeros((R, K // 2), np.uint8)
+    scales = np.zeros((R, K // 32), np.uint8)
+    L = lib()
+
+    def run(r0, r1):
+        L.oracle_mx_quant_fp4(ctypes.c_void_p(x.ctypes.data + 2 * r0 * K), r1 - r0, K,
+                              ctypes.c_void_p(codes.ctypes.data + r0 * (K // 2)),
+                              ctypes.c_void_p(scales.ctypes.data + r0 * (K // 32)))
+
+    _fan_out(run, R, threads)
+    return codes, scales
+
+
+def mx_values(codes, scales):
+    """The values of MXFP4 rows (codes [R, K/2], row-major scales [R, K/32]) as float64, through
+    the oracle's own E2M1 decoder."""
+    codes = np.asarray(codes, np.uint8)
+    tab = np.array([e2m1_value(c) for c in range(16)])
+    R, H = codes.shape
+    v = np.empty((R, 2 * H))
+    v[:, 0::2] = tab[codes & 15]
+    v[:, 1::2] = tab[codes >> 4]
+    return v * np.exp2(np.repeat(np.asarray(scales, np.float64) - 127.0, 32, axis=1))
+
+
+def out_proj_mxfp4(a_codes, a_scales, w_codes, w_scales, d, rows_sel=None, threads=4):
+    """Oracle of the MXFP4 W4A4 out-projection with gated residual on the rows rows_sel of the
+    activation codes/scales [M, 3584] / [M, 224] (row-major) and weight codes/scales [5376, 3584] /
+    [5376, 224]; gate, gate_index and residual come from d.  Returns out [R, 5376] uint16.  Each
+    call holds W's values in 308 MB of doubles, so few threads."""
+    M = d["M"]
+    sel = np.arange(M, dtype=np.int64) if rows_sel is None else np.asarray(rows_sel, np.int64)
+    R = sel.size
+    ac = _c(np.asarray(a_codes)[sel], np.uint8)
+    asc = _c(np.asarray(a_scales)[sel], np.uint8)
+    wc = _c(w_codes, np.uint8)
+    wsc = _c(w_scales, np.uint8)
+    gi = _c(d["gate_index"][sel], np.int32)
+    res = _c(d["residual"].reshape(M, HIDDEN)[sel], np.uint16)
+    g_b, g_o, rows, ld = _table(d["gate"])
+    out = np.zeros((R, HIDDEN), np.uint16)
+    L = lib()
+
+    def run(r0, r1):
+        L.oracle_out_proj_mxfp4(r0, r1, _ptr(ac), _ptr(asc), _ptr(wc), _ptr(wsc), _table_ptr(g_b, g_o), rows, ld,
+                                _ptr(gi), _ptr(res), _ptr(out))
 
     _fan_out(run, R, threads)
     return out

@@ -13,7 +13,8 @@
  *    and AdaLN, QKV projection, per-head Q/K RMSNorm, split-half NeoX RoPE on dims [0,96),
  *    destination-major pack.
  *  - "minimax_h3_nvfp4_out_proj", description: out = BF16(residual + BF16(gate[gate_index]*o)),
- *    gate 0 for indices outside [0, rows).
+ *    gate 0 for indices outside [0, rows); and, not on the pages, its MXFP4 (OCP
+ *    Microscaling) W4A4 counterpart (see the MXFP4 section).
  *
  * Arithmetic: every value between two rounding points the pages print is carried in
  * IEEE double; each bf16(...), e4m3(...) or RN(...) on the page is one round-to-nearest-even
@@ -198,6 +199,18 @@ void oracle_pre_attn(int64_t m0, int64_t m1, const uint16_t* x, const uint16_t* 
 
 /* ---- bf16 out-projection with gated residual ------------------------------------------- */
 
+/* out[m][n] = bf16(res + bf16(g * o)) for one row given o (already bf16); g = gate[i][n] when
+ * 0 <= i < rows, else 0. */
+static void gated_row(const double* o, int64_t i, const uint16_t* gate, int64_t rows, int64_t ld,
+                      const uint16_t* res, uint16_t* out) {
+    int valid = (i >= 0 && i < rows);
+    for (int n = 0; n < HID; n++) {
+        double g = valid ? bf(gate[i * ld + n]) : 0.0;
+        double go = bf(oracle_round_bf16(g * o[n]));
+        out[n] = oracle_round_bf16(bf(res[n]) + go);
+    }
+}
+
 /*
  * Rows [m0, m1): o = bf16(attn[m] . Wo[n]); g = gate[gi[m]][n] if 0 <= gi[m] < rows else 0;
  * out = bf16(res + bf16(g * o)).  attn[M][7168], Wo[5376][7168], gate row i at gate + i*ld.
@@ -206,20 +219,116 @@ void oracle_out_proj(int64_t m0, int64_t m1, const uint16_t* attn, const uint16_
                      const uint16_t* gate, int64_t rows, int64_t ld, const int32_t* gi,
                      const uint16_t* res, uint16_t* out) {
     double* a = (double*)malloc(sizeof(double) * ATTW);
+    double* o = (double*)malloc(sizeof(double) * HID);
     for (int64_t m = m0; m < m1; m++) {
         for (int k = 0; k < ATTW; k++) a[k] = bf(attn[m * ATTW + k]);
-        int64_t i = gi[m];
-        int valid = (i >= 0 && i < rows);
         for (int n = 0; n < HID; n++) {
             const uint16_t* wr = Wo + (int64_t)n * ATTW;
             double acc = 0.0;
             for (int k = 0; k < ATTW; k++) acc += a[k] * bf(wr[k]);
-            double o = bf(oracle_round_bf16(acc));
-            double g = valid ? bf(gate[i * ld + n]) : 0.0;
-            double go = bf(oracle_round_bf16(g * o));
-            out[m * HID + n] = oracle_round_bf16(bf(res[m * HID + n]) + go);
+            o[n] = bf(oracle_round_bf16(acc));
+        }
+        gated_row(o, gi[m], gate, rows, ld, res + m * HID, out + m * HID);
+    }
+    free(o);
+    free(a);
+}
+
+/* ---- MXFP4 (OCP Microscaling): E2M1 elements, one E8M0 scale per 32 along K --------------
+ * Not on the pages.  The gfx950-native counterpart of the NVFP4 W4A4 out-projection
+ * ("minimax_h3_nvfp4_out_proj": block-16 E2M1 with UE4M3 block scales and a global scale)
+ * in the format the hardware scales natively, OCP Microscaling Formats (MX) v1.0, MXFP4:
+ *  - a block is 32 consecutive values of a row along K; its scale is X = 2^(E - 127), stored
+ *    as the E8M0 byte E;
+ *  - E is the MX conversion's shared exponent: floor(log2(amax)) - 2 (2 is the largest E2M1
+ *    exponent), biased by 127 and clamped to [0, 254]; an all-zero block gets E = 0;
+ *  - each element is the E2M1 value nearest v / X (exact: X is a power of two), ties to the
+ *    even significand, magnitudes beyond 6 saturating to 6, the sign kept (so -0 is code 8);
+ *  - codes pack two per byte along K, element 2j in the low nibble of byte j.
+ */
+static const double e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double oracle_e2m1_value(uint8_t c) {
+    double v = e2m1_mag[c & 7];
+    return (c & 8) ? -v : v;
+}
+
+uint8_t oracle_round_e2m1(double v) {
+    uint8_t sign = signbit(v) ? 8u : 0u;
+    double a = fabs(v);
+    if (a >= 6.0) return (uint8_t)(sign | 7);     /* saturate (for huge a the distances below tie) */
+    int best = 0;
+    for (int c = 1; c < 8; c++) {
+        double d = fabs(a - e2m1_mag[c]), db = fabs(a - e2m1_mag[best]);
+        if (d < db || (d == db && (c & 1) == 0)) best = c;   /* the code's last bit is the significand */
+    }
+    return (uint8_t)(sign | best);
+}
+
+int oracle_mx_scale_exp(double amax) {
+    if (amax == 0.0) return 0;
+    int e;
+    frexp(amax, &e);                       /* amax = f 2^e, f in [0.5, 1): floor(log2) = e - 1 */
+    int E = (e - 1) - 2 + 127;
+    return E < 0 ? 0 : (E > 254 ? 254 : E);
+}
+
+/* x[R][K] bf16 -> codes[R][K/2], scales[R][K/32] (row-major E8M0 bytes).  K % 32 == 0. */
+void oracle_mx_quant_fp4(const uint16_t* x, int64_t R, int64_t K, uint8_t* codes, uint8_t* scales) {
+    for (int64_t r = 0; r < R; r++) {
+        for (int64_t b = 0; b < K / 32; b++) {
+            const uint16_t* v = x + r * K + b * 32;
+            double amax = 0.0;
+            for (int k = 0; k < 32; k++) {
+                double t = fabs(bf(v[k]));
+                if (t > amax) amax = t;
+            }
+            int E = oracle_mx_scale_exp(amax);
+            scales[r * (K / 32) + b] = (uint8_t)E;
+            for (int k = 0; k < 32; k += 2) {
+                uint8_t lo = oracle_round_e2m1(ldexp(bf(v[k]), 127 - E));
+                uint8_t hi = oracle_round_e2m1(ldexp(bf(v[k + 1]), 127 - E));
+                codes[r * (K / 2) + b * 16 + k / 2] = (uint8_t)(lo | (hi << 4));
+            }
         }
     }
+}
+
+/* the values of one MXFP4 row of n elements (n % 32 == 0) */
+static void mx_row_values(const uint8_t* codes, const uint8_t* scales, int64_t n, double* v) {
+    for (int64_t k = 0; k < n; k++) {
+        uint8_t c = (codes[k / 2] >> (4 * (k & 1))) & 15;
+        v[k] = ldexp(oracle_e2m1_value(c), (int)scales[k / 32] - 127);
+    }
+}
+
+/*
+ * Rows [m0, m1) of the MXFP4 W4A4 out-projection: o = bf16(A[m] . W[n]) with A and W the
+ * values of their MXFP4 codes and scales (exact products, exact double sum of 7168 terms up to
+ * rounding far below a bf16 ulp), then the gated residual of oracle_out_proj.
+ * a_codes[M][3584], a_scales[M][224], w_codes[5376][3584], w_scales[5376][224] (row-major).
+ */
+void oracle_out_proj_mxfp4(int64_t m0, int64_t m1, const uint8_t* a_codes, const uint8_t* a_scales,
+                           const uint8_t* w_codes, const uint8_t* w_scales, const uint16_t* gate,
+                           int64_t rows, int64_t ld, const int32_t* gi, const uint16_t* res, uint16_t* out) {
+    double* a = (double*)malloc(sizeof(double) * ATTW);
+    double* w = (double*)malloc(sizeof(double) * ATTW * HID);    /* all of W's values, 308 MB */
+    double* o = (double*)malloc(sizeof(double) * HID);
+    for (int n = 0; n < HID; n++)
+        mx_row_values(w_codes + (int64_t)n * (ATTW / 2), w_scales + (int64_t)n * (ATTW / 32), ATTW,
+                      w + (int64_t)n * ATTW);
+    for (int64_t m = m0; m < m1; m++) {
+        mx_row_values(a_codes + m * (ATTW / 2), a_scales + m * (ATTW / 32), ATTW, a);
+        for (int n = 0; n < HID; n++) {
+            const double* wr = w + (int64_t)n * ATTW;
+            double acc = 0.0;
+            for (int k = 0; k < ATTW; k++) acc += a[k] * wr[k];
+            o[n] = bf(oracle_round_bf16(acc));
+        }
+        gated_row(o, gi[m], gate, rows, ld, res + m * HID, out + m * HID);
+    }
+    free(o);
+    free(w);
     free(a);
 }
 

@@ -603,3 +603,144 @@ def test_quant_out_e4m3_divides_and_saturates():
     assert np.all(oracle.quant_out_e4m3(big | 0x8000, 1.0, 1.0, 1.0) == 0xFE)
     tie = np.full((1, 3, HD), oracle.round_bf16(1.0625), np.uint16)   # midway 1 and 1.125
     assert np.all(oracle.quant_out_e4m3(tie, 1.0, 1.0, 1.0) == 0x38)  # ties to even
+
+
+# ---------------------------------------------------------------- MXFP4 (OCP Microscaling)
+
+E2M1_GRID = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def test_e2m1_values_match_the_bit_fields():
+    # OCP MX v1.0, FP4 E2M1: sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is
+    # subnormal (m * 2^-1)
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        v = m / 2.0 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2.0)
+        v = -v if s else v
+        got = oracle.e2m1_value(c)
+        assert got == v and math.copysign(1.0, got) == math.copysign(1.0, v), c
+
+
+def test_golden_e2m1_encodings():
+    for v, c in _golden("e2m1_codes.txt"):
+        assert oracle.round_e2m1(v) == c, (v, hex(c), hex(oracle.round_e2m1(v)))
+
+
+def test_round_e2m1_is_nearest_with_the_sign_kept():
+    rng = np.random.default_rng(11)
+    grid = np.array(E2M1_GRID)
+    for v in np.concatenate([rng.uniform(-9, 9, 3000), rng.uniform(-1, 1, 1000)]):
+        c = oracle.round_e2m1(float(v))
+        got = oracle.e2m1_value(c)
+        assert abs(abs(v) - abs(got)) <= np.min(np.abs(abs(v) - grid)) + 0.0
+        assert math.copysign(1.0, got) == math.copysign(1.0, v)
+    # monotone in v
+    vs = np.linspace(-8, 8, 4001)
+    vals = [oracle.e2m1_value(oracle.round_e2m1(float(v))) for v in vs]
+    assert all(a <= b for a, b in zip(vals, vals[1:]))
+
+
+def test_mx_scale_exp_closed_forms():
+    assert oracle.mx_scale_exp(0.0) == 0
+    for k in range(-125, 128, 3):
+        for f in (1.0, 1.25, 1.5, 1.99609375):
+            assert oracle.mx_scale_exp(f * 2.0 ** k) == k - 2 + 127, (k, f)
+    assert oracle.mx_scale_exp(2.0 ** -126) == 0          # below the byte range: clamped
+    assert oracle.mx_scale_exp(2.0 ** -133) == 0          # smallest bf16 subnormal
+    assert oracle.mx_scale_exp(2.0 ** 200) == 254         # above it
+
+
+def _mx_exact_rows(rng, R, K):
+    """bf16 rows whose every 32-block is exactly representable in MXFP4 with scale 2^k: E2M1
+    grid values times 2^k, one element of magnitude 4 or 6 (so floor(log2 amax) = k + 2)."""
+    k = rng.integers(-8, 3, (R, K // 32))
+    mag = rng.choice(np.array(E2M1_GRID), (R, K))
+    sign = rng.choice([-1.0, 1.0], (R, K))
+    v = mag * sign
+    v[:, ::32] = rng.choice([-6.0, -4.0, 4.0, 6.0], (R, K // 32))
+    v = v * np.exp2(np.repeat(k, 32, axis=1))
+    return synth.to_bf16_bits(v.astype(np.float32)), k
+
+
+def test_mx_quant_fp4_is_exact_on_representable_blocks():
+    rng = np.random.default_rng(12)
+    x, k = _mx_exact_rows(rng, 6, 512)
+    codes, scales = oracle.mx_quant_fp4(x)
+    assert np.array_equal(scales.astype(np.int64), k + 127)
+    assert np.array_equal(oracle.mx_values(codes, scales), bf16_val(x))
+
+
+def test_mx_quant_fp4_worked_block():
+    # one 32-block: amax 7 -> floor(log2 7) = 2 -> E = 127 (X = 1); 7 saturates to 6, 0.3 -> 0.5,
+    # -2 -> -2, 2.5 -> 2 (tie to even), -0.1 -> -0, the rest 0
+    v = np.zeros(32, np.float32)
+    v[:6] = [1.0, -2.0, 0.3, 7.0, 2.5, -0.1]
+    codes, scales = oracle.mx_quant_fp4(synth.to_bf16_bits(v)[None, :])
+    assert scales.tolist() == [[127]]
+    nib = [(int(b) >> s) & 15 for b in codes[0] for s in (0, 4)]   # element 2j in the low nibble
+    assert nib[:6] == [0x2, 0xC, 0x1, 0x7, 0x4, 0x8] and nib[6:] == [0] * 26
+    # scaled: the same block times 2^-20 gets E = 107 and the same codes
+    codes2, scales2 = oracle.mx_quant_fp4(synth.to_bf16_bits(v * np.float32(2.0 ** -20))[None, :])
+    assert scales2.tolist() == [[107]] and np.array_equal(codes2, codes)
+
+
+def test_mx_quant_fp4_block_properties():
+    rng = np.random.default_rng(13)
+    R, K = 8, 1024
+    v = rng.standard_normal((R, K)) * np.exp2(rng.integers(-30, 30, (R, 1)))
+    v[0, 64:96] = 0.0                                         # an all-zero block
+    x = synth.to_bf16_bits(v.astype(np.float32))
+    codes, scales = oracle.mx_quant_fp4(x)
+    xv = bf16_val(x).reshape(R, K // 32, 32)
+    q = oracle.mx_values(codes, scales).reshape(R, K // 32, 32)
+    amax = np.abs(xv).max(axis=2)
+    X = np.exp2(scales.astype(np.float64) - 127)
+    assert scales[0, 2] == 0 and np.all(q[0, 2] == 0)
+    nz = amax > 0
+    assert np.all((amax[nz] / X[nz] >= 4) & (amax[nz] / X[nz] < 8))
+    # every element is within half a grid step of its value (or saturated at 6 X)
+    y = np.abs(xv) / X[:, :, None]
+    step = np.where(y < 2, 0.5, np.where(y < 4, 1.0, 2.0))
+    err = np.abs(np.abs(q) / X[:, :, None] - np.minimum(y, 6.0))
+    assert np.all(err <= step / 2 + 1e-12)
+
+
+def _mx_d(rng, M, gate_rows=9):
+    g = rng.standard_normal((gate_rows, H)).astype(np.float32)
+    gate = synth.Table(synth.to_bf16_bits(g), 0, gate_rows, H)
+    return {"M": M, "gate": gate,
+            "gate_index": rng.integers(-1, gate_rows + 1, M).astype(np.int32),
+            "residual": synth.to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))}
+
+
+def test_out_proj_mxfp4_equals_the_bf16_oracle_on_representable_inputs():
+    # attn and W exactly representable in MXFP4: the W4A4 out-projection of their codes must give
+    # the bf16 out-projection's result bit for bit
+    rng = np.random.default_rng(14)
+    M = 3
+    attn, _ = _mx_exact_rows(rng, M, synth.ATTN_WIDTH)
+    W, _ = _mx_exact_rows(rng, H, synth.ATTN_WIDTH)
+    d = _mx_d(rng, M)
+    d["gate_index"][:3] = [0, -1, 8]
+    d.update(attn_out=attn, o_weight=W)
+    ac, asc = oracle.mx_quant_fp4(attn)
+    wc, wsc = oracle.mx_quant_fp4(W)
+    got = oracle.out_proj_mxfp4(ac, asc, wc, wsc, d)
+    assert np.array_equal(got, oracle.out_proj(d))
+
+
+def test_out_proj_mxfp4_matches_float64_matmul_of_the_values():
+    # gate 1 and residual 0: out = bf16(o) = bf16(A . W), A and W the MXFP4 values
+    rng = np.random.default_rng(15)
+    M = 2
+    a = rng.integers(0, 256, (M, synth.ATTN_WIDTH // 2)).astype(np.uint8)
+    a_s = rng.integers(118, 130, (M, synth.ATTN_WIDTH // 32)).astype(np.uint8)
+    w = rng.integers(0, 256, (H, synth.ATTN_WIDTH // 2)).astype(np.uint8)
+    w_s = rng.integers(118, 130, (H, synth.ATTN_WIDTH // 32)).astype(np.uint8)
+    d = {"M": M, "gate": synth.Table(synth.to_bf16_bits(np.ones((1, H), np.float32)), 0, 1, H),
+         "gate_index": np.zeros(M, np.int32), "residual": np.zeros((M, H), np.uint16)}
+    got = oracle.out_proj_mxfp4(a, a_s, w, w_s, d)
+    A = torch.from_numpy(oracle.mx_values(a, a_s))
+    Wv = torch.from_numpy(oracle.mx_values(w, w_s))
+    want = (A @ Wv.T).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
