@@ -17,6 +17,7 @@ import torch
 
 __all__ = ["dit_pre_attn_bf16", "dit_pre_attn_e4m3", "dit_norm_adaln_bf16", "dit_qkv_rope_pack_bf16",
            "dit_qkv_rope_pack_e4m3", "dit_out_proj_gated_bf16", "dit_mlp_fp8", "dit_mlp_fp8_flags_elems",
+           "dit_mx_scale_bytes", "dit_mx_quant_fp4", "dit_out_proj_gated_mxfp4",
            "DitError", "load_library", "LIB_PATH", "HIDDEN", "HEADS", "HEAD_DIM", "QKV_ROWS", "ATTN_WIDTH",
            "INTER", "FC1_ROWS", "MLP_MAX_M"]
 
@@ -77,6 +78,12 @@ def load_library(path: str = LIB_PATH):
     L.dit_qkv_rope_pack_e4m3.argtypes = [_p, _i64, _p, _p, _p, _p, _i64, _p, _i32, _f, _f, _f, _f, _p, _p]
     L.dit_out_proj_gated_bf16.restype = _i32
     L.dit_out_proj_gated_bf16.argtypes = [_p, _i64, _p, Table, _p, _p, _p, _p]
+    L.dit_mx_scale_bytes.restype = _i64
+    L.dit_mx_scale_bytes.argtypes = [_i64, _i64]
+    L.dit_mx_quant_fp4.restype = _i32
+    L.dit_mx_quant_fp4.argtypes = [_p, _i64, _i64, _p, _p, _p]
+    L.dit_out_proj_gated_mxfp4.restype = _i32
+    L.dit_out_proj_gated_mxfp4.argtypes = [_p, _i64, _p, _p, Table, _p, _p, _p, _p, _p, _p]
     L.dit_mlp_fp8.restype = _i32
     L.dit_mlp_fp8.argtypes = [_p, _i64, _p, Table, Table, Table, _p, _p, _p, _p, _p, _p, _f, _p, _p, _p, _p, _p, _p,
                               _p, _p]
@@ -261,6 +268,55 @@ def dit_out_proj_gated_bf16(attn_out, o_weight, gate, gate_index, residual, *, o
     st = L.dit_out_proj_gated_bf16(_ptr(attn_out), M, _ptr(o_weight), tg, _ptr(gate_index), _ptr(residual),
                                    _ptr(out), _stream())
     _check("dit_out_proj_gated_bf16", st)
+    return out
+
+
+def dit_mx_scale_bytes(rows: int, K: int) -> int:
+    return int(load_library().dit_mx_scale_bytes(int(rows), int(K)))
+
+
+def dit_mx_quant_fp4(x, *, codes=None, scales=None):
+    """MXFP4 of bf16 rows x [R, K] (K % 256 == 0): returns (codes uint8 [R, K/2], scales uint8
+    [dit_mx_scale_bytes(R, K)] in the MX scale layout)."""
+    L = load_library()
+    R, K = (x.shape[0], x.shape[1]) if x.dim() == 2 else (-1, -1)
+    _need(x, "x", torch.bfloat16, (R, K))
+    if codes is None:
+        codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((dit_mx_scale_bytes(R, K),), dtype=torch.uint8, device=x.device)
+    _need(codes, "codes", torch.uint8, (R, K // 2))
+    _need(scales, "scales", torch.uint8, (dit_mx_scale_bytes(R, K),))
+    st = L.dit_mx_quant_fp4(_ptr(x), R, K, _ptr(codes), _ptr(scales), _stream())
+    _check("dit_mx_quant_fp4", st)
+    return codes, scales
+
+
+def dit_out_proj_gated_mxfp4(attn_out, w_codes, w_scales, gate, gate_index, residual, *, out=None, act_codes=None,
+                             act_scales=None):
+    """MXFP4 W4A4 out-projection with the gated residual; returns out [M, 5376].  w_codes /
+    w_scales come from dit_mx_quant_fp4 of the bf16 weight [5376, 7168]."""
+    L = load_library()
+    M = attn_out.shape[0] if attn_out.dim() == 2 else -1
+    dev = attn_out.device
+    _need(attn_out, "attn_out", torch.bfloat16, (M, ATTN_WIDTH))
+    _need(w_codes, "w_codes", torch.uint8, (HIDDEN, ATTN_WIDTH // 2))
+    _need(w_scales, "w_scales", torch.uint8, (dit_mx_scale_bytes(HIDDEN, ATTN_WIDTH),))
+    tg = _table(gate, "gate")
+    _need(gate_index, "gate_index", torch.int32, (M,))
+    _need(residual, "residual", torch.bfloat16, (M, HIDDEN))
+    if out is None:
+        out = torch.empty((M, HIDDEN), dtype=torch.bfloat16, device=dev)
+    if act_codes is None:
+        act_codes = torch.empty((M, ATTN_WIDTH // 2), dtype=torch.uint8, device=dev)
+    if act_scales is None:
+        act_scales = torch.empty((dit_mx_scale_bytes(M, ATTN_WIDTH),), dtype=torch.uint8, device=dev)
+    _need(out, "out", torch.bfloat16, (M, HIDDEN))
+    _need(act_codes, "act_codes", torch.uint8, (M, ATTN_WIDTH // 2))
+    _need(act_scales, "act_scales", torch.uint8, (dit_mx_scale_bytes(M, ATTN_WIDTH),))
+    st = L.dit_out_proj_gated_mxfp4(_ptr(attn_out), M, _ptr(w_codes), _ptr(w_scales), tg, _ptr(gate_index),
+                                    _ptr(residual), _ptr(act_codes), _ptr(act_scales), _ptr(out), _stream())
+    _check("dit_out_proj_gated_mxfp4", st)
     return out
 
 

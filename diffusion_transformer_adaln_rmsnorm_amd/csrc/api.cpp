@@ -190,6 +190,44 @@ dit_status dit_out_proj_gated_bf16(const void* attn_out, int64_t M, const void* 
         static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
 }
 
+int64_t dit_mx_scale_bytes(int64_t rows, int64_t K) {
+    if (rows < 0 || K < 0) return 0;
+    return dit::mx_scale_bytes(rows, K);
+}
+
+dit_status dit_mx_quant_fp4(const void* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales, void* stream) {
+    if (rows < 0 || K < 256 || K % 256 != 0) return DIT_ERR_SHAPE;
+    // one thread per 32-value block of the padded rows: the grid must fit 2^31 threads
+    if ((rows + 127) / 128 * 128 > ((int64_t)1 << 31) / (K / 32)) return DIT_ERR_SHAPE;
+    if (!x || !codes || !scales) return DIT_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(codes, 16)) return DIT_ERR_ALIGN;
+    if (rows == 0) return DIT_OK;
+    return launched(dit::launch_mx_quant_fp4(static_cast<const uint16_t*>(x), rows, K, codes, scales,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+dit_status dit_out_proj_gated_mxfp4(const void* attn_out, int64_t M, const uint8_t* w_codes, const uint8_t* w_scales,
+                                    dit_bf16_table gate, const int32_t* gate_index, const void* residual,
+                                    uint8_t* act_codes, uint8_t* act_scales, void* out, void* stream) {
+    if (M < 0 || M > kMaxRows) return DIT_ERR_SHAPE;
+    if (!attn_out || !w_codes || !w_scales || !gate_index || !residual || !act_codes || !act_scales || !out)
+        return DIT_ERR_NULL;
+    dit_status st = check_table(gate);
+    if (st != DIT_OK) return st;
+    if (!aligned(attn_out, 16) || !aligned(w_codes, 16) || !aligned(residual, 16) || !aligned(out, 16) ||
+        !aligned(act_codes, 16) || !aligned(w_scales, 16) || !aligned(act_scales, 16) || !aligned(gate_index, 4))
+        return DIT_ERR_ALIGN;
+    if (M == 0) return DIT_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launched(dit::launch_mx_quant_fp4(static_cast<const uint16_t*>(attn_out), M, DIT_ATTN_WIDTH, act_codes,
+                                           act_scales, s));
+    if (st != DIT_OK) return st;
+    return launched(dit::launch_out_proj_mxfp4(act_codes, act_scales, M, w_codes, w_scales,
+                                               static_cast<const uint16_t*>(gate.ptr), gate.rows, gate.row_stride,
+                                               gate_index, static_cast<const uint16_t*>(residual),
+                                               static_cast<uint16_t*>(out), s));
+}
+
 dit_status dit_mlp_fp8(const void* x, int64_t M, const void* x_norm_weight, dit_bf16_table adaln_scale,
                        dit_bf16_table adaln_shift, dit_bf16_table gate, const int64_t* adaln_index,
                        const void* residual, const uint8_t* fc1_q, const float* fc1_scale, const uint8_t* fc2_q,

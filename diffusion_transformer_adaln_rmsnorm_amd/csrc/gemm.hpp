@@ -6,8 +6,9 @@
 // Workgroup: 8 waves, two per SIMD, and one 256 x 256 output tile; each wave owns a 128 x 64
 // wave tile of 8 x 4 blocks of 16 x 16 (128 FP32 accumulators per lane, so a wave fits in 256
 // registers):
-//   bf16: v_mfma_f32_16x16x32_bf16, two k-steps per stage;
-//   e4m3: v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), one k-step per stage.
+//   bf16:  v_mfma_f32_16x16x32_bf16, two k-steps per stage;
+//   e4m3:  v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), one k-step per stage;
+//   mxfp4: the same instruction on E2M1 operands with their E8M0 block scales, two k-steps.
 // Under a full-chip load the shader clock is set by power.  For the same MACs the 16x16 forms
 // move fewer register bytes than the 32x32 ones (bf16: operands plus accumulator read and
 // write, 0.5 against 0.625 bytes per MAC), and a register-only MFMA loop sustains about 12%
@@ -35,7 +36,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWN = 4;                          // waves across n (two across m)
 constexpr int kWaveN = kBN / kWN;               // wave tile: 128 rows x 64 columns
 constexpr int kOpBytes = 256 * kRowB;           // one operand of one stage (an LDS slot)
-constexpr int kMainBytes = 4 * kOpBytes;        // two slots per operand
+constexpr int kScaleSlot = 2048;               // MXFP4 scales of one operand of one stage
+constexpr int kMainBytes = 4 * kOpBytes + 4 * kScaleSlot;   // two slots per operand and per scale set
 constexpr int kEpiPitch = kBN * 2 + 16;         // bf16 epilogue tile, padded row pitch (bytes)
 constexpr int kEpiBytes = kBM * kEpiPitch;      // 132 KiB
 constexpr int kSmemBytes = kMainBytes > kEpiBytes ? kMainBytes : kEpiBytes;
@@ -48,6 +50,19 @@ constexpr int kRowsPerPiece = 1024 / kRowB;     // rows filled by one 1 KiB wave
 // 16-byte bank groups of the 64-bank LDS.  Fills are 64 lanes writing 1 KiB contiguously,
 // conflict-free.
 __host__ __device__ constexpr int swz(int r) { return (r >> 1) & 7; }
+
+// What the operands hold: bf16 values, e4m3 codes, or MXFP4 (E2M1 codes, two per byte, with
+// E8M0 scales of 32-value blocks in the MX scale layout below).
+enum class Mma { kBf16, kE4m3, kMxFp4 };
+
+// MX scale layout.  For a matrix of R rows (padded to a multiple of 128) and K values per row
+// (a multiple of 256), the E8M0 scale of row r, block b (values 32 b .. 32 b + 31) is the byte
+//   ((r / 128) (K / 256) + b / 8) 1024 + 16 l + 2 ((r % 128) / 16) + (b % 8) / 4,
+//   l = r % 16 + 16 (b % 4).
+// So each 128 rows x 256 values (one GEMM stage of a wave-row of 128) own 1 KiB, in which lane
+// l's 16 bytes are the scales it hands the MFMA: the instruction takes the scale of row l % 16
+// and block l / 16 of a 16 x 128 operand from lane l, for each of the 8 16-row blocks and the
+// 2 k-steps of the stage.
 
 // Workgroup id -> (m tile, n tile).  Workgroups are dispatched round-robin over the 8 XCDs,
 // so id % 8 names the XCD: each XCD gets one contiguous range of the logical order, and the
@@ -98,6 +113,8 @@ constexpr int kVPat = 2;
 struct Stage {
     const uint8_t* a;
     const uint8_t* b;
+    const uint8_t* sa;     // MXFP4 scale slots (unused otherwise)
+    const uint8_t* sb;
 };
 
 // Accumulators of one wave: 8 x 4 blocks of 16 x 16.  Lane l, register r of a block holds
@@ -119,11 +136,15 @@ struct Acc {
 constexpr int kBlk = 16 * kRowB;                // bytes between 16-row blocks
 struct FragAddr {
     uint32_t a[2], b[2];
+    uint32_t sa, sb;       // MXFP4: this lane's scale bytes in an A / B scale slot
     __device__ __forceinline__ void init() {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / kWN, wn = wave % kWN;
         const int r = lane % 16, g = lane / 16;
         const int sw = swz(r);
+        // A: the 1 KiB of the wave's 128 rows; B: the wave's 64 rows are half of a 128-row group
+        sa = (uint32_t)(wm * 1024 + lane * 16);
+        sb = (uint32_t)((wn / 2) * 1024 + lane * 16 + (wn % 2) * 8);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int c = 4 * q + g;
@@ -182,6 +203,12 @@ struct PPFill {
     uint32_t vb[kVPat];       // B: row-in-piece + chunk offset, by piece parity (per lane)
     uint32_t sb[kPPBPieces];  // B: offset of piece j's first row (uniform)
     uint32_t lds_a, lds_b;    // this wave's rows within an A slot / a B slot
+    // MXFP4 scales: a wave moves 256-byte quarters (4 bytes per lane) of 1 KiB scale blocks
+    __amdgpu_buffer_rsrc_t rsa, rsb;   // A: the wave's 128-row group; B: from the tile's first
+    uint32_t vs;              // per lane: its 4 bytes of the wave's quarter of a stage's 1 KiB
+    uint32_t vsb1;            // the same in the tile's second B group (relative to rsb)
+    uint32_t lds_sa;          // the quarter's offset within an A scale slot
+    uint32_t lds_q;           // the quarter's offset within a 1 KiB group (uniform)
     // Stage kt of this wave's rows into `slot`.  A load past the last stage (live false) goes
     // through rnull: it reads no memory and writes zeros into a slot that has no reader left,
     // but still counts in vmcnt, so every phase issues the same number of loads.
@@ -200,13 +227,48 @@ struct PPFill {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + j * 1024, 16, (int)vb[j % kVPat], (int)sb[j] + kt * kRowB,
                                                      0, 0);
     }
+    __device__ __forceinline__ void a_scales(uint8_t* smem, int slot, int kt, bool live) const {
+        lds_u8* S = (lds_u8*)smem + 4 * kOpBytes + slot * kScaleSlot + lds_sa;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsa : rnull, S, 4, (int)(vs + kt * 1024), 0, 0, 0);
+    }
+    // both B groups (G0 moves all B scales: every wave reads the whole of a group)
+    __device__ __forceinline__ void b_scales(uint8_t* smem, int slot, int kt, bool live) const {
+        lds_u8* S = (lds_u8*)smem + 4 * kOpBytes + (2 + slot) * kScaleSlot + lds_q;
+        const __amdgpu_buffer_rsrc_t r = live ? rsb : rnull;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S, 4, (int)(vs + kt * 1024), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + 1024, 4, (int)(vsb1 + kt * 1024), 0, 0, 0);
+    }
 };
 
-// Every fragment of one stage in registers (24 16-byte reads, 96 registers).
-template <bool kFp8>
+// v_mfma_scale_f32_16x16x128_f8f6f4 on E2M1 operands (4 registers each, format 4 for both),
+// scale_a / scale_b the E8M0 bytes OA / OB of the lanes' scale words.  The four-register form
+// of the intrinsic is named directly: the builtin only takes the eight-register (fp8) operands.
+extern "C" __device__ f32x4 __dit_mfma_scale_f4(i32x4 a, i32x4 b, f32x4 c, int cbsz, int blgp, int opsel_a,
+                                                int scale_a, int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
+// byte selectors as immediates: oa, ob are constants once the MFMA loops are unrolled, and each
+// case passes literal ones
+__device__ __forceinline__ f32x4 mfma_mxfp4(const i32x4& a, const i32x4& b, const f32x4& c, uint32_t sa,
+                                            uint32_t sb, int oa, int ob) {
+#define DIT_MX_CASE(A_, B_) \
+    case A_ * 4 + B_:       \
+        return __dit_mfma_scale_f4(a, b, c, 4, 4, A_, (int)sa, B_, (int)sb);
+    switch (oa * 4 + ob) {
+        DIT_MX_CASE(0, 0) DIT_MX_CASE(0, 1) DIT_MX_CASE(0, 2) DIT_MX_CASE(0, 3)
+        DIT_MX_CASE(1, 0) DIT_MX_CASE(1, 1) DIT_MX_CASE(1, 2) DIT_MX_CASE(1, 3)
+        DIT_MX_CASE(2, 0) DIT_MX_CASE(2, 1) DIT_MX_CASE(2, 2) DIT_MX_CASE(2, 3)
+        DIT_MX_CASE(3, 0) DIT_MX_CASE(3, 1) DIT_MX_CASE(3, 2) default:
+            return __dit_mfma_scale_f4(a, b, c, 4, 4, 3, (int)sa, 3, (int)sb);
+    }
+#undef DIT_MX_CASE
+}
+
+// Every fragment of one stage in registers (24 16-byte reads, 96 registers; MXFP4 adds 24
+// bytes of scales).
+template <Mma kKind>
 struct PPFrags;
 template <>
-struct PPFrags<false> {
+struct PPFrags<Mma::kBf16> {
     static constexpr int MB = Acc::MB, NB = Acc::NB;
     bf16x8 a[2][MB], b[2][NB];
     __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
@@ -229,7 +291,7 @@ struct PPFrags<false> {
     }
 };
 template <>
-struct PPFrags<true> {
+struct PPFrags<Mma::kE4m3> {
     static constexpr int MB = Acc::MB, NB = Acc::NB;
     i32x8 a[MB], b[NB];
     __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
@@ -246,6 +308,37 @@ struct PPFrags<true> {
                 acc.v[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc.v[i][j], 0, 0, 0, 0, 0, 0);
     }
 };
+// MXFP4: a 128-byte stage row is 256 E2M1 values, two k-steps of 128; lane group g reads 16
+// bytes (32 values, block 4 ks + g) of its row, the same chunks as the bf16 reads.  Scale byte
+// 2 i + ks of the lane's A record belongs to block row i, k-step ks (B: 2 j + ks).
+template <>
+struct PPFrags<Mma::kMxFp4> {
+    static constexpr int MB = Acc::MB, NB = Acc::NB;
+    i32x4 a[2][MB], b[2][NB];
+    u32x4 sa;
+    u32x2 sb;
+    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i) a[ks][i] = __builtin_bit_cast(i32x4, lds_ld16(st.a, fa.a[ks] + i * kBlk));
+#pragma unroll
+            for (int j = 0; j < NB; ++j) b[ks][j] = __builtin_bit_cast(i32x4, lds_ld16(st.b, fa.b[ks] + j * kBlk));
+        }
+        sa = lds_ld16(st.sa, fa.sa);
+        sb = *reinterpret_cast<const u32x2*>(st.sb + fa.sb);
+    }
+    __device__ __forceinline__ void mma(Acc& acc) const {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+                for (int j = 0; j < NB; ++j)
+                    acc.v[i][j] = mfma_mxfp4(a[ks][i], b[ks][j], acc.v[i][j], sa[i / 2], sb[j / 2], 2 * (i % 2) + ks,
+                                             2 * (j % 2) + ks);
+    }
+};
 
 // Phase-ending barrier: wait for vmcnt(kVm) and lgkmcnt(0), then a bare s_barrier.  These
 // waits are all the hand-over needs, so younger fill loads stay in flight across it (the
@@ -258,12 +351,25 @@ __device__ __forceinline__ void pp_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-template <bool kFp8>
+// MXFP4 scale arrays of A and B in the MX scale layout, and their sizes in bytes (unused for
+// the other operand kinds).
+struct MxScales {
+    const uint8_t* a = nullptr;
+    uint32_t a_bytes = 0;
+    const uint8_t* b = nullptr;
+    uint32_t b_bytes = 0;
+};
+
+template <Mma kKind>
 __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                             const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                            int ktiles, uint8_t* smem, Acc& acc) {
+                                            int ktiles, uint8_t* smem, Acc& acc, const MxScales& mxs) {
     static_assert(kWaves == 8 && kRowB == 128, "ping-pong layout");
-    static_assert(4 * kOpBytes <= kSmemBytes, "two slots per operand");
+    static_assert(kMainBytes <= kSmemBytes, "two slots per operand and per scale set");
+    constexpr bool kMx = kKind == Mma::kMxFp4;
+    // loads per wave and memory phase: A rows (+ A scales), and G1's B rows
+    constexpr int kAF = kPPAPieces + (kMx ? 1 : 0);
+    constexpr int kBF = kPPBPieces;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const bool g0 = wave < 4;
@@ -289,6 +395,22 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     }
     sf.lds_a = (uint32_t)(32 * wave * kRowB);
     sf.lds_b = (uint32_t)(64 * c * kRowB);
+    if constexpr (kMx) {
+        // A scales: each group moves those of its own rows (read only by its waves), wave c one
+        // quarter of each 1 KiB; a group past the end of the array (the last m tile's second
+        // half) reads zeros.  B scales: G0 moves both groups (a B group is read by waves of both
+        // groups, so its refill waits until both have read it, as G0's memory phase does).
+        const int64_t group_bytes = (int64_t)ktiles * 1024;
+        const int64_t ga = m0 / 128 + (g0 ? 0 : 1);
+        const int64_t a_rest = (int64_t)mxs.a_bytes - ga * group_bytes;
+        sf.rsa = make_rsrc(mxs.a + (a_rest > 0 ? ga * group_bytes : 0), (uint32_t)(a_rest > 0 ? a_rest : 0));
+        const int64_t gb0 = nb0 / 128, gb1 = nb1 / 128;
+        sf.rsb = make_rsrc(mxs.b + gb0 * group_bytes, (uint32_t)((int64_t)mxs.b_bytes - gb0 * group_bytes));
+        sf.vs = (uint32_t)(c * 256 + lane * 4);
+        sf.vsb1 = sf.vs + (uint32_t)((gb1 - gb0) * group_bytes);
+        sf.lds_q = (uint32_t)(c * 256);
+        sf.lds_sa = (g0 ? 0u : 1024u) + sf.lds_q;
+    }
     FragAddr fa;
     fa.init();
 #pragma unroll
@@ -298,20 +420,24 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
 
     auto slot = [&](int kt) -> Stage {
         const int s = kt & 1;
-        return Stage{smem + s * kOpBytes, smem + 2 * kOpBytes + s * kOpBytes};
+        return Stage{smem + s * kOpBytes, smem + (2 + s) * kOpBytes, smem + 4 * kOpBytes + s * kScaleSlot,
+                     smem + 4 * kOpBytes + (2 + s) * kScaleSlot};
     };
-    PPFrags<kFp8> fr;
+    PPFrags<kKind> fr;
 
-    // prologue: A of stage 0 (each wave its rows), B of stages 0 and 1 (G1).  Only stage 0 must
-    // have landed here; B of stage 1 is first read in phase 2, after G1's memory-phase barrier
-    // (whose vmcnt limit counts only younger loads).
+    // prologue: A of stage 0 (each wave its rows, with their MXFP4 scales), B of stages 0 and 1
+    // (G1), the B scales of stage 0 (G0; those of stage s+1 follow in G0's memory phase s).
+    // Only stage 0 must have landed here; B of stage 1 is first read in phase 2, after G1's
+    // memory-phase barrier (whose vmcnt limit counts only younger loads).
     sf.a_rows(smem, 0, 0, true);
+    if constexpr (kMx) sf.a_scales(smem, 0, 0, true);
     if (!g0) {
         sf.b_rows(smem, 0, 0, true);
         sf.b_rows(smem, 1, 1, ktiles > 1);
-        pp_barrier<kPPBPieces>();
+        pp_barrier<kBF>();
         pp_barrier<63>();            // G1 starts one phase behind
     } else {
+        if constexpr (kMx) sf.b_scales(smem, 0, 0, true);
         pp_barrier<0>();
     }
     // Not unrolled or peeled: in a peeled copy the scheduler reorders the MFMAs of the two
@@ -320,9 +446,15 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     for (int kt = 0; kt < ktiles; ++kt) {
         const int s = kt & 1;
         // memory phase.  First this wave's A rows of stage kt+1 into the other slot: its
-        // group read them (stage kt-1) in its last memory phase.
+        // group read them (stage kt-1) in its last memory phase.  MXFP4: their scales, and
+        // G0 the B scales of stage kt+1 (stage kt-1 in that slot was read by G1 in the last
+        // phase).
         __builtin_amdgcn_sched_barrier(0);
         sf.a_rows(smem, s ^ 1, kt + 1, kt + 1 < ktiles);
+        if constexpr (kMx) {
+            sf.a_scales(smem, s ^ 1, kt + 1, kt + 1 < ktiles);
+            if (g0) sf.b_scales(smem, s ^ 1, kt + 1, kt + 1 < ktiles);
+        }
         __builtin_amdgcn_sched_barrier(0);
         fr.read(slot(kt), fa);
         __builtin_amdgcn_sched_barrier(0);
@@ -333,17 +465,17 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
             // last phase, this wave's reads land here
             __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));    // lgkmcnt(0)
             sf.b_rows(smem, s, kt + 2, kt + 2 < ktiles);
-            // landed: B of stage kt+1 (issued before the A rows and B rows of this phase)
-            pp_barrier<kPPAPieces + kPPBPieces>();
+            // landed: B of stage kt+1 (issued before the A and B loads of this phase)
+            pp_barrier<kAF + kBF>();
         }
         // compute phase: MFMAs only
         __builtin_amdgcn_sched_barrier(0);
         fr.mma(acc);
         __builtin_amdgcn_sched_barrier(0);
         if (g0) {
-            pp_barrier<0>();                 // G0: A rows of stage kt+1 landed
+            pp_barrier<0>();                 // G0: A (and B-scale) loads of stage kt+1 landed
         } else {
-            pp_barrier<kPPBPieces>();        // G1: A rows of stage kt+1 landed (B of kt+2 may fly)
+            pp_barrier<kBF>();               // G1: A loads of stage kt+1 landed (B of kt+2 may fly)
         }
     }
     if (g0) pp_barrier<63>();        // G1's last compute phase
@@ -352,12 +484,13 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
 
 // Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
 // [0,128) are global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a
-// plain tile).  Ends with all loads drained and a barrier, so the caller may reuse the LDS.
-template <bool kFp8>
+// plain tile; for MXFP4 both multiples of 128).  Ends with all loads drained and a barrier, so
+// the caller may reuse the LDS.
+template <Mma kKind>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                         int ktiles, uint8_t* smem, Acc& acc) {
-    mainloop_pp<kFp8>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc);
+                                         int ktiles, uint8_t* smem, Acc& acc, const MxScales& mxs = MxScales{}) {
+    mainloop_pp<kKind>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs);
 }
 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS

@@ -29,6 +29,15 @@ hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t*
                                 int64_t gate_rows, int64_t gate_ld, const int32_t* gate_index,
                                 const uint16_t* residual, uint16_t* out, hipStream_t stream);
 
+// MXFP4: scale bytes of a [rows, K] matrix in the MX scale layout; quantisation; W4A4 out-proj
+int64_t mx_scale_bytes(int64_t rows, int64_t K);
+hipError_t launch_mx_quant_fp4(const uint16_t* x, int64_t R, int64_t K, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream);
+hipError_t launch_out_proj_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales, int64_t M, const uint8_t* w_codes,
+                                 const uint8_t* w_scales, const uint16_t* gate, int64_t gate_rows, int64_t gate_ld,
+                                 const int32_t* gate_index, const uint16_t* residual, uint16_t* out,
+                                 hipStream_t stream);
+
 hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M, const uint8_t* W1,
                              const float* w1s, uint16_t* y, float* y_amax, hipStream_t stream);
 

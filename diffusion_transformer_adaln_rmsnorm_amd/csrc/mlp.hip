@@ -32,7 +32,7 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
     const int64_t m0 = (int64_t)tm * kBM;
     const int j0 = tn * 128;
     Acc acc;
-    mainloop<true>(a_q, kHidden, m0, M, W1, kHidden, j0, kInter + j0, kHidden / kRowB, smem, acc);
+    mainloop<Mma::kE4m3>(a_q, kHidden, m0, M, W1, kHidden, j0, kInter + j0, kHidden / kRowB, smem, acc);
     stage_tile_bf16(acc, smem, a_scale, m0, M, w1s + j0, w1s + kInter + j0);
     __syncthreads();
 
@@ -113,7 +113,7 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
     const int64_t m0 = (int64_t)tm * kBM;
     const int n0 = tn * kBN;
     Acc acc;
-    mainloop<true>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc);
+    mainloop<Mma::kE4m3>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc);
     GatedResidual<int64_t> gr;
     gr.load_index(idx, m0, M);
     stage_tile_bf16(acc, smem, y_scale, m0, M, w2s + n0, w2s + n0 + 128);

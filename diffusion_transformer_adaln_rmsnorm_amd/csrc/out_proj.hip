@@ -27,7 +27,7 @@ void k_out_proj_gemm(const uint16_t* __restrict__ attn, int64_t M, const uint16_
     const int64_t m0 = (int64_t)tm * kBM;
     const int n0 = tn * kBN;
     Acc acc;
-    mainloop<false>(reinterpret_cast<const uint8_t*>(attn), kAttnWidth * 2, m0, M,
+    mainloop<Mma::kBf16>(reinterpret_cast<const uint8_t*>(attn), kAttnWidth * 2, m0, M,
                     reinterpret_cast<const uint8_t*>(Wo), kAttnWidth * 2, n0, n0 + 128, kAttnWidth * 2 / kRowB, smem,
                     acc);
     GatedResidual<int32_t> gr;

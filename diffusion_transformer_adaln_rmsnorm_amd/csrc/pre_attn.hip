@@ -123,7 +123,6 @@ __device__ __forceinline__ float div_sat(float a, float s, float y) {
 // e4m3 output mode ("minimax_h3_nvfp4_pre_attention", Parameters: out_mode "e4m3" with
 // per-tensor q/k/v dequantization scales): the 8 bf16 values of o become e4m3(fl32(v / ds)),
 // saturating at 448, packed little-endian into 8 bytes.  y = RN(1 / ds).
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x2 e4m3_codes8(const u32x4& o, float ds, float y) {
     float v[8];
     unpack8(o, v);
@@ -147,7 +146,7 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     const int64_t m0 = (int64_t)tm * kBM;
     const int n0 = tn * kBN;
     Acc acc;
-    mainloop<false>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M, reinterpret_cast<const uint8_t*>(W),
+    mainloop<Mma::kBf16>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M, reinterpret_cast<const uint8_t*>(W),
                     kHidden * 2, n0, n0 + 128, kHidden * 2 / kRowB, smem, acc);
 
     const int t = threadIdx.x;

@@ -5,7 +5,9 @@
  *   dit_pre_attn_bf16       "minimax_h3_bf16_pre_attention" (description, Parameters, Notes),
  *                           and its e4m3 output mode dit_pre_attn_e4m3 ("minimax_h3_nvfp4_pre_attention",
  *                           Parameters: out_mode, q/k/v_descale)
- *   dit_out_proj_gated_bf16 "minimax_h3_nvfp4_out_proj" gated-residual epilogue, bf16 operands
+ *   dit_out_proj_gated_bf16 "minimax_h3_nvfp4_out_proj" gated-residual epilogue, bf16 operands,
+ *                           and its W4A4 form dit_out_proj_gated_mxfp4 (same page's description,
+ *                           with OCP MXFP4 in place of NVFP4; quantiser dit_mx_quant_fp4)
  *   dit_mlp_fp8             "minimax_h3_mlp_fp8_sm120" (per-row formula block, Parameters)
  *
  * Conventions shared by every entry point:
@@ -216,6 +218,51 @@ dit_status dit_mlp_fp8(const void* x, int64_t M, const void* x_norm_weight,
  * FC2 by stream order and needs none: it returns 0 for every M, and ws_flags is ignored.
  */
 int64_t dit_mlp_fp8_flags_elems(int64_t M);
+
+/*
+ * MXFP4 (OCP Microscaling Formats v1.0) quantisation, the W4A4 format gfx950's block-scaled
+ * MFMA takes natively; it stands where "minimax_h3_nvfp4_out_proj" (description) quantises to
+ * NVFP4 (block 16, UE4M3 scales, a global scale):
+ *   per block of 32 consecutive values of a row:  E = floor(log2(amax)) - 2 + 127, clamped to
+ *   [0, 254] (E = 0 for an all-zero block); scale 2^(E - 127) stored as the E8M0 byte E;
+ *   code = E2M1 value nearest v / 2^(E - 127), ties to the even significand, saturating at 6,
+ *   sign kept (-0 is code 8).
+ * Arguments:
+ *   x       bf16 [rows, K], K a positive multiple of 256
+ *   codes   uint8 [rows, K / 2]: element 2j of a row in the low nibble of byte j
+ *   scales  uint8, dit_mx_scale_bytes(rows, K) bytes, in the MX scale layout: with rows padded
+ *           to a multiple of 128, the scale of row r, block b (values 32 b .. 32 b + 31) is the
+ *           byte ((r / 128) (K / 256) + b / 8) 1024 + 16 l + 2 ((r % 128) / 16) + (b % 8) / 4,
+ *           l = r % 16 + 16 (b % 4) (the order in which the MFMA lanes take them).  Padding rows
+ *           get scale byte 0.
+ * rows = 0 is a no-op.  One kernel is enqueued.  Used for the weight once and by
+ * dit_out_proj_gated_mxfp4 for the activation on every call.
+ */
+int64_t dit_mx_scale_bytes(int64_t rows, int64_t K);
+dit_status dit_mx_quant_fp4(const void* x, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                            void* stream);
+
+/*
+ * MXFP4 W4A4 attention output projection with the fused gated residual ("minimax_h3_nvfp4_out_proj",
+ * description, with MXFP4 operands):
+ *   (act_codes, act_scales) = dit_mx_quant_fp4(attn_out)
+ *   o = bf16(A[m] . W[n]), A and W the values of the activation's and the weight's MXFP4
+ *       codes and scales (FP32 accumulation)
+ *   out[m] = bf16(residual[m] + bf16(g * o)),  g as in dit_out_proj_gated_bf16
+ * Arguments:
+ *   attn_out    bf16 [M, 7168]; M = 0 is a no-op
+ *   w_codes     uint8 [5376, 3584] and w_scales (dit_mx_scale_bytes(5376, 7168) bytes): the
+ *               weight quantised by dit_mx_quant_fp4
+ *   gate, gate_index, residual, out   as in dit_out_proj_gated_bf16
+ *   act_codes   uint8 [M, 3584] workspace; act_scales dit_mx_scale_bytes(M, 7168) bytes of
+ *               workspace (both written, then read by the GEMM)
+ *   16-byte alignment for every pointer except gate_index (4)
+ * Two kernels are enqueued (quantisation, then the block-scaled GEMM with its epilogue).
+ */
+dit_status dit_out_proj_gated_mxfp4(const void* attn_out, int64_t M, const uint8_t* w_codes,
+                                    const uint8_t* w_scales, dit_bf16_table gate,
+                                    const int32_t* gate_index, const void* residual,
+                                    uint8_t* act_codes, uint8_t* act_scales, void* out, void* stream);
 
 #ifdef __cplusplus
 }

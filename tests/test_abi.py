@@ -28,7 +28,8 @@ def _declared():
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dit_pre_attn_bf16", "dit_pre_attn_e4m3", "dit_qkv_rope_pack_e4m3", "dit_out_proj_gated_bf16",
-              "dit_mlp_fp8", "dit_mlp_fp8_flags_elems", "dit_status_string", "dit_abi_version"):
+              "dit_mlp_fp8", "dit_mlp_fp8_flags_elems", "dit_status_string", "dit_abi_version",
+              "dit_mx_scale_bytes", "dit_mx_quant_fp4", "dit_out_proj_gated_mxfp4"):
         assert n in names
 
 
@@ -135,6 +136,53 @@ def test_out_proj_contract_checks(kw, status):
     assert outp(**kw) == status
 
 
+def test_mx_scale_bytes():
+    L = dit.load_library()
+    # rows padded to 128, one byte per 32 values
+    assert L.dit_mx_scale_bytes(1, 256) == 128 * 8
+    assert L.dit_mx_scale_bytes(128, 7168) == 128 * 224
+    assert L.dit_mx_scale_bytes(129, 7168) == 256 * 224
+    assert L.dit_mx_scale_bytes(32760, 7168) == 32768 * 224
+    assert L.dit_mx_scale_bytes(0, 7168) == 0 and L.dit_mx_scale_bytes(-1, 7168) == 0
+
+
+def mxq(**kw):
+    a = dict(x=_p(1), R=8, K=7168, codes=_p(2), scales=_p(3))
+    a.update(kw)
+    return dit.load_library().dit_mx_quant_fp4(a["x"], a["R"], a["K"], a["codes"], a["scales"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=7000), SHAPE), (dict(K=128), SHAPE), (dict(K=0), SHAPE), (dict(R=-1), SHAPE),
+    (dict(R=(1 << 31) // 224 + 1), SHAPE),
+    (dict(x=None), NULL), (dict(codes=None), NULL), (dict(scales=None), NULL),
+    (dict(x=ctypes.c_void_p(A + 2)), ALIGN), (dict(codes=ctypes.c_void_p(A + 8)), ALIGN),
+    (dict(R=0), OK),
+])
+def test_mx_quant_contract_checks(kw, status):
+    assert mxq(**kw) == status
+
+
+def outp_mx(**kw):
+    a = dict(attn=_p(1), M=8, wc=_p(2), ws=_p(3), gate=_T(rows=9, stride=5376), gi=_p(4), res=_p(5), ac=_p(6),
+             as_=_p(7), out=_p(8))
+    a.update(kw)
+    return dit.load_library().dit_out_proj_gated_mxfp4(a["attn"], a["M"], a["wc"], a["ws"], a["gate"], a["gi"],
+                                                         a["res"], a["ac"], a["as_"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(attn=None), NULL), (dict(wc=None), NULL), (dict(ws=None), NULL), (dict(ac=None), NULL),
+    (dict(as_=None), NULL), (dict(out=None), NULL),
+    (dict(ws=ctypes.c_void_p(A + 4)), ALIGN), (dict(as_=ctypes.c_void_p(A + 4)), ALIGN),
+    (dict(gi=ctypes.c_void_p(A + 2)), ALIGN),
+    (dict(gate=_T(rows=0, stride=5376)), SHAPE), (dict(gate=_T(rows=9, stride=5380)), STRIDE),
+    (dict(M=-3), SHAPE), (dict(M=(1 << 24) + 1), SHAPE), (dict(M=0), OK),
+])
+def test_out_proj_mxfp4_contract_checks(kw, status):
+    assert outp_mx(**kw) == status
+
+
 def mlp(**kw):
     a = dict(x=_p(1), M=8, xw=_p(2), sc=_T(), sh=_T(A + 0x200000), g=_T(A + 0x300000), idx=_p(3), res=_p(4),
              w1=_p(5), s1=_p(6), w2=_p(7), s2=_p(8), eps=1e-5, aq=_p(9), as_=_p(10), y=_p(11), yq=_p(12), ys=_p(13),
@@ -163,6 +211,8 @@ def test_binding_refuses_host_tensors():
                                     torch.zeros(dit.HIDDEN, dit.ATTN_WIDTH, dtype=torch.bfloat16),
                                     torch.zeros(9, dit.HIDDEN, dtype=torch.bfloat16),
                                     torch.zeros(4, dtype=torch.int32), x)
+    with pytest.raises(ValueError, match="GPU"):
+        dit.dit_mx_quant_fp4(torch.zeros(4, dit.ATTN_WIDTH, dtype=torch.bfloat16))
     with pytest.raises(ValueError, match="GPU"):
         dit.dit_pre_attn_bf16(x, torch.zeros(dit.HIDDEN, dtype=torch.bfloat16), x[:1], x[:1],
                               torch.zeros(4, dtype=torch.int64), None, None, None, None, ulysses_degree=1, out=None)

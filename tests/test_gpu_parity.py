@@ -428,6 +428,121 @@ def test_out_proj_config3_sampled():
     check_out_proj(d, out, sample_rows(d["M"], d, n_random=256))
 
 
+# ---------------------------------------------------------------- MXFP4 W4A4 out-projection
+
+def mx_scales_rowmajor(scales_gpu, R, K):
+    """Scales in the MX scale layout (as include/dit.h states it) read back as [R, K/32]
+    row-major bytes, plus the bytes of the padding rows up to a multiple of 128."""
+    sc = scales_gpu.cpu().numpy()
+    R_pad = (R + 127) // 128 * 128
+    r = np.arange(R_pad)[:, None]
+    b = np.arange(K // 32)[None, :]
+    lane = r % 16 + 16 * (b % 4)
+    off = ((r // 128) * (K // 256) + b // 8) * 1024 + lane * 16 + 2 * ((r % 128) // 16) + (b % 8) // 4
+    assert sc.size == R_pad * (K // 32) and np.array_equal(np.sort(off.ravel()), np.arange(sc.size))
+    full = sc[off]
+    return full[:R], full[R:]
+
+
+def _bf16_cuda(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _mx_special_rows(R, K, seed):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal((R, K)) * np.exp2(rng.integers(-40, 40, (R, 1)))
+    v[0, :32] = 0.0                                                    # zero block
+    v[0, 32:64] = -0.0                                                 # negative zeros
+    v[1, :32] = rng.integers(-3, 4, 32) * 2.0 ** -131                  # bf16 subnormals
+    v[1, 32:64] = rng.uniform(-3e38, 3e38, 32)                         # near the bf16 maximum
+    k = 2.0 ** -5                                                      # exact E2M1 midpoints, amax 4 k
+    v[2, :32] = np.resize([4.0, 0.25, -0.75, 1.25, 1.75, -2.5, 3.5, 5.0, 0.3, -5.5], 32) * k
+    v[2, 32:64] = np.resize([7.0, -6.5, 7.99, 0.1], 32)                # saturation (amax in [4, 8))
+    return synth.to_bf16_bits(v.astype(np.float32))
+
+
+@pytest.mark.parametrize("R,K", [(300, 7168), (3, 256), (128, 512)])
+def test_mx_quant_fp4_matches_the_oracle_bit_for_bit(R, K):
+    _say(f"mx quant R={R} K={K}")
+    x = _mx_special_rows(R, K, seed=R + K)
+    codes, scales = _dit().dit_mx_quant_fp4(_bf16_cuda(x))
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.mx_quant_fp4(x)
+    assert np.array_equal(codes.cpu().numpy(), c_ref), "codes"
+    rm, pad = mx_scales_rowmajor(scales, R, K)
+    assert np.array_equal(rm, s_ref), "scales"
+    assert np.all(pad == 0), "padding rows' scales"
+
+
+_MXW = {}
+
+
+def _mx_weight():
+    """A bf16 o_weight, its MXFP4 form from the GPU quantiser and from the oracle's (checked equal)."""
+    if "w" not in _MXW:
+        W = synth.to_bf16_bits(synth.normal(91, "o_weight", (H, synth.ATTN_WIDTH), 1.0 / np.sqrt(synth.ATTN_WIDTH)))
+        wc, ws = _dit().dit_mx_quant_fp4(_bf16_cuda(W))
+        torch.cuda.synchronize()
+        wc_ref, ws_ref = oracle.mx_quant_fp4(W)
+        assert np.array_equal(wc.cpu().numpy(), wc_ref)
+        rm, _ = mx_scales_rowmajor(ws, H, synth.ATTN_WIDTH)
+        assert np.array_equal(rm, ws_ref)
+        _MXW["w"] = (W, wc, ws, wc_ref, ws_ref)
+    return _MXW["w"]
+
+
+def run_out_proj_mx(d, alias=False):
+    W, wc, ws, _, _ = _mx_weight()
+    t = synth.to_torch("out_proj", d)
+    M = d["M"]
+    ac = torch.empty((M, synth.ATTN_WIDTH // 2), dtype=torch.uint8, device="cuda")
+    asc = torch.empty((_dit().dit_mx_scale_bytes(M, synth.ATTN_WIDTH),), dtype=torch.uint8, device="cuda")
+    out = t["residual"] if alias else None
+    out = _dit().dit_out_proj_gated_mxfp4(t["attn_out"], wc, ws, t["gate"], t["gate_index"], t["residual"], out=out,
+                                          act_codes=ac, act_scales=asc)
+    torch.cuda.synchronize()
+    return out, ac, asc
+
+
+def check_out_proj_mx(d, out_gpu, ac, asc, rows):
+    M = d["M"]
+    _, _, _, wc_ref, ws_ref = _mx_weight()
+    a_c, a_s = oracle.mx_quant_fp4(d["attn_out"].reshape(M, synth.ATTN_WIDTH)[rows])
+    assert np.array_equal(ac.cpu().numpy()[rows], a_c), "activation codes"
+    rm, pad = mx_scales_rowmajor(asc, M, synth.ATTN_WIDTH)
+    assert np.array_equal(rm[rows], a_s) and np.all(pad == 0), "activation scales"
+    ref = oracle.out_proj_mxfp4(a_c, a_s, wc_ref, ws_ref, dict(d, M=rows.size, gate_index=d["gate_index"][rows],
+                                                                residual=d["residual"].reshape(M, H)[rows]))
+    got = synth.bits(out_gpu)[rows]
+    gi = d["gate_index"][rows]
+    bad = (gi < 0) | (gi >= d["gate"].rows)
+    assert np.array_equal(got[bad], d["residual"].reshape(M, H)[rows][bad]), "guarded rows must equal residual"
+    ok, rel, mx = bf16_tolerance_ok(got, ref)
+    _say(f"out_proj mxfp4 M={M} rows={rows.size} relL2={rel:.2e} max|err|={mx:.3e} mismatch={np.mean(got != ref):.2e}")
+    assert ok, (rel, mx)
+
+
+@pytest.mark.parametrize("M", [1, 300])
+def test_out_proj_mxfp4_against_oracle(M):
+    _say(f"out_proj mxfp4 M={M}")
+    d = synth.out_proj_inputs(M, seed=400 + M, weight=_mx_weight()[0])
+    out, ac, asc = run_out_proj_mx(d)
+    rows = np.arange(M) if M <= 4 else np.unique(np.r_[np.arange(8), np.arange(250, 262), np.arange(M - 12, M),
+                                                       np.nonzero(d["gate_index"] < 0)[0][:4]])
+    check_out_proj_mx(d, out, ac, asc, rows)
+
+
+def test_out_proj_mxfp4_alias_residual_and_full_size():
+    M = 32760
+    _say(f"out_proj mxfp4 M={M}, out is residual")
+    d = synth.out_proj_inputs(M, seed=7, weight=_mx_weight()[0])
+    out, ac, asc = run_out_proj_mx(d, alias=True)
+    g = np.random.default_rng(8)
+    rows = np.unique(np.r_[np.arange(16), np.arange(M - 16, M), np.nonzero(d["gate_index"] < 0)[0][:16],
+                           g.choice(M, 24, replace=False)])
+    check_out_proj_mx(d, out, ac, asc, rows)
+
+
 # ---------------------------------------------------------------- FP8 MLP
 
 _MW = {}
