@@ -33,6 +33,7 @@ MLP_FLOP = 2.0 * M_TOKENS * 28672 * 5376 + 2.0 * M_TOKENS * 5376 * 14336   # 1.5
 # Published MI355X dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 PEAK_BF16 = 2500.0
 PEAK_FP8 = 5000.0
+PEAK_FP4 = 10100.0
 PEAK_HBM = 8000.0
 # Minimum HBM bytes of the norm/AdaLN launch per row: read x (5376 bf16), write the workspace
 # (5376 bf16), read the int64 index; tables and the norm weight stay in cache.
@@ -196,6 +197,26 @@ def main():
     torch.cuda.synchronize()
     e4m3_ms = e8[0].elapsed_time(e8[1]) / n8
     del out_e4m3
+    mx_ms = None
+    if "out_proj" in stages:
+        # the MXFP4 W4A4 out-projection on the same inputs (weight quantised once, outside the
+        # timing; each call quantises attn_out and runs the block-scaled GEMM; not part of the step)
+        w_c, w_s = dit.dit_mx_quant_fp4(to["o_weight"])
+        a_c = torch.empty((M_TOKENS, 3584), dtype=torch.uint8, device=dev)
+        a_s = torch.empty((dit.dit_mx_scale_bytes(M_TOKENS, 7168),), dtype=torch.uint8, device=dev)
+
+        def op_mx():
+            dit.dit_out_proj_gated_mxfp4(to["attn_out"], w_c, w_s, to["gate"], to["gate_index"], to["residual"],
+                                         out=out_op, act_codes=a_c, act_scales=a_s)
+        for _ in range(3):
+            op_mx()
+        e8[0].record()
+        for _ in range(n8):
+            op_mx()
+        e8[1].record()
+        torch.cuda.synchronize()
+        mx_ms = e8[0].elapsed_time(e8[1]) / n8
+        del w_c, w_s, a_c, a_s
     norm_ms, gemm_ms, op_ms, mlp_ms = seg.mean(axis=0)
     pre_ms = norm_ms + gemm_ms
     ms_per_step = wall * 1e3 / args.steps
@@ -230,6 +251,11 @@ def main():
         r = OUTP_FLOP / (op_ms * 1e-3) / 1e12
         res["stage_rates"]["out_proj_TFLOPs"] = round(r, 2)
         res["stage_rates"]["out_proj_frac_bf16"] = round(r / PEAK_BF16, 4)
+    if mx_ms is not None:
+        r = OUTP_FLOP / (mx_ms * 1e-3) / 1e12
+        res["stages_ms"]["out_proj_mxfp4"] = round(float(mx_ms), 4)
+        res["stage_rates"]["out_proj_mxfp4_TFLOPs"] = round(r, 2)
+        res["stage_rates"]["out_proj_mxfp4_frac_fp4"] = round(r / PEAK_FP4, 4)
     if "mlp" in stages:
         r = MLP_FLOP / (mlp_ms * 1e-3) / 1e12
         res["stage_rates"]["mlp_fp8_TFLOPs"] = round(r, 2)
