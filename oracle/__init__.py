@@ -65,6 +65,10 @@ def lib():
         L.oracle_mx_quant_fp4.argtypes = [_p, _i64, _i64, _p, _p]
         L.oracle_out_proj_mxfp4.restype = None
         L.oracle_out_proj_mxfp4.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p]
+        L.oracle_norm_adaln.restype = None
+        L.oracle_norm_adaln.argtypes = [_i64, _i64, _p, _p, _p, _p, _i64, _i64, _p, _d, _p]
+        L.oracle_qkv_mxfp4.restype = None
+        L.oracle_qkv_mxfp4.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _d, _p]
         L.oracle_mlp.restype = None
         L.oracle_mlp.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _d,
                                  _p, _p, _p, _p, _p, _p]
@@ -276,6 +280,59 @@ def out_proj_mxfp4(a_codes, a_scales, w_codes, w_scales, d, rows_sel=None, threa
 
     _fan_out(run, R, threads)
     return out
+
+
+def norm_adaln(d, rows_sel=None, threads=None):
+    """The pre-attention workspace a [R, 5376] (uint16 bits) of the rows rows_sel."""
+    M = d["M"]
+    sel = np.arange(M, dtype=np.int64) if rows_sel is None else np.asarray(rows_sel, np.int64)
+    R = sel.size
+    x = _c(d["x"].reshape(M, HIDDEN)[sel], np.uint16)
+    idx = _c(d["adaln_index"][sel], np.int64)
+    sc_b, sc_o, rows, ld = _table(d["adaln_scale"])
+    sh_b, sh_o, _, _ = _table(d["adaln_shift"])
+    xw = _c(d["x_norm_weight"], np.uint16)
+    ws = np.zeros((R, HIDDEN), np.uint16)
+    L = lib()
+
+    def run(r0, r1):
+        L.oracle_norm_adaln(r0, r1, _ptr(x), _ptr(xw), _table_ptr(sc_b, sc_o), _table_ptr(sh_b, sh_o), rows, ld,
+                            _ptr(idx), float(np.float32(d["eps"])), _ptr(ws))
+
+    _fan_out(run, R, threads)
+    return ws
+
+
+def qkv_mxfp4(ws_codes, ws_scales, w_codes, w_scales, d, rows_sel=None, threads=None):
+    """The MXFP4 QKV GEMM and the pre-attention epilogue on the workspace codes/scales of rows
+    rows_sel ([R, 2688] / [R, 168] row-major, already selected) and the weight's ([21504, 2688] /
+    [21504, 168]); positions, cos/sin and norm weights from d.  Returns out [R, 56, 3, 128]."""
+    M = d["M"]
+    sel = np.arange(M, dtype=np.int64) if rows_sel is None else np.asarray(rows_sel, np.int64)
+    R = sel.size
+    pos = sel.copy() if d.get("rope_positions") is None else _c(d["rope_positions"][sel], np.int64)
+    qk_eps = d["qk_eps"] if d.get("qk_eps") is not None else d["eps"]
+    ac, asc = _c(ws_codes, np.uint8), _c(ws_scales, np.uint8)
+    wc, wsc = _c(w_codes, np.uint8), _c(w_scales, np.uint8)
+    qw, kw = _c(d["q_norm_weight"], np.uint16), _c(d["k_norm_weight"], np.uint16)
+    cs = _c(d["rope_cos_sin"], np.uint16)
+    out = np.zeros((R, HEADS, 3, HEAD_DIM), np.uint16)
+    L = lib()
+
+    def run(r0, r1):
+        L.oracle_qkv_mxfp4(r0, r1, _ptr(ac), _ptr(asc), _ptr(wc), _ptr(wsc), _ptr(qw), _ptr(kw), _ptr(cs),
+                           int(d["S"]), _ptr(pos), float(np.float32(qk_eps)), _ptr(out))
+
+    _fan_out(run, R, threads)
+    return out
+
+
+def pre_attn_mxfp4(d, w_codes, w_scales, rows_sel=None, threads=None):
+    """The MXFP4 W4A4 pre-attention of the rows rows_sel: the workspace a, its MXFP4 codes and
+    scales (row-major), and out [R, 56, 3, 128]."""
+    ws = norm_adaln(d, rows_sel, threads)
+    c, s = mx_quant_fp4(ws, threads)
+    return ws, c, s, qkv_mxfp4(c, s, w_codes, w_scales, d, rows_sel, threads)
 
 
 def mlp(d, rows_sel=None, threads=None):

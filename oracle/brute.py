@@ -100,11 +100,16 @@ def pre_attn(d, rows_sel):
     M = d["M"]
     sel = np.asarray(rows_sel, np.int64)
     eps = float(np.float32(d["eps"]))
-    qk_eps = float(np.float32(d["qk_eps"] if d.get("qk_eps") is not None else d["eps"]))
     a, _ = norm_adaln(d["x"].reshape(M, HIDDEN)[sel], d["x_norm_weight"], d["adaln_scale"], d["adaln_shift"],
                       d["adaln_index"][sel], eps)
     W = bf16_of_bits(d["qkv_weight"]).reshape(3, HEADS, HEAD_DIM, HIDDEN)
     qkv = rne_bf16(np.einsum("rk,thdk->rthd", a, W))           # [R, kind, head, dim]
+    return bits_of_bf16(a), _qkv_epilogue(d, sel, qkv)
+
+
+def _qkv_epilogue(d, sel, qkv):
+    """qkv [R, kind, head, dim] (bf16 values) -> packed out bits [R, head, kind, dim]."""
+    qk_eps = float(np.float32(d["qk_eps"] if d.get("qk_eps") is not None else d["eps"]))
     S = d["S"]
     cs = bf16_of_bits(d["rope_cos_sin"]).reshape(S, 96)
     pos = sel if d.get("rope_positions") is None else d["rope_positions"][sel]
@@ -124,7 +129,54 @@ def pre_attn(d, rows_sel):
         out[:, kind, :, 48:96] = rne_bf16(x2 * c + x1 * s)
         out[:, kind, :, 96:] = u[..., 96:]
     packed = np.transpose(out, (0, 2, 1, 3))                    # [R, head, kind, dim]
-    return bits_of_bf16(a), bits_of_bf16(packed)
+    return bits_of_bf16(packed)
+
+
+# ---- MXFP4 (OCP Microscaling): its own NumPy reading of the format, for the cross-check
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def mx_quant(x_bits):
+    """bf16 rows [R, K] -> (codes [R, K/2], scales [R, K/32]): per 32-block, X = 2^(floor(log2
+    amax) - 2) (byte clamped to [0, 254], 0 for a zero block); each element the nearest E2M1
+    magnitude of |v| / X (the two grid neighbours compared, a tie going to the even index),
+    6 beyond the grid, sign bit from v."""
+    v = bf16_of_bits(x_bits)
+    R, K = v.shape
+    v = v.reshape(R, K // 32, 32)
+    amax = np.abs(v).max(axis=2)
+    _, e = np.frexp(amax)
+    E = np.where(amax > 0, np.clip(e - 3 + 127, 0, 254), 0)
+    y = np.abs(v) / np.exp2(E - 127.0)[..., None]
+    lo = np.clip(np.searchsorted(E2M1, y, side="right") - 1, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    d_lo, d_hi = y - E2M1[lo], E2M1[hi] - y
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    idx = np.where(y >= 6.0, 7, np.where(up, hi, lo))
+    code = (idx | (np.signbit(v).astype(np.int64) << 3)).reshape(R, K).astype(np.uint8)
+    return (code[:, 0::2] | (code[:, 1::2] << 4)).astype(np.uint8), E.astype(np.uint8)
+
+
+def mx_values(codes, scales):
+    c = np.asarray(codes, np.uint8)
+    R, H = c.shape
+    nib = np.empty((R, 2 * H), np.int64)
+    nib[:, 0::2], nib[:, 1::2] = c & 15, c >> 4
+    mag = E2M1[nib & 7] * np.where(nib & 8, -1.0, 1.0)
+    return mag * np.exp2(np.repeat(np.asarray(scales, np.float64) - 127.0, 32, axis=1))
+
+
+def qkv_mxfp4(d, rows_sel, ws_codes, ws_scales, w_codes, w_scales):
+    """The MXFP4 QKV product of the given workspace codes (rows rows_sel) and weight codes, then
+    the pre-attention epilogue."""
+    sel = np.asarray(rows_sel, np.int64)
+    A = mx_values(ws_codes, ws_scales)
+    acc = np.empty((A.shape[0], 3 * HEADS * HEAD_DIM))
+    for n0 in range(0, acc.shape[1], 2048):                     # W's values a slab at a time
+        acc[:, n0:n0 + 2048] = A @ mx_values(w_codes[n0:n0 + 2048], w_scales[n0:n0 + 2048]).T
+    qkv = rne_bf16(acc).reshape(-1, 3, HEADS, HEAD_DIM)
+    return _qkv_epilogue(d, sel, qkv)
 
 
 def out_proj(d, rows_sel):

@@ -140,6 +140,45 @@ static int norm_adaln_row(const uint16_t* x, const uint16_t* w, const uint16_t* 
 
 /* ---- bf16 pre-attention --------------------------------------------------------------- */
 
+/* The epilogue of one row: qkv[21504] (bf16, rows [q | k | v] x 56 heads x 128) -> the packed
+ * out row [56][3][128] (P = 1): per-head Q/K RMSNorm, RoPE at cache row clamp(p), V as is. */
+static void qkv_epilogue_row(const uint16_t* qkv, int64_t p, const uint16_t* qw, const uint16_t* kw,
+                             const uint16_t* cs, int64_t S, double qk_eps, uint16_t* orow) {
+    if (p < 0) p = 0;
+    if (p > S - 1) p = S - 1;
+    const uint16_t* crow = cs + p * NROT;
+    for (int kind = 0; kind < 3; kind++) {
+        for (int h = 0; h < NHEAD; h++) {
+            const uint16_t* v = qkv + kind * ATTW + h * HDIM;
+            uint16_t* o = orow + (h * 3 + kind) * HDIM;
+            if (kind == 2) {            /* V: bf16(acc) only */
+                for (int d = 0; d < HDIM; d++) o[d] = v[d];
+                continue;
+            }
+            const uint16_t* nw = kind == 0 ? qw : kw;
+            double ss = 0.0;
+            for (int d = 0; d < HDIM; d++) ss += bf(v[d]) * bf(v[d]);
+            double r2 = 1.0 / sqrt(ss / HDIM + qk_eps);
+            double u[HDIM];
+            for (int d = 0; d < HDIM; d++) u[d] = bf(oracle_round_bf16(bf(v[d]) * r2 * bf(nw[d])));
+            for (int j = 0; j < NFREQ; j++) {
+                double c = bf(crow[j]), sn = bf(crow[NFREQ + j]);
+                o[j] = oracle_round_bf16(u[j] * c - u[j + NFREQ] * sn);
+                o[j + NFREQ] = oracle_round_bf16(u[j + NFREQ] * c + u[j] * sn);
+            }
+            for (int d = NROT; d < HDIM; d++) o[d] = oracle_round_bf16(u[d]);
+        }
+    }
+}
+
+/* Rows [m0, m1) of the workspace alone: ws[m] = a of row m (the first launch of the stage). */
+void oracle_norm_adaln(int64_t m0, int64_t m1, const uint16_t* x, const uint16_t* xw, const uint16_t* scale,
+                       const uint16_t* shift, int64_t rows, int64_t ld, const int64_t* idx, double eps,
+                       uint16_t* ws) {
+    for (int64_t m = m0; m < m1; m++)
+        norm_adaln_row(x + m * HID, xw, scale, shift, rows, ld, idx[m], eps, ws + m * HID);
+}
+
 /*
  * Rows [m0, m1) of the pre-attention stage.
  *   x[M][5376], xw[5376]; scale/shift: row i at scale + i*ld (ld >= 5376); idx[M] int64;
@@ -166,32 +205,7 @@ void oracle_pre_attn(int64_t m0, int64_t m1, const uint16_t* x, const uint16_t* 
             for (int k = 0; k < HID; k++) acc += a[k] * bf(wr[k]);
             qkv[n] = oracle_round_bf16(acc);
         }
-        int64_t p = pos[m];
-        if (p < 0) p = 0;
-        if (p > S - 1) p = S - 1;
-        const uint16_t* crow = cs + p * NROT;
-        for (int kind = 0; kind < 3; kind++) {
-            for (int h = 0; h < NHEAD; h++) {
-                const uint16_t* v = qkv + kind * ATTW + h * HDIM;
-                uint16_t* o = out + ((m * NHEAD + h) * 3 + kind) * HDIM;
-                if (kind == 2) {            /* V: bf16(acc) only */
-                    for (int d = 0; d < HDIM; d++) o[d] = v[d];
-                    continue;
-                }
-                const uint16_t* nw = kind == 0 ? qw : kw;
-                double ss = 0.0;
-                for (int d = 0; d < HDIM; d++) ss += bf(v[d]) * bf(v[d]);
-                double r2 = 1.0 / sqrt(ss / HDIM + qk_eps);
-                double u[HDIM];
-                for (int d = 0; d < HDIM; d++) u[d] = bf(oracle_round_bf16(bf(v[d]) * r2 * bf(nw[d])));
-                for (int j = 0; j < NFREQ; j++) {
-                    double c = bf(crow[j]), s = bf(crow[NFREQ + j]);
-                    o[j] = oracle_round_bf16(u[j] * c - u[j + NFREQ] * s);
-                    o[j + NFREQ] = oracle_round_bf16(u[j + NFREQ] * c + u[j] * s);
-                }
-                for (int d = NROT; d < HDIM; d++) o[d] = oracle_round_bf16(u[d]);
-            }
-        }
+        qkv_epilogue_row(qkv, pos[m], qw, kw, cs, S, qk_eps, out + m * NHEAD * 3 * HDIM);
     }
     free(a);
     free(qkv);
@@ -296,9 +310,12 @@ void oracle_mx_quant_fp4(const uint16_t* x, int64_t R, int64_t K, uint8_t* codes
 
 /* the values of one MXFP4 row of n elements (n % 32 == 0) */
 static void mx_row_values(const uint8_t* codes, const uint8_t* scales, int64_t n, double* v) {
-    for (int64_t k = 0; k < n; k++) {
-        uint8_t c = (codes[k / 2] >> (4 * (k & 1))) & 15;
-        v[k] = ldexp(oracle_e2m1_value(c), (int)scales[k / 32] - 127);
+    for (int64_t b = 0; b < n / 32; b++) {
+        const double X = ldexp(1.0, (int)scales[b] - 127);
+        for (int64_t k = 32 * b; k < 32 * b + 32; k++) {
+            uint8_t c = (codes[k / 2] >> (4 * (k & 1))) & 15;
+            v[k] = oracle_e2m1_value(c) * X;
+        }
     }
 }
 
@@ -328,6 +345,35 @@ void oracle_out_proj_mxfp4(int64_t m0, int64_t m1, const uint8_t* a_codes, const
         gated_row(o, gi[m], gate, rows, ld, res + m * HID, out + m * HID);
     }
     free(o);
+    free(w);
+    free(a);
+}
+
+/*
+ * Rows [m0, m1) of the MXFP4 W4A4 pre-attention GEMM and epilogue (not on the pages; the
+ * MXFP4 counterpart of the NVFP4 pre-attention, whose activation is the quantised workspace):
+ * qkv = bf16(A[m] . W[n]) with A the values of the workspace's MXFP4 codes/scales
+ * (ws_codes[M][2688], ws_scales[M][168], row-major) and W those of the weight
+ * (w_codes[21504][2688], w_scales[21504][168]); then the bf16 pre-attention's epilogue.
+ * pos[M] cache rows (the row numbers for identity positions); out[M][56][3][128].
+ */
+void oracle_qkv_mxfp4(int64_t m0, int64_t m1, const uint8_t* ws_codes, const uint8_t* ws_scales,
+                      const uint8_t* w_codes, const uint8_t* w_scales, const uint16_t* qw, const uint16_t* kw,
+                      const uint16_t* cs, int64_t S, const int64_t* pos, double qk_eps, uint16_t* out) {
+    double* a = (double*)malloc(sizeof(double) * HID);
+    double* w = (double*)malloc(sizeof(double) * HID);
+    uint16_t* qkv = (uint16_t*)malloc(sizeof(uint16_t) * QKVN);
+    for (int64_t m = m0; m < m1; m++) {
+        mx_row_values(ws_codes + m * (HID / 2), ws_scales + m * (HID / 32), HID, a);
+        for (int n = 0; n < QKVN; n++) {
+            mx_row_values(w_codes + (int64_t)n * (HID / 2), w_scales + (int64_t)n * (HID / 32), HID, w);
+            double acc = 0.0;
+            for (int k = 0; k < HID; k++) acc += a[k] * w[k];
+            qkv[n] = oracle_round_bf16(acc);
+        }
+        qkv_epilogue_row(qkv, pos[m], qw, kw, cs, S, qk_eps, out + m * NHEAD * 3 * HDIM);
+    }
+    free(qkv);
     free(w);
     free(a);
 }

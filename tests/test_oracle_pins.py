@@ -744,3 +744,26 @@ def test_out_proj_mxfp4_matches_float64_matmul_of_the_values():
     Wv = torch.from_numpy(oracle.mx_values(w, w_s))
     want = (A @ Wv.T).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(got, want)
+
+
+def test_brute_force_mx_quant_matches_the_oracle():
+    # an independent NumPy reading of the MXFP4 conversion, bit for bit
+    x = _mx_exact_rows(np.random.default_rng(16), 3, 512)[0]
+    rng = np.random.default_rng(17)
+    y = synth.to_bf16_bits((rng.standard_normal((5, 1024)) * np.exp2(rng.integers(-20, 20, (5, 1)))).astype(np.float32))
+    y[0, 96:128] = synth.to_bf16_bits(np.float32(-0.0))
+    for v in (x, y, synth.to_bf16_bits(np.resize(np.float32([0.25, -0.75, 5.0, 4.0, 7.5, 1.25]), (1, 256)))):
+        c, s = oracle.mx_quant_fp4(v)
+        bc, bs = brute.mx_quant(v)
+        assert np.array_equal(c, bc) and np.array_equal(s, bs)
+
+
+@pytest.mark.parametrize("M", [1, 2])
+def test_brute_force_pre_attn_mxfp4(M):
+    d = _pre(M, _random_qkv_weight(), rows=2, wide_tables=True, bad_index_frac=0.0, S=16, positions="random",
+             n_bad_positions=1)
+    wc, wsc = oracle.mx_quant_fp4(d["qkv_weight"])
+    ws, c, s, out = oracle.pre_attn_mxfp4(d, wc, wsc)
+    assert np.array_equal(ws, oracle.pre_attn(d)[0])             # the same workspace a
+    bout = brute.qkv_mxfp4(d, np.arange(M), c, s, wc, wsc)
+    assert ulp_diff_bf16(out, bout).max() <= 1 and np.mean(out != bout) < 1e-3
