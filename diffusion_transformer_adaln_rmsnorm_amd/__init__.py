@@ -17,7 +17,7 @@ import torch
 
 __all__ = ["dit_pre_attn_bf16", "dit_pre_attn_e4m3", "dit_norm_adaln_bf16", "dit_qkv_rope_pack_bf16",
            "dit_qkv_rope_pack_e4m3", "dit_out_proj_gated_bf16", "dit_mlp_fp8", "dit_mlp_fp8_flags_elems",
-           "dit_mx_scale_bytes", "dit_mx_quant_fp4", "dit_out_proj_gated_mxfp4",
+           "dit_mx_scale_bytes", "dit_mx_quant_fp4", "dit_out_proj_gated_mxfp4", "dit_pre_attn_mxfp4",
            "DitError", "load_library", "LIB_PATH", "HIDDEN", "HEADS", "HEAD_DIM", "QKV_ROWS", "ATTN_WIDTH",
            "INTER", "FC1_ROWS", "MLP_MAX_M"]
 
@@ -82,6 +82,9 @@ def load_library(path: str = LIB_PATH):
     L.dit_mx_scale_bytes.argtypes = [_i64, _i64]
     L.dit_mx_quant_fp4.restype = _i32
     L.dit_mx_quant_fp4.argtypes = [_p, _i64, _i64, _p, _p, _p]
+    L.dit_pre_attn_mxfp4.restype = _i32
+    L.dit_pre_attn_mxfp4.argtypes = [_p, _i64, _p, Table, Table, _p, _p, _p, _p, _p, _p, _i64, _p, _i32, _f, _f, _p,
+                                     _p, _p, _p]
     L.dit_out_proj_gated_mxfp4.restype = _i32
     L.dit_out_proj_gated_mxfp4.argtypes = [_p, _i64, _p, _p, Table, _p, _p, _p, _p, _p, _p]
     L.dit_mlp_fp8.restype = _i32
@@ -193,6 +196,46 @@ def _pre_attn(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weigh
     else:
         st = L.dit_pre_attn_e4m3(*args, *(float(d) for d in descale), _ptr(workspace), _ptr(out), _stream())
         _check("dit_pre_attn_e4m3", st)
+    return out
+
+
+def dit_pre_attn_mxfp4(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, w_codes, w_scales, q_norm_weight,
+                       k_norm_weight, rope_cos_sin, *, ulysses_degree: int, out, eps: float = 1e-5,
+                       qk_eps: float | None = None, rope_positions=None, ws_codes=None, ws_scales=None):
+    """MXFP4 W4A4 pre-attention; w_codes / w_scales come from dit_mx_quant_fp4 of the bf16 qkv weight
+    [21504, 5376].  Writes out [P, M, 56 // P, 3, 128] bf16 and returns it; the workspace codes and
+    scales (allocated when omitted) receive the quantised activation."""
+    L = load_library()
+    M = x.shape[0] if x.dim() == 2 else -1
+    dev = x.device
+    _need(x, "x", torch.bfloat16, (M, HIDDEN))
+    _need(x_norm_weight, "x_norm_weight", torch.bfloat16, (HIDDEN,))
+    ts, th = _table(adaln_scale, "adaln_scale"), _table(adaln_shift, "adaln_shift")
+    _need(adaln_index, "adaln_index", torch.int64, (M,))
+    _need(w_codes, "w_codes", torch.uint8, (QKV_ROWS, HIDDEN // 2))
+    _need(w_scales, "w_scales", torch.uint8, (dit_mx_scale_bytes(QKV_ROWS, HIDDEN),))
+    _need(q_norm_weight, "q_norm_weight", torch.bfloat16, (HEAD_DIM,))
+    _need(k_norm_weight, "k_norm_weight", torch.bfloat16, (HEAD_DIM,))
+    if rope_cos_sin.dim() != 2:
+        raise ValueError("rope_cos_sin must be [S, 96]")
+    S = rope_cos_sin.shape[0]
+    _need(rope_cos_sin, "rope_cos_sin", torch.bfloat16, (S, 96))
+    if rope_positions is not None:
+        _need(rope_positions, "rope_positions", torch.int64, (M,))
+    P = int(ulysses_degree)
+    _need_out(out, False, P, M)
+    if ws_codes is None:
+        ws_codes = torch.empty((M, HIDDEN // 2), dtype=torch.uint8, device=dev)
+    if ws_scales is None:
+        ws_scales = torch.empty((dit_mx_scale_bytes(M, HIDDEN),), dtype=torch.uint8, device=dev)
+    _need(ws_codes, "ws_codes", torch.uint8, (M, HIDDEN // 2))
+    _need(ws_scales, "ws_scales", torch.uint8, (dit_mx_scale_bytes(M, HIDDEN),))
+    qk = eps if qk_eps is None else qk_eps
+    st = L.dit_pre_attn_mxfp4(_ptr(x), M, _ptr(x_norm_weight), ts, th, _ptr(adaln_index), _ptr(w_codes),
+                              _ptr(w_scales), _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(rope_cos_sin), S,
+                              _ptr(rope_positions), P, float(eps), float(qk), _ptr(ws_codes), _ptr(ws_scales),
+                              _ptr(out), _stream())
+    _check("dit_pre_attn_mxfp4", st)
     return out
 
 

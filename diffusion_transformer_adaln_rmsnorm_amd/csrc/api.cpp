@@ -190,6 +190,46 @@ dit_status dit_out_proj_gated_bf16(const void* attn_out, int64_t M, const void* 
         static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out), static_cast<hipStream_t>(stream)));
 }
 
+dit_status dit_pre_attn_mxfp4(const void* x, int64_t M, const void* x_norm_weight, dit_bf16_table adaln_scale,
+                              dit_bf16_table adaln_shift, const int64_t* adaln_index, const uint8_t* w_codes,
+                              const uint8_t* w_scales, const void* q_norm_weight, const void* k_norm_weight,
+                              const void* rope_cos_sin, int64_t S, const int64_t* rope_positions, int ulysses_degree,
+                              float eps, float qk_eps, uint8_t* ws_codes, uint8_t* ws_scales, void* out,
+                              void* stream) {
+    if (ulysses_degree != 1 && ulysses_degree != 2 && ulysses_degree != 4 && ulysses_degree != 8)
+        return DIT_ERR_VALUE;
+    if (!eps_ok(eps) || !eps_ok(qk_eps)) return DIT_ERR_VALUE;
+    if (M < 0 || M > kMaxRows) return DIT_ERR_SHAPE;
+    if (!x || !x_norm_weight || !adaln_index || !w_codes || !w_scales || !q_norm_weight || !k_norm_weight ||
+        !rope_cos_sin || !ws_codes || !ws_scales || !out)
+        return DIT_ERR_NULL;
+    dit_status st = check_table(adaln_scale);
+    if (st != DIT_OK) return st;
+    st = check_table(adaln_shift);
+    if (st != DIT_OK) return st;
+    if (adaln_scale.rows != adaln_shift.rows) return DIT_ERR_SHAPE;
+    if (!aligned(x, 16) || !aligned(x_norm_weight, 16) || !aligned(w_codes, 16) || !aligned(w_scales, 16) ||
+        !aligned(q_norm_weight, 16) || !aligned(k_norm_weight, 16) || !aligned(rope_cos_sin, 16) ||
+        !aligned(ws_codes, 16) || !aligned(ws_scales, 16) || !aligned(out, 16) || !aligned(adaln_index, 8) ||
+        (rope_positions && !aligned(rope_positions, 8)))
+        return DIT_ERR_ALIGN;
+    if (S < 1) return DIT_ERR_SHAPE;
+    if (!rope_positions && S < M) return DIT_ERR_SHAPE;
+    if (M == 0) return DIT_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launched(dit::launch_norm_adaln_mxfp4(
+        static_cast<const uint16_t*>(x), M, static_cast<const uint16_t*>(x_norm_weight),
+        static_cast<const uint16_t*>(adaln_scale.ptr), adaln_scale.row_stride,
+        static_cast<const uint16_t*>(adaln_shift.ptr), adaln_shift.row_stride, adaln_scale.rows, adaln_index, eps,
+        ws_codes, ws_scales, s));
+    if (st != DIT_OK) return st;
+    return launched(dit::launch_qkv_gemm_mxfp4(ws_codes, ws_scales, M, w_codes, w_scales,
+                                               static_cast<const uint16_t*>(q_norm_weight),
+                                               static_cast<const uint16_t*>(k_norm_weight),
+                                               static_cast<const uint16_t*>(rope_cos_sin), S, rope_positions, qk_eps,
+                                               ulysses_degree, static_cast<uint16_t*>(out), s));
+}
+
 int64_t dit_mx_scale_bytes(int64_t rows, int64_t K) {
     if (rows < 0 || K < 0) return 0;
     return dit::mx_scale_bytes(rows, K);

@@ -29,6 +29,16 @@ hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t*
                                 int64_t gate_rows, int64_t gate_ld, const int32_t* gate_index,
                                 const uint16_t* residual, uint16_t* out, hipStream_t stream);
 
+// MXFP4 pre-attention: the norm/AdaLN rows quantised to MXFP4 codes and scales (M rows, scales
+// for M rounded up to 128), then the QKV GEMM on MXFP4 operands with the bf16 epilogue
+hipError_t launch_norm_adaln_mxfp4(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,
+                                   int64_t ld_scale, const uint16_t* shift, int64_t ld_shift, int64_t rows,
+                                   const int64_t* idx, float eps, uint8_t* codes, uint8_t* scales, hipStream_t stream);
+hipError_t launch_qkv_gemm_mxfp4(const uint8_t* ws_codes, const uint8_t* ws_scales, int64_t M, const uint8_t* w_codes,
+                                 const uint8_t* w_scales, const uint16_t* qw, const uint16_t* kw, const uint16_t* cs,
+                                 int64_t S, const int64_t* pos, float qk_eps, int P, uint16_t* out,
+                                 hipStream_t stream);
+
 // MXFP4: scale bytes of a [rows, K] matrix in the MX scale layout; quantisation; W4A4 out-proj
 int64_t mx_scale_bytes(int64_t rows, int64_t K);
 hipError_t launch_mx_quant_fp4(const uint16_t* x, int64_t R, int64_t K, uint8_t* codes, uint8_t* scales,

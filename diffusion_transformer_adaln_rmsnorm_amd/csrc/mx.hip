@@ -18,32 +18,11 @@
 #include "gated.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
+#include "mx.hpp"
 
 namespace dit {
 
 using namespace gemm;
-
-namespace {
-
-// E2M1 code (sign in bit 3) of the FP32 value y = v 2^(127 - E): the magnitude index counts the
-// midpoints between neighbouring E2M1 values that |y| passes; at a midpoint it moves up only
-// onto an even significand (midpoints after indices 1, 3, 5 count with >=, after 0, 2, 4, 6
-// with >).  |y| >= 6 gives 7, the saturated maximum.
-__device__ __forceinline__ uint32_t e2m1_code(float y) {
-    const float a = fabsf(y);
-    const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-    return m | ((__float_as_uint(y) >> 28) & 8u);
-}
-
-// floor(log2(a)) of a positive finite float (normal or subnormal)
-__device__ __forceinline__ int ilog2f(float a) {
-    const uint32_t b = __float_as_uint(a);
-    const int ex = (int)(b >> 23);
-    return ex != 0 ? ex - 127 : (31 - __builtin_clz(b & 0x7FFFFFu)) - 149;
-}
-
-}  // namespace
 
 // x [R, K] bf16 rows (K % 256 == 0) -> codes [R, K / 2], scales in the MX scale layout for
 // ceil(R / 128) * 128 rows.  Thread = (row, block of 32); rows R .. padded end write scale 0.
@@ -65,30 +44,15 @@ __global__ __launch_bounds__(256) void k_mx_quant_fp4(const uint16_t* __restrict
         for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(w[q][e])), fabsf(bf_hi(w[q][e]))));
-        if (amax > 0.f) {
-            const int e = ilog2f(amax) - 2 + 127;
-            E = (uint32_t)(e < 0 ? 0 : (e > 254 ? 254 : e));
-        }
-        // 2^(127 - E) as a normal float: amax < 2^128 gives E <= 252
-        const float inv = __uint_as_float((254u - E) << 23);
+        E = mx_scale_byte(amax);
+        const float inv = mx_inv_scale(E);
         u32x4 out;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            // 8 values -> 8 codes -> 4 bytes, element 2j in the low nibble of byte j
-            uint32_t word = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t lo = e2m1_code(bf_lo(w[q][e]) * inv), hi = e2m1_code(bf_hi(w[q][e]) * inv);
-                word |= (lo | (hi << 4)) << (8 * e);
-            }
-            out[q] = word;
-        }
+        for (int q = 0; q < 4; ++q)
+            out[q] = e2m1_pack4(w[q][0], w[q][1], inv) | (e2m1_pack4(w[q][2], w[q][3], inv) << 16);
         st16(codes + r * (K / 2) + b * 16, out);
     }
-    // MX scale layout: group r / 128, stage b / 8, lane r % 16 + 16 (b % 4), byte 2 ((r % 128) / 16) + (b % 8) / 4
-    const int64_t lane = r % 16 + 16 * (b % 4);
-    const int64_t off = ((r / 128) * (K / 256) + b / 8) * 1024 + lane * 16 + 2 * ((r % 128) / 16) + (b % 8) / 4;
-    scales[off] = (uint8_t)E;
+    scales[mx_scale_offset(r, b, K)] = (uint8_t)E;
 }
 
 // out = bf16(residual + bf16(gate[gate_index[m]] * bf16(A . W))) with A, W MXFP4 (codes

@@ -15,6 +15,7 @@
 // norm weight and the few table rows stay in L2.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mx.hpp"
 
 namespace dit {
 
@@ -100,6 +101,65 @@ __global__ __launch_bounds__(256) void k_norm_adaln_bf16(const uint16_t* __restr
     }
 }
 
+// MXFP4 pre-attention, launch 1: the same row steps, then a quantised to MXFP4 in registers
+// instead of written as bf16.  The 32-value block of chunks 4c .. 4c + 3 belongs to the four
+// lanes of one quad (a lane's chunks are 64 apart), so the block maximum is two DPP steps.
+// Codes [M, 2688] (4 bytes per lane and chunk); scales in the MX scale layout for R_pad rows
+// (rows M .. R_pad write only their zero scales).  Guarded rows quantise a = 0: codes 0, scale 0.
+__global__ __launch_bounds__(256) void k_norm_adaln_mxfp4(const uint16_t* __restrict__ x, int64_t M,
+                                                          const uint16_t* __restrict__ xw,
+                                                          const uint16_t* __restrict__ scale, int64_t ld_scale,
+                                                          const uint16_t* __restrict__ shift, int64_t ld_shift,
+                                                          int64_t rows, const int64_t* __restrict__ idx, float eps,
+                                                          int64_t R_pad, uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= R_pad) return;
+    if (m >= M) {
+#pragma unroll
+        for (int j = 0; j < kMaxPerLane; ++j)
+            if (chunk_ok(j, lane) && (lane & 3) == 0) scales[mx_scale_offset(m, (j * 64 + lane) / 4, kHidden)] = 0;
+        return;
+    }
+    const int64_t i = idx[m];
+    const bool valid = i >= 0 && i < rows;            // full-width int64 guard
+    u32x4 av[kMaxPerLane];
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) av[j] = u32x4{0u, 0u, 0u, 0u};
+    if (valid) {
+        u32x4 xv[kMaxPerLane];
+        const float r = load_row_rms(x + m * kHidden, lane, eps, xv);
+        const uint16_t* scr = scale + i * ld_scale;
+        const uint16_t* shr = shift + i * ld_shift;
+#pragma unroll
+        for (int j = 0; j < kMaxPerLane; ++j) {
+            if (!chunk_ok(j, lane)) continue;
+            const int c = (j * 64 + lane) * 8;
+            uint32_t a[4];
+            modulate_chunk(xv[j], ld16(xw + c), ld16(scr + c), ld16(shr + c), r, a);
+            av[j] = u32x4{a[0], a[1], a[2], a[3]};
+        }
+    }
+    uint8_t* cr = codes + m * (kHidden / 2);
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (!chunk_ok(j, lane)) continue;             // whole quads drop out together
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(av[j][e])), fabsf(bf_hi(av[j][e]))));
+        // quad_perm(1,0,3,2) then (2,3,0,1): the maximum over the block's four lanes
+        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, true)));
+        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0x4E, 0xF, 0xF, true)));
+        const uint32_t E = mx_scale_byte(amax);
+        const float inv = mx_inv_scale(E);
+        const int c = j * 64 + lane;
+        *reinterpret_cast<uint32_t*>(cr + c * 4) =
+            e2m1_pack4(av[j][0], av[j][1], inv) | (e2m1_pack4(av[j][2], av[j][3], inv) << 16);
+        if ((lane & 3) == 0) scales[mx_scale_offset(m, c / 4, kHidden)] = (uint8_t)E;
+    }
+}
+
 // MLP kernel A: the same row steps, then s_a = RN(amax|a| / 448) and a_q = e4m3(a / s_a).
 // Also clears y_amax[m], the per-row |y| maximum that the FC1 epilogue accumulates.
 __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restrict__ x, int64_t M,
@@ -169,6 +229,15 @@ hipError_t launch_norm_adaln_bf16(const uint16_t* x, int64_t M, const uint16_t* 
     const int64_t blocks = (M + 3) / 4;
     hipLaunchKernelGGL(k_norm_adaln_bf16, dim3((unsigned)blocks), dim3(256), 0, stream, x, M, xw, scale, ld_scale,
                        shift, ld_shift, rows, idx, eps, ws);
+    return hipGetLastError();
+}
+
+hipError_t launch_norm_adaln_mxfp4(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,
+                                   int64_t ld_scale, const uint16_t* shift, int64_t ld_shift, int64_t rows,
+                                   const int64_t* idx, float eps, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+    const int64_t R_pad = (M + 127) / 128 * 128;
+    hipLaunchKernelGGL(k_norm_adaln_mxfp4, dim3((unsigned)(R_pad / 4)), dim3(256), 0, stream, x, M, xw, scale, ld_scale,
+                       shift, ld_shift, rows, idx, eps, R_pad, codes, scales);
     return hipGetLastError();
 }
 

@@ -132,23 +132,15 @@ __device__ __forceinline__ u32x2 e4m3_codes8(const u32x4& o, float ds, float y) 
     return q;
 }
 
-// kE4m3: out holds e4m3 codes (one byte per element) of the bf16 results divided by the
-// descale of their kind (dq, dk, dv); else bf16 values (the descales are unused).
+// The QKV epilogue of one 256 x 256 tile after the main loop (acc of this wave): Q/K RMSNorm,
+// RoPE and the pack, or V as is.  kE4m3: out holds e4m3 codes (one byte per element) of the
+// bf16 results divided by the descale of their kind (dq, dk, dv); else bf16 values.
 template <bool kE4m3>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
-void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __restrict__ W,
-                const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
-                const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
-                int hpd, float dq, float dk, float dv, void* __restrict__ out, int mt, int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    int tm, tn;
-    tile_coords(blockIdx.x, mt, nt, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM;
-    const int n0 = tn * kBN;
-    Acc acc;
-    mainloop<Mma::kBf16>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M, reinterpret_cast<const uint8_t*>(W),
-                    kHidden * 2, n0, n0 + 128, kHidden * 2 / kRowB, smem, acc);
-
+__device__ __forceinline__ void qkv_epilogue(Acc& acc, uint8_t* smem, int64_t m0, int64_t M, int n0,
+                                             const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
+                                             const uint16_t* __restrict__ cs, int64_t S,
+                                             const int64_t* __restrict__ pos, float qk_eps, int hpd, float dq,
+                                             float dk, float dv, void* __restrict__ out) {
     const int t = threadIdx.x;
     const int li = t & 15;              // lane within the (row, head) group
     // 8-dim chunk of the head held by this lane (partner chunk q +/- 6 sits at lane li ^ 8)
@@ -241,6 +233,50 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
     }
 }
 
+// kE4m3: out holds e4m3 codes (one byte per element) of the bf16 results divided by the
+// descale of their kind (dq, dk, dv); else bf16 values (the descales are unused).
+template <bool kE4m3>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __restrict__ W,
+                const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
+                const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
+                int hpd, float dq, float dk, float dv, void* __restrict__ out, int mt, int nt) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    int tm, tn;
+    tile_coords(blockIdx.x, mt, nt, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM;
+    const int n0 = tn * kBN;
+    Acc acc;
+    mainloop<Mma::kBf16>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M, reinterpret_cast<const uint8_t*>(W),
+                    kHidden * 2, n0, n0 + 128, kHidden * 2 / kRowB, smem, acc);
+    qkv_epilogue<kE4m3>(acc, smem, m0, M, n0, qw, kw, cs, S, pos, qk_eps, hpd, dq, dk, dv, out);
+}
+
+// The same tile on MXFP4 operands: the workspace's and the weight's E2M1 codes ([M, 2688],
+// [21504, 2688]) with their scales in the MX scale layout; bf16 output.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void k_qkv_gemm_mxfp4(const uint8_t* __restrict__ ws_codes, const uint8_t* __restrict__ ws_scales, uint32_t ws_sbytes,
+                      int64_t M, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
+                      uint32_t w_sbytes, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
+                      const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
+                      int hpd, void* __restrict__ out, int mt, int nt) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    int tm, tn;
+    tile_coords(blockIdx.x, mt, nt, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM;
+    const int n0 = tn * kBN;
+    Acc acc;
+    MxScales mxs;
+    mxs.a = ws_scales;
+    mxs.a_bytes = ws_sbytes;
+    mxs.b = w_scales;
+    mxs.b_bytes = w_sbytes;
+    constexpr int kRowBytes = kHidden / 2;
+    mainloop<Mma::kMxFp4>(ws_codes, kRowBytes, m0, M, w_codes, kRowBytes, n0, n0 + 128, kRowBytes / kRowB, smem, acc,
+                          mxs);
+    qkv_epilogue<false>(acc, smem, m0, M, n0, qw, kw, cs, S, pos, qk_eps, hpd, 1.0f, 1.0f, 1.0f, out);
+}
+
 hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
                            const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos, float qk_eps,
                            int P, uint16_t* out, hipStream_t stream) {
@@ -248,6 +284,19 @@ hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, con
     const int nt = kQkvRows / kBN;
     hipLaunchKernelGGL(k_qkv_gemm<false>, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs,
                        S, pos, qk_eps, kHeads / P, 1.0f, 1.0f, 1.0f, out, mt, nt);
+    return hipGetLastError();
+}
+
+hipError_t launch_qkv_gemm_mxfp4(const uint8_t* ws_codes, const uint8_t* ws_scales, int64_t M, const uint8_t* w_codes,
+                                 const uint8_t* w_scales, const uint16_t* qw, const uint16_t* kw, const uint16_t* cs,
+                                 int64_t S, const int64_t* pos, float qk_eps, int P, uint16_t* out,
+                                 hipStream_t stream) {
+    const int mt = (int)((M + kBM - 1) / kBM);
+    const int nt = kQkvRows / kBN;
+    const uint32_t a_sb = (uint32_t)mx_scale_bytes(M, kHidden);
+    const uint32_t w_sb = (uint32_t)mx_scale_bytes(kQkvRows, kHidden);
+    hipLaunchKernelGGL(k_qkv_gemm_mxfp4, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws_codes, ws_scales, a_sb,
+                       M, w_codes, w_scales, w_sb, qw, kw, cs, S, pos, qk_eps, kHeads / P, out, mt, nt);
     return hipGetLastError();
 }
 

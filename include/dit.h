@@ -4,7 +4,8 @@
  * Three operations, each following the tensor contract of one FlashInfer diffusion_ops page:
  *   dit_pre_attn_bf16       "minimax_h3_bf16_pre_attention" (description, Parameters, Notes),
  *                           and its e4m3 output mode dit_pre_attn_e4m3 ("minimax_h3_nvfp4_pre_attention",
- *                           Parameters: out_mode, q/k/v_descale)
+ *                           Parameters: out_mode, q/k/v_descale); its W4A4 form dit_pre_attn_mxfp4
+ *                           (that page's description, OCP MXFP4 in place of NVFP4)
  *   dit_out_proj_gated_bf16 "minimax_h3_nvfp4_out_proj" gated-residual epilogue, bf16 operands,
  *                           and its W4A4 form dit_out_proj_gated_mxfp4 (same page's description,
  *                           with OCP MXFP4 in place of NVFP4; quantiser dit_mx_quant_fp4)
@@ -259,6 +260,32 @@ dit_status dit_mx_quant_fp4(const void* x, int64_t rows, int64_t K, uint8_t* cod
  *   16-byte alignment for every pointer except gate_index (4)
  * Two kernels are enqueued (quantisation, then the block-scaled GEMM with its epilogue).
  */
+/*
+ * MXFP4 W4A4 pre-attention ("minimax_h3_nvfp4_pre_attention", description: the normalised and
+ * modulated activation is quantised to 4 bits with block scales and the QKV GEMM runs on it and
+ * the pre-quantised weight; here in MXFP4, as for dit_out_proj_gated_mxfp4):
+ *   a as in dit_pre_attn_bf16 (the bf16 workspace value; a = 0 for guarded rows), written only
+ *       as its MXFP4 codes and scales (dit_mx_quant_fp4 of a)
+ *   qkv = bf16(A[m] . W[n]) over the MXFP4 values (FP32 accumulation), then the Q/K RMSNorm,
+ *       RoPE and pack of dit_pre_attn_bf16
+ * Arguments:
+ *   x, x_norm_weight, adaln_*, q/k_norm_weight, rope_cos_sin, S, rope_positions,
+ *   ulysses_degree, eps, qk_eps, out   as in dit_pre_attn_bf16 (out bf16 [P, M, 56/P, 3, 128])
+ *   w_codes    uint8 [21504, 2688] and w_scales (dit_mx_scale_bytes(21504, 5376) bytes): the
+ *              qkv weight quantised by dit_mx_quant_fp4
+ *   ws_codes   uint8 [M, 2688] workspace; ws_scales dit_mx_scale_bytes(M, 5376) bytes of workspace
+ *   16-byte alignment for every pointer except adaln_index and rope_positions (8)
+ * Two kernels are enqueued (norm + AdaLN + quantisation, then the block-scaled QKV GEMM).
+ */
+dit_status dit_pre_attn_mxfp4(const void* x, int64_t M, const void* x_norm_weight,
+                              dit_bf16_table adaln_scale, dit_bf16_table adaln_shift,
+                              const int64_t* adaln_index, const uint8_t* w_codes,
+                              const uint8_t* w_scales, const void* q_norm_weight,
+                              const void* k_norm_weight, const void* rope_cos_sin, int64_t S,
+                              const int64_t* rope_positions, int ulysses_degree, float eps,
+                              float qk_eps, uint8_t* ws_codes, uint8_t* ws_scales, void* out,
+                              void* stream);
+
 dit_status dit_out_proj_gated_mxfp4(const void* attn_out, int64_t M, const uint8_t* w_codes,
                                     const uint8_t* w_scales, dit_bf16_table gate,
                                     const int32_t* gate_index, const void* residual,

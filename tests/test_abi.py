@@ -29,7 +29,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("dit_pre_attn_bf16", "dit_pre_attn_e4m3", "dit_qkv_rope_pack_e4m3", "dit_out_proj_gated_bf16",
               "dit_mlp_fp8", "dit_mlp_fp8_flags_elems", "dit_status_string", "dit_abi_version",
-              "dit_mx_scale_bytes", "dit_mx_quant_fp4", "dit_out_proj_gated_mxfp4"):
+              "dit_mx_scale_bytes", "dit_mx_quant_fp4", "dit_out_proj_gated_mxfp4", "dit_pre_attn_mxfp4"):
         assert n in names
 
 
@@ -181,6 +181,28 @@ def outp_mx(**kw):
 ])
 def test_out_proj_mxfp4_contract_checks(kw, status):
     assert outp_mx(**kw) == status
+
+
+def pre_mx(**kw):
+    a = dict(x=_p(1), M=16, xw=_p(2), sc=_T(), sh=_T(A + 0x200000), idx=_p(3), wc=_p(4), ws=_p(5), qw=_p(6),
+             kw=_p(7), cs=_p(8), S=16, pos=None, P=1, eps=1e-5, qk_eps=1e-5, wsc=_p(9), wss=_p(10), out=_p(11))
+    a.update(kw)
+    return dit.load_library().dit_pre_attn_mxfp4(a["x"], a["M"], a["xw"], a["sc"], a["sh"], a["idx"], a["wc"],
+                                                   a["ws"], a["qw"], a["kw"], a["cs"], a["S"], a["pos"], a["P"],
+                                                   a["eps"], a["qk_eps"], a["wsc"], a["wss"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=3), VALUE), (dict(eps=0.0), VALUE), (dict(qk_eps=float("nan")), VALUE),
+    (dict(x=None), NULL), (dict(wc=None), NULL), (dict(ws=None), NULL), (dict(wsc=None), NULL),
+    (dict(wss=None), NULL), (dict(out=None), NULL),
+    (dict(ws=ctypes.c_void_p(A + 4)), ALIGN), (dict(wss=ctypes.c_void_p(A + 8)), ALIGN),
+    (dict(pos=ctypes.c_void_p(A + 4)), ALIGN),
+    (dict(S=8), SHAPE), (dict(sh=_T(rows=3)), SHAPE), (dict(M=-1), SHAPE),
+    (dict(M=0), OK),
+])
+def test_pre_attn_mxfp4_contract_checks(kw, status):
+    assert pre_mx(**kw) == status
 
 
 def mlp(**kw):

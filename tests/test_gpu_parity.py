@@ -543,6 +543,93 @@ def test_out_proj_mxfp4_alias_residual_and_full_size():
     check_out_proj_mx(d, out, ac, asc, rows)
 
 
+# ---------------------------------------------------------------- MXFP4 W4A4 pre-attention
+
+_MXQ = {}
+
+
+def _mx_qkv_weight():
+    """The shared qkv weight's MXFP4 form from the GPU quantiser and from the oracle's (checked equal)."""
+    if "w" not in _MXQ:
+        W = _shared_weight()
+        wc, ws = _dit().dit_mx_quant_fp4(_bf16_cuda(W))
+        torch.cuda.synchronize()
+        wc_ref, ws_ref = oracle.mx_quant_fp4(W)
+        assert np.array_equal(wc.cpu().numpy(), wc_ref)
+        rm, _ = mx_scales_rowmajor(ws, synth.QKV_ROWS, H)
+        assert np.array_equal(rm, ws_ref)
+        _MXQ["w"] = (wc, ws, wc_ref, ws_ref)
+    return _MXQ["w"]
+
+
+def run_pre_mx(d, P=1):
+    t = synth.to_torch("pre_attn", d)
+    wc, ws, _, _ = _mx_qkv_weight()
+    M = d["M"]
+    out = torch.empty((P, M, 56 // P, 3, 128), dtype=torch.bfloat16, device="cuda")
+    wsc = torch.empty((M, H // 2), dtype=torch.uint8, device="cuda")
+    wss = torch.empty((_dit().dit_mx_scale_bytes(M, H),), dtype=torch.uint8, device="cuda")
+    _dit().dit_pre_attn_mxfp4(t["x"], t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], t["adaln_index"], wc, ws,
+                              t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"], ulysses_degree=P, out=out,
+                              eps=t["eps"], qk_eps=t["qk_eps"], rope_positions=t["rope_positions"], ws_codes=wsc,
+                              ws_scales=wss)
+    # the bf16 workspace of the same rows: the fused quantisation must be its MXFP4
+    wsb = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    _dit().dit_norm_adaln_bf16(t["x"], t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], t["adaln_index"],
+                               workspace=wsb, eps=t["eps"])
+    torch.cuda.synchronize()
+    return out, wsc, wss, wsb
+
+
+def check_pre_mx(d, out, wsc, wss, wsb, rows):
+    M = d["M"]
+    c_ref, s_ref = oracle.mx_quant_fp4(synth.bits(wsb)[rows])
+    assert np.array_equal(wsc.cpu().numpy()[rows], c_ref), "workspace codes"
+    rm, pad = mx_scales_rowmajor(wss, M, H)
+    assert np.array_equal(rm[rows], s_ref) and np.all(pad == 0), "workspace scales"
+    _, _, wc_ref, ws_ref = _mx_qkv_weight()
+    ref = oracle.qkv_mxfp4(c_ref, s_ref, wc_ref, ws_ref, d, rows_sel=rows)
+    got = synth.bits(out).reshape(M, 56, 3, 128)[rows]
+    idx = d["adaln_index"][rows]
+    bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
+    assert np.all(bf16_val(got[bad]) == 0.0), "guarded output rows must be zero"
+    ok, rel, mx = bf16_tolerance_ok(got, ref, mag=qkv_magnitude(ref))
+    _say(f"pre_attn mxfp4 M={M} rows={rows.size} relL2={rel:.2e} max|err|={mx:.3e} "
+         f"mismatch={np.mean(got != ref):.2e} guarded={bad.sum()}")
+    assert ok, (rel, mx)
+
+
+def test_pre_attn_mxfp4_against_oracle():
+    M = 300
+    _say(f"pre_attn mxfp4 M={M}")
+    d = synth.pre_attn_inputs(M, seed=600, rows=2, S=512, positions="random", n_bad_positions=4,
+                              bad_index_frac=0.02, weight=_shared_weight())
+    out, wsc, wss, wsb = run_pre_mx(d)
+    bad = np.nonzero((d["adaln_index"] < 0) | (d["adaln_index"] >= 2))[0]
+    rows = np.unique(np.r_[np.arange(8), np.arange(250, 262), np.arange(M - 8, M), bad[:4]])
+    check_pre_mx(d, out, wsc, wss, wsb, rows)
+
+
+def test_pre_attn_mxfp4_ulysses_pack():
+    M = 300
+    _say(f"pre_attn mxfp4 P=2 against P=1, M={M}")
+    d = synth.pre_attn_inputs(M, seed=601, rows=2, S=512, positions="random", n_bad_positions=4,
+                              weight=_shared_weight())
+    one = synth.bits(run_pre_mx(d, P=1)[0]).reshape(M, 56, 3, 128)
+    two = synth.bits(run_pre_mx(d, P=2)[0])
+    assert np.array_equal(two, oracle.ulysses_pack(one, 2))
+
+
+def test_pre_attn_mxfp4_full_size_sampled():
+    M = 32760
+    _say(f"pre_attn mxfp4 M={M}")
+    d = synth.pre_attn_inputs(M, seed=602, rows=2, S=M, positions="identity", weight=_shared_weight())
+    out, wsc, wss, wsb = run_pre_mx(d)
+    g = np.random.default_rng(9)
+    rows = np.unique(np.r_[np.arange(8), np.arange(M - 8, M), g.choice(M, 16, replace=False)])
+    check_pre_mx(d, out, wsc, wss, wsb, rows)
+
+
 # ---------------------------------------------------------------- FP8 MLP
 
 _MW = {}
