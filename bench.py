@@ -197,6 +197,26 @@ def main():
     torch.cuda.synchronize()
     e4m3_ms = e8[0].elapsed_time(e8[1]) / n8
     del out_e4m3
+    # the MXFP4 W4A4 pre-attention on the same inputs (qkv weight quantised once, outside the
+    # timing; each call runs the fused norm + quantisation and the block-scaled QKV GEMM)
+    wq_c, wq_s = dit.dit_mx_quant_fp4(tp["qkv_weight"])
+    ws_c = torch.empty((M_TOKENS, 2688), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty((dit.dit_mx_scale_bytes(M_TOKENS, 5376),), dtype=torch.uint8, device=dev)
+
+    def pre_mx():
+        dit.dit_pre_attn_mxfp4(tp["x"], tp["x_norm_weight"], tp["adaln_scale"], tp["adaln_shift"], tp["adaln_index"],
+                               wq_c, wq_s, tp["q_norm_weight"], tp["k_norm_weight"], tp["rope_cos_sin"],
+                               ulysses_degree=1, out=out_qkv, eps=tp["eps"], qk_eps=tp["qk_eps"],
+                               rope_positions=tp["rope_positions"], ws_codes=ws_c, ws_scales=ws_s)
+    for _ in range(3):
+        pre_mx()
+    e8[0].record()
+    for _ in range(n8):
+        pre_mx()
+    e8[1].record()
+    torch.cuda.synchronize()
+    pre_mx_ms = e8[0].elapsed_time(e8[1]) / n8
+    del wq_c, wq_s, ws_c, ws_s
     mx_ms = None
     if "out_proj" in stages:
         # the MXFP4 W4A4 out-projection on the same inputs (weight quantised once, outside the
@@ -251,6 +271,10 @@ def main():
         r = OUTP_FLOP / (op_ms * 1e-3) / 1e12
         res["stage_rates"]["out_proj_TFLOPs"] = round(r, 2)
         res["stage_rates"]["out_proj_frac_bf16"] = round(r / PEAK_BF16, 4)
+    r = QKV_FLOP / (pre_mx_ms * 1e-3) / 1e12
+    res["stages_ms"]["pre_attn_mxfp4"] = round(float(pre_mx_ms), 4)
+    res["stage_rates"]["pre_attn_mxfp4_TFLOPs"] = round(r, 2)
+    res["stage_rates"]["pre_attn_mxfp4_frac_fp4"] = round(r / PEAK_FP4, 4)
     if mx_ms is not None:
         r = OUTP_FLOP / (mx_ms * 1e-3) / 1e12
         res["stages_ms"]["out_proj_mxfp4"] = round(float(mx_ms), 4)
