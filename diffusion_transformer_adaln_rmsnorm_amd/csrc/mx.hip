@@ -8,10 +8,9 @@
 // OCP MXFP4: block 32 along K with one E8M0 (power-of-two) scale, so no global scale.
 //  - k_mx_quant_fp4: one thread per 32-value block.  E = floor(log2(amax)) - 2 + 127 clamped to
 //    [0, 254] (0 for an all-zero block), code = E2M1 nearest to v 2^(127 - E), ties to the even
-//    significand, saturating at 6, the sign kept.  v 2^(127 - E) is exact in FP32 wherever it
-//    can round to a nonzero code, and the thresholds between E2M1 values are exact, so the codes
-//    are the correctly rounded ones.  Scales go to the MX scale layout (gemm.hpp); the scales of
-//    padding rows up to the next multiple of 128 are written as 0.
+//    significand, saturating at 6, the sign kept (mx.hpp: the magnitude by the hardware's
+//    round-to-nearest-even fp4 conversion of the exact scaled value).  Scales go to the MX scale
+//    layout (gemm.hpp); the scales of padding rows up to the next multiple of 128 are written as 0.
 //  - k_out_proj_mxfp4: the GEMM core on E2M1 codes (128 bytes = 256 values per stage), scales
 //    through LDS, then bf16(o) staged and the shared gated-residual epilogue.
 #include "common.hpp"

@@ -5,17 +5,6 @@
 
 namespace dit {
 
-// E2M1 code (sign in bit 3) of the FP32 value y = v 2^(127 - E): the magnitude index counts the
-// midpoints between neighbouring E2M1 values that |y| passes; at a midpoint it moves up only
-// onto an even significand (midpoints after indices 1, 3, 5 count with >=, after 0, 2, 4, 6
-// with >).  |y| >= 6 gives 7, the saturated maximum.
-__device__ __forceinline__ uint32_t e2m1_code(float y) {
-    const float a = fabsf(y);
-    const uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
-    return m | ((__float_as_uint(y) >> 28) & 8u);
-}
-
 // floor(log2(a)) of a positive finite float (normal or subnormal)
 __device__ __forceinline__ int ilog2f(float a) {
     const uint32_t b = __float_as_uint(a);
@@ -34,11 +23,17 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
 // 2^(127 - E) as a normal float (E <= 252 for any finite bf16 amax)
 __device__ __forceinline__ float mx_inv_scale(uint32_t E) { return __uint_as_float((254u - E) << 23); }
 
-// four E2M1 codes of two packed bf16 pairs, element 2j in the low nibble of byte j
+// four E2M1 codes of two packed bf16 pairs, element 2j in the low nibble of byte j.  The
+// magnitudes |v| 2^(127 - E) (exact in FP32 wherever they can round to a nonzero code) go
+// through v_cvt_scalef32_pk_fp4_f32 with a unit scale: round to nearest, ties to the even
+// significand, saturating at 6.  The sign bits are taken from the bf16 values themselves, so
+// -0 and negative values that round to 0 keep their sign.
 __device__ __forceinline__ uint32_t e2m1_pack4(uint32_t w0, uint32_t w1, float inv) {
-    const uint32_t c0 = e2m1_code(bf_lo(w0) * inv), c1 = e2m1_code(bf_hi(w0) * inv);
-    const uint32_t c2 = e2m1_code(bf_lo(w1) * inv), c3 = e2m1_code(bf_hi(w1) * inv);
-    return (c0 | (c1 << 4)) | ((c2 | (c3 << 4)) << 8);
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, fabsf(bf_lo(w0) * inv), fabsf(bf_hi(w0) * inv), 1.0f, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, fabsf(bf_lo(w1) * inv), fabsf(bf_hi(w1) * inv), 1.0f, 1);
+    // bf16 sign bits 15 and 31 of each word -> bit 3 of nibbles 0, 1 (w0) and 2, 3 (w1)
+    const uint32_t sgn = ((w0 >> 12) & 0x8u) | ((w0 >> 24) & 0x80u) | ((w1 >> 4) & 0x800u) | ((w1 >> 16) & 0x8000u);
+    return (r & 0xFFFFu) | sgn;
 }
 
 // byte offset of the scale of row r, block b (values 32 b ..) of a [*, K] matrix in the MX scale
