@@ -536,7 +536,9 @@ def test_out_proj_mxfp4_alias_residual_and_full_size():
     M = 32760
     _say(f"out_proj mxfp4 M={M}, out is residual")
     d = synth.out_proj_inputs(M, seed=7, weight=_mx_weight()[0])
+    again = synth.bits(run_out_proj_mx(d)[0])
     out, ac, asc = run_out_proj_mx(d, alias=True)
+    assert np.array_equal(synth.bits(out), again), "not deterministic (or aliasing changed the result)"
     g = np.random.default_rng(8)
     rows = np.unique(np.r_[np.arange(16), np.arange(M - 16, M), np.nonzero(d["gate_index"] < 0)[0][:16],
                            g.choice(M, 24, replace=False)])
@@ -625,6 +627,9 @@ def test_pre_attn_mxfp4_full_size_sampled():
     _say(f"pre_attn mxfp4 M={M}")
     d = synth.pre_attn_inputs(M, seed=602, rows=2, S=M, positions="identity", weight=_shared_weight())
     out, wsc, wss, wsb = run_pre_mx(d)
+    out2, wsc2, wss2, _ = run_pre_mx(d)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(wsc, wsc2) and \
+        torch.equal(wss, wss2), "not deterministic"
     g = np.random.default_rng(9)
     rows = np.unique(np.r_[np.arange(8), np.arange(M - 8, M), g.choice(M, 16, replace=False)])
     check_pre_mx(d, out, wsc, wss, wsb, rows)
