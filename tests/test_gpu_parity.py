@@ -614,12 +614,14 @@ def test_pre_attn_mxfp4_against_oracle():
 
 def test_pre_attn_mxfp4_ulysses_pack():
     M = 300
-    _say(f"pre_attn mxfp4 P=2 against P=1, M={M}")
+    _say(f"pre_attn mxfp4 P=2, 4, 8 against P=1, M={M}")
     d = synth.pre_attn_inputs(M, seed=601, rows=2, S=512, positions="random", n_bad_positions=4,
                               weight=_shared_weight())
     one = synth.bits(run_pre_mx(d, P=1)[0]).reshape(M, 56, 3, 128)
-    two = synth.bits(run_pre_mx(d, P=2)[0])
-    assert np.array_equal(two, oracle.ulysses_pack(one, 2))
+    for P in (2, 4, 8):
+        got = synth.bits(run_pre_mx(d, P=P)[0])
+        assert got.shape == (P, M, 56 // P, 3, 128)
+        assert np.array_equal(got, oracle.ulysses_pack(one, P)), P
 
 
 def test_pre_attn_mxfp4_full_size_sampled():
