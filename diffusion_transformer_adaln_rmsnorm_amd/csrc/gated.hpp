@@ -8,11 +8,11 @@
 // Thread t owns 8 consecutive columns (c8 = (t % 32) * 8) of the tile rows it * 16 + t / 32,
 // it = 0..15.  Residual and out are addressed through buffer descriptors over the tile's rows,
 // so rows past M read zeros and their stores are dropped with no branch, and each row costs
-// one 32-bit add of address arithmetic.  The row indices are requested before the
-// accumulators are staged (load_index), the residual and gate chunks of all 16 rows right
-// after (run), so a tile pays about one memory latency rather than one per row.  Each thread
-// reads its residual chunk before it writes the same chunk of out, so out may be the residual
-// buffer.
+// one 32-bit add of address arithmetic.  The row indices (load_index) and, where registers
+// allow, the residual chunks (load_residual) are requested before the accumulators are staged,
+// the gate chunks of all 16 rows right after, so a tile pays about one memory latency rather
+// than one per row.  Each thread reads its residual chunk before it writes the same chunk of
+// out, so out may be the residual buffer.
 #pragma once
 
 #include "gemm.hpp"
@@ -26,6 +26,7 @@ struct GatedResidual {
     static constexpr int kIters = kBM / kRowsPerPass;
     static constexpr uint32_t kPassB = (uint32_t)(kRowsPerPass * kHidden * 2);
     int64_t gi[kIters];
+    u32x4 rr[kIters];       // the residual chunks of this thread's rows
 
     // index[m] of this thread's rows (0 for rows past M: their stores are dropped)
     __device__ __forceinline__ void load_index(const Idx* index, int64_t m0, int64_t M) {
@@ -43,22 +44,37 @@ struct GatedResidual {
         }
     }
 
-    // After the bf16 tile is staged in LDS (and a barrier): out = bf16(r + bf16(g * o)).
+    // the residual chunks of all rows (the out-projections request them before the accumulators
+    // are staged, so their latency hides behind the staging; FC2's row and column scales leave
+    // no registers for that, and it requests them after)
+    __device__ __forceinline__ void load_residual(int64_t m0, int64_t M, int n0, const uint16_t* residual) {
+        const int t = threadIdx.x;
+        const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
+        const __amdgpu_buffer_rsrc_t rres = make_rsrc(residual + m0 * kHidden, (uint32_t)(tile_rows * kHidden * 2));
+        const uint32_t o1 = (uint32_t)(((t >> 5) * kHidden + n0 + (t & 31) * 8) * 2);
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) rr[it] = buf_ld16(rres, o1 + it * kPassB);
+    }
+
+    // After the bf16 tile is staged in LDS (and a barrier): the residual chunks, then finish().
     __device__ __forceinline__ void run(const uint8_t* smem, int64_t m0, int64_t M, int n0, const uint16_t* gate,
-                                        int64_t gate_rows, int64_t gate_ld, const uint16_t* residual,
-                                        uint16_t* out) const {
+                                        int64_t gate_rows, int64_t gate_ld, const uint16_t* residual, uint16_t* out) {
+        load_residual(m0, M, n0, residual);
+        finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
+    }
+
+    // With the residual chunks requested: out = bf16(r + bf16(g * o)).
+    __device__ __forceinline__ void finish(const uint8_t* smem, int64_t m0, int64_t M, int n0, const uint16_t* gate,
+                                           int64_t gate_rows, int64_t gate_ld, uint16_t* out) const {
         const int t = threadIdx.x;
         const int c8 = (t & 31) * 8;
         const int rsub = t >> 5;
         const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
         const uint32_t bytes = (uint32_t)(tile_rows * kHidden * 2);
-        const __amdgpu_buffer_rsrc_t rres = make_rsrc(residual + m0 * kHidden, bytes);
         const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + m0 * kHidden, bytes);
         const uint32_t o1 = (uint32_t)((rsub * kHidden + n0 + c8) * 2);
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        u32x4 rr[kIters], gg[kIters];
-#pragma unroll
-        for (int it = 0; it < kIters; ++it) rr[it] = buf_ld16(rres, o1 + it * kPassB);
+        u32x4 gg[kIters];
 #pragma unroll
         for (int it = 0; it < kIters; ++it) {
             gg[it] = zero;

@@ -78,9 +78,10 @@ void k_out_proj_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __rest
                           mxs);
     GatedResidual<int32_t> gr;
     gr.load_index(gate_index, m0, M);
+    gr.load_residual(m0, M, n0, residual);
     stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
     __syncthreads();
-    gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);
+    gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
 }
 
 int64_t mx_scale_bytes(int64_t rows, int64_t K) { return (rows + 127) / 128 * 128 * (K / 32); }

@@ -32,9 +32,10 @@ void k_out_proj_gemm(const uint16_t* __restrict__ attn, int64_t M, const uint16_
                     acc);
     GatedResidual<int32_t> gr;
     gr.load_index(gate_index, m0, M);
+    gr.load_residual(m0, M, n0, residual);
     stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
     __syncthreads();
-    gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);
+    gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
 }
 
 hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t* Wo, const uint16_t* gate,
