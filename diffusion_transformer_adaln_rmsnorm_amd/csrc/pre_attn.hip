@@ -158,7 +158,7 @@ __device__ __forceinline__ void qkv_epilogue(Acc& acc, uint8_t* smem, int64_t m0
     // Every global operand of the epilogue is requested before it is needed, so the loop
     // below pays one memory latency per tile rather than one per row: the positions of this
     // thread's kIters rows now (they land while the accumulators are staged), the cos/sin
-    // rows right after.  All epilogue loads and stores go through buffer descriptors and are
+    // rows right after the staging.  All epilogue loads and stores go through buffer descriptors and are
     // issued unconditionally (out-of-range lanes read zeros, stores past M are dropped).
     constexpr int kRowsPerPass = kThreads / 32;
     constexpr int kIters = kBM / kRowsPerPass;
@@ -187,14 +187,8 @@ __device__ __forceinline__ void qkv_epilogue(Acc& acc, uint8_t* smem, int64_t m0
     }
 
     stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
-    __syncthreads();
-
-    u32x4 nwlo, nwhi;                   // the norm weights, one bf16 of each pair kept
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        nwlo[e] = nwv[e] & 0xFFFFu;
-        nwhi[e] = nwv[e] & 0xFFFF0000u;
-    }
+    // the cos/sin rows are requested once the accumulators are free and before the barrier, so
+    // they are in flight while the other waves finish staging
     u32x4 cv[kIters], sv[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
@@ -204,6 +198,14 @@ __device__ __forceinline__ void qkv_epilogue(Acc& acc, uint8_t* smem, int64_t m0
         const uint32_t off = need_cs ? (uint32_t)((pc * kRopeCols + j0) * 2) : kOffNone;
         cv[it] = buf_ld16(rcs, off);
         sv[it] = buf_ld16(rcs, off + (need_cs ? kNFreq * 2 : 0u));
+    }
+    __syncthreads();
+
+    u32x4 nwlo, nwhi;                   // the norm weights, one bf16 of each pair kept
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        nwlo[e] = nwv[e] & 0xFFFFu;
+        nwhi[e] = nwv[e] & 0xFFFF0000u;
     }
 
 #pragma unroll
