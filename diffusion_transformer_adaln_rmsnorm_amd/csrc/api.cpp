@@ -15,7 +15,7 @@ bool eps_ok(float e) { return isfinite(e) && e > 0.f; }
 dit_status check_table(const dit_bf16_table& t) {
     if (!t.ptr) return DIT_ERR_NULL;
     if (!aligned(t.ptr, 16)) return DIT_ERR_ALIGN;
-    if (t.rows < 1) return DIT_ERR_SHAPE;
+    if (t.rows < 1 || t.rows > INT32_MAX) return DIT_ERR_SHAPE;      // row numbers fit 32 bits on the device
     if (t.row_stride < DIT_HIDDEN || (t.row_stride & 7) != 0) return DIT_ERR_STRIDE;
     return DIT_OK;
 }

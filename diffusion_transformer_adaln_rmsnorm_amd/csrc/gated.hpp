@@ -25,22 +25,25 @@ struct GatedResidual {
     static constexpr int kRowsPerPass = kThreads / 32;
     static constexpr int kIters = kBM / kRowsPerPass;
     static constexpr uint32_t kPassB = (uint32_t)(kRowsPerPass * kHidden * 2);
-    int64_t gi[kIters];
+    int32_t gi[kIters];     // the gate row of each of this thread's rows, -1 for gate 0
     u32x4 rr[kIters];       // the residual chunks of this thread's rows
 
-    // index[m] of this thread's rows (0 for rows past M: their stores are dropped)
-    __device__ __forceinline__ void load_index(const Idx* index, int64_t m0, int64_t M) {
+    // index[m] of this thread's rows, checked against [0, gate_rows) at full width and kept
+    // as a 32-bit row or -1 (rows past M read index 0: their stores are dropped)
+    __device__ __forceinline__ void load_index(const Idx* index, int64_t m0, int64_t M, int64_t gate_rows) {
         const int rsub = threadIdx.x >> 5;
         const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
         const __amdgpu_buffer_rsrc_t ri = make_rsrc(index + m0, (uint32_t)(tile_rows * sizeof(Idx)));
 #pragma unroll
         for (int it = 0; it < kIters; ++it) {
             const uint32_t off = (uint32_t)((it * kRowsPerPass + rsub) * sizeof(Idx));
+            int64_t i;
             if constexpr (sizeof(Idx) == 8) {
-                gi[it] = buf_ld_i64(ri, off);
+                i = buf_ld_i64(ri, off);
             } else {
-                gi[it] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (int)off, 0, 0);
+                i = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (int)off, 0, 0);
             }
+            gi[it] = (i >= 0 && i < gate_rows) ? (int32_t)i : -1;
         }
     }
 
@@ -78,7 +81,7 @@ struct GatedResidual {
 #pragma unroll
         for (int it = 0; it < kIters; ++it) {
             gg[it] = zero;
-            if (gi[it] >= 0 && gi[it] < gate_rows) gg[it] = ld16(gate + gi[it] * gate_ld + n0 + c8);
+            if (gi[it] >= 0) gg[it] = ld16(gate + (int64_t)gi[it] * gate_ld + n0 + c8);
         }
 #pragma unroll
         for (int it = 0; it < kIters; ++it) {

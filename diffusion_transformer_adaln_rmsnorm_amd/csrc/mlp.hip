@@ -115,7 +115,7 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
     Acc acc;
     mainloop<Mma::kE4m3>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc);
     GatedResidual<int64_t> gr;
-    gr.load_index(idx, m0, M);
+    gr.load_index(idx, m0, M, gate_rows);
     stage_tile_bf16(acc, smem, y_scale, m0, M, w2s + n0, w2s + n0 + 128);
     __syncthreads();
     gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);

@@ -77,7 +77,7 @@ void k_out_proj_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __rest
     mainloop<Mma::kMxFp4>(a_codes, kRowBytes, m0, M, w_codes, kRowBytes, n0, n0 + 128, kRowBytes / kRowB, smem, acc,
                           mxs);
     GatedResidual<int32_t> gr;
-    gr.load_index(gate_index, m0, M);
+    gr.load_index(gate_index, m0, M, gate_rows);
     gr.load_residual(m0, M, n0, residual);
     stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
     __syncthreads();

@@ -31,7 +31,7 @@ void k_out_proj_gemm(const uint16_t* __restrict__ attn, int64_t M, const uint16_
                     reinterpret_cast<const uint8_t*>(Wo), kAttnWidth * 2, n0, n0 + 128, kAttnWidth * 2 / kRowB, smem,
                     acc);
     GatedResidual<int32_t> gr;
-    gr.load_index(gate_index, m0, M);
+    gr.load_index(gate_index, m0, M, gate_rows);
     gr.load_residual(m0, M, n0, residual);
     stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
     __syncthreads();

@@ -58,7 +58,7 @@ typedef enum {
 /*
  * A bf16 [rows, 5376] table view with unit column stride, as the pre-attention page's
  * adaln_scale/adaln_shift entries allow: row r starts at ptr + r * row_stride ELEMENTS.
- * row_stride >= 5376 and a multiple of 8; ptr 16-byte aligned.  A column chunk of a wider
+ * row_stride >= 5376 and a multiple of 8; 1 <= rows <= 2^31 - 1; ptr 16-byte aligned.  A column chunk of a wider
  * [rows, 6 * 5376] modulation matrix is passed as-is (ptr = chunk start, row_stride = 32256).
  */
 typedef struct {

@@ -130,6 +130,7 @@ def outp(**kw):
     (dict(attn=None), NULL), (dict(gi=None), NULL), (dict(res=None), NULL), (dict(out=None), NULL),
     (dict(attn=ctypes.c_void_p(A + 4)), ALIGN), (dict(gi=ctypes.c_void_p(A + 2)), ALIGN),
     (dict(gate=_T(rows=0, stride=5376)), SHAPE), (dict(gate=_T(rows=9, stride=5380)), STRIDE),
+    (dict(gate=_T(rows=1 << 31, stride=5376)), SHAPE),
     (dict(M=-3), SHAPE), (dict(M=0), OK),
 ])
 def test_out_proj_contract_checks(kw, status):
