@@ -612,6 +612,17 @@ def test_pre_attn_mxfp4_against_oracle():
     check_pre_mx(d, out, wsc, wss, wsb, rows)
 
 
+@pytest.mark.parametrize("M", [1, 129])
+def test_pre_attn_mxfp4_small_M(M):
+    # one row (127 padding scale rows), and one row past a 128-row scale block
+    _say(f"pre_attn mxfp4 M={M}")
+    d = synth.pre_attn_inputs(M, seed=603 + M, rows=2, S=64, positions="random", n_bad_positions=1,
+                              bad_index_frac=0.05, weight=_shared_weight())
+    out, wsc, wss, wsb = run_pre_mx(d)
+    rows = np.unique(np.r_[np.arange(min(M, 4)), np.arange(max(M - 6, 0), M)])
+    check_pre_mx(d, out, wsc, wss, wsb, rows)
+
+
 def test_pre_attn_mxfp4_ulysses_pack():
     M = 300
     _say(f"pre_attn mxfp4 P=2, 4, 8 against P=1, M={M}")
