@@ -1,6 +1,7 @@
 // C ABI entry points: host-side contract checks, then the kernel launches, all on the
 // caller's stream.  Nothing here allocates, copies, or synchronises.
 #include <hip/hip_runtime_api.h>
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 
@@ -11,6 +12,9 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool eps_ok(float e) { return isfinite(e) && e > 0.f; }
+// A per-tensor e4m3 descale divides each output; its reciprocal must be a finite float, which
+// every normal float has (1 / FLT_MIN = 2^126) and some subnormals do not.
+bool descale_ok(float d) { return isfinite(d) && d >= FLT_MIN; }
 
 dit_status check_table(const dit_bf16_table& t) {
     if (!t.ptr) return DIT_ERR_NULL;
@@ -24,6 +28,9 @@ dit_status launched(hipError_t e) { return e == hipSuccess ? DIT_OK : DIT_ERR_LA
 
 // Upper row bound: keeps every grid below 2^32 work-items (x alone is 180 GB at this M).
 constexpr int64_t kMaxRows = (int64_t)1 << 24;
+// Upper bound on the rows S of the [S, 96] bf16 cos/sin cache: the QKV epilogue reads it
+// through one buffer descriptor, whose byte range and offsets are 32-bit (S * 192 < 2^32).
+constexpr int64_t kMaxRopeRows = (int64_t)0xFFFFFFFF / (DIT_ROPE_COLS * 2);
 
 }  // namespace
 
@@ -79,14 +86,15 @@ static dit_status qkv_rope_pack(const void* workspace, int64_t M, const void* qk
     if (ulysses_degree != 1 && ulysses_degree != 2 && ulysses_degree != 4 && ulysses_degree != 8)
         return DIT_ERR_VALUE;
     if (!eps_ok(qk_eps)) return DIT_ERR_VALUE;
-    if (descale && (!eps_ok(descale[0]) || !eps_ok(descale[1]) || !eps_ok(descale[2]))) return DIT_ERR_VALUE;
+    if (descale && (!descale_ok(descale[0]) || !descale_ok(descale[1]) || !descale_ok(descale[2])))
+        return DIT_ERR_VALUE;
     if (M < 0 || M > kMaxRows) return DIT_ERR_SHAPE;
     if (!workspace || !qkv_weight || !q_norm_weight || !k_norm_weight || !rope_cos_sin || !out) return DIT_ERR_NULL;
     if (!aligned(workspace, 16) || !aligned(qkv_weight, 16) || !aligned(q_norm_weight, 16) ||
         !aligned(k_norm_weight, 16) || !aligned(rope_cos_sin, 16) || !aligned(out, 16) ||
         (rope_positions && !aligned(rope_positions, 8)))
         return DIT_ERR_ALIGN;
-    if (S < 1) return DIT_ERR_SHAPE;
+    if (S < 1 || S > kMaxRopeRows) return DIT_ERR_SHAPE;
     if (!rope_positions && S < M) return DIT_ERR_SHAPE;
     if (M == 0) return DIT_OK;
     const uint16_t* ws = static_cast<const uint16_t*>(workspace);
@@ -112,7 +120,8 @@ static dit_status pre_attn(const void* x, int64_t M, const void* x_norm_weight, 
     if (ulysses_degree != 1 && ulysses_degree != 2 && ulysses_degree != 4 && ulysses_degree != 8)
         return DIT_ERR_VALUE;
     if (!eps_ok(eps) || !eps_ok(qk_eps)) return DIT_ERR_VALUE;
-    if (descale && (!eps_ok(descale[0]) || !eps_ok(descale[1]) || !eps_ok(descale[2]))) return DIT_ERR_VALUE;
+    if (descale && (!descale_ok(descale[0]) || !descale_ok(descale[1]) || !descale_ok(descale[2])))
+        return DIT_ERR_VALUE;
     if (M < 0 || M > kMaxRows) return DIT_ERR_SHAPE;
     if (!x || !x_norm_weight || !adaln_index || !qkv_weight || !q_norm_weight || !k_norm_weight ||
         !rope_cos_sin || !workspace || !out)
@@ -126,7 +135,7 @@ static dit_status pre_attn(const void* x, int64_t M, const void* x_norm_weight, 
         !aligned(k_norm_weight, 16) || !aligned(rope_cos_sin, 16) || !aligned(workspace, 16) || !aligned(out, 16) ||
         !aligned(adaln_index, 8) || (rope_positions && !aligned(rope_positions, 8)))
         return DIT_ERR_ALIGN;
-    if (S < 1) return DIT_ERR_SHAPE;
+    if (S < 1 || S > kMaxRopeRows) return DIT_ERR_SHAPE;
     if (!rope_positions && S < M) return DIT_ERR_SHAPE;
     if (M == 0) return DIT_OK;
     st = dit_norm_adaln_bf16(x, M, x_norm_weight, adaln_scale, adaln_shift, adaln_index, eps, workspace, stream);
@@ -213,7 +222,7 @@ dit_status dit_pre_attn_mxfp4(const void* x, int64_t M, const void* x_norm_weigh
         !aligned(ws_codes, 16) || !aligned(ws_scales, 16) || !aligned(out, 16) || !aligned(adaln_index, 8) ||
         (rope_positions && !aligned(rope_positions, 8)))
         return DIT_ERR_ALIGN;
-    if (S < 1) return DIT_ERR_SHAPE;
+    if (S < 1 || S > kMaxRopeRows) return DIT_ERR_SHAPE;
     if (!rope_positions && S < M) return DIT_ERR_SHAPE;
     if (M == 0) return DIT_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);

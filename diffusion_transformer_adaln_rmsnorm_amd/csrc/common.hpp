@@ -57,6 +57,14 @@ __device__ __forceinline__ float div_by(float a, float s, float y) {
     return r == 0.0f ? q0 : fmaf(r, y, q0);
 }
 
+// fl32(a / s) for a positive per-row scale s: div_by with y = RN(1 / s) when s is a normal
+// float, an IEEE division when s is subnormal.  Below 2^-126 the reciprocal can overflow (s <
+// 2^-128), which would turn div_by's product into inf or NaN, and the fma remainder is no
+// longer exact.  The choice is uniform over a row, so a wavefront that owns a row never splits.
+__device__ __forceinline__ float div_row(float a, float s, float y, bool s_normal) {
+    return s_normal ? div_by(a, s, y) : a / s;
+}
+
 // silu(t) = t / (1 + e^-t) from the hardware exp2 and reciprocal (each ~1 ulp); e^-t -> inf
 // gives 0 and e^-t -> 0 gives t, the limits
 __device__ __forceinline__ float silu_fast(float t) {

@@ -204,6 +204,7 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
     amax = wave_max(amax);
     const float s = amax / 448.0f;             // IEEE division: RN(amax / 448)
     const float inv = 1.0f / s;                // RN(1 / s); unused when s == 0
+    const bool s_normal = s >= 1.17549435e-38f;    // FLT_MIN
     if (lane == 0) a_scale[m] = s;
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
@@ -214,10 +215,10 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
         if (s == 0.f) {
             q = make_uint2(0u, 0u);
         } else {
-            q.x = f2e4m3x2(div_by(a[0], s, inv), div_by(a[1], s, inv)) |
-                  (f2e4m3x2(div_by(a[2], s, inv), div_by(a[3], s, inv)) << 16);
-            q.y = f2e4m3x2(div_by(a[4], s, inv), div_by(a[5], s, inv)) |
-                  (f2e4m3x2(div_by(a[6], s, inv), div_by(a[7], s, inv)) << 16);
+            q.x = f2e4m3x2(div_row(a[0], s, inv, s_normal), div_row(a[1], s, inv, s_normal)) |
+                  (f2e4m3x2(div_row(a[2], s, inv, s_normal), div_row(a[3], s, inv, s_normal)) << 16);
+            q.y = f2e4m3x2(div_row(a[4], s, inv, s_normal), div_row(a[5], s, inv, s_normal)) |
+                  (f2e4m3x2(div_row(a[6], s, inv, s_normal), div_row(a[7], s, inv, s_normal)) << 16);
         }
         *reinterpret_cast<uint2*>(qr + (j * 64 + lane) * 8) = q;
     }

@@ -43,16 +43,22 @@ extern "C" {
 #define DIT_INTER 14336       /* MLP intermediate width */
 #define DIT_FC1_ROWS 28672    /* gate | up */
 #define DIT_MLP_MAX_M 149796  /* row limit of the fp8 MLP page */
+#define DIT_MAX_ROWS 16777216 /* 2^24: row limit of the pre-attention and out-projection calls
+                                 (keeps every launch grid below 2^32 work-items) */
+#define DIT_MAX_ROPE_ROWS 22369621 /* floor((2^32 - 1) / 192): rows of the [S, 96] bf16 cos/sin
+                                      cache, whose byte offsets are 32-bit on the device */
 
 typedef enum {
     DIT_OK = 0,
     DIT_ERR_NULL = 1,        /* a required pointer is NULL */
-    DIT_ERR_SHAPE = 2,       /* a size is out of range (M, rows, S, S < M with identity positions) */
+    DIT_ERR_SHAPE = 2,       /* a size is out of range (M, rows, S, S < M with identity positions);
+                                M <= DIT_MAX_ROWS and S <= DIT_MAX_ROPE_ROWS wherever they apply */
     DIT_ERR_ALIGN = 3,       /* a pointer is not 16-byte aligned (8 for int64 vectors, 4 for int32/f32) */
     DIT_ERR_STRIDE = 4,      /* table row stride < 5376 or not a multiple of 8 elements, or mismatched */
     DIT_ERR_UNSUPPORTED = 5, /* a valid argument this build does not implement (none at present) */
     DIT_ERR_LAUNCH = 6,      /* the HIP runtime rejected a kernel launch */
-    DIT_ERR_VALUE = 7        /* a scalar is invalid (eps <= 0 or not finite, ulysses_degree not 1/2/4/8) */
+    DIT_ERR_VALUE = 7        /* a scalar is invalid (eps <= 0 or not finite, ulysses_degree not 1/2/4/8,
+                                an e4m3 descale below FLT_MIN or not finite) */
 } dit_status;
 
 /*
@@ -93,13 +99,13 @@ int dit_abi_version(void);
  *
  * Arguments:
  *   x              bf16 [M, 5376], contiguous, 16-B aligned
- *   M              rows; 0 is a no-op returning DIT_OK
+ *   M              rows, 0 <= M <= DIT_MAX_ROWS; 0 is a no-op returning DIT_OK
  *   x_norm_weight  bf16 [5376]
  *   adaln_scale, adaln_shift  tables with equal rows (>= 1)
  *   adaln_index    int64 [M]; any value is allowed (see the guard above)
  *   qkv_weight     bf16 [21504, 5376]
  *   q_norm_weight, k_norm_weight  bf16 [128]
- *   rope_cos_sin   bf16 [S, 96], S >= 1
+ *   rope_cos_sin   bf16 [S, 96], 1 <= S <= DIT_MAX_ROPE_ROWS
  *   rope_positions int64 [M] or NULL for the identity (then S >= M is required)
  *   ulysses_degree destination count P: 1, 2, 4 or 8 (else DIT_ERR_VALUE)
  *   eps, qk_eps    positive finite RMSNorm epsilons (the Python binding maps qk_eps=None to eps)
@@ -145,7 +151,8 @@ dit_status dit_qkv_rope_pack_bf16(const void* workspace, int64_t M, const void* 
  * (float8_e4m3fn, round to nearest even, saturating at +-448; descale_kind = q_descale,
  * k_descale or v_descale), so that code * descale approximates o.
  * Arguments as the bf16 calls, plus:
- *   q_descale, k_descale, v_descale  positive finite fp32 scales (else DIT_ERR_VALUE)
+ *   q_descale, k_descale, v_descale  finite fp32 scales >= FLT_MIN (2^-126), so that each
+ *                  reciprocal is finite (else DIT_ERR_VALUE)
  *   out            uint8 e4m3 codes [P, M, 56/P, 3, 128], 16-B aligned; must not overlap any input
  */
 dit_status dit_pre_attn_e4m3(const void* x, int64_t M, const void* x_norm_weight,
@@ -169,7 +176,7 @@ dit_status dit_qkv_rope_pack_e4m3(const void* workspace, int64_t M, const void* 
  *   g = gate[gate_index[m]] if 0 <= gate_index[m] < gate.rows else 0
  *   out[m] = bf16(residual[m] + bf16(g * o))
  * Arguments:
- *   attn_out   bf16 [M, 7168];  M = 0 is a no-op
+ *   attn_out   bf16 [M, 7168];  0 <= M <= DIT_MAX_ROWS, M = 0 is a no-op
  *   o_weight   bf16 [5376, 7168]
  *   gate       table view [rows, 5376] (the page's gate_msa rows, rows = 9 there)
  *   gate_index int32 [M], any value
@@ -251,7 +258,7 @@ dit_status dit_mx_quant_fp4(const void* x, int64_t rows, int64_t K, uint8_t* cod
  *       codes and scales (FP32 accumulation)
  *   out[m] = bf16(residual[m] + bf16(g * o)),  g as in dit_out_proj_gated_bf16
  * Arguments:
- *   attn_out    bf16 [M, 7168]; M = 0 is a no-op
+ *   attn_out    bf16 [M, 7168]; 0 <= M <= DIT_MAX_ROWS, M = 0 is a no-op
  *   w_codes     uint8 [5376, 3584] and w_scales (dit_mx_scale_bytes(5376, 7168) bytes): the
  *               weight quantised by dit_mx_quant_fp4
  *   gate, gate_index, residual, out   as in dit_out_proj_gated_bf16

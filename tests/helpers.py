@@ -60,31 +60,75 @@ def ordered_e4m3(c):
     return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
 
 
-def bf16_tolerance_ok(got_bits, ref_bits, max_rel_l2=2e-3, elem=1e-2, mag=None):
-    """The acceptance bar for bf16 outputs: relative L2 error and |err| <= elem*(1+|ref|).
-
-    mag, when given, replaces |ref| as the element's magnitude (same shape as ref)."""
+def bf16_tolerance_ok(got_bits, ref_bits, max_rel_l2=2e-3, elem=1e-2):
+    """The acceptance bar for bf16 outputs: relative L2 error and |err| <= elem*(1+|ref|)."""
     g = bf16_val(got_bits).ravel()
     r = bf16_val(ref_bits).ravel()
-    m = np.abs(r) if mag is None else np.asarray(mag, np.float64).ravel()
+    m = np.abs(r)
     err = np.abs(g - r)
     rel_l2 = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
     ok_elem = np.all(err <= elem * (1.0 + m))
     return bool(rel_l2 <= max_rel_l2 and ok_elem), float(rel_l2), float(err.max() if err.size else 0.0)
 
 
-def qkv_magnitude(out_ref_bits):
-    """Per-element magnitude of packed q/k/v outputs [..., 3, 128] for the elementwise bar.
+def rope_elem_bound(out_ref_bits, cos_sin_bits):
+    """Derived per-element bound for the RoPE-rotated q/k outputs [R, 56, 3, 128].
 
-    RoPE rotates each (j, j+48) pair of q and k (j < 48) and preserves the pair's norm, so a
-    rotated element is judged against that norm: a one-ulp difference in a large u_j may land
-    in an output that the rotation made small.  V and the pass-through dims use |ref|."""
-    r = bf16_val(out_ref_bits)
-    mag = np.abs(r).copy()
-    pair = np.hypot(r[..., :2, :48], r[..., :2, 48:96])
-    mag[..., :2, :48] = pair
-    mag[..., :2, 48:96] = pair
-    return mag
+    cos_sin_bits [R, 96] holds each row's cache row (cos in [0, 48), sin in [48, 96)).  The
+    GEMM accumulates in FP32 (the pages' precision), so v = bf16(acc) may sit one bf16 ulp
+    from the oracle's bf16(exact acc).  Through u = bf16(v * r2 * w) that is at most two ulps
+    of u (ulp(v) |r2 w| <= 2 ulp(u)), plus one more where u's own rounding flips: |du| <= 3
+    ulp(u).  The rotation o_j = bf16(u_j c - u_{j+48} s) carries it as |c| du_j + |s| du_{j+48},
+    and o's rounding may flip once more.  So
+        |o_gpu - o_ref| <= 3 (|c| ulp(u_j) + |s| ulp(u_{j+48})) + ulp(o_ref)   (j < 48)
+    and the same with u_j, u_{j+48} exchanged for o_{j+48}.  u is recovered from the oracle's
+    o by the inverse rotation; its magnitude is raised by 2^-6 (the bf16 rounding of o, c and
+    s) so that the ulp taken is never below u's own.  Returns the bound for the q/k rotated
+    dims and +inf elsewhere (those elements are held to the plain bar only)."""
+    o = bf16_val(out_ref_bits)
+    cs = bf16_val(cos_sin_bits)
+    c = np.abs(cs[:, None, None, :48])
+    s = cs[:, None, None, 48:96]
+    cc = cs[:, None, None, :48]
+    lo, hi = o[:, :, :2, :48], o[:, :, :2, 48:96]
+    u_lo = lo * cc + hi * s
+    u_hi = hi * cc - lo * s
+    grow = 1.0 + 2.0 ** -6
+    ul_lo = ulp_bf16(np.abs(u_lo) * grow + 2.0 ** -133)
+    ul_hi = ulp_bf16(np.abs(u_hi) * grow + 2.0 ** -133)
+    sa = np.abs(s)
+    bound = np.full(o.shape, np.inf)
+    bound[:, :, :2, :48] = 3.0 * (c * ul_lo + sa * ul_hi) + ulp_bf16(lo)
+    bound[:, :, :2, 48:96] = 3.0 * (c * ul_hi + sa * ul_lo) + ulp_bf16(hi)
+    return bound
+
+
+def qkv_check(got_bits, ref_bits, cos_sin_bits, max_rel_l2=2e-3, elem=1e-2, max_relaxed=None):
+    """The QKV output bar: relative L2 <= max_rel_l2, and each element within the plain
+    elem * (1 + |ref|) or, for a RoPE-rotated q/k element, within rope_elem_bound.  The number of
+    elements that need the derived bound is returned and, when max_relaxed is given, must not
+    exceed it.  Returns (ok, rel_l2, max|err|, n_relaxed, worst err/bound over relaxed elements)."""
+    g = bf16_val(got_bits)
+    r = bf16_val(ref_bits)
+    err = np.abs(g - r)
+    rel_l2 = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    plain = err <= elem * (1.0 + np.abs(r))
+    bound = rope_elem_bound(ref_bits, cos_sin_bits)
+    derived = err <= bound
+    ok_elem = np.all(plain | derived)
+    relaxed = ~plain
+    n_relaxed = int(relaxed.sum())
+    worst = float((err[relaxed] / bound[relaxed]).max()) if n_relaxed else 0.0
+    ok = bool(rel_l2 <= max_rel_l2 and ok_elem and (max_relaxed is None or n_relaxed <= max_relaxed))
+    return ok, float(rel_l2), float(err.max() if err.size else 0.0), n_relaxed, worst
+
+
+def e4m3_half_step(v, s):
+    """Half the e4m3 code spacing at |v| / s, in v's units (s the per-row scale): 2^(e-4) s for
+    a normal quotient in [2^e, 2^(e+1)), 2^-10 s in the subnormal range (below 2^-6)."""
+    q = np.abs(np.asarray(v, np.float64)) / np.where(s > 0, s, 1.0)
+    e = np.floor(np.log2(np.maximum(q, 2.0 ** -6)))
+    return np.exp2(e - 4) * s
 
 
 def ulp_bf16(v):

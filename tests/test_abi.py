@@ -17,6 +17,9 @@ HEADER = os.path.join(ROOT, "include", "dit.h")
 
 OK, NULL, SHAPE, ALIGN, STRIDE, UNSUP, LAUNCH, VALUE = range(8)
 A = 0x7F0000000000          # fake 16-byte aligned device addresses; never dereferenced
+MAX_ROWS = 1 << 24          # row limit of the pre-attention and out-projection calls
+MAX_S = (2 ** 32 - 1) // 192    # cos/sin cache rows whose byte offsets fit 32 bits
+FLT_MIN = 2.0 ** -126
 
 
 def _declared():
@@ -31,6 +34,12 @@ def test_header_declares_the_entry_points():
               "dit_mlp_fp8", "dit_mlp_fp8_flags_elems", "dit_status_string", "dit_abi_version",
               "dit_mx_scale_bytes", "dit_mx_quant_fp4", "dit_out_proj_gated_mxfp4", "dit_pre_attn_mxfp4"):
         assert n in names
+
+
+def test_header_states_the_limits_the_library_checks():
+    src = open(HEADER).read()
+    assert re.search(r"#define DIT_MAX_ROWS 16777216\b", src)
+    assert re.search(r"#define DIT_MAX_ROPE_ROWS %d\b" % MAX_S, src)
 
 
 def test_library_exports_every_declared_symbol():
@@ -72,6 +81,8 @@ def pre(**kw):
     (dict(eps=0.0), VALUE), (dict(eps=-1e-5), VALUE), (dict(qk_eps=float("nan")), VALUE),
     (dict(eps=float("inf")), VALUE),
     (dict(M=0), OK),
+    (dict(M=MAX_ROWS + 1, S=MAX_ROWS + 1), SHAPE), (dict(M=0, S=MAX_S), OK), (dict(M=0, S=MAX_S + 1), SHAPE),
+    (dict(S=MAX_S + 1), SHAPE), (dict(S=1 << 40, pos=_p(10)), SHAPE),
 ])
 def test_pre_attn_contract_checks(kw, status):
     assert pre(**kw) == status
@@ -100,6 +111,9 @@ def pack8(**kw):
     (dict(out=None), NULL), (dict(x=None), NULL), (dict(out=ctypes.c_void_p(A + 8)), ALIGN),
     (dict(P=3), VALUE), (dict(S=15), SHAPE), (dict(M=-1), SHAPE),
     (dict(M=0), OK), (dict(M=0, P=4), OK),
+    # a descale must have a finite reciprocal: normal floats only
+    (dict(dq=1e-39), VALUE), (dict(dk=2.0 ** -130), VALUE), (dict(dv=FLT_MIN / 2), VALUE),
+    (dict(M=0, dq=FLT_MIN, dk=FLT_MIN, dv=FLT_MIN), OK), (dict(M=0, S=MAX_S + 1), SHAPE),
 ])
 def test_pre_attn_e4m3_contract_checks(kw, status):
     assert pre8(**kw) == status
@@ -109,6 +123,8 @@ def test_pre_attn_e4m3_contract_checks(kw, status):
     (dict(dq=0.0), VALUE), (dict(dv=-2.0), VALUE), (dict(dk=float("nan")), VALUE),
     (dict(out=None), NULL), (dict(ws=None), NULL), (dict(out=ctypes.c_void_p(A + 4)), ALIGN),
     (dict(P=5), VALUE), (dict(qk_eps=0.0), VALUE), (dict(M=0), OK),
+    (dict(dk=1e-40), VALUE), (dict(M=0, dq=FLT_MIN), OK), (dict(S=MAX_S + 1), SHAPE),
+    (dict(M=MAX_ROWS + 1, S=MAX_ROWS + 1), SHAPE),
 ])
 def test_qkv_rope_pack_e4m3_contract_checks(kw, status):
     assert pack8(**kw) == status
@@ -131,7 +147,7 @@ def outp(**kw):
     (dict(attn=ctypes.c_void_p(A + 4)), ALIGN), (dict(gi=ctypes.c_void_p(A + 2)), ALIGN),
     (dict(gate=_T(rows=0, stride=5376)), SHAPE), (dict(gate=_T(rows=9, stride=5380)), STRIDE),
     (dict(gate=_T(rows=1 << 31, stride=5376)), SHAPE),
-    (dict(M=-3), SHAPE), (dict(M=0), OK),
+    (dict(M=-3), SHAPE), (dict(M=0), OK), (dict(M=MAX_ROWS + 1), SHAPE),
 ])
 def test_out_proj_contract_checks(kw, status):
     assert outp(**kw) == status
@@ -200,7 +216,8 @@ def pre_mx(**kw):
     (dict(ws=ctypes.c_void_p(A + 4)), ALIGN), (dict(wss=ctypes.c_void_p(A + 8)), ALIGN),
     (dict(pos=ctypes.c_void_p(A + 4)), ALIGN),
     (dict(S=8), SHAPE), (dict(sh=_T(rows=3)), SHAPE), (dict(M=-1), SHAPE),
-    (dict(M=0), OK),
+    (dict(M=0), OK), (dict(S=MAX_S + 1), SHAPE), (dict(M=0, S=MAX_S), OK),
+    (dict(M=MAX_ROWS + 1, S=MAX_ROWS + 1), SHAPE),
 ])
 def test_pre_attn_mxfp4_contract_checks(kw, status):
     assert pre_mx(**kw) == status

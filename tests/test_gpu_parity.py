@@ -3,17 +3,23 @@ inputs.
 
 Bars (bf16 pre-attention, out-projection and fp8 MLP):
   - the AdaLN workspace within 1 bf16 ulp at each rounding point of a = bf16(shift + n*s1):
-    |a_gpu - a_ref| <= ulp(a_ref) + 2 ulp(a_ref - shift), at most 0.1% of elements differing
+    |a_gpu - a_ref| <= ulp(a_ref) + 2 ulp(a_ref - shift), at most 1e-4 of elements differing
     (n's own rounding may land on the other neighbour; shift can cancel n*s1);
-  - e4m3 codes within one code step, per-token activation scales within 1 bf16 ulp; the y
-    quantisation is checked at its own step (s_y = RN(amax|y_gpu|/448) exactly, y_q within one
-    code step of the library e4m3 conversion of y_gpu/s_y) and s_y within 2^-5 of the oracle's;
-  - every bf16 output: relative L2 error <= 2e-3 and |err| <= 1e-2 * (1 + |ref|) per element,
-    where for the RoPE-rotated q/k dims |ref| is the norm of the rotated (j, j+48) pair (the
-    rotation preserves it; an FP32-accumulated v may round to the other bf16 neighbour, and
-    the rotation can carry that ulp of a large u into a small output);
-  - the bf16 intermediate y (three roundings after a GEMM): relative L2 <= 2e-3 and
-    |err| <= 2^-5 |ref| + 1e-2;
+  - every bf16 output: relative L2 error <= 2e-3 and |err| <= 1e-2 * (1 + |ref|) per element.
+    A RoPE-rotated q/k element may instead meet the derived bound of
+    helpers.rope_elem_bound (an FP32-accumulated v may round to the other bf16 neighbour, and
+    the rotation can carry that ulp of a large u into a small output), but at most
+    4 + 4e-6 of the rotated elements may need it;
+  - e4m3 activation codes within one code step and per-token activation scales within 1 bf16
+    ulp of the oracle's;
+  - the bf16 intermediate y: the same 1e-2 * (1 + |ref|) bar, relaxed to 4 ulp(ref) for at most
+    1e-4 of its elements (y is three roundings past an FP32-accumulated GEMM);
+  - the y quantisation: s_y == RN(amax|y_gpu|/448) and y_q == e4m3(y_gpu/s_y) on the GPU's own
+    y; against the oracle, s_y bit-equal on every row whose amax|y| equals the oracle's and
+    within |amax_gpu - amax_ref| / 448 (plus one fp32 ulp) elsewhere, and y_q bit-equal
+    wherever y and s_y agree bit for bit, within |y_gpu - y_ref| plus both half code steps in
+    value elsewhere (near zero a code step of y/s_y is 2^-9 s_y, far below the GEMM's
+    accumulation error in y, so a code-step count is no bar there);
   - rows with a guarded index: workspace/codes exactly zero, outputs zero (pre-attention) or
     equal to the residual (out-projection, MLP).
 At the full workload sizes the oracle runs on a sampled row set (rows are independent, so
@@ -30,8 +36,8 @@ import torch
 
 import oracle
 import synth
-from tests.helpers import (bf16_tolerance_ok, bf16_val, ordered_e4m3, qkv_magnitude, torch_e4m3, ulp_bf16,
-                           ulp_diff_bf16, workspace_ok)
+from tests.helpers import (bf16_tolerance_ok, bf16_val, e4m3_half_step, e4m3_val, ordered_e4m3, qkv_check,
+                           torch_e4m3, ulp_bf16, ulp_diff_bf16, workspace_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,7 +119,27 @@ def e4m3_of_bf16(bits, descale):
     return out
 
 
-def check_pre(d, ws_gpu, out_gpu, rows=None):
+def row_cos_sin(d, rows):
+    """Each selected row's [96] cos/sin cache row: position clamp(pos[m], 0, S-1), or m."""
+    pos = d.get("rope_positions")
+    p = rows if pos is None else np.clip(pos[rows], 0, d["S"] - 1)
+    return d["rope_cos_sin"].reshape(-1, 96)[p]
+
+
+def max_relaxed_qk(n_rows):
+    """Ceiling on the rotated q/k elements allowed past the plain bar (4 + 4e-6 of them)."""
+    return 4 + int(4e-6 * n_rows * 56 * 2 * 96)
+
+
+def check_qkv(got, ref, cs_rows, label):
+    ok, rel, mx, n_rel, worst = qkv_check(got, ref, cs_rows, max_relaxed=max_relaxed_qk(got.shape[0]))
+    _say(f"  {label}: relL2={rel:.2e} max|err|={mx:.3e} past the plain bar={n_rel} "
+         f"(ceiling {max_relaxed_qk(got.shape[0])}, worst err/derived bound {worst:.2f})")
+    assert ok, (label, rel, mx, n_rel, worst)
+    return rel, mx, n_rel
+
+
+def check_pre(d, ws_gpu, out_gpu, rows=None, max_mismatch=1e-4):
     M = d["M"]
     rows = np.arange(M) if rows is None else rows
     ws_ref, out_ref = oracle.pre_attn(d, rows_sel=rows)
@@ -122,22 +148,14 @@ def check_pre(d, ws_gpu, out_gpu, rows=None):
     idx = d["adaln_index"][rows]
     bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
     shift = bf16_val(d["adaln_shift"].dense())[np.where(bad, 0, idx)]
-    wok, wmis, wratio = workspace_ok(ws[~bad], ws_ref[~bad], shift[~bad])
+    wok, wmis, wratio = workspace_ok(ws[~bad], ws_ref[~bad], shift[~bad], max_mismatch=max_mismatch)
     du = ulp_diff_bf16(ws, ws_ref)
+    _say(f"pre_attn M={M} rows={rows.size} ws max ulp={du.max()} ws mismatch={wmis:.2e} (err/bound {wratio:.2f}) "
+         f"guarded={bad.sum()} v mismatch={np.mean(out[:, :, 2] != out_ref[:, :, 2]):.2e}")
     assert wok, f"workspace: mismatch {wmis:.2e}, worst err/bound {wratio:.2f}"
     assert np.all(ws[bad] == 0), "guarded workspace rows must be +0"
     assert np.all(bf16_val(out[bad]) == 0.0), "guarded output rows must be zero"
-    mag = qkv_magnitude(out_ref)
-    ok, rel, mx = bf16_tolerance_ok(out, out_ref, mag=mag)
-    err = np.abs(bf16_val(out) - bf16_val(out_ref))
-    worst = np.unravel_index(np.argmax(err / (1.0 + mag)), err.shape)
-    _say(f"  worst element (row, head, kind, dim)={tuple(int(t) for t in worst)} ref={bf16_val(out_ref)[worst]:.5f} "
-         f"got={bf16_val(out)[worst]:.5f} pair-norm={mag[worst]:.4f} |ref|-bound violations="
-         f"{int(np.sum(err > 1e-2 * (1 + np.abs(bf16_val(out_ref)))))} v mismatch="
-         f"{np.mean(out[:, :, 2] != out_ref[:, :, 2]):.2e}")
-    _say(f"pre_attn M={M} rows={rows.size} ws max ulp={du.max()} ws mismatch={wmis:.2e} (err/bound {wratio:.2f}) "
-         f"out relL2={rel:.2e} max|err|={mx:.3e} guarded={bad.sum()}")
-    assert ok, (rel, mx)
+    check_qkv(out, out_ref, row_cos_sin(d, rows), f"pre_attn M={M} out")
     return ws, out
 
 
@@ -179,6 +197,39 @@ def run_mlp(d, alias=None):
     return out, ws
 
 
+def check_y_quant(y, y_q, y_s, ref, label):
+    """The y quantisation against the GPU's own y and against the oracle (see the module
+    docstring).  y, y_q, y_s: the GPU's y bits, codes and scales of the checked rows."""
+    yg, yr = bf16_val(y), bf16_val(ref["y"])
+    s_r = ref["y_scale"].astype(np.float32)
+    # on the GPU's own y: s_y = RN(amax/448) exactly, and every code is e4m3(y/s_y)
+    amax_g = np.max(np.abs(yg), axis=1)
+    amax_r = np.max(np.abs(yr), axis=1)
+    assert np.array_equal(y_s, (amax_g.astype(np.float32) / np.float32(448.0)).astype(np.float32)), \
+        "s_y != RN(amax|y|/448)"
+    nz = y_s > 0
+    q_lib = np.zeros_like(y_q)
+    q_lib[nz] = torch_e4m3((yg[nz].astype(np.float32) / y_s[nz, None]).astype(np.float32))
+    assert np.array_equal(y_q, q_lib), "y_q != e4m3(y/s_y) on the GPU's own y"
+    # against the oracle: s_y
+    same_amax = amax_g == amax_r
+    assert np.array_equal(y_s[same_amax], s_r[same_amax]), "s_y differs on a row whose amax|y| is the oracle's"
+    lip = np.abs(amax_g - amax_r) / 448.0 * (1 + 2.0 ** -22) + np.spacing(s_r).astype(np.float64)
+    assert np.all(np.abs(y_s.astype(np.float64) - s_r) <= lip), "s_y beyond |d amax| / 448"
+    s_ulps = np.abs(y_s.astype(np.float64) - s_r) / ulp_bf16(np.maximum(s_r, 2.0 ** -126))
+    # y_q: bit-equal where y and s_y are; in value space elsewhere
+    same = (y == ref["y"]) & (y_s == s_r)[:, None]
+    assert np.array_equal(y_q[same], ref["y_q"][same]), "y_q differs where y and s_y equal the oracle's"
+    vg = e4m3_val(y_q) * y_s[:, None].astype(np.float64)
+    vr = e4m3_val(ref["y_q"]) * s_r[:, None].astype(np.float64)
+    bound = np.abs(yg - yr) + e4m3_half_step(yg, y_s[:, None].astype(np.float64)) + \
+        e4m3_half_step(yr, s_r[:, None].astype(np.float64))
+    assert np.all(np.abs(vg - vr) <= bound * (1 + 1e-9)), "y_q beyond |dy| + half code steps"
+    step = np.abs(ordered_e4m3(y_q) - ordered_e4m3(ref["y_q"]))
+    _say(f"  {label} y_q: mismatch={np.mean(y_q != ref['y_q']):.2e} beyond one step={np.mean(step > 1):.2e} "
+         f"(max step {step.max()}); s_y: rows equal={np.mean(y_s == s_r):.3f}, max off {s_ulps.max():.2f} bf16 ulp")
+
+
 def check_mlp(d, out_gpu, ws, rows=None):
     M = d["M"]
     rows = np.arange(M) if rows is None else rows
@@ -191,24 +242,17 @@ def check_mlp(d, out_gpu, ws, rows=None):
     out = synth.bits(out_gpu)[rows]
     da = np.abs(ordered_e4m3(a_q) - ordered_e4m3(ref["a_q"]))
     assert da.max() <= 1, f"a_q off by {da.max()} code steps"
-    with np.errstate(invalid="ignore", divide="ignore"):
-        rs = np.where(ref["a_scale"] > 0, np.abs(a_s / ref["a_scale"] - 1), np.abs(a_s))
-        ry = np.where(ref["y_scale"] > 0, np.abs(y_s / ref["y_scale"] - 1), np.abs(y_s))
-    assert np.all(np.abs(a_s - ref["a_scale"]) <= ulp_bf16(ref["a_scale"])), f"a_scale rel err {rs.max()}"
-    assert ry.max() <= 2 ** -5, f"y_scale rel err {ry.max()}"
+    assert np.all(np.abs(a_s.astype(np.float64) - ref["a_scale"]) <= ulp_bf16(np.maximum(ref["a_scale"], 2.0 ** -126))), \
+        "a_scale beyond 1 bf16 ulp"
+    # y: 1e-2 (1 + |ref|), or 4 ulp(ref) for at most 1e-4 of the elements
     yg, yr = bf16_val(y), bf16_val(ref["y"])
+    erry = np.abs(yg - yr)
     rely = np.linalg.norm(yg - yr) / max(np.linalg.norm(yr), 1e-30)
-    mxy = float(np.max(np.abs(yg - yr)))
-    assert rely <= 2e-3 and np.all(np.abs(yg - yr) <= 2.0 ** -5 * np.abs(yr) + 1e-2), ("y", rely, mxy)
-    # the y quantisation step itself, on the GPU's own y
-    amax = np.max(np.abs(yg), axis=1).astype(np.float32)
-    assert np.array_equal(y_s, (amax / np.float32(448.0)).astype(np.float32)), "s_y != RN(amax|y|/448)"
-    nz = y_s > 0
-    q_lib = np.zeros_like(y_q)
-    q_lib[nz] = torch_e4m3((yg[nz].astype(np.float32) / y_s[nz, None]).astype(np.float32))
-    dql = np.abs(ordered_e4m3(y_q) - ordered_e4m3(q_lib))
-    assert dql.max() <= 1, f"y_q off by {dql.max()} code steps from e4m3(y/s_y)"
-    dq = np.abs(ordered_e4m3(y_q) - ordered_e4m3(ref["y_q"]))
+    plain = erry <= 1e-2 * (1.0 + np.abs(yr))
+    n_relaxed = int(np.sum(~plain))
+    assert rely <= 2e-3 and np.all(plain | (erry <= 4.0 * ulp_bf16(yr))), ("y", rely, float(erry.max()))
+    assert n_relaxed <= 4 + 1e-4 * erry.size, f"{n_relaxed} y elements past the plain bar"
+    check_y_quant(y, y_q, y_s, ref, f"mlp M={M}")
     idx = d["adaln_index"][rows]
     bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
     assert np.all(a_q[bad] == 0) and np.all(a_s[bad] == 0) and np.all(y_s[bad] == 0)
@@ -216,9 +260,10 @@ def check_mlp(d, out_gpu, ws, rows=None):
     assert np.array_equal(out[bad], res[bad]), "guarded rows must equal the residual"
     ok, rel, mx = bf16_tolerance_ok(out, ref["out"])
     _say(f"mlp M={M} rows={rows.size} a_q mismatch={np.mean(a_q != ref['a_q']):.2e} "
-         f"a_s exact={np.mean(a_s == ref['a_scale']):.3f} y relL2={rely:.2e} y max|err|={mxy:.3e} y_q vs own "
-         f"e4m3 mismatch={np.mean(y_q != q_lib):.2e} y_q vs oracle max step={dq.max()} out relL2={rel:.2e} max|err|={mx:.3e} guarded={bad.sum()}")
+         f"a_s exact={np.mean(a_s == ref['a_scale']):.3f} y relL2={rely:.2e} y max|err|={erry.max():.3e} "
+         f"y past plain bar={n_relaxed} out relL2={rel:.2e} max|err|={mx:.3e} guarded={bad.sum()}")
     assert ok, (rel, mx)
+    return ref
 
 
 # ---------------------------------------------------------------- pre-attention
@@ -306,11 +351,10 @@ def test_pre_attn_ulysses_degree8_against_oracle():
     _, outp = run_pre(d, workspace=ws, P=8)
     got = synth.bits(outp)
     ws_ref, out_ref = oracle.pre_attn(d)
-    ref = oracle.ulysses_pack(out_ref, 8)
-    mag = oracle.ulysses_pack(qkv_magnitude(out_ref), 8)
-    ok, rel, mx = bf16_tolerance_ok(got, ref, mag=mag)
-    _say(f"  P=8 relL2={rel:.2e} max|err|={mx:.3e}")
-    assert ok, (rel, mx)
+    assert got.shape == (8, 16, 7, 3, 128)
+    # destination p holds heads [7 p, 7 p + 7): put them back side by side and compare per row
+    unpacked = np.concatenate(list(got), axis=1)
+    check_qkv(unpacked, out_ref, row_cos_sin(d, np.arange(16)), "P=8")
     idx = d["adaln_index"]
     bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
     assert np.all(bf16_val(got[:, bad]) == 0.0), "guarded rows must be zero in every destination"
@@ -333,6 +377,61 @@ def test_pre_attn_identity_positions_ragged():
     ws = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
     _, out = run_pre(d, workspace=ws)
     check_pre(d, ws, out)
+
+
+def _eps_visible_inputs(M, seed, eps, qk_eps):
+    """Pre-attention inputs on which eps and qk_eps both move the result by far more than an ulp:
+    rows 0-63 of x scaled by 1e-2 (mean(x^2) ~ 1e-4 ~ eps), rows 64-67 constant
+    (2^-8, 2^-7, -2^-6, 2^-5: c^2 within a few decades of eps), the q and k weight rows of heads
+    0-3 scaled by 0.2 (mean(v^2) ~ 0.04 ~ qk_eps) and of heads 4-7 by 0.01 (mean(v^2) ~ 1e-4)."""
+    d = synth.pre_attn_inputs(M, seed=seed, rows=2, S=512, positions="random", n_bad_positions=4,
+                              bad_index_frac=0.02, weight=_shared_weight())
+    x = bf16_val(d["x"]).reshape(M, H)
+    x[:64] *= 0.01
+    for r, c in zip(range(64, 68), (2.0 ** -8, 2.0 ** -7, -(2.0 ** -6), 2.0 ** -5)):
+        x[r] = c
+    d["x"] = synth.to_bf16_bits(x.astype(np.float32))
+    W = _shared_weight().copy()
+    for kind in (0, 1):
+        for h, f in [(h, 0.2) for h in range(4)] + [(h, 0.01) for h in range(4, 8)]:
+            r0 = kind * 7168 + h * 128
+            W[r0:r0 + 128] = synth.to_bf16_bits((bf16_val(W[r0:r0 + 128]) * f).astype(np.float32))
+    d["qkv_weight"] = W
+    d["eps"], d["qk_eps"] = eps, qk_eps
+    return d
+
+
+def test_pre_attn_eps_and_qk_eps_are_both_visible():
+    """eps = 1e-4 and qk_eps = 0.05 on rows and heads whose mean squares are of the same order
+    (_eps_visible_inputs), against the oracle.  The oracle run with eps and qk_eps swapped (a
+    mistake planted on the CPU) must fail the same bars, so the test tells the two apart."""
+    M = 300
+    eps, qk_eps = 1e-4, 0.05
+    _say(f"pre_attn eps={eps} qk_eps={qk_eps}, M={M}")
+    d = _eps_visible_inputs(M, 710, eps, qk_eps)
+    ws = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    _, out = run_pre(d, workspace=ws)
+    check_pre(d, ws, out)
+    rows = np.r_[np.arange(0, 8), np.arange(64, 72)]
+    _, swapped = oracle.pre_attn(dict(d, eps=qk_eps, qk_eps=eps), rows_sel=rows)
+    got = synth.bits(out).reshape(M, 56, 3, 128)[rows]
+    assert not qkv_check(got, swapped, row_cos_sin(d, rows))[0], "the bar cannot tell eps from qk_eps"
+
+
+def test_pre_attn_qk_eps_none_means_eps():
+    """qk_eps=None through the binding: the q/k heads are normalised with eps (the page's
+    default), checked against the oracle with qk_eps = eps; the oracle with qk_eps = 0.05 must fail."""
+    M = 257
+    eps = 1e-4
+    _say(f"pre_attn qk_eps=None, eps={eps}, M={M}")
+    d = _eps_visible_inputs(M, 711, eps, None)
+    ws = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    _, out = run_pre(d, workspace=ws)
+    check_pre(d, ws, out)
+    rows = np.arange(0, 16)
+    _, other = oracle.pre_attn(dict(d, qk_eps=0.05), rows_sel=rows)
+    got = synth.bits(out).reshape(M, 56, 3, 128)[rows]
+    assert not qkv_check(got, other, row_cos_sin(d, rows))[0]
 
 
 def test_pre_attn_one_hot_pack_bit_exact():
@@ -595,10 +694,8 @@ def check_pre_mx(d, out, wsc, wss, wsb, rows):
     idx = d["adaln_index"][rows]
     bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
     assert np.all(bf16_val(got[bad]) == 0.0), "guarded output rows must be zero"
-    ok, rel, mx = bf16_tolerance_ok(got, ref, mag=qkv_magnitude(ref))
-    _say(f"pre_attn mxfp4 M={M} rows={rows.size} relL2={rel:.2e} max|err|={mx:.3e} "
-         f"mismatch={np.mean(got != ref):.2e} guarded={bad.sum()}")
-    assert ok, (rel, mx)
+    _say(f"pre_attn mxfp4 M={M} rows={rows.size} mismatch={np.mean(got != ref):.2e} guarded={bad.sum()}")
+    check_qkv(got, ref, row_cos_sin(d, rows), f"pre_attn mxfp4 M={M} out")
 
 
 def test_pre_attn_mxfp4_against_oracle():
@@ -675,6 +772,54 @@ def test_mlp_alias(alias):
     d = synth.mlp_inputs(M, seed=400, weights=_mlp_weights(), bad_index_frac=0.05)
     out, ws = run_mlp(d, alias=alias)
     check_mlp(d, out, ws)
+
+
+def test_mlp_subnormal_scales_and_visible_eps():
+    """Per-token scales below 2^-126, where 1 / s overflows fp32, and eps = 1e-4 on rows with
+    mean(x^2) ~ 1e-4.
+    - Table row 2 has scale -1 (bf16(1 + scale) = 0) and shift values ~1e-37, so a = shift
+      exactly, amax ~ 3e-37 and s_a = RN(amax / 448) is subnormal: the codes must equal the
+      oracle's e4m3(fl32(a / s_a)) and the scales must be bit-equal.
+    - A second run scales every FC1 column scale by 2^-63, so y ~ 1e-38 and s_y is subnormal
+      (the y quantisation's own division path), checked with check_mlp's bars."""
+    M = 40
+    _say(f"mlp subnormal scales, eps visible, M={M}")
+    d = synth.mlp_inputs(M, seed=420, rows=3, weights=_mlp_weights(), bad_index_frac=0.0)
+    sc, sh = d["adaln_scale"], d["adaln_shift"]
+    base = sc.base.copy()
+    base[sc.offset + 2 * sc.row_stride:sc.offset + 2 * sc.row_stride + H] = 0xBF80          # -1.0
+    tiny = synth.normal(421, "tiny_shift", (H,), 1e-37)
+    base[sh.offset + 2 * sh.row_stride:sh.offset + 2 * sh.row_stride + H] = synth.to_bf16_bits(tiny)
+    for t in ("adaln_scale", "adaln_shift", "gate"):
+        d[t] = synth.Table(base, d[t].offset, d[t].rows, d[t].row_stride)
+    d["adaln_index"][:8] = 2
+    x = bf16_val(d["x"]).reshape(M, H)
+    x[8:16] *= 0.01
+    d["x"] = synth.to_bf16_bits(x.astype(np.float32))
+    d["eps"] = 1e-4
+    out, ws = run_mlp(d)
+    ref = check_mlp(d, out, ws)
+    a_q = synth.bits(ws["workspace_a_q"])
+    a_s = ws["workspace_a_scale"].cpu().numpy()
+    assert np.all((a_s[:8] > 0) & (a_s[:8] < 2.0 ** -128)), "row scales meant to be subnormal"
+    assert np.array_equal(a_s[:8], ref["a_scale"][:8]) and np.array_equal(a_q[:8], ref["a_q"][:8])
+    # subnormal s_y
+    q1, s1, q2, s2 = _mlp_weights()
+    d2 = dict(d, fc1_scale=(s1 * np.float32(2.0 ** -63)).astype(np.float32))
+    out2, ws2 = run_mlp(d2)
+    ref2 = check_mlp(d2, out2, ws2)
+    y_s = ws2["workspace_y_scale"].cpu().numpy()
+    live = ref2["y_scale"] > 0
+    _say(f"  subnormal s_y: {live.sum()} rows with y != 0, {np.sum(live & (y_s < 2.0 ** -128))} of them below "
+         f"2^-128, max {y_s.max():.3e}")
+    assert live.sum() >= 16 and np.all(y_s[live] < 2.0 ** -126), "y scales meant to be subnormal"
+    assert np.any(y_s[live] < 2.0 ** -128), "some 1 / s_y meant to overflow"
+    # at this scale the bar's 1e-2 absolute term says nothing about y: hold its normal-range
+    # elements to 4 ulp of the oracle's
+    yg, yr = bf16_val(synth.bits(ws2["workspace_y"])), bf16_val(ref2["y"])
+    normal = np.abs(yr) >= 2.0 ** -125
+    assert normal.sum() > 1000
+    assert np.all(np.abs(yg - yr)[normal] <= 4.0 * ulp_bf16(yr[normal])), "y at 1e-38"
 
 
 def test_mlp_maximum_M():

@@ -457,6 +457,30 @@ def test_mlp_codes_match_library_conversion():
         assert np.array_equal(o["y_q"][m], torch_e4m3((y / s).astype(np.float32)))
 
 
+def test_mlp_subnormal_row_scale_codes_match_library_division():
+    # a table row with scale -1 (bf16(1 + scale) = 0) and shift ~1e-37: a = shift exactly, so
+    # s_a = RN(amax / 448) is a subnormal fp32 below 2^-128 (1 / s_a overflows); the codes must
+    # still be the library e4m3 of the IEEE fp32 quotients a / s_a
+    M = 2
+    d = _mlp_one_hot(M, seed=23)
+    sc, sh = d["adaln_scale"], d["adaln_shift"]
+    base = sc.base.copy()
+    base[sc.offset + sc.row_stride:sc.offset + sc.row_stride + H] = 0xBF80
+    tiny = synth.to_bf16_bits(synth.normal(24, "tiny", (H,), 1e-37))
+    base[sh.offset + sh.row_stride:sh.offset + sh.row_stride + H] = tiny
+    for t in ("adaln_scale", "adaln_shift", "gate"):
+        d[t] = synth.Table(base, d[t].offset, d[t].rows, d[t].row_stride)
+    d["adaln_index"][:] = [1, 0]
+    o = oracle.mlp(d)
+    a = bf16_val(tiny).astype(np.float32)
+    s = np.float32(np.max(np.abs(a)) / np.float32(448.0))
+    with np.errstate(over="ignore"):
+        assert 0 < s < 2.0 ** -128 and not np.isfinite(np.float32(1.0) / s)
+    assert np.float32(o["a_scale"][0]) == s
+    assert np.array_equal(o["a_q"][0], torch_e4m3((a / s).astype(np.float32)))
+    assert np.max(np.abs(e4m3_val(o["a_q"][0]))) == 448.0
+
+
 def test_mlp_fc2_gated_residual_closed_forms():
     M = 4
     d = _mlp_one_hot(M)
