@@ -15,11 +15,11 @@ import os
 
 import torch
 
-__all__ = ["dit_pre_attn_bf16", "dit_pre_attn_e4m3", "dit_norm_adaln_bf16", "dit_qkv_rope_pack_bf16",
+__all__ = ["dit_pre_attn_bf16", "dit_pre_attn_bf16_static_ws", "dit_pre_attn_e4m3", "dit_norm_adaln_bf16", "dit_qkv_rope_pack_bf16",
            "dit_qkv_rope_pack_e4m3", "dit_out_proj_gated_bf16", "dit_mlp_fp8", "dit_mlp_fp8_flags_elems",
            "dit_mx_scale_bytes", "dit_mx_quant_fp4", "dit_out_proj_gated_mxfp4", "dit_pre_attn_mxfp4",
            "DitError", "load_library", "LIB_PATH", "HIDDEN", "HEADS", "HEAD_DIM", "QKV_ROWS", "ATTN_WIDTH",
-           "INTER", "FC1_ROWS", "MLP_MAX_M"]
+           "INTER", "FC1_ROWS", "MLP_MAX_M", "STATIC_WS_MAX_ROWS"]
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libdit.so")
@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(PKG, "libdit.so")
 HIDDEN, HEADS, HEAD_DIM = 5376, 56, 128
 QKV_ROWS, ATTN_WIDTH, INTER, FC1_ROWS = 21504, 7168, 14336, 28672
 MLP_MAX_M = 149796
+STATIC_WS_MAX_ROWS = 4096      # rows of dit_pre_attn_bf16_static_ws's static workspace
 
 STATUS = {0: "DIT_OK", 1: "DIT_ERR_NULL", 2: "DIT_ERR_SHAPE", 3: "DIT_ERR_ALIGN", 4: "DIT_ERR_STRIDE",
           5: "DIT_ERR_UNSUPPORTED", 6: "DIT_ERR_LAUNCH", 7: "DIT_ERR_VALUE"}
@@ -67,6 +68,9 @@ def load_library(path: str = LIB_PATH):
     L.dit_pre_attn_bf16.restype = _i32
     L.dit_pre_attn_bf16.argtypes = [_p, _i64, _p, Table, Table, _p, _p, _p, _p, _p, _i64, _p, _i32, _f, _f, _p, _p,
                                     _p]
+    L.dit_pre_attn_bf16_static_ws.restype = _i32
+    L.dit_pre_attn_bf16_static_ws.argtypes = [_p, _i64, _p, Table, Table, _p, _p, _p, _p, _p, _i64, _p, _i32, _f, _f,
+                                              _p, _p]
     L.dit_norm_adaln_bf16.restype = _i32
     L.dit_norm_adaln_bf16.argtypes = [_p, _i64, _p, Table, Table, _p, _f, _p, _p]
     L.dit_qkv_rope_pack_bf16.restype = _i32
@@ -154,6 +158,18 @@ def dit_pre_attn_bf16(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, q
                      k_norm_weight, rope_cos_sin, ulysses_degree, out, eps, qk_eps, rope_positions, workspace, None)
 
 
+def dit_pre_attn_bf16_static_ws(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight,
+                                q_norm_weight, k_norm_weight, rope_cos_sin, *, ulysses_degree: int, out,
+                                eps: float = 1e-5, qk_eps: float | None = None, rope_positions=None):
+    """dit_pre_attn_bf16 with the workspace in the library's static per-GPU buffer (M <=
+    STATIC_WS_MAX_ROWS), for callers that cannot allocate; `out` must be given, and nothing is
+    allocated.  Calls that overlap in time on one GPU race on that buffer."""
+    if out is None:
+        raise ValueError("dit_pre_attn_bf16_static_ws allocates nothing: pass out")
+    return _pre_attn(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight,
+                     k_norm_weight, rope_cos_sin, ulysses_degree, out, eps, qk_eps, rope_positions, _STATIC, None)
+
+
 def dit_pre_attn_e4m3(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight,
                       k_norm_weight, rope_cos_sin, *, ulysses_degree: int, out, q_descale: float, k_descale: float,
                       v_descale: float, eps: float = 1e-5, qk_eps: float | None = None, rope_positions=None,
@@ -163,6 +179,9 @@ def dit_pre_attn_e4m3(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, q
     return _pre_attn(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight,
                      k_norm_weight, rope_cos_sin, ulysses_degree, out, eps, qk_eps, rope_positions, workspace,
                      (q_descale, k_descale, v_descale))
+
+
+_STATIC = object()     # workspace marker: the library's static buffer
 
 
 def _pre_attn(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weight, q_norm_weight, k_norm_weight,
@@ -184,12 +203,15 @@ def _pre_attn(x, x_norm_weight, adaln_scale, adaln_shift, adaln_index, qkv_weigh
         _need(rope_positions, "rope_positions", torch.int64, (M,))
     P = int(ulysses_degree)
     _need_out(out, descale is not None, P, M)
-    if workspace is None:
-        workspace = torch.empty((M, HIDDEN), dtype=torch.bfloat16, device=x.device)
-    _need(workspace, "workspace", torch.bfloat16, (M, HIDDEN))
     qk = eps if qk_eps is None else qk_eps
     args = (_ptr(x), M, _ptr(x_norm_weight), ts, th, _ptr(adaln_index), _ptr(qkv_weight), _ptr(q_norm_weight),
             _ptr(k_norm_weight), _ptr(rope_cos_sin), S, _ptr(rope_positions), P, float(eps), float(qk))
+    if workspace is _STATIC:
+        _check("dit_pre_attn_bf16_static_ws", L.dit_pre_attn_bf16_static_ws(*args, _ptr(out), _stream()))
+        return out
+    if workspace is None:
+        workspace = torch.empty((M, HIDDEN), dtype=torch.bfloat16, device=x.device)
+    _need(workspace, "workspace", torch.bfloat16, (M, HIDDEN))
     if descale is None:
         st = L.dit_pre_attn_bf16(*args, _ptr(workspace), _ptr(out), _stream())
         _check("dit_pre_attn_bf16", st)

@@ -124,6 +124,30 @@ dit_status dit_pre_attn_bf16(const void* x, int64_t M, const void* x_norm_weight
                              void* stream);
 
 /*
+ * For callers that cannot allocate: code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc.  dit_pre_attn_bf16 without the workspace argument: the workspace
+ * [M, 5376] bf16 lives in the library's own static device buffer of DIT_STATIC_WS_MAX_ROWS
+ * rows (42 MiB), one per GPU, held from the library's load on that GPU until the process
+ * ends.  Same kernels, arguments, checks and results as dit_pre_attn_bf16; the call allocates
+ * and frees nothing (the first call on a device looks up the buffer's device address with
+ * hipGetSymbolAddress, which allocates nothing either).
+ *   M      0 <= M <= DIT_STATIC_WS_MAX_ROWS, else DIT_ERR_SHAPE; 0 is a no-op
+ *   out    as in dit_pre_attn_bf16; the caller passes it (it is never allocated here)
+ * Every call on one GPU uses that GPU's one buffer, which keeps the last call's contents:
+ * calls that overlap in time on one GPU (on different streams, or from several threads) race
+ * and must be serialised, for example by issuing them on one stream.  Nothing in the buffer
+ * needs to start at zero.
+ */
+#define DIT_STATIC_WS_MAX_ROWS 4096
+dit_status dit_pre_attn_bf16_static_ws(const void* x, int64_t M, const void* x_norm_weight,
+                                       dit_bf16_table adaln_scale, dit_bf16_table adaln_shift,
+                                       const int64_t* adaln_index, const void* qkv_weight,
+                                       const void* q_norm_weight, const void* k_norm_weight,
+                                       const void* rope_cos_sin, int64_t S,
+                                       const int64_t* rope_positions, int ulysses_degree, float eps,
+                                       float qk_eps, void* out, void* stream);
+
+/*
  * The two launches of dit_pre_attn_bf16, callable one at a time (same kernels, same
  * arguments and checks).  dit_norm_adaln_bf16 writes the modulated activation a into
  * workspace [M, 5376] (launch 1: input RMSNorm + indexed AdaLN + guard);

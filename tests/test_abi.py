@@ -30,7 +30,7 @@ def _declared():
 
 def test_header_declares_the_entry_points():
     names = _declared()
-    for n in ("dit_pre_attn_bf16", "dit_pre_attn_e4m3", "dit_qkv_rope_pack_e4m3", "dit_out_proj_gated_bf16",
+    for n in ("dit_pre_attn_bf16", "dit_pre_attn_bf16_static_ws", "dit_pre_attn_e4m3", "dit_qkv_rope_pack_e4m3", "dit_out_proj_gated_bf16",
               "dit_mlp_fp8", "dit_mlp_fp8_flags_elems", "dit_status_string", "dit_abi_version",
               "dit_mx_scale_bytes", "dit_mx_quant_fp4", "dit_out_proj_gated_mxfp4", "dit_pre_attn_mxfp4"):
         assert n in names
@@ -86,6 +86,32 @@ def pre(**kw):
 ])
 def test_pre_attn_contract_checks(kw, status):
     assert pre(**kw) == status
+
+
+def pre_static(**kw):
+    a = dict(x=_p(1), M=16, xw=_p(2), sc=_T(), sh=_T(A + 0x200000), idx=_p(3), W=_p(4), qw=_p(5), kw=_p(6),
+             cs=_p(7), S=16, pos=None, P=1, eps=1e-5, qk_eps=1e-5, out=_p(9))
+    a.update(kw)
+    return dit.load_library().dit_pre_attn_bf16_static_ws(a["x"], a["M"], a["xw"], a["sc"], a["sh"], a["idx"],
+                                                            a["W"], a["qw"], a["kw"], a["cs"], a["S"], a["pos"],
+                                                            a["P"], a["eps"], a["qk_eps"], a["out"], None)
+
+
+# every check runs before the device is touched (these need no GPU): M beyond the static
+# workspace, and each argument the allocating form checks
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=4097, S=4097), SHAPE), (dict(M=-1), SHAPE), (dict(M=1 << 40), SHAPE), (dict(M=0), OK),
+    (dict(x=None), NULL), (dict(out=None), NULL), (dict(idx=None), NULL),
+    (dict(out=ctypes.c_void_p(A + 8)), ALIGN), (dict(sc=_T(rows=3)), SHAPE), (dict(S=15), SHAPE),
+    (dict(M=4096, S=4095), SHAPE), (dict(S=MAX_S + 1), SHAPE), (dict(P=3), VALUE), (dict(eps=0.0), VALUE),
+    (dict(M=0, S=1, pos=_p(10)), OK),
+])
+def test_pre_attn_static_ws_contract_checks(kw, status):
+    assert pre_static(**kw) == status
+
+
+def test_static_ws_limit_matches_the_header():
+    assert re.search(r"#define DIT_STATIC_WS_MAX_ROWS %d\b" % dit.STATIC_WS_MAX_ROWS, open(HEADER).read())
 
 
 def pre8(**kw):
