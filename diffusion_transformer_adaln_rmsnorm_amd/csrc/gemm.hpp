@@ -41,6 +41,10 @@ constexpr int kMainBytes = 4 * kOpBytes + 4 * kScaleSlot;   // two slots per ope
 constexpr int kEpiPitch = kBN * 2 + 16;         // bf16 epilogue tile, padded row pitch (bytes)
 constexpr int kEpiBytes = kBM * kEpiPitch;      // 132 KiB
 constexpr int kSmemBytes = kMainBytes > kEpiBytes ? kMainBytes : kEpiBytes;
+// bf16 and e4m3 operands: two A slots and a ring of three B slots, all of gfx950's 160 KiB
+constexpr int kBSlots3 = 3;
+constexpr int kMain3Bytes = (2 + kBSlots3) * kOpBytes;
+constexpr int kSmem3Bytes = kMain3Bytes > kEpiBytes ? kMain3Bytes : kEpiBytes;
 constexpr int kSlots = kRowB / 16;              // 16-byte chunks per row
 constexpr int kRowsPerPiece = 1024 / kRowB;     // rows filled by one 1 KiB wave load
 
@@ -482,15 +486,136 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     __syncthreads();
 }
 
+// ---------------------------------------------------------------------------------------
+// Ping-pong main loop with a ring of three B slots (bf16 and e4m3 operands).
+//
+// The same two groups, phases and barriers as mainloop_pp, but B stage s sits in slot s % 3
+// (A stage s still in slot s % 2).  The slot a wave refills with B of stage s+2 held stage
+// s-1, which both groups finished reading before the barrier that opens stage s's first
+// phase, so every wave may refill B as soon as its memory phase starts, before its own
+// fragment reads, and both groups move the same bytes: each wave of a group fills its 32 rows
+// of A (stage s+1) and 32 rows of B (stage s+2) at the start of its memory phase for stage s,
+// 8 KiB, 8 loads.  (With two B slots a B slot is free only after the second group's reads, so
+// one group had to move all of B after its reads, three quarters of the stage's fills in one
+// phase.)  Each wave waits only for its own loads before a barrier:
+//   G0, end of its compute phase for s:  vmcnt(4): A(s+1) and B(s+1) landed, B(s+2) may fly;
+//   G1, end of its memory phase for s:   vmcnt(8): B(s+1) landed (G0 reads it next phase);
+//   G1, end of its compute phase for s:  vmcnt(4): A(s+1) landed (its next memory phase).
+// G0's rows of A and B are read by G1 one phase after G0 has waited for them, and G1's rows
+// of B by G0 one phase after G1 has.  Loads past the last stage go through the zero-length
+// descriptor as in mainloop_pp.
+struct PP3Fill {
+    __amdgpu_buffer_rsrc_t ra, rb, rnull;
+    uint32_t va[kPPAPieces];  // A: row + chunk offset of piece j (per lane; bounds-checked)
+    uint32_t vb[kVPat];       // B: row-in-piece + chunk offset, by piece parity (per lane)
+    uint32_t sb[kPPAPieces];  // B: offset of piece j's first row (uniform)
+    uint32_t lds_rows;        // this wave's 32 rows within an A or B slot
+    __device__ __forceinline__ void a_rows(uint8_t* smem, int slot, int kt, bool live) const {
+        lds_u8* S = (lds_u8*)smem + slot * kOpBytes + lds_rows;
+        const __amdgpu_buffer_rsrc_t r = live ? ra : rnull;
+#pragma unroll
+        for (int j = 0; j < kPPAPieces; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + j * 1024, 16, (int)va[j], kt * kRowB, 0, 0);
+    }
+    __device__ __forceinline__ void b_rows(uint8_t* smem, int slot, int kt, bool live) const {
+        lds_u8* S = (lds_u8*)smem + (2 + slot) * kOpBytes + lds_rows;
+        const __amdgpu_buffer_rsrc_t r = live ? rb : rnull;
+#pragma unroll
+        for (int j = 0; j < kPPAPieces; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + j * 1024, 16, (int)vb[j % kVPat], (int)sb[j] + kt * kRowB,
+                                                     0, 0);
+    }
+};
+
+template <Mma kKind>
+__device__ __forceinline__ void mainloop_pp3(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
+                                             const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
+                                             int ktiles, uint8_t* smem, Acc& acc) {
+    static_assert(kWaves == 8 && kRowB == 128, "ping-pong layout");
+    static_assert(kKind != Mma::kMxFp4, "the MXFP4 scales keep the two-slot loop");
+    constexpr int kLoads = 2 * kPPAPieces;          // loads per wave and memory phase
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+    const bool g0 = wave < 4;
+    PP3Fill sf;
+    const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
+    sf.ra = make_rsrc(A + m0 * lda, (uint32_t)(arows * lda));
+    sf.rb = make_rsrc(B + nb0 * ldb, (uint32_t)((nb1 - nb0 + 128) * ldb));
+    sf.rnull = make_rsrc(B, 0u);
+#pragma unroll
+    for (int j = 0; j < kPPAPieces; ++j) {
+        const int row = 32 * wave + j * kRowsPerPiece + lane / kSlots;
+        sf.va[j] = (uint32_t)(row * lda) + (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
+        const int64_t r0 = 32 * wave + j * kRowsPerPiece;                // piece's first row (uniform)
+        sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
+        if (j < kVPat) {
+            const int brow = (int)r0 + lane / kSlots;
+            sf.vb[j] = (uint32_t)((lane / kSlots) * ldb) + (uint32_t)(((lane % kSlots) ^ swz(brow)) << 4);
+        }
+    }
+    sf.lds_rows = (uint32_t)(32 * wave * kRowB);
+    FragAddr fa;
+    fa.init();
+#pragma unroll
+    for (int i = 0; i < Acc::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < Acc::NB; ++j) acc.v[i][j] = 0.f;
+
+    PPFrags<kKind> fr;
+    // prologue: this wave's rows of A(0), B(0) and B(1); A(0) and B(0) must land before the
+    // first reads, B(1) before the end of this wave's first memory-phase barrier (G1) or its
+    // first compute-phase barrier (G0)
+    sf.a_rows(smem, 0, 0, true);
+    sf.b_rows(smem, 0, 0, true);
+    sf.b_rows(smem, 1, 1, ktiles > 1);
+    pp_barrier<kPPAPieces>();
+    if (!g0) pp_barrier<63>();       // G1 starts one phase behind
+    int sb_read = 0;                 // B slot of stage kt (kt % 3)
+    // Not unrolled or peeled (see mainloop_pp).
+#pragma nounroll
+    for (int kt = 0; kt < ktiles; ++kt) {
+        const int sa = kt & 1;
+        const int sb_fill = sb_read == 0 ? 2 : sb_read - 1;              // (kt + 2) % 3
+        // memory phase: refill first (A of stage kt+1, B of stage kt+2), then read stage kt
+        __builtin_amdgcn_sched_barrier(0);
+        sf.a_rows(smem, sa ^ 1, kt + 1, kt + 1 < ktiles);
+        sf.b_rows(smem, sb_fill, kt + 2, kt + 2 < ktiles);
+        __builtin_amdgcn_sched_barrier(0);
+        fr.read(Stage{smem + sa * kOpBytes, smem + (2 + sb_read) * kOpBytes, nullptr, nullptr}, fa);
+        __builtin_amdgcn_sched_barrier(0);
+        if (g0) {
+            pp_barrier<63>();
+        } else {
+            pp_barrier<kLoads>();        // B(kt+1) of this wave landed
+        }
+        // compute phase: MFMAs only
+        __builtin_amdgcn_sched_barrier(0);
+        fr.mma(acc);
+        __builtin_amdgcn_sched_barrier(0);
+        pp_barrier<kPPAPieces>();        // A(kt+1) (and for G0 B(kt+1)) landed; B(kt+2) may fly
+        sb_read = sb_read == 2 ? 0 : sb_read + 1;
+    }
+    if (g0) pp_barrier<63>();        // G1's last compute phase
+    __syncthreads();
+}
+
 // Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
 // [0,128) are global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a
 // plain tile; for MXFP4 both multiples of 128).  Ends with all loads drained and a barrier, so
-// the caller may reuse the LDS.
+// the caller may reuse the LDS.  smem must hold kSmemFor<kKind> bytes.
+template <Mma kKind>
+constexpr int kSmemFor = kKind == Mma::kMxFp4 ? kSmemBytes : kSmem3Bytes;
+
 template <Mma kKind>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
                                          int ktiles, uint8_t* smem, Acc& acc, const MxScales& mxs = MxScales{}) {
-    mainloop_pp<kKind>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs);
+    if constexpr (kKind == Mma::kMxFp4) {
+        mainloop_pp<kKind>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs);
+    } else {
+        (void)mxs;
+        mainloop_pp3<kKind>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc);
+    }
 }
 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS

@@ -20,6 +20,10 @@ hipError_t launch_norm_adaln_fp8q(const uint16_t* x, int64_t M, const uint16_t* 
 hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
                            const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos, float qk_eps,
                            int P, uint16_t* out, hipStream_t stream);
+// M <= 16: one workgroup per head of each kind, K split over its waves (weight streaming)
+hipError_t launch_qkv_small(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw, const uint16_t* kw,
+                            const uint16_t* cs, int64_t S, const int64_t* pos, float qk_eps, int P, uint16_t* out,
+                            hipStream_t stream);
 // the same with e4m3 output codes: out[...] = e4m3(bf16 result / descale of its kind)
 hipError_t launch_qkv_gemm_e4m3(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
                                 const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos,

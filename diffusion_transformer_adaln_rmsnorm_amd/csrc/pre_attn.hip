@@ -21,96 +21,11 @@
 #include "common.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
+#include "qk_epi.hpp"
 
 namespace dit {
 
 using namespace gemm;
-
-// Cross-lane moves inside a 16-lane DPP row (VALU, no LDS round trip).
-template <int kCtrl>
-__device__ __forceinline__ float dpp_f(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xF, 0xF, false));
-}
-// (for moves whose source lane always exists, e.g. row rotations)
-template <int kCtrl>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, kCtrl, 0xF, 0xF, true);
-}
-constexpr int kDppXor1 = 0xB1;         // quad_perm(1,0,3,2): lane i <- i ^ 1
-constexpr int kDppXor2 = 0x4E;         // quad_perm(2,3,0,1): lane i <- i ^ 2
-constexpr int kDppHalfMirror = 0x141;  // lane i <- 7 - i within each 8 lanes
-constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within each 16 lanes
-constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- (i + 8) mod 16
-
-// v_perm_b32 selectors on (src0, src1): low halves (src1.lo | src0.lo << 16) and high halves
-// (src1.hi | src0.hi << 16).
-constexpr uint32_t kPermLo = 0x05040100u;
-constexpr uint32_t kPermHi = 0x07060302u;
-// a.lo b.lo + a.hi b.hi (+ c) for two packed bf16 pairs (v_dot2_f32_bf16, fp32 result; the
-// bf16 products are exact)
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c = 0.0f) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-// Sum over the 16 lanes of a DPP row, left in every lane of it.
-__device__ __forceinline__ float row16_sum(float x) {
-    x += dpp_f<kDppXor1>(x);
-    x += dpp_f<kDppXor2>(x);
-    x += dpp_f<kDppHalfMirror>(x);    // pairs the two quads of each 8
-    x += dpp_f<kDppMirror>(x);        // pairs the two 8s of the row
-    return x;
-}
-
-// Q/K output of one (row, head) for the 16 lanes of a DPP row: vp holds this lane's 8 dims
-// (chunk q) of the head as bf16; nwlo / nwhi its 8 norm weights as bf16 pairs with the high /
-// low half zeroed; cv / sv the cos and sin of frequencies 8 (q mod 6) .. + 7 for the row's
-// position (q < 12).  All 16 lanes of the row must be active.
-__device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const u32x4& nwlo, const u32x4& nwhi, float qk_eps,
-                                              int q, const u32x4& cv, const u32x4& sv) {
-    // per-head RMSNorm in fp32 on the packed bf16 values: the squares and v w are exact
-    // bf16 products (v_dot2; a zero half picks one product), the sum of squares carries fp32
-    // rounding only, and u = bf16((v w) r2); two partial sums halve the dependent chain
-    const float s0 = dot2_bf16(vp[1], vp[1], dot2_bf16(vp[0], vp[0]));
-    const float s1 = dot2_bf16(vp[3], vp[3], dot2_bf16(vp[2], vp[2]));
-    const float ss = row16_sum(s0 + s1);   // the 16 lanes of a (row, head) are one DPP row
-    // v_rsq_f32 directly: its argument is at least qk_eps, a normal float, where the library
-    // rsqrtf adds only a denormal-range rescaling around the same instruction
-    const float r2 = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + qk_eps);
-    float u[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        u[2 * e] = dot2_bf16(vp[e], nwlo[e]) * r2;
-        u[2 * e + 1] = dot2_bf16(vp[e], nwhi[e]) * r2;
-    }
-    const u32x4 up = pack8(u);          // the bf16 u, packed
-    // RoPE partner chunk q + 6 (q < 6) or q - 6 (6 <= q < 12), 8 lanes away; its sign flipped
-    // for the first half, so both halves take o = u c + w s:
-    // o_j = u_j c - u_{j+48} s, o_{j+48} = u_{j+48} c + u_j s
-    const uint32_t sgn = q < 6 ? 0x80008000u : 0u;   // negates both bf16 halves of a word
-    u32x4 pv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = dpp_u<kDppRor8>(up[e]) ^ sgn;
-    if (q >= 12) return up;
-    // o = u c + w s per element as one v_dot2 of the bf16 pairs (u, w) and (c, s): the two
-    // products are exact in fp32 and their sum is rounded once, as the fma form u c + (w s) is
-    u32x4 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t uw0 = __builtin_amdgcn_perm(pv[e], up[e], kPermLo);   // (u_2e, w_2e)
-        const uint32_t uw1 = __builtin_amdgcn_perm(pv[e], up[e], kPermHi);   // (u_2e+1, w_2e+1)
-        const uint32_t cs0 = __builtin_amdgcn_perm(sv[e], cv[e], kPermLo);
-        const uint32_t cs1 = __builtin_amdgcn_perm(sv[e], cv[e], kPermHi);
-        r[e] = pack_bf2(dot2_bf16(uw0, cs0), dot2_bf16(uw1, cs1));
-    }
-    return r;
-}
-
-// 8-dim chunk of a head held by lane li of its DPP row (the partner chunk q +/- 6 sits at
-// lane li ^ 8): lanes 0-5 hold chunks 0-5, lanes 8-13 chunks 6-11, lanes 6, 7, 14, 15 the
-// pass-through chunks 12-15.
-__device__ __forceinline__ int chunk_of_lane(int li) {
-    return li < 6 ? li : (li < 8 ? 12 + (li - 6) : (li < 14 ? li - 2 : li));
-}
 
 // a / s rounded to nearest (div_by), except that quotients far beyond the largest e4m3 value
 // (which saturate either way) skip the correction, which an infinite first guess would turn
@@ -243,7 +158,7 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
                 const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
                 const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
                 int hpd, float dq, float dk, float dv, void* __restrict__ out, int mt, int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemFor<Mma::kBf16>];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
@@ -262,7 +177,7 @@ void k_qkv_gemm_mxfp4(const uint8_t* __restrict__ ws_codes, const uint8_t* __res
                       uint32_t w_sbytes, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
                       const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
                       int hpd, void* __restrict__ out, int mt, int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemFor<Mma::kMxFp4>];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
@@ -282,6 +197,8 @@ void k_qkv_gemm_mxfp4(const uint8_t* __restrict__ ws_codes, const uint8_t* __res
 hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
                            const uint16_t* kw, const uint16_t* cs, int64_t S, const int64_t* pos, float qk_eps,
                            int P, uint16_t* out, hipStream_t stream) {
+    // up to 16 rows the weight stream bounds the launch: spread it over one workgroup per head
+    if (M <= 16) return launch_qkv_small(ws, M, W, qw, kw, cs, S, pos, qk_eps, P, out, stream);
     const int mt = (int)((M + kBM - 1) / kBM);
     const int nt = kQkvRows / kBN;
     hipLaunchKernelGGL(k_qkv_gemm<false>, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs,
