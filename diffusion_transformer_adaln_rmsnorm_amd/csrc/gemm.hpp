@@ -344,6 +344,21 @@ struct PPFrags<Mma::kMxFp4> {
     }
 };
 
+// Keeps a compute phase's MFMAs between its two barriers.  The MFMA builtins touch no memory,
+// so passes that move pure operations may otherwise carry them across the s_barrier statements
+// (whose memory clobber binds only memory accesses): in one build all 64 MFMAs of a phase sank
+// past the barrier that ends it into the loop latch, so the two waves of a SIMD issued MFMAs at
+// the same time and the ping-pong was lost.  An empty volatile asm that reads and writes every
+// accumulator, placed after the opening barrier and after the MFMAs, orders them: volatile asm
+// statements keep their program order, and the MFMAs consume the first one's outputs and feed the
+// second one's inputs.
+__device__ __forceinline__ void pin_acc(Acc& acc) {
+#pragma unroll
+    for (int i = 0; i < Acc::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < Acc::NB; ++j) asm volatile("" : "+v"(acc.v[i][j]));
+}
+
 // Phase-ending barrier: wait for vmcnt(kVm) and lgkmcnt(0), then a bare s_barrier.  These
 // waits are all the hand-over needs, so younger fill loads stay in flight across it (the
 // __syncthreads() fence would drain them).  The asm's memory clobber keeps the compiler from
@@ -352,6 +367,15 @@ template <int kVm>
 __device__ __forceinline__ void pp_barrier() {
     static_assert(kVm >= 0 && kVm < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((kVm & 15) | ((kVm >> 4) << 14) | (7 << 4) | (0 << 8));
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Barrier after the accumulators are staged in LDS: waits for this wave's LDS writes only
+// (lgkmcnt(0)), not for its global loads.  The epilogues request their global operands (cos/sin
+// rows, residual chunks, row indices) before staging, to be in flight across the barrier;
+// __syncthreads() would drain them there (its fence waits for vmcnt(0) too).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));    // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
 }
 
@@ -474,7 +498,9 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         }
         // compute phase: MFMAs only
         __builtin_amdgcn_sched_barrier(0);
+        pin_acc(acc);
         fr.mma(acc);
+        pin_acc(acc);
         __builtin_amdgcn_sched_barrier(0);
         if (g0) {
             pp_barrier<0>();                 // G0: A (and B-scale) loads of stage kt+1 landed
@@ -590,7 +616,9 @@ __device__ __forceinline__ void mainloop_pp3(const uint8_t* __restrict__ A, int6
         }
         // compute phase: MFMAs only
         __builtin_amdgcn_sched_barrier(0);
+        pin_acc(acc);
         fr.mma(acc);
+        pin_acc(acc);
         __builtin_amdgcn_sched_barrier(0);
         pp_barrier<kPPAPieces>();        // A(kt+1) (and for G0 B(kt+1)) landed; B(kt+2) may fly
         sb_read = sb_read == 2 ? 0 : sb_read + 1;

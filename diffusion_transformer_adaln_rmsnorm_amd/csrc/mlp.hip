@@ -34,7 +34,7 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
     Acc acc;
     mainloop<Mma::kE4m3>(a_q, kHidden, m0, M, W1, kHidden, j0, kInter + j0, kHidden / kRowB, smem, acc);
     stage_tile_bf16(acc, smem, a_scale, m0, M, w1s + j0, w1s + kInter + j0);
-    __syncthreads();
+    lds_barrier();
 
     const int t = threadIdx.x;
     const int c8 = (t & 15) * 8;
@@ -118,7 +118,7 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
     GatedResidual<int64_t> gr;
     gr.load_index(idx, m0, M, gate_rows);
     stage_tile_bf16(acc, smem, y_scale, m0, M, w2s + n0, w2s + n0 + 128);
-    __syncthreads();
+    lds_barrier();
     gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);
 }
 

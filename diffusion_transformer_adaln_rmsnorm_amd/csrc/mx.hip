@@ -80,7 +80,7 @@ void k_out_proj_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __rest
     gr.load_index(gate_index, m0, M, gate_rows);
     gr.load_residual(m0, M, n0, residual);
     stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
-    __syncthreads();
+    lds_barrier();
     gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
 }
 

@@ -114,7 +114,7 @@ __device__ __forceinline__ void qkv_epilogue(Acc& acc, uint8_t* smem, int64_t m0
         cv[it] = buf_ld16(rcs, off);
         sv[it] = buf_ld16(rcs, off + (need_cs ? kNFreq * 2 : 0u));
     }
-    __syncthreads();
+    lds_barrier();
 
     u32x4 nwlo, nwhi;                   // the norm weights, one bf16 of each pair kept
 #pragma unroll

@@ -21,6 +21,7 @@ namespace dit {
 
 using gemm::buf_ld16;
 using gemm::buf_ld_i64;
+using gemm::lds_barrier;
 using gemm::make_rsrc;
 
 constexpr int kSmallM = 16;
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kSmThreads) void k_qkv_small(const uint16_t* __rest
         sv = buf_ld16(rcs, off + kNFreq * 2);
     }
     if (epi && kind < 2) nwv = ld16((kind == 0 ? qw : kw) + d0);
-    __syncthreads();
+    lds_barrier();
     if (!epi) return;
     float v[8];
 #pragma unroll
