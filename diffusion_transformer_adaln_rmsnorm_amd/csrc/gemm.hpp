@@ -16,11 +16,11 @@
 // A and B fragments take their k values from the same (lane group, byte) positions, so the
 // product is the same whatever order the instruction assigns to k inside a fragment.
 //
-// K is consumed in stages of 128 bytes per row (64 bf16 or 128 e4m3, one cache line).  Each
-// stage (A 256 rows + B 256 rows) is filled straight from global memory into LDS by
-// buffer_load_dwordx4 ... lds (no register staging, no LDS store instructions), two slots
-// per operand.  Rows of A past M read as zeros (buffer descriptor bound) and are never
-// stored.
+// K is consumed in stages of 128 bytes per row (64 bf16, 128 e4m3 or 256 E2M1, one cache
+// line).  Each stage (A 256 rows + B 256 rows) is filled straight from global memory into LDS
+// by buffer_load_dwordx4 ... lds (no register staging, no LDS store instructions), into two A
+// slots and a ring of three B slots.  Rows of A past M read as zeros (buffer descriptor bound)
+// and are never stored.
 #pragma once
 
 #include "common.hpp"
@@ -36,15 +36,11 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kWN = 4;                          // waves across n (two across m)
 constexpr int kWaveN = kBN / kWN;               // wave tile: 128 rows x 64 columns
 constexpr int kOpBytes = 256 * kRowB;           // one operand of one stage (an LDS slot)
-constexpr int kScaleSlot = 2048;               // MXFP4 scales of one operand of one stage
-constexpr int kMainBytes = 4 * kOpBytes + 4 * kScaleSlot;   // two slots per operand and per scale set
 constexpr int kEpiPitch = kBN * 2 + 16;         // bf16 epilogue tile, padded row pitch (bytes)
 constexpr int kEpiBytes = kBM * kEpiPitch;      // 132 KiB
+// main loop: two A slots and a ring of three B slots, all of gfx950's 160 KiB of LDS
+constexpr int kMainBytes = 5 * kOpBytes;
 constexpr int kSmemBytes = kMainBytes > kEpiBytes ? kMainBytes : kEpiBytes;
-// bf16 and e4m3 operands: two A slots and a ring of three B slots, all of gfx950's 160 KiB
-constexpr int kBSlots3 = 3;
-constexpr int kMain3Bytes = (2 + kBSlots3) * kOpBytes;
-constexpr int kSmem3Bytes = kMain3Bytes > kEpiBytes ? kMain3Bytes : kEpiBytes;
 constexpr int kSlots = kRowB / 16;              // 16-byte chunks per row
 constexpr int kRowsPerPiece = 1024 / kRowB;     // rows filled by one 1 KiB wave load
 
@@ -117,8 +113,6 @@ constexpr int kVPat = 2;
 struct Stage {
     const uint8_t* a;
     const uint8_t* b;
-    const uint8_t* sa;     // MXFP4 scale slots (unused otherwise)
-    const uint8_t* sb;
 };
 
 // Accumulators of one wave: 8 x 4 blocks of 16 x 16.  Lane l, register r of a block holds
@@ -140,15 +134,11 @@ struct Acc {
 constexpr int kBlk = 16 * kRowB;                // bytes between 16-row blocks
 struct FragAddr {
     uint32_t a[2], b[2];
-    uint32_t sa, sb;       // MXFP4: this lane's scale bytes in an A / B scale slot
     __device__ __forceinline__ void init() {
         const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
         const int wm = wave / kWN, wn = wave % kWN;
         const int r = lane % 16, g = lane / 16;
         const int sw = swz(r);
-        // A: the 1 KiB of the wave's 128 rows; B: the wave's 64 rows are half of a 128-row group
-        sa = (uint32_t)(wm * 1024 + lane * 16);
-        sb = (uint32_t)((wn / 2) * 1024 + lane * 16 + (wn % 2) * 8);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int c = 4 * q + g;
@@ -168,81 +158,6 @@ __device__ __forceinline__ i32x8 lds_i32x8(const uint8_t* smem, uint32_t off0, u
     const u32x4 lo = lds_ld16(smem, off0), up = lds_ld16(smem, off1);
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
 }
-
-// ---------------------------------------------------------------------------------------
-// Ping-pong main loop (8 waves, 128-byte stage rows, two slots per operand).
-//
-// Group G0 = waves 0-3 (tile rows 0-127) and group G1 = waves 4-7 (rows 128-255); waves w
-// and w + 4 share a SIMD.  Each wave alternates a memory phase (read every fragment of one
-// stage from LDS into registers) and a compute phase (that stage's MFMAs, from registers
-// only).  G1 runs one phase behind G0, so on every SIMD one wave issues MFMAs back to back
-// while the other waits on LDS; a workgroup barrier ends every phase.  G1 enters one extra
-// barrier before its first phase and G0 one after its last, so both groups pass the same
-// number of barriers.
-//
-// Phase 2s: G0 memory(s), G1 compute(s-1).  Phase 2s+1: G0 compute(s), G1 memory(s).
-// Stage s sits in slot s % 2.  All fill loads are issued in memory phases (a compute phase
-// is MFMAs only: a wave issues in order, so a fill load that waits for the memory pipeline
-// would hold back the MFMAs behind it), and every wave refills only rows whose readers are
-// done:
-//   A rows 0-127 are read by G0 alone: at the start of its memory phase for stage s, G0 wave
-//     w refills rows 32w.. of the other slot (stage s-1, read in its previous memory phase)
-//     with stage s+1;
-//   A rows 128-255 likewise by G1, at the start of its memory phase for stage s;
-//   B rows 64c.. are read by waves c and 4+c only: G1 wave 4+c refills them in its slot of
-//     stage s with stage s+2 at the end of its memory phase for s, once its own reads have
-//     landed (wave c read them a phase earlier).
-// Each group waits for its A rows of stage s+1 before the barrier that ends its compute phase
-// for s, and G1 for the B rows of stage s+1 before the barrier that ends its memory phase for
-// s; those are the last barriers before the first reads.  Loads for stages past the end go
-// through a zero-length descriptor (no memory read, zeros into a slot with no reader left),
-// so every phase issues the same loads and the vmcnt limits hold throughout.
-constexpr int kPPAPieces = 32 / kRowsPerPiece;      // A: 32 rows per wave
-constexpr int kPPBPieces = 64 / kRowsPerPiece;      // B: 64 rows per G1 wave
-
-struct PPFill {
-    __amdgpu_buffer_rsrc_t ra, rb;
-    __amdgpu_buffer_rsrc_t rnull;   // zero records: every load through it is out of range
-    uint32_t va[kPPAPieces];  // A: row + chunk offset of piece j (per lane; bounds-checked)
-    uint32_t vb[kVPat];       // B: row-in-piece + chunk offset, by piece parity (per lane)
-    uint32_t sb[kPPBPieces];  // B: offset of piece j's first row (uniform)
-    uint32_t lds_a, lds_b;    // this wave's rows within an A slot / a B slot
-    // MXFP4 scales: a wave moves 256-byte quarters (4 bytes per lane) of 1 KiB scale blocks
-    __amdgpu_buffer_rsrc_t rsa, rsb;   // A: the wave's 128-row group; B: from the tile's first
-    uint32_t vs;              // per lane: its 4 bytes of the wave's quarter of a stage's 1 KiB
-    uint32_t vsb1;            // the same in the tile's second B group (relative to rsb)
-    uint32_t lds_sa;          // the quarter's offset within an A scale slot
-    uint32_t lds_q;           // the quarter's offset within a 1 KiB group (uniform)
-    // Stage kt of this wave's rows into `slot`.  A load past the last stage (live false) goes
-    // through rnull: it reads no memory and writes zeros into a slot that has no reader left,
-    // but still counts in vmcnt, so every phase issues the same number of loads.
-    __device__ __forceinline__ void a_rows(uint8_t* smem, int slot, int kt, bool live) const {
-        lds_u8* S = (lds_u8*)smem + slot * kOpBytes + lds_a;
-        const __amdgpu_buffer_rsrc_t r = live ? ra : rnull;
-#pragma unroll
-        for (int j = 0; j < kPPAPieces; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + j * 1024, 16, (int)va[j], kt * kRowB, 0, 0);
-    }
-    __device__ __forceinline__ void b_rows(uint8_t* smem, int slot, int kt, bool live) const {
-        lds_u8* S = (lds_u8*)smem + 2 * kOpBytes + slot * kOpBytes + lds_b;
-        const __amdgpu_buffer_rsrc_t r = live ? rb : rnull;
-#pragma unroll
-        for (int j = 0; j < kPPBPieces; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + j * 1024, 16, (int)vb[j % kVPat], (int)sb[j] + kt * kRowB,
-                                                     0, 0);
-    }
-    __device__ __forceinline__ void a_scales(uint8_t* smem, int slot, int kt, bool live) const {
-        lds_u8* S = (lds_u8*)smem + 4 * kOpBytes + slot * kScaleSlot + lds_sa;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsa : rnull, S, 4, (int)(vs + kt * 1024), 0, 0, 0);
-    }
-    // both B groups (G0 moves all B scales: every wave reads the whole of a group)
-    __device__ __forceinline__ void b_scales(uint8_t* smem, int slot, int kt, bool live) const {
-        lds_u8* S = (lds_u8*)smem + 4 * kOpBytes + (2 + slot) * kScaleSlot + lds_q;
-        const __amdgpu_buffer_rsrc_t r = live ? rsb : rnull;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S, 4, (int)(vs + kt * 1024), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + 1024, 4, (int)(vsb1 + kt * 1024), 0, 0, 0);
-    }
-};
 
 // v_mfma_scale_f32_16x16x128_f8f6f4 on E2M1 operands (4 registers each, format 4 for both),
 // scale_a / scale_b the E8M0 bytes OA / OB of the lanes' scale words.  The four-register form
@@ -267,8 +182,8 @@ __device__ __forceinline__ f32x4 mfma_mxfp4(const i32x4& a, const i32x4& b, cons
 #undef DIT_MX_CASE
 }
 
-// Every fragment of one stage in registers (24 16-byte reads, 96 registers; MXFP4 adds 24
-// bytes of scales).
+// Every fragment of one stage in registers (24 16-byte reads, 96 registers; MXFP4 adds its 24
+// bytes of scales, which the main loop loads from global memory).
 template <Mma kKind>
 struct PPFrags;
 template <>
@@ -319,7 +234,7 @@ template <>
 struct PPFrags<Mma::kMxFp4> {
     static constexpr int MB = Acc::MB, NB = Acc::NB;
     i32x4 a[2][MB], b[2][NB];
-    u32x4 sa;
+    u32x4 sa;      // this lane's E8M0 scale records of the stage (loaded by the main loop)
     u32x2 sb;
     __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
 #pragma unroll
@@ -329,8 +244,6 @@ struct PPFrags<Mma::kMxFp4> {
 #pragma unroll
             for (int j = 0; j < NB; ++j) b[ks][j] = __builtin_bit_cast(i32x4, lds_ld16(st.b, fa.b[ks] + j * kBlk));
         }
-        sa = lds_ld16(st.sa, fa.sa);
-        sb = *reinterpret_cast<const u32x2*>(st.sb + fa.sb);
     }
     __device__ __forceinline__ void mma(Acc& acc) const {
 #pragma unroll
@@ -388,154 +301,57 @@ struct MxScales {
     uint32_t b_bytes = 0;
 };
 
-template <Mma kKind>
-__device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
-                                            const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                            int ktiles, uint8_t* smem, Acc& acc, const MxScales& mxs) {
-    static_assert(kWaves == 8 && kRowB == 128, "ping-pong layout");
-    static_assert(kMainBytes <= kSmemBytes, "two slots per operand and per scale set");
-    constexpr bool kMx = kKind == Mma::kMxFp4;
-    // loads per wave and memory phase: A rows (+ A scales), and G1's B rows
-    constexpr int kAF = kPPAPieces + (kMx ? 1 : 0);
-    constexpr int kBF = kPPBPieces;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
-    const bool g0 = wave < 4;
-    const int c = wave & 3;                          // B rows 64c.. (G1 fills them)
-    PPFill sf;
-    const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
-    sf.ra = make_rsrc(A + m0 * lda, (uint32_t)(arows * lda));
-    sf.rb = make_rsrc(B + nb0 * ldb, (uint32_t)((nb1 - nb0 + 128) * ldb));
-    sf.rnull = make_rsrc(B, 0u);
-#pragma unroll
-    for (int j = 0; j < kPPAPieces; ++j) {
-        const int row = 32 * wave + j * kRowsPerPiece + lane / kSlots;
-        sf.va[j] = (uint32_t)(row * lda) + (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
-    }
-#pragma unroll
-    for (int j = 0; j < kPPBPieces; ++j) {
-        const int64_t r0 = 64 * c + j * kRowsPerPiece;               // piece's first row (uniform)
-        sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
-        if (j < kVPat) {
-            const int row = (int)r0 + lane / kSlots;
-            sf.vb[j] = (uint32_t)((lane / kSlots) * ldb) + (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
-        }
-    }
-    sf.lds_a = (uint32_t)(32 * wave * kRowB);
-    sf.lds_b = (uint32_t)(64 * c * kRowB);
-    if constexpr (kMx) {
-        // A scales: each group moves those of its own rows (read only by its waves), wave c one
-        // quarter of each 1 KiB; a group past the end of the array (the last m tile's second
-        // half) reads zeros.  B scales: G0 moves both groups (a B group is read by waves of both
-        // groups, so its refill waits until both have read it, as G0's memory phase does).
-        const int64_t group_bytes = (int64_t)ktiles * 1024;
-        const int64_t ga = m0 / 128 + (g0 ? 0 : 1);
-        const int64_t a_rest = (int64_t)mxs.a_bytes - ga * group_bytes;
-        sf.rsa = make_rsrc(mxs.a + (a_rest > 0 ? ga * group_bytes : 0), (uint32_t)(a_rest > 0 ? a_rest : 0));
-        const int64_t gb0 = nb0 / 128, gb1 = nb1 / 128;
-        sf.rsb = make_rsrc(mxs.b + gb0 * group_bytes, (uint32_t)((int64_t)mxs.b_bytes - gb0 * group_bytes));
-        sf.vs = (uint32_t)(c * 256 + lane * 4);
-        sf.vsb1 = sf.vs + (uint32_t)((gb1 - gb0) * group_bytes);
-        sf.lds_q = (uint32_t)(c * 256);
-        sf.lds_sa = (g0 ? 0u : 1024u) + sf.lds_q;
-    }
-    FragAddr fa;
-    fa.init();
-#pragma unroll
-    for (int i = 0; i < Acc::MB; ++i)
-#pragma unroll
-        for (int j = 0; j < Acc::NB; ++j) acc.v[i][j] = 0.f;
-
-    auto slot = [&](int kt) -> Stage {
-        const int s = kt & 1;
-        return Stage{smem + s * kOpBytes, smem + (2 + s) * kOpBytes, smem + 4 * kOpBytes + s * kScaleSlot,
-                     smem + 4 * kOpBytes + (2 + s) * kScaleSlot};
-    };
-    PPFrags<kKind> fr;
-
-    // prologue: A of stage 0 (each wave its rows, with their MXFP4 scales), B of stages 0 and 1
-    // (G1), the B scales of stage 0 (G0; those of stage s+1 follow in G0's memory phase s).
-    // Only stage 0 must have landed here; B of stage 1 is first read in phase 2, after G1's
-    // memory-phase barrier (whose vmcnt limit counts only younger loads).
-    sf.a_rows(smem, 0, 0, true);
-    if constexpr (kMx) sf.a_scales(smem, 0, 0, true);
-    if (!g0) {
-        sf.b_rows(smem, 0, 0, true);
-        sf.b_rows(smem, 1, 1, ktiles > 1);
-        pp_barrier<kBF>();
-        pp_barrier<63>();            // G1 starts one phase behind
-    } else {
-        if constexpr (kMx) sf.b_scales(smem, 0, 0, true);
-        pp_barrier<0>();
-    }
-    // Not unrolled or peeled: in a peeled copy the scheduler reorders the MFMAs of the two
-    // k-steps and the register allocator then spills accumulators to scratch.
-#pragma nounroll
-    for (int kt = 0; kt < ktiles; ++kt) {
-        const int s = kt & 1;
-        // memory phase.  First this wave's A rows of stage kt+1 into the other slot: its
-        // group read them (stage kt-1) in its last memory phase.  MXFP4: their scales, and
-        // G0 the B scales of stage kt+1 (stage kt-1 in that slot was read by G1 in the last
-        // phase).
-        __builtin_amdgcn_sched_barrier(0);
-        sf.a_rows(smem, s ^ 1, kt + 1, kt + 1 < ktiles);
-        if constexpr (kMx) {
-            sf.a_scales(smem, s ^ 1, kt + 1, kt + 1 < ktiles);
-            if (g0) sf.b_scales(smem, s ^ 1, kt + 1, kt + 1 < ktiles);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        fr.read(slot(kt), fa);
-        __builtin_amdgcn_sched_barrier(0);
-        if (g0) {
-            pp_barrier<63>();
-        } else {
-            // B rows 64c.. of this slot, stage kt+2: the partner G0 wave read them in the
-            // last phase, this wave's reads land here
-            __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));    // lgkmcnt(0)
-            sf.b_rows(smem, s, kt + 2, kt + 2 < ktiles);
-            // landed: B of stage kt+1 (issued before the A and B loads of this phase)
-            pp_barrier<kAF + kBF>();
-        }
-        // compute phase: MFMAs only
-        __builtin_amdgcn_sched_barrier(0);
-        pin_acc(acc);
-        fr.mma(acc);
-        pin_acc(acc);
-        __builtin_amdgcn_sched_barrier(0);
-        if (g0) {
-            pp_barrier<0>();                 // G0: A (and B-scale) loads of stage kt+1 landed
-        } else {
-            pp_barrier<kBF>();               // G1: A loads of stage kt+1 landed (B of kt+2 may fly)
-        }
-    }
-    if (g0) pp_barrier<63>();        // G1's last compute phase
-    __syncthreads();
-}
-
 // ---------------------------------------------------------------------------------------
-// Ping-pong main loop with a ring of three B slots (bf16 and e4m3 operands).
+// Ping-pong main loop (8 waves, 128-byte stage rows; two A slots and a ring of three B slots).
 //
-// The same two groups, phases and barriers as mainloop_pp, but B stage s sits in slot s % 3
-// (A stage s still in slot s % 2).  The slot a wave refills with B of stage s+2 held stage
-// s-1, which both groups finished reading before the barrier that opens stage s's first
-// phase, so every wave may refill B as soon as its memory phase starts, before its own
-// fragment reads, and both groups move the same bytes: each wave of a group fills its 32 rows
-// of A (stage s+1) and 32 rows of B (stage s+2) at the start of its memory phase for stage s,
-// 8 KiB, 8 loads.  (With two B slots a B slot is free only after the second group's reads, so
-// one group had to move all of B after its reads, three quarters of the stage's fills in one
-// phase.)  Each wave waits only for its own loads before a barrier:
-//   G0, end of its compute phase for s:  vmcnt(4): A(s+1) and B(s+1) landed, B(s+2) may fly;
-//   G1, end of its memory phase for s:   vmcnt(8): B(s+1) landed (G0 reads it next phase);
-//   G1, end of its compute phase for s:  vmcnt(4): A(s+1) landed (its next memory phase).
+// Group G0 = waves 0-3 (tile rows 0-127) and group G1 = waves 4-7 (rows 128-255); waves w
+// and w + 4 share a SIMD.  Each wave alternates a memory phase (refill, then read every
+// fragment of one stage from LDS into registers) and a compute phase (that stage's MFMAs, from
+// registers only).  G1 runs one phase behind G0, so on every SIMD one wave issues MFMAs back
+// to back while the other works on LDS; a workgroup barrier ends every phase.  G1 enters one
+// extra barrier before its first phase and G0 one after its last, so both groups pass the
+// same number of barriers.
+//
+// Phase 2s: G0 memory(s), G1 compute(s-1).  Phase 2s+1: G0 compute(s), G1 memory(s).
+// A stage s sits in A slot s % 2 and B slot s % 3.  The B slot a wave refills with stage s+2
+// held stage s-1, which both groups finished reading before the barrier that opens stage s's
+// first phase, so every wave refills as soon as its memory phase starts, before its own
+// fragment reads, and both groups move the same bytes: each wave fills its 32 rows of A (stage
+// s+1; its group alone reads them, and read stage s-1 from that slot a phase earlier) and its
+// 32 rows of B (stage s+2), 8 KiB in 8 loads.  (With two B slots a B slot is free only after
+// the second group's reads, so one group moved three quarters of the stage's fills after its
+// reads.)  All fills are issued in memory phases: a wave issues in order, so a load that waits
+// for the memory pipeline would hold back the MFMAs behind it.  Loads for stages past the end
+// go through a zero-length descriptor (no memory read, zeros into a slot with no reader left),
+// so every phase issues the same loads and the vmcnt limits hold throughout.
+//
+// MXFP4: the E8M0 scales of a stage are not staged in LDS (the five slots fill it): in the MX
+// scale layout each wave's scales for a stage are one contiguous 1 KiB record of its group, 16
+// bytes per lane for A and 8 for B, which it loads straight into the registers the MFMAs take
+// them from, right after the compute phase that used the previous ones.
+//
+// Each wave waits only for its own loads before a barrier (per wave and stage: 8 fills, and
+// for MXFP4 2 scale loads after the MFMAs):
+//   G0, end of its compute phase for s:  A(s+1) and B(s+1) landed, B(s+2) (and the scales of
+//                                        s+1) may fly;
+//   G1, end of its memory phase for s:   B(s+1) landed (G0 reads it next phase); MXFP4: the
+//                                        scales of s landed;
+//   G0, end of its memory phase for s:   MXFP4: the scales of s landed;
+//   G1, end of its compute phase for s:  A(s+1) landed (its next memory phase).
 // G0's rows of A and B are read by G1 one phase after G0 has waited for them, and G1's rows
-// of B by G0 one phase after G1 has.  Loads past the last stage go through the zero-length
-// descriptor as in mainloop_pp.
-struct PP3Fill {
+// of B by G0 one phase after G1 has.
+constexpr int kPPAPieces = 32 / kRowsPerPiece;      // rows per wave and operand: 4 loads of 1 KiB
+
+struct PPFill {
     __amdgpu_buffer_rsrc_t ra, rb, rnull;
     uint32_t va[kPPAPieces];  // A: row + chunk offset of piece j (per lane; bounds-checked)
     uint32_t vb[kVPat];       // B: row-in-piece + chunk offset, by piece parity (per lane)
     uint32_t sb[kPPAPieces];  // B: offset of piece j's first row (uniform)
     uint32_t lds_rows;        // this wave's 32 rows within an A or B slot
+    // MXFP4: this wave's scale records (A: its group's rows; B: the 128-row group holding its
+    // columns), and this lane's bytes in them
+    __amdgpu_buffer_rsrc_t rsa, rsb;
+    uint32_t vsa, vsb;
     __device__ __forceinline__ void a_rows(uint8_t* smem, int slot, int kt, bool live) const {
         lds_u8* S = (lds_u8*)smem + slot * kOpBytes + lds_rows;
         const __amdgpu_buffer_rsrc_t r = live ? ra : rnull;
@@ -551,19 +367,26 @@ struct PP3Fill {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, S + j * 1024, 16, (int)vb[j % kVPat], (int)sb[j] + kt * kRowB,
                                                      0, 0);
     }
+    // MXFP4 scales of stage kt into the fragment registers (through rnull past the last stage)
+    __device__ __forceinline__ void scales(u32x4& sa, u32x2& sbv, int kt, bool live) const {
+        sa = __builtin_amdgcn_raw_buffer_load_b128(live ? rsa : rnull, (int)(vsa + kt * 1024), 0, 0);
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(live ? rsb : rnull, (int)(vsb + kt * 1024), 0, 0);
+        sbv = u32x2{(uint32_t)v[0], (uint32_t)v[1]};
+    }
 };
 
 template <Mma kKind>
-__device__ __forceinline__ void mainloop_pp3(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
-                                             const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                             int ktiles, uint8_t* smem, Acc& acc) {
+__device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
+                                            const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
+                                            int ktiles, uint8_t* smem, Acc& acc, const MxScales& mxs) {
     static_assert(kWaves == 8 && kRowB == 128, "ping-pong layout");
-    static_assert(kKind != Mma::kMxFp4, "the MXFP4 scales keep the two-slot loop");
-    constexpr int kLoads = 2 * kPPAPieces;          // loads per wave and memory phase
+    constexpr bool kMx = kKind == Mma::kMxFp4;
+    constexpr int kFills = 2 * kPPAPieces;          // fill loads per wave and memory phase
+    constexpr int kScl = kMx ? 2 : 0;               // scale loads per wave, after its MFMAs
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
     const bool g0 = wave < 4;
-    PP3Fill sf;
+    PPFill sf;
     const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
     sf.ra = make_rsrc(A + m0 * lda, (uint32_t)(arows * lda));
     sf.rb = make_rsrc(B + nb0 * ldb, (uint32_t)((nb1 - nb0 + 128) * ldb));
@@ -580,6 +403,19 @@ __device__ __forceinline__ void mainloop_pp3(const uint8_t* __restrict__ A, int6
         }
     }
     sf.lds_rows = (uint32_t)(32 * wave * kRowB);
+    if constexpr (kMx) {
+        // A: the 128-row group of this wave's rows (the last m tile's second group may lie past
+        // the array: zero records, scales read as 0); B: the group of this wave's 64 columns
+        const int wm = wave / kWN, wn = wave % kWN;
+        const int64_t group_bytes = (int64_t)ktiles * 1024;
+        const int64_t ga = m0 / 128 + wm;
+        const int64_t a_rest = (int64_t)mxs.a_bytes - ga * group_bytes;
+        sf.rsa = make_rsrc(mxs.a + (a_rest > 0 ? ga * group_bytes : 0), (uint32_t)(a_rest > 0 ? a_rest : 0));
+        const int64_t gb = (wn < 2 ? nb0 : nb1) / 128;
+        sf.rsb = make_rsrc(mxs.b + gb * group_bytes, (uint32_t)((int64_t)mxs.b_bytes - gb * group_bytes));
+        sf.vsa = (uint32_t)(lane * 16);
+        sf.vsb = (uint32_t)(lane * 16 + (wn % 2) * 8);
+    }
     FragAddr fa;
     fa.init();
 #pragma unroll
@@ -588,16 +424,18 @@ __device__ __forceinline__ void mainloop_pp3(const uint8_t* __restrict__ A, int6
         for (int j = 0; j < Acc::NB; ++j) acc.v[i][j] = 0.f;
 
     PPFrags<kKind> fr;
-    // prologue: this wave's rows of A(0), B(0) and B(1); A(0) and B(0) must land before the
-    // first reads, B(1) before the end of this wave's first memory-phase barrier (G1) or its
-    // first compute-phase barrier (G0)
+    // prologue: this wave's rows of A(0), B(0) (and the scales of stage 0), then B(1).  A(0)
+    // and B(0) must land before the first reads; B(1) before this wave's first wait that
+    // covers it (G1: the end of its first memory phase; G0: the end of its first compute phase)
     sf.a_rows(smem, 0, 0, true);
     sf.b_rows(smem, 0, 0, true);
+    if constexpr (kMx) sf.scales(fr.sa, fr.sb, 0, true);
     sf.b_rows(smem, 1, 1, ktiles > 1);
-    pp_barrier<kPPAPieces>();
+    pp_barrier<kPPAPieces + kScl>();
     if (!g0) pp_barrier<63>();       // G1 starts one phase behind
     int sb_read = 0;                 // B slot of stage kt (kt % 3)
-    // Not unrolled or peeled (see mainloop_pp).
+    // Not unrolled or peeled: in a peeled copy the scheduler reordered the MFMAs of the two
+    // k-steps and the register allocator then spilled accumulators to scratch.
 #pragma nounroll
     for (int kt = 0; kt < ktiles; ++kt) {
         const int sa = kt & 1;
@@ -607,44 +445,40 @@ __device__ __forceinline__ void mainloop_pp3(const uint8_t* __restrict__ A, int6
         sf.a_rows(smem, sa ^ 1, kt + 1, kt + 1 < ktiles);
         sf.b_rows(smem, sb_fill, kt + 2, kt + 2 < ktiles);
         __builtin_amdgcn_sched_barrier(0);
-        fr.read(Stage{smem + sa * kOpBytes, smem + (2 + sb_read) * kOpBytes, nullptr, nullptr}, fa);
+        fr.read(Stage{smem + sa * kOpBytes, smem + (2 + sb_read) * kOpBytes}, fa);
         __builtin_amdgcn_sched_barrier(0);
         if (g0) {
-            pp_barrier<63>();
+            pp_barrier<kMx ? kFills : 63>();         // MXFP4: the scales of stage kt landed
         } else {
-            pp_barrier<kLoads>();        // B(kt+1) of this wave landed
+            pp_barrier<kFills>();                    // B(kt+1) (and the scales of kt) landed
         }
-        // compute phase: MFMAs only
+        // compute phase: MFMAs only, then the next stage's scales into the registers they used
         __builtin_amdgcn_sched_barrier(0);
         pin_acc(acc);
         fr.mma(acc);
         pin_acc(acc);
         __builtin_amdgcn_sched_barrier(0);
-        pp_barrier<kPPAPieces>();        // A(kt+1) (and for G0 B(kt+1)) landed; B(kt+2) may fly
+        if constexpr (kMx) sf.scales(fr.sa, fr.sb, kt + 1, kt + 1 < ktiles);
+        __builtin_amdgcn_sched_barrier(0);
+        pp_barrier<kPPAPieces + kScl>();             // A(kt+1) (G0: and B(kt+1)) landed
         sb_read = sb_read == 2 ? 0 : sb_read + 1;
     }
     if (g0) pp_barrier<63>();        // G1's last compute phase
+    // drain every load (the dead ones too: they write zeros into the slots the caller reuses)
     __syncthreads();
 }
 
 // Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
 // [0,128) are global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a
 // plain tile; for MXFP4 both multiples of 128).  Ends with all loads drained and a barrier, so
-// the caller may reuse the LDS.  smem must hold kSmemFor<kKind> bytes.
-template <Mma kKind>
-constexpr int kSmemFor = kKind == Mma::kMxFp4 ? kSmemBytes : kSmem3Bytes;
-
+// the caller may reuse the LDS (kSmemBytes).
 template <Mma kKind>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
                                          int ktiles, uint8_t* smem, Acc& acc, const MxScales& mxs = MxScales{}) {
-    if constexpr (kKind == Mma::kMxFp4) {
-        mainloop_pp<kKind>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs);
-    } else {
-        (void)mxs;
-        mainloop_pp3<kKind>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc);
-    }
+    mainloop_pp<kKind>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs);
 }
+
 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS
 // (row pitch kEpiPitch), the products in fp32 as printed, then RNE to bf16.

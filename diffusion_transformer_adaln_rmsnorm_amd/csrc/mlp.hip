@@ -26,7 +26,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale, int64_t M,
                   const uint8_t* __restrict__ W1, const float* __restrict__ w1s, uint16_t* __restrict__ y,
                   float* __restrict__ y_amax, int mt, int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemFor<Mma::kE4m3>];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
@@ -108,7 +108,7 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
                  const uint8_t* __restrict__ W2, const float* __restrict__ w2s, const uint16_t* __restrict__ gate,
                  int64_t gate_rows, int64_t gate_ld, const int64_t* __restrict__ idx, const uint16_t* residual,
                  uint16_t* out, int mt, int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemFor<Mma::kE4m3>];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;

@@ -62,7 +62,7 @@ void k_out_proj_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __rest
                       uint32_t w_sbytes, const uint16_t* __restrict__ gate, int64_t gate_rows, int64_t gate_ld,
                       const int32_t* __restrict__ gate_index, const uint16_t* residual, uint16_t* out, int mt,
                       int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemFor<Mma::kMxFp4>];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;

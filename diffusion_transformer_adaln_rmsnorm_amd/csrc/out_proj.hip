@@ -21,7 +21,7 @@ void k_out_proj_gemm(const uint16_t* __restrict__ attn, int64_t M, const uint16_
                      const uint16_t* __restrict__ gate, int64_t gate_rows, int64_t gate_ld,
                      const int32_t* __restrict__ gate_index, const uint16_t* residual, uint16_t* out, int mt,
                      int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemFor<Mma::kBf16>];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;

@@ -158,7 +158,7 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
                 const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
                 const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
                 int hpd, float dq, float dk, float dv, void* __restrict__ out, int mt, int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemFor<Mma::kBf16>];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
@@ -177,7 +177,7 @@ void k_qkv_gemm_mxfp4(const uint8_t* __restrict__ ws_codes, const uint8_t* __res
                       uint32_t w_sbytes, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
                       const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
                       int hpd, void* __restrict__ out, int mt, int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemFor<Mma::kMxFp4>];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     int tm, tn;
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
