@@ -6,12 +6,17 @@
 //
 // At M <= 16 the GEMM is bound by streaming the 231 MB weight (16 flop per weight byte), and
 // a 256-row tile would put the whole weight on 84 workgroups.  Here one workgroup owns one head
-// of one kind (168 workgroups): its 128 weight rows are split along K over 12 waves (448 values
-// each, 14 k-steps of 32), which stream them from global memory straight into MFMA operand
-// registers, three k-steps ahead (each weight element feeds exactly one MFMA lane, so nothing is
-// staged in LDS).  The 16 x 128 fp32 partial sums of the 12 waves are added in LDS in a fixed
-// order, rounded to bf16, and the head goes through the same per-head Q/K RMSNorm, RoPE and pack
-// as the tile kernel's epilogue.
+// of one kind (168 workgroups, 8 waves), and each wave owns 16 of the head's 128 weight rows
+// (one 16-column block of the output) over the whole K:
+//   - the wave copies its rows into its own ring of LDS slots with buffer_load ... lds, 128 K
+//     values (256 contiguous bytes of each row) per stage and four stages ahead;
+//   - the 16-byte chunks of a row are XOR-swizzled by the row (on the global side, since the 64
+//     lanes of a fill write 1 KiB of LDS in lane order), so the MFMA operand reads of 16 rows
+//     hit 16 distinct bank groups;
+//   - the activation's operand (16 rows of the workspace, 172 KB, read by every wave) is loaded
+//     from L2 straight into registers.
+// No wave reads another's rows, so the main loop has no barrier.  The 16 x 128 fp32 result goes
+// through LDS to the same per-head Q/K RMSNorm, RoPE and pack code as the tile kernel's epilogue.
 #include "common.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
@@ -22,16 +27,28 @@ namespace dit {
 using gemm::buf_ld16;
 using gemm::buf_ld_i64;
 using gemm::lds_barrier;
+using gemm::lds_u8;
 using gemm::make_rsrc;
 
-constexpr int kSmallM = 16;
-constexpr int kSmWaves = 12;
+constexpr int kSmWaves = 8;                       // 8 x 16 = the head's 128 weight rows
 constexpr int kSmThreads = 64 * kSmWaves;
-constexpr int kSmKPerWave = kHidden / kSmWaves;   // 448
-constexpr int kSmSteps = kSmKPerWave / 32;        // 14 k-steps of 32 bf16
-constexpr int kSmDepth = 3;                       // k-steps of operands in flight per wave
-constexpr int kSmPitch = kHeadDim + 4;            // fp32 row pitch of the partial sums in LDS
-static_assert(kSmKPerWave * kSmWaves == kHidden && kSmKPerWave % 32 == 0, "K split");
+constexpr int kSmStageK = 128;                    // K values per stage (256 contiguous bytes of a row)
+constexpr int kSmStages = kHidden / kSmStageK;
+constexpr int kSmChunks = kSmStageK / 8;          // 16-byte chunks of a row per stage
+constexpr int kSmSlot = 16 * kSmStageK * 2;       // one stage of a wave's 16 rows
+constexpr int kSmAhead = 4;                       // stages in flight per wave
+constexpr int kSmRing = kSmAhead + 1;             // slots per wave (one being read)
+constexpr int kSmPieces = kSmSlot / 1024;         // 1 KiB fill loads per stage
+constexpr int kSmSteps = kSmStageK / 32;          // MFMA k-steps per stage
+constexpr int kSmLoads = kSmPieces + kSmSteps;    // loads per stage: fills, then A operands
+static_assert(kHidden % kSmStageK == 0 && kSmStages > kSmAhead && kSmChunks % 16 == 0, "K stages");
+static_assert(kSmLoads * kSmAhead < 64, "vmcnt range");
+static_assert(kSmWaves * kSmRing * kSmSlot <= 160 * 1024, "LDS");
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 __global__ __launch_bounds__(kSmThreads) void k_qkv_small(const uint16_t* __restrict__ ws, int64_t M,
                                                           const uint16_t* __restrict__ W,
@@ -40,58 +57,87 @@ __global__ __launch_bounds__(kSmThreads) void k_qkv_small(const uint16_t* __rest
                                                           const uint16_t* __restrict__ cs, int64_t S,
                                                           const int64_t* __restrict__ pos, float qk_eps, int hpd,
                                                           uint16_t* __restrict__ out) {
-    // partial sums of each wave: rows 16 x head dims 128 (row pitch padded: the 4 lane groups of a
-    // write land 16 banks apart)
-    __shared__ __attribute__((aligned(16))) float red[kSmWaves * kSmallM * kSmPitch];
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kSmWaves * kSmRing * kSmSlot];
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int kind = blockIdx.x / kHeads, head = blockIdx.x % kHeads;
-    const int n0 = kind * kAttnWidth + head * kHeadDim;
-    // A: the workspace (rows past M read as zeros); B: the head's 128 weight rows
+    const int n0 = kind * kAttnWidth + head * kHeadDim + 16 * wave;   // this wave's first weight row
+    uint8_t* ring = lds + wave * kSmRing * kSmSlot;
+    // A: the workspace (rows past M read as zeros); B: this wave's 16 weight rows
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(ws, (uint32_t)(M * kHidden * 2));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * kHidden, (uint32_t)(kHeadDim * kHidden * 2));
-    // lane l supplies row (A) or column (B) l % 16 of a 16-block and k values 8 (l / 16) .. + 7 of
-    // a k-step, the same (lane group, k) assignment for both operands
-    const uint32_t koff = (uint32_t)((wave * kSmKPerWave + 8 * (lane >> 4)) * 2);
-    const uint32_t a_off = (uint32_t)((lane & 15) * kHidden * 2) + koff;
-    const uint32_t b_off = a_off;
-    constexpr uint32_t kBlkB = 16 * kHidden * 2;      // bytes between 16-row weight blocks
-    f32x4 acc[8];
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(W + (int64_t)n0 * kHidden, (uint32_t)(16 * kHidden * 2));
+    // fill: the slot holds the stage's 16 rows one after the other, kSmChunks 16-byte chunks
+    // each; lane i of piece q lands at slot chunk p = 64 q + i, i.e. row p / kSmChunks, position
+    // p % kSmChunks, and loads the row's chunk (position) ^ (row % 16)
+    uint32_t fill_off[kSmPieces];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 aq[kSmDepth], bq[kSmDepth][8];
-#pragma unroll
-    for (int s = 0; s < kSmDepth; ++s) {
-        aq[s] = buf_ld16(ra, a_off + s * 64);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bq[s][j] = buf_ld16(rb, b_off + j * kBlkB + s * 64);
+    for (int q = 0; q < kSmPieces; ++q) {
+        const int p = 64 * q + lane;
+        const int r = p / kSmChunks, c = p % kSmChunks;
+        fill_off[q] = (uint32_t)(r * kHidden * 2 + ((c ^ (r % 16)) << 4));
     }
+    // MFMA operands, k-step s (32 values) of a stage: lane l supplies row (A) or column (B) l % 16
+    // and k values 8 (l / 16) .. + 7, i.e. 16-byte chunk 4 s + l / 16 of the stage
+    const int r = lane % 16, g = lane / 16;
+    const uint32_t a_off = (uint32_t)(r * kHidden * 2 + g * 16);
+    auto ra_at = [&](int st, int s) { return a_off + (uint32_t)(st * kSmStageK * 2 + s * 64); };
+    auto rd_at = [&](int s) { return (uint32_t)(r * kSmStageK * 2 + (((4 * s + g) ^ r) << 4)); };
+    static_assert(kSmAhead <= 4, "waits below");
+    auto fill = [&](int st) {
+        lds_u8* S = (lds_u8*)ring + (st % kSmRing) * kSmSlot;
 #pragma unroll
-    for (int s = 0; s < kSmSteps; ++s) {
-        const int slot = s % kSmDepth;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, aq[slot]);
+        for (int q = 0; q < kSmPieces; ++q)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, S + q * 1024, 16, (int)fill_off[q], st * kSmStageK * 2, 0,
+                                                     0);
+    };
+    u32x4 aq[kSmRing][kSmSteps];     // A operands of the stages in flight, by stage % kSmRing
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bq[slot][j]), acc[j], 0, 0,
-                                                             0);
-        if (s + kSmDepth < kSmSteps) {
-            aq[slot] = buf_ld16(ra, a_off + (s + kSmDepth) * 64);
+    for (int st = 0; st < kSmAhead; ++st) {
+        fill(st);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) bq[slot][j] = buf_ld16(rb, b_off + j * kBlkB + (s + kSmDepth) * 64);
+        for (int s = 0; s < kSmSteps; ++s) aq[st][s] = buf_ld16(ra, ra_at(st, s));
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < kSmStages; ++st) {
+        // the ring slot refilled next held stage st - 1, whose operand reads fed the MFMAs above
+        asm volatile("" ::: "memory");
+        if (st + kSmAhead < kSmStages) {
+            fill(st + kSmAhead);
+#pragma unroll
+            for (int s = 0; s < kSmSteps; ++s)
+                aq[(st + kSmAhead) % kSmRing][s] = buf_ld16(ra, ra_at(st + kSmAhead, s));
+        }
+        // stage st's fill and A operands have landed once at most the later stages' loads are
+        // outstanding (kSmLoads per stage)
+        const int later = kSmStages - 1 - st < kSmAhead ? kSmStages - 1 - st : kSmAhead;
+        if (later >= 4) wait_vm<4 * kSmLoads>();
+        else if (later == 3) wait_vm<3 * kSmLoads>();
+        else if (later == 2) wait_vm<2 * kSmLoads>();
+        else if (later == 1) wait_vm<kSmLoads>();
+        else wait_vm<0>();
+        asm volatile("" ::: "memory");   // the operand reads below stay after the wait
+        const uint8_t* S = ring + (st % kSmRing) * kSmSlot;
+#pragma unroll
+        for (int s = 0; s < kSmSteps; ++s) {
+            const u32x4 b = *reinterpret_cast<const u32x4*>(S + rd_at(s));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aq[st % kSmRing][s]),
+                                                          __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
         }
     }
-    // lane l, register r of block j: row 4 (l / 16) + r, head dim 16 j + l % 16
+    // every wave's result (16 x 16, lane l register v: row 4 (l / 16) + v, column l % 16) into
+    // the first 8 KiB of LDS as a [16][128] fp32 tile, once every wave has finished its reads
+    __syncthreads();
+    float* res = reinterpret_cast<float*>(lds);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            red[(wave * kSmallM + 4 * (lane >> 4) + r) * kSmPitch + 16 * j + (lane & 15)] = acc[j][r];
+    for (int v = 0; v < 4; ++v) res[(4 * g + v) * kHeadDim + 16 * wave + r] = acc[v];
 
     // epilogue: threads 0..255, the 16 lanes of a DPP row on one token row, 8 dims each
     const int row = t >> 4, li = t & 15;
     const int q = chunk_of_lane(li);
     const int d0 = q * 8;
     const int j0 = (q % 6) * 8;                     // frequency index of this chunk (q < 12)
-    const bool epi = t < kSmallM * 16;
+    const bool epi = t < 16 * 16;
     const bool need_cs = epi && kind < 2 && q < 12;
     u32x4 cv = {0u, 0u, 0u, 0u}, sv = cv, nwv = cv;
     if (need_cs) {
@@ -108,18 +154,14 @@ __global__ __launch_bounds__(kSmThreads) void k_qkv_small(const uint16_t* __rest
     lds_barrier();
     if (!epi) return;
     float v[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    // the 12 partial sums in wave order (a fixed order: the result is deterministic)
-#pragma unroll
-    for (int w = 0; w < kSmWaves; ++w) {
-        const float* p = red + (w * kSmallM + row) * kSmPitch + d0;
+    {
+        const float* p = res + row * kHeadDim + d0;
         const f32x4 lo = *reinterpret_cast<const f32x4*>(p);
         const f32x4 hi = *reinterpret_cast<const f32x4*>(p + 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            v[e] += lo[e];
-            v[4 + e] += hi[e];
+            v[e] = lo[e];
+            v[4 + e] = hi[e];
         }
     }
     const u32x4 vp = pack8(v);                      // qkv = bf16(acc)
