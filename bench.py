@@ -38,6 +38,7 @@ PEAK_HBM = 8000.0
 # Minimum HBM bytes of the norm/AdaLN launch per row: read x (5376 bf16), write the workspace
 # (5376 bf16), read the int64 index; tables and the norm weight stay in cache.
 NORM_BYTES_PER_ROW = 5376 * 2 * 2 + 8
+FLUSH_BYTES = 512 << 20
 
 
 def log(msg):
@@ -46,7 +47,7 @@ def log(msg):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("gemm.hpp", "pre_attn.hip", "common.hpp"):
+    for f in ("gemm.hpp", "pre_attn.hip", "qk_epi.hpp", "common.hpp"):
         with open(os.path.join(ROOT, "diffusion_transformer_adaln_rmsnorm_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -65,10 +66,21 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(d, seconds_target=15.0):
     import numpy as np
     import oracle
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = max(1, os.cpu_count() or 1)
     # one warm call sizes the sample so that the timed call lasts about seconds_target
     t0 = time.perf_counter()
     oracle.pre_attn(d, rows_sel=np.arange(threads, dtype=np.int64), threads=threads)
@@ -80,9 +92,13 @@ def cpu_baseline(d, seconds_target=15.0):
     oracle.pre_attn(d, rows_sel=rows, threads=threads)
     dt = time.perf_counter() - t0
     flop = 2.0 * rows.size * 21504 * 5376
+    rows_per_s = rows.size / dt
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"pre-attention oracle (fp64, C) on {rows.size} seeded random rows of the M=32760 workload, "
-                      f"{dt:.1f} s wall; value = QKV flops of those rows / wall time"}
+            "model": cpu_model(), "rows_per_s": round(rows_per_s, 2),
+            "full_M_s_extrapolated": round(d["M"] / rows_per_s, 1),
+            "sample": f"pre-attention oracle (fp64, C) on {rows.size} seeded random rows of the M={d['M']} workload, "
+                      f"{dt:.1f} s wall on {threads} threads (os.cpu_count()); value = QKV flops of those rows / "
+                      f"wall time; full_M_s_extrapolated = M / rows_per_s (rows are independent), not measured"}
 
 
 def main():
@@ -144,6 +160,14 @@ def main():
                "workspace_y_q": torch.empty((M_TOKENS, 14336), dtype=torch.float8_e4m3fn, device=dev),
                "workspace_y_scale": torch.empty((M_TOKENS,), dtype=torch.float32, device=dev)}
         out_mlp = torch.empty((M_TOKENS, 5376), dtype=torch.bfloat16, device=dev)
+    # cache flush between timed iterations: a 512 MiB device copy (1 GiB of traffic) evicts the
+    # 4 MiB L2 of every XCD and the 256 MiB Infinity Cache, so no launch finds its inputs there
+    flush_src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+
+    def flush():
+        flush_dst.copy_(flush_src)
+
     torch.cuda.synchronize()
     log(f"inputs resident in HBM ({time.perf_counter() - t_gen:.1f} s)")
 
@@ -168,6 +192,7 @@ def main():
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
     for i in range(args.warmup):
+        flush()
         step(mk())
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); timing {args.steps} steps")
@@ -175,27 +200,36 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        flush()
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     seg = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in evs])   # ms
+    def time_calls(fn, n, warm=3):
+        """Mean event time (ms) of fn over n calls, each after a cache flush, on the stream the
+        kernels run on (torch's current stream, which the binding passes to the library)."""
+        for _ in range(warm):
+            flush()
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for a, b in ev:
+            flush()
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    n8 = max(3, min(args.steps, 10))
     # the e4m3 output mode of the QKV launch (same workspace and weights; not part of the step)
     out_e4m3 = torch.empty((1, M_TOKENS, 56, 3, 128), dtype=torch.uint8, device=dev)
+
     def qkv_e4m3():
         dit.dit_qkv_rope_pack_e4m3(ws, tp["qkv_weight"], tp["q_norm_weight"], tp["k_norm_weight"],
                                    tp["rope_cos_sin"], ulysses_degree=1, out=out_e4m3, q_descale=1.0 / 96.0,
                                    k_descale=0.015, v_descale=0.0075, qk_eps=tp["qk_eps"],
                                    rope_positions=tp["rope_positions"])
-    for _ in range(3):
-        qkv_e4m3()
-    e8 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    n8 = max(3, min(args.steps, 10))
-    e8[0].record()
-    for _ in range(n8):
-        qkv_e4m3()
-    e8[1].record()
-    torch.cuda.synchronize()
-    e4m3_ms = e8[0].elapsed_time(e8[1]) / n8
+    e4m3_ms = time_calls(qkv_e4m3, n8)
     del out_e4m3
     # the MXFP4 W4A4 pre-attention on the same inputs (qkv weight quantised once, outside the
     # timing; each call runs the fused norm + quantisation and the block-scaled QKV GEMM)
@@ -208,14 +242,7 @@ def main():
                                wq_c, wq_s, tp["q_norm_weight"], tp["k_norm_weight"], tp["rope_cos_sin"],
                                ulysses_degree=1, out=out_qkv, eps=tp["eps"], qk_eps=tp["qk_eps"],
                                rope_positions=tp["rope_positions"], ws_codes=ws_c, ws_scales=ws_s)
-    for _ in range(3):
-        pre_mx()
-    e8[0].record()
-    for _ in range(n8):
-        pre_mx()
-    e8[1].record()
-    torch.cuda.synchronize()
-    pre_mx_ms = e8[0].elapsed_time(e8[1]) / n8
+    pre_mx_ms = time_calls(pre_mx, n8)
     del wq_c, wq_s, ws_c, ws_s
     mx_ms = None
     if "out_proj" in stages:
@@ -228,15 +255,35 @@ def main():
         def op_mx():
             dit.dit_out_proj_gated_mxfp4(to["attn_out"], w_c, w_s, to["gate"], to["gate_index"], to["residual"],
                                          out=out_op, act_codes=a_c, act_scales=a_s)
-        for _ in range(3):
-            op_mx()
-        e8[0].record()
-        for _ in range(n8):
-            op_mx()
-        e8[1].record()
-        torch.cuda.synchronize()
-        mx_ms = e8[0].elapsed_time(e8[1]) / n8
+        mx_ms = time_calls(op_mx, n8)
         del w_c, w_s, a_c, a_s
+    # the two smaller pre-attention workloads (M = 16: W streaming, HBM-bound; M = 4096), each
+    # with its own seeded inputs, both launches timed, a cache flush before each call
+    small = {}
+    for cid in (0, 1):
+        _, dc = synth.config(cid)
+        tc = synth.to_torch("pre_attn", dc, dev)
+        Mc = dc["M"]
+        wsc = torch.empty((Mc, 5376), dtype=torch.bfloat16, device=dev)
+        outc = torch.empty((1, Mc, 56, 3, 128), dtype=torch.bfloat16, device=dev)
+
+        def pre_c():
+            dit.dit_pre_attn_bf16(tc["x"], tc["x_norm_weight"], tc["adaln_scale"], tc["adaln_shift"],
+                                  tc["adaln_index"], tc["qkv_weight"], tc["q_norm_weight"], tc["k_norm_weight"],
+                                  tc["rope_cos_sin"], ulysses_degree=1, out=outc, eps=tc["eps"], qk_eps=tc["qk_eps"],
+                                  rope_positions=tc["rope_positions"], workspace=wsc)
+        ms = time_calls(pre_c, 20, warm=5)
+        idx = dc["adaln_index"]
+        rows_touched = len(set(int(i) for i in idx if 0 <= i < dc["adaln_scale"].rows))
+        # minimum bytes of both launches: x, workspace write + read, index, the touched table rows
+        # (scale and shift), x_norm_weight, W, q/k norm weights, one cos/sin row per token, out
+        byts = (Mc * (5376 * 2 * 3 + 8 + 192 + 21504 * 2) + rows_touched * 2 * 5376 * 2 + 5376 * 2
+                + 21504 * 5376 * 2 + 2 * 128 * 2 + (Mc * 8 if dc["rope_positions"] is not None else 0))
+        flop = 2.0 * Mc * 21504 * 5376
+        small[cid] = (Mc, ms, byts, flop)
+        log(f"config {cid}: pre-attn M={Mc} {ms * 1e3:.1f} us = {byts / ms / 1e6:.0f} GB/s, "
+            f"{flop / ms / 1e9:.1f} TFLOP/s")
+        del tc, wsc, outc, dc
     norm_ms, gemm_ms, op_ms, mlp_ms = seg.mean(axis=0)
     pre_ms = norm_ms + gemm_ms
     ms_per_step = wall * 1e3 / args.steps
@@ -252,7 +299,9 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded PCG64, shapes of the MiniMax-H3 block)",
         "config": {"workload": "bf16 pre-attention M=32760 (QKV 32760x21504x5376, rows=2 AdaLN tables, S=32760 "
                                "identity positions); step also runs the M=32760 bf16 gated out-projection and "
-                               "fp8 W8A8 MLP", "tokens": M_TOKENS, "stages": stages},
+                               "fp8 W8A8 MLP", "tokens": M_TOKENS, "stages": stages,
+                   "cache_flush": "512 MiB device copy before each step and each timed call, outside the "
+                                  "kernel events (ms_per_step includes it)"},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16, 2),
         "roofline": {"bound": "mfma", "kernel": "k_qkv_gemm", "achieved": round(gemm_tflops, 2),
                      "peak": PEAK_BF16, "unit": "TFLOP/s", "frac": round(gemm_tflops / PEAK_BF16, 4),
@@ -280,6 +329,15 @@ def main():
         res["stages_ms"]["out_proj_mxfp4"] = round(float(mx_ms), 4)
         res["stage_rates"]["out_proj_mxfp4_TFLOPs"] = round(r, 2)
         res["stage_rates"]["out_proj_mxfp4_frac_fp4"] = round(r / PEAK_FP4, 4)
+    M0, ms0, b0, f0 = small[0]
+    res["stages_ms"]["pre_attn_m16"] = round(ms0, 5)
+    res["stage_rates"]["pre_attn_m16_GBps"] = round(b0 / (ms0 * 1e-3) / 1e9, 1)
+    res["stage_rates"]["pre_attn_m16_frac_hbm"] = round(b0 / (ms0 * 1e-3) / 1e9 / PEAK_HBM, 4)
+    res["stage_rates"]["pre_attn_m16_bytes"] = b0
+    M1, ms1, b1, f1 = small[1]
+    res["stages_ms"]["pre_attn_m4096"] = round(ms1, 4)
+    res["stage_rates"]["pre_attn_m4096_TFLOPs"] = round(f1 / (ms1 * 1e-3) / 1e12, 2)
+    res["stage_rates"]["pre_attn_m4096_frac_bf16"] = round(f1 / (ms1 * 1e-3) / 1e12 / PEAK_BF16, 4)
     if "mlp" in stages:
         r = MLP_FLOP / (mlp_ms * 1e-3) / 1e12
         res["stage_rates"]["mlp_fp8_TFLOPs"] = round(r, 2)
