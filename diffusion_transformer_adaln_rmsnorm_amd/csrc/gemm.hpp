@@ -103,6 +103,9 @@ __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off,
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
 }
 constexpr uint32_t kOffNone = 0xFFFFFFF0u;   // an offset past every descriptor's bound
+// Cache-policy operand of the buffer instructions: nt (non-temporal: streamed through the caches
+// without being kept), for data a kernel touches once.
+constexpr int kCpolNt = 2;
 
 // Within a wave's slice the swizzle of a fill piece's rows depends only on the piece's
 // parity, so B needs two per-lane offsets; A keeps the row in the per-lane offset because only
