@@ -79,7 +79,18 @@ __global__ __launch_bounds__(256) void k_norm_adaln_bf16(const uint16_t* __restr
     const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
     uint16_t* wr = ws + m * kHidden;
+    // Every load that does not depend on the index is issued before the guard: at small M the
+    // kernel is a chain of memory latencies (index -> table rows, x), not a stream.
     const int64_t i = idx[m];
+    u32x4 xv[kMaxPerLane], wv[kMaxPerLane];
+    const uint16_t* xr = x + m * kHidden;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (chunk_ok(j, lane)) {
+            xv[j] = ld16_nt(xr + (j * 64 + lane) * 8);
+            wv[j] = ld16(xw + (j * 64 + lane) * 8);
+        }
+    }
     if (!(i >= 0 && i < rows)) {               // full-width int64 guard
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -87,16 +98,34 @@ __global__ __launch_bounds__(256) void k_norm_adaln_bf16(const uint16_t* __restr
             if (chunk_ok(j, lane)) st16(wr + (j * 64 + lane) * 8, z);
         return;
     }
-    u32x4 xv[kMaxPerLane];
-    const float r = load_row_rms(x + m * kHidden, lane, eps, xv);
     const uint16_t* scr = scale + i * ld_scale;
     const uint16_t* shr = shift + i * ld_shift;
+    u32x4 scv[kMaxPerLane], shv[kMaxPerLane];
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (chunk_ok(j, lane)) {
+            scv[j] = ld16(scr + (j * 64 + lane) * 8);
+            shv[j] = ld16(shr + (j * 64 + lane) * 8);
+        }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (chunk_ok(j, lane)) {
+            float f[8];
+            unpack8(xv[j], f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+        }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)kHidden + eps);
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (!chunk_ok(j, lane)) continue;
         const int c = (j * 64 + lane) * 8;
         uint32_t a[4];
-        modulate_chunk(xv[j], ld16(xw + c), ld16(scr + c), ld16(shr + c), r, a);
+        modulate_chunk(xv[j], wv[j], scv[j], shv[j], r, a);
         st16(wr + c, u32x4{a[0], a[1], a[2], a[3]});
     }
 }
