@@ -4,15 +4,20 @@
 // [M, K], weights [N, K]), FP32 accumulation.
 //
 // Workgroup: 8 waves, two per SIMD, and one 256 x 256 output tile; each wave owns a 128 x 64
-// wave tile of 8 x 4 blocks of 16 x 16 (128 FP32 accumulators per lane, so a wave fits in 256
-// registers):
-//   bf16:  v_mfma_f32_16x16x32_bf16, two k-steps per stage;
-//   e4m3:  v_mfma_scale_f32_16x16x128_f8f6f4 (unit scales), one k-step per stage;
-//   mxfp4: the same instruction on E2M1 operands with their E8M0 block scales, two k-steps.
+// wave tile (128 FP32 accumulators per lane, so a wave fits in 256 registers):
+//   bf16:  8 x 4 blocks of 16 x 16, v_mfma_f32_16x16x32_bf16, two k-steps per stage;
+//   e4m3:  8 x 4 blocks of 16 x 16, v_mfma_f32_16x16x128_f8f6f4 (the scaled builtin with zero
+//          scale operands, which the compiler emits as the unscaled instruction), one k-step per
+//          stage;
+//   mxfp4: 4 x 2 blocks of 32 x 32, v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1 operands with
+//          their E8M0 block scales, four k-steps per stage.
 // Under a full-chip load the shader clock is set by power.  For the same MACs the 16x16 forms
 // move fewer register bytes than the 32x32 ones (bf16: operands plus accumulator read and
 // write, 0.5 against 0.625 bytes per MAC), and a register-only MFMA loop sustains about 12%
-// (bf16) and 7% (e4m3) more FLOP/s with them.
+// (bf16) and 7% (e4m3) more FLOP/s with them.  The scaled MFMA is the exception: while one
+// wave of a SIMD issues the 16x16x128 scaled form, the other wave's fill and LDS-read
+// instructions issue at about half their usual rate (a memory phase of ~1430 cycles against
+// ~980), and the 32x32x64 form, half as many instructions for the same work, removes that.
 // A and B fragments take their k values from the same (lane group, byte) positions, so the
 // product is the same whatever order the instruction assigns to k inside a fragment.
 //
@@ -57,12 +62,12 @@ enum class Mma { kBf16, kE4m3, kMxFp4 };
 
 // MX scale layout.  For a matrix of R rows (padded to a multiple of 128) and K values per row
 // (a multiple of 256), the E8M0 scale of row r, block b (values 32 b .. 32 b + 31) is the byte
-//   ((r / 128) (K / 256) + b / 8) 1024 + 16 l + 2 ((r % 128) / 16) + (b % 8) / 4,
-//   l = r % 16 + 16 (b % 4).
+//   ((r / 128) (K / 256) + b / 8) 1024 + 16 l + 4 ((r % 128) / 32) + (b % 8) / 2,
+//   l = r % 32 + 32 (b % 2).
 // So each 128 rows x 256 values (one GEMM stage of a wave-row of 128) own 1 KiB, in which lane
-// l's 16 bytes are the scales it hands the MFMA: the instruction takes the scale of row l % 16
-// and block l / 16 of a 16 x 128 operand from lane l, for each of the 8 16-row blocks and the
-// 2 k-steps of the stage.
+// l's 16 bytes are the scales it hands the MFMA: the 32x32x64 instruction takes the scale of
+// row l % 32 and block l / 32 of a 32 x 64 operand from lane l; register I of the four holds
+// the 32-row block I, byte q the stage's k-step q.
 
 // Workgroup id -> (m tile, n tile).  Workgroups are dispatched round-robin over the 8 XCDs,
 // so id % 8 names the XCD: each XCD gets one contiguous range of the logical order, and the
@@ -124,6 +129,12 @@ struct Acc {
     static constexpr int MB = 8, NB = 4;
     f32x4 v[MB][NB];
 };
+// MXFP4: 4 x 2 blocks of 32 x 32.  Lane l, register r of a block holds row
+// 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32.
+struct AccMx {
+    static constexpr int MB = 4, NB = 2;
+    f32x16 w[MB][NB];
+};
 
 // Per-lane LDS offsets of the fragment reads (relative to an operand slot).  Lane l reads row
 // l % 16 of each 16-row block and, in lane group g = l / 16, chunks g and g + 4 of it:
@@ -151,6 +162,25 @@ struct FragAddr {
     }
 };
 
+// MXFP4 (32x32x64): lane l reads row l % 32 of each 32-row block and, for k-step q, chunk
+// 2 q + l / 32 (32 E2M1 values).  The 16 lanes of a read quarter sit on 16 consecutive rows of
+// one chunk, so the swizzle keeps them on 16 distinct bank groups.
+struct FragAddrMx {
+    uint32_t a[4], b[4];
+    __device__ __forceinline__ void init() {
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int wm = wave / kWN, wn = wave % kWN;
+        const int r = lane % 32, h = lane / 32;
+        const int sw = swz(r);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = 2 * q + h;
+            a[q] = (uint32_t)((wm * 128 + r) * kRowB + ((c ^ sw) << 4));
+            b[q] = (uint32_t)((wn * kWaveN + r) * kRowB + ((c ^ sw) << 4));
+        }
+    }
+};
+
 __device__ __forceinline__ u32x4 lds_ld16(const uint8_t* smem, uint32_t off) {
     return *reinterpret_cast<const u32x4*>(smem + off);
 }
@@ -162,27 +192,22 @@ __device__ __forceinline__ i32x8 lds_i32x8(const uint8_t* smem, uint32_t off0, u
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)up[0], (int)up[1], (int)up[2], (int)up[3]};
 }
 
-// v_mfma_scale_f32_16x16x128_f8f6f4 on E2M1 operands (4 registers each, format 4 for both),
+// v_mfma_scale_f32_32x32x64_f8f6f4 on E2M1 operands (4 registers each, format 4 for both),
 // scale_a / scale_b the E8M0 bytes OA / OB of the lanes' scale words.  The four-register form
 // of the intrinsic is named directly: the builtin only takes the eight-register (fp8) operands.
-extern "C" __device__ f32x4 __dit_mfma_scale_f4(i32x4 a, i32x4 b, f32x4 c, int cbsz, int blgp, int opsel_a,
-                                                int scale_a, int opsel_b, int scale_b)
-    __asm("llvm.amdgcn.mfma.scale.f32.16x16x128.f8f6f4.v4i32.v4i32");
-// byte selectors as immediates: oa, ob are constants once the MFMA loops are unrolled, and each
-// case passes literal ones
-__device__ __forceinline__ f32x4 mfma_mxfp4(const i32x4& a, const i32x4& b, const f32x4& c, uint32_t sa,
-                                            uint32_t sb, int oa, int ob) {
-#define DIT_MX_CASE(A_, B_) \
-    case A_ * 4 + B_:       \
-        return __dit_mfma_scale_f4(a, b, c, 4, 4, A_, (int)sa, B_, (int)sb);
-    switch (oa * 4 + ob) {
-        DIT_MX_CASE(0, 0) DIT_MX_CASE(0, 1) DIT_MX_CASE(0, 2) DIT_MX_CASE(0, 3)
-        DIT_MX_CASE(1, 0) DIT_MX_CASE(1, 1) DIT_MX_CASE(1, 2) DIT_MX_CASE(1, 3)
-        DIT_MX_CASE(2, 0) DIT_MX_CASE(2, 1) DIT_MX_CASE(2, 2) DIT_MX_CASE(2, 3)
-        DIT_MX_CASE(3, 0) DIT_MX_CASE(3, 1) DIT_MX_CASE(3, 2) default:
-            return __dit_mfma_scale_f4(a, b, c, 4, 4, 3, (int)sa, 3, (int)sb);
+extern "C" __device__ f32x16 __dit_mfma_scale_f4_32(i32x4 a, i32x4 b, f32x16 c, int cbsz, int blgp, int opsel_a,
+                                                    int scale_a, int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v4i32");
+// byte selectors as immediates: q is a constant once the MFMA loop is unrolled, and each case
+// passes literal ones
+__device__ __forceinline__ f32x16 mfma_mxfp4(const i32x4& a, const i32x4& b, const f32x16& c, uint32_t sa,
+                                             uint32_t sb, int q) {
+    switch (q) {
+        case 0: return __dit_mfma_scale_f4_32(a, b, c, 4, 4, 0, (int)sa, 0, (int)sb);
+        case 1: return __dit_mfma_scale_f4_32(a, b, c, 4, 4, 1, (int)sa, 1, (int)sb);
+        case 2: return __dit_mfma_scale_f4_32(a, b, c, 4, 4, 2, (int)sa, 2, (int)sb);
+        default: return __dit_mfma_scale_f4_32(a, b, c, 4, 4, 3, (int)sa, 3, (int)sb);
     }
-#undef DIT_MX_CASE
 }
 
 // Every fragment of one stage in registers (24 16-byte reads, 96 registers; MXFP4 adds its 24
@@ -230,33 +255,31 @@ struct PPFrags<Mma::kE4m3> {
                 acc.v[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a[i], b[j], acc.v[i][j], 0, 0, 0, 0, 0, 0);
     }
 };
-// MXFP4: a 128-byte stage row is 256 E2M1 values, two k-steps of 128; lane group g reads 16
-// bytes (32 values, block 4 ks + g) of its row, the same chunks as the bf16 reads.  Scale byte
-// 2 i + ks of the lane's A record belongs to block row i, k-step ks (B: 2 j + ks).
+// MXFP4: a 128-byte stage row is 256 E2M1 values, four k-steps of 64; lane l reads 16 bytes
+// (32 values, block 2 q + l / 32) of its row.  Scale byte q of the lane's A record I belongs
+// to block row I, k-step q (B: record J).
 template <>
 struct PPFrags<Mma::kMxFp4> {
-    static constexpr int MB = Acc::MB, NB = Acc::NB;
-    i32x4 a[2][MB], b[2][NB];
+    static constexpr int MB = AccMx::MB, NB = AccMx::NB;
+    i32x4 a[4][MB], b[4][NB];
     u32x4 sa;      // this lane's E8M0 scale records of the stage (loaded by the main loop)
     u32x2 sb;
-    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
+    __device__ __forceinline__ void read(const Stage& st, const FragAddrMx& fa) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int q = 0; q < 4; ++q) {
 #pragma unroll
-            for (int i = 0; i < MB; ++i) a[ks][i] = __builtin_bit_cast(i32x4, lds_ld16(st.a, fa.a[ks] + i * kBlk));
+            for (int i = 0; i < MB; ++i) a[q][i] = __builtin_bit_cast(i32x4, lds_ld16(st.a, fa.a[q] + i * 2 * kBlk));
 #pragma unroll
-            for (int j = 0; j < NB; ++j) b[ks][j] = __builtin_bit_cast(i32x4, lds_ld16(st.b, fa.b[ks] + j * kBlk));
+            for (int j = 0; j < NB; ++j) b[q][j] = __builtin_bit_cast(i32x4, lds_ld16(st.b, fa.b[q] + j * 2 * kBlk));
         }
     }
-    __device__ __forceinline__ void mma(Acc& acc) const {
+    __device__ __forceinline__ void mma(AccMx& acc) const {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
             for (int i = 0; i < MB; ++i)
 #pragma unroll
-                for (int j = 0; j < NB; ++j)
-                    acc.v[i][j] = mfma_mxfp4(a[ks][i], b[ks][j], acc.v[i][j], sa[i / 2], sb[j / 2], 2 * (i % 2) + ks,
-                                             2 * (j % 2) + ks);
+                for (int j = 0; j < NB; ++j) acc.w[i][j] = mfma_mxfp4(a[q][i], b[q][j], acc.w[i][j], sa[i], sb[j], q);
     }
 };
 
@@ -274,6 +297,24 @@ __device__ __forceinline__ void pin_acc(Acc& acc) {
 #pragma unroll
         for (int j = 0; j < Acc::NB; ++j) asm volatile("" : "+v"(acc.v[i][j]));
 }
+__device__ __forceinline__ void pin_acc(AccMx& acc) {
+#pragma unroll
+    for (int i = 0; i < AccMx::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < AccMx::NB; ++j) asm volatile("" : "+v"(acc.w[i][j]));
+}
+
+// Accumulator and fragment-address types of an operand kind.
+template <Mma kKind>
+struct KindTypes {
+    using AccT = Acc;
+    using FragAddrT = FragAddr;
+};
+template <>
+struct KindTypes<Mma::kMxFp4> {
+    using AccT = AccMx;
+    using FragAddrT = FragAddrMx;
+};
 
 // Phase-ending barrier: wait for vmcnt(kVm) and lgkmcnt(0), then a bare s_barrier.  These
 // waits are all the hand-over needs, so younger fill loads stay in flight across it (the
@@ -381,7 +422,8 @@ struct PPFill {
 template <Mma kKind>
 __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                             const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                            int ktiles, uint8_t* smem, Acc& acc, const MxScales& mxs) {
+                                            int ktiles, uint8_t* smem, typename KindTypes<kKind>::AccT& acc,
+                                            const MxScales& mxs) {
     static_assert(kWaves == 8 && kRowB == 128, "ping-pong layout");
     constexpr bool kMx = kKind == Mma::kMxFp4;
     constexpr int kFills = 2 * kPPAPieces;          // fill loads per wave and memory phase
@@ -419,12 +461,19 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         sf.vsa = (uint32_t)(lane * 16);
         sf.vsb = (uint32_t)(lane * 16 + (wn % 2) * 8);
     }
-    FragAddr fa;
+    typename KindTypes<kKind>::FragAddrT fa;
     fa.init();
+    if constexpr (kMx) {
 #pragma unroll
-    for (int i = 0; i < Acc::MB; ++i)
+        for (int i = 0; i < AccMx::MB; ++i)
 #pragma unroll
-        for (int j = 0; j < Acc::NB; ++j) acc.v[i][j] = 0.f;
+            for (int j = 0; j < AccMx::NB; ++j) acc.w[i][j] = 0.f;
+    } else {
+#pragma unroll
+        for (int i = 0; i < Acc::MB; ++i)
+#pragma unroll
+            for (int j = 0; j < Acc::NB; ++j) acc.v[i][j] = 0.f;
+    }
 
     PPFrags<kKind> fr;
     // prologue: this wave's rows of A(0), B(0) (and the scales of stage 0), then B(1).  A(0)
@@ -478,7 +527,8 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
 template <Mma kKind>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                         int ktiles, uint8_t* smem, Acc& acc, const MxScales& mxs = MxScales{}) {
+                                         int ktiles, uint8_t* smem, typename KindTypes<kKind>::AccT& acc,
+                                         const MxScales& mxs = MxScales{}) {
     mainloop_pp<kKind>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs);
 }
 
@@ -544,6 +594,31 @@ __device__ __forceinline__ void stage_tile_bf16(const Acc& acc, uint8_t* smem, c
         if (rowscale) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) rs[r] = rs_nx[r];
+        }
+    }
+}
+
+// The same staging (no scales) for the 32 x 32 blocks of the MXFP4 accumulators: registers
+// r and r + 1 (r even) of a block again hold rows R and R + 1 of one column, so the lane-pair
+// swap is the same.
+__device__ __forceinline__ void stage_tile_bf16(const AccMx& acc, uint8_t* smem) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave / kWN, wn = wave % kWN;
+    const int col_in = lane % 32, row_in = (lane / 32) * 4;
+    const int odd = lane & 1;
+    const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+#pragma unroll
+    for (int i = 0; i < AccMx::MB; ++i) {
+#pragma unroll
+        for (int j = 0; j < AccMx::NB; ++j) {
+            const int col = wn * kWaveN + j * 32 + col_in - odd;
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                const int row = wm * 128 + i * 32 + 8 * (r / 4) + row_in + r % 4 + odd;
+                const uint32_t b = pack_bf2(acc.w[i][j][r], acc.w[i][j][r + 1]);
+                const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0xB1, 0xF, 0xF, true);
+                *reinterpret_cast<uint32_t*>(smem + row * kEpiPitch + col * 2) = __builtin_amdgcn_perm(nb, b, sel);
+            }
         }
     }
 }

@@ -67,7 +67,7 @@ void k_out_proj_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __rest
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
     const int n0 = tn * kBN;
-    Acc acc;
+    AccMx acc;
     MxScales mxs;
     mxs.a = a_scales;
     mxs.a_bytes = a_sbytes;
@@ -79,7 +79,7 @@ void k_out_proj_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __rest
     GatedResidual<int32_t> gr;
     gr.load_index(gate_index, m0, M, gate_rows);
     gr.load_residual(m0, M, n0, residual);
-    stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
+    stage_tile_bf16(acc, smem);
     lds_barrier();
     gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
 }

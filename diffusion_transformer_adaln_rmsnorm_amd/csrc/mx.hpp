@@ -37,10 +37,10 @@ __device__ __forceinline__ uint32_t e2m1_pack4(uint32_t w0, uint32_t w1, float i
 }
 
 // byte offset of the scale of row r, block b (values 32 b ..) of a [*, K] matrix in the MX scale
-// layout: group r / 128, stage b / 8, lane r % 16 + 16 (b % 4), byte 2 ((r % 128) / 16) + (b % 8) / 4
+// layout: group r / 128, stage b / 8, lane r % 32 + 32 (b % 2), byte 4 ((r % 128) / 32) + (b % 8) / 2
 __device__ __forceinline__ int64_t mx_scale_offset(int64_t r, int64_t b, int64_t K) {
-    const int64_t lane = r % 16 + 16 * (b % 4);
-    return ((r / 128) * (K / 256) + b / 8) * 1024 + lane * 16 + 2 * ((r % 128) / 16) + (b % 8) / 4;
+    const int64_t lane = r % 32 + 32 * (b % 2);
+    return ((r / 128) * (K / 256) + b / 8) * 1024 + lane * 16 + 4 * ((r % 128) / 32) + (b % 8) / 2;
 }
 
 }  // namespace dit

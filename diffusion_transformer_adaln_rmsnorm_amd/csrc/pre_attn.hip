@@ -18,6 +18,8 @@
 // lane-dependent choice (a DPP move must run with its source lanes active, which a select
 // lowered to a branch would break).  Each lane writes 16 contiguous bytes of out, so the 16
 // lanes of a head store its 256 bytes in one piece.
+#include <type_traits>
+
 #include "common.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
@@ -50,8 +52,8 @@ __device__ __forceinline__ u32x2 e4m3_codes8(const u32x4& o, float ds, float y) 
 // The QKV epilogue of one 256 x 256 tile after the main loop (acc of this wave): Q/K RMSNorm,
 // RoPE and the pack, or V as is.  kE4m3: out holds e4m3 codes (one byte per element) of the
 // bf16 results divided by the descale of their kind (dq, dk, dv); else bf16 values.
-template <bool kE4m3>
-__device__ __forceinline__ void qkv_epilogue(Acc& acc, uint8_t* smem, int64_t m0, int64_t M, int n0,
+template <bool kE4m3, class AccT>
+__device__ __forceinline__ void qkv_epilogue(AccT& acc, uint8_t* smem, int64_t m0, int64_t M, int n0,
                                              const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
                                              const uint16_t* __restrict__ cs, int64_t S,
                                              const int64_t* __restrict__ pos, float qk_eps, int hpd, float dq,
@@ -101,7 +103,11 @@ __device__ __forceinline__ void qkv_epilogue(Acc& acc, uint8_t* smem, int64_t m0
             praw[it] = buf_ld_i64(rpos, (uint32_t)((m0 + it * kRowsPerPass + rsub) * 8));
     }
 
-    stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
+    if constexpr (std::is_same_v<AccT, AccMx>) {
+        stage_tile_bf16(acc, smem);
+    } else {
+        stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
+    }
     // the cos/sin rows are requested once the accumulators are free and before the barrier, so
     // they are in flight while the other waves finish staging
     u32x4 cv[kIters], sv[kIters];
@@ -182,7 +188,7 @@ void k_qkv_gemm_mxfp4(const uint8_t* __restrict__ ws_codes, const uint8_t* __res
     tile_coords(blockIdx.x, mt, nt, tm, tn);
     const int64_t m0 = (int64_t)tm * kBM;
     const int n0 = tn * kBN;
-    Acc acc;
+    AccMx acc;
     MxScales mxs;
     mxs.a = ws_scales;
     mxs.a_bytes = ws_sbytes;

@@ -264,9 +264,9 @@ int64_t dit_mlp_fp8_flags_elems(int64_t M);
  *   codes   uint8 [rows, K / 2]: element 2j of a row in the low nibble of byte j
  *   scales  uint8, dit_mx_scale_bytes(rows, K) bytes, in the MX scale layout: with rows padded
  *           to a multiple of 128, the scale of row r, block b (values 32 b .. 32 b + 31) is the
- *           byte ((r / 128) (K / 256) + b / 8) 1024 + 16 l + 2 ((r % 128) / 16) + (b % 8) / 4,
- *           l = r % 16 + 16 (b % 4) (the order in which the MFMA lanes take them).  Padding rows
- *           get scale byte 0.
+ *           byte ((r / 128) (K / 256) + b / 8) 1024 + 16 l + 4 ((r % 128) / 32) + (b % 8) / 2,
+ *           l = r % 32 + 32 (b % 2) (the order in which the lanes of the 32 x 32 x 64 MFMA take
+ *           them).  Padding rows get scale byte 0.
  * rows = 0 is a no-op.  One kernel is enqueued.  Used for the weight once and by
  * dit_out_proj_gated_mxfp4 for the activation on every call.
  */

@@ -536,8 +536,8 @@ def mx_scales_rowmajor(scales_gpu, R, K):
     R_pad = (R + 127) // 128 * 128
     r = np.arange(R_pad)[:, None]
     b = np.arange(K // 32)[None, :]
-    lane = r % 16 + 16 * (b % 4)
-    off = ((r // 128) * (K // 256) + b // 8) * 1024 + lane * 16 + 2 * ((r % 128) // 16) + (b % 8) // 4
+    lane = r % 32 + 32 * (b % 2)
+    off = ((r // 128) * (K // 256) + b // 8) * 1024 + lane * 16 + 4 * ((r % 128) // 32) + (b % 8) // 2
     assert sc.size == R_pad * (K // 32) and np.array_equal(np.sort(off.ravel()), np.arange(sc.size))
     full = sc[off]
     return full[:R], full[R:]
