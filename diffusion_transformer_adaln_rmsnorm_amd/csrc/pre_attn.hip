@@ -110,15 +110,15 @@ __device__ __forceinline__ void qkv_epilogue(AccT& acc, uint8_t* smem, int64_t m
     }
     // the cos/sin rows are requested once the accumulators are free and before the barrier, so
     // they are in flight while the other waves finish staging
-    u32x4 cv[kIters], sv[kIters];
+    // this lane's half of the row's cos/sin: the cos chunk (q < 6) or the sin chunk (6 <= q < 12)
+    const int cs_col = q < 6 ? j0 : kNFreq + j0;
+    u32x4 csv[kIters];
 #pragma unroll
     for (int it = 0; it < kIters; ++it) {
         const int64_t m = m0 + it * kRowsPerPass + rsub;
         const int64_t p = pos != nullptr ? praw[it] : m;      // identity positions: the row
         const int64_t pc = p < 0 ? 0 : (p > S - 1 ? S - 1 : p);
-        const uint32_t off = need_cs ? (uint32_t)((pc * kRopeCols + j0) * 2) : kOffNone;
-        cv[it] = buf_ld16(rcs, off);
-        sv[it] = buf_ld16(rcs, off + (need_cs ? kNFreq * 2 : 0u));
+        csv[it] = buf_ld16(rcs, need_cs ? (uint32_t)((pc * kRopeCols + cs_col) * 2) : kOffNone);
     }
     lds_barrier();
 
@@ -134,7 +134,7 @@ __device__ __forceinline__ void qkv_epilogue(AccT& acc, uint8_t* smem, int64_t m
         const int row = it * kRowsPerPass + rsub;
         const u32x4 vp = epi_ld(smem, row, hh * 128 + d0);
         u32x4 o = vp;
-        if (kind < 2) o = qk_norm_rope(vp, nwlo, nwhi, qk_eps, q, cv[it], sv[it]);
+        if (kind < 2) o = qk_norm_rope(vp, nwlo, nwhi, qk_eps, q, csv[it]);
         // one destination: rows past M fall outside rout and are dropped; else out[dst, m, hl, ...]
         const uint32_t e1 = o1 + (uint32_t)it * kPassB;
         const int64_t m = m0 + row;

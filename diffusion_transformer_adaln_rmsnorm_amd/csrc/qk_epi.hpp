@@ -34,9 +34,12 @@ constexpr int kDppMirror = 0x140;      // lane i <- 15 - i within each 16 lanes
 constexpr int kDppRor8 = 0x128;        // row_ror:8: lane i <- (i + 8) mod 16
 
 // v_perm_b32 selectors on (src0, src1): low halves (src1.lo | src0.lo << 16) and high halves
-// (src1.hi | src0.hi << 16).
+// (src1.hi | src0.hi << 16), and the same with the sources' places swapped (src0.lo | src1.lo << 16,
+// src0.hi | src1.hi << 16).
 constexpr uint32_t kPermLo = 0x05040100u;
 constexpr uint32_t kPermHi = 0x07060302u;
+constexpr uint32_t kPermLoSwap = 0x01000504u;
+constexpr uint32_t kPermHiSwap = 0x03020706u;
 // a.lo b.lo + a.hi b.hi (+ c) for two packed bf16 pairs (v_dot2_f32_bf16, fp32 result; the
 // bf16 products are exact)
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c = 0.0f) {
@@ -54,10 +57,12 @@ __device__ __forceinline__ float row16_sum(float x) {
 
 // Q/K output of one (row, head) for the 16 lanes of a DPP row: vp holds this lane's 8 dims
 // (chunk q) of the head as bf16; nwlo / nwhi its 8 norm weights as bf16 pairs with the high /
-// low half zeroed; cv / sv the cos and sin of frequencies 8 (q mod 6) .. + 7 for the row's
-// position (q < 12).  All 16 lanes of the row must be active.
+// low half zeroed; cs this lane's 16 bytes of the row's cos/sin: the cos of frequencies
+// 8 q .. 8 q + 7 (q < 6) or the sin of frequencies 8 (q - 6) .. (6 <= q < 12).  The partner
+// lane (chunk q +/- 6, 8 lanes away) holds the other one, so each lane loads half of what its
+// rotation takes and one row rotation completes it.  All 16 lanes of the row must be active.
 __device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const u32x4& nwlo, const u32x4& nwhi, float qk_eps,
-                                              int q, const u32x4& cv, const u32x4& sv) {
+                                              int q, const u32x4& cs) {
     // per-head RMSNorm in fp32 on the packed bf16 values: the squares and v w are exact
     // bf16 products (v_dot2; a zero half picks one product), the sum of squares carries fp32
     // rounding only, and u = bf16((v w) r2); two partial sums halve the dependent chain
@@ -78,19 +83,24 @@ __device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const u32x4& nwlo
     // for the first half, so both halves take o = u c + w s:
     // o_j = u_j c - u_{j+48} s, o_{j+48} = u_{j+48} c + u_j s
     const uint32_t sgn = q < 6 ? 0x80008000u : 0u;   // negates both bf16 halves of a word
-    u32x4 pv;
+    u32x4 pv, pc;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = dpp_u<kDppRor8>(up[e]) ^ sgn;
+    for (int e = 0; e < 4; ++e) {
+        pv[e] = dpp_u<kDppRor8>(up[e]) ^ sgn;
+        pc[e] = dpp_u<kDppRor8>(cs[e]);     // the partner's cos/sin half: sin (q < 6) or cos
+    }
     if (q >= 12) return up;
     // o = u c + w s per element as one v_dot2 of the bf16 pairs (u, w) and (c, s): the two
-    // products are exact in fp32 and their sum is rounded once, as the fma form u c + (w s) is
+    // products are exact in fp32 and their sum is rounded once, as the fma form u c + (w s) is.
+    // (c, s) pairs: cos from this lane (q < 6) or from the partner, through the selector.
+    const uint32_t sel_lo = q < 6 ? kPermLo : kPermLoSwap, sel_hi = q < 6 ? kPermHi : kPermHiSwap;
     u32x4 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const uint32_t uw0 = __builtin_amdgcn_perm(pv[e], up[e], kPermLo);   // (u_2e, w_2e)
         const uint32_t uw1 = __builtin_amdgcn_perm(pv[e], up[e], kPermHi);   // (u_2e+1, w_2e+1)
-        const uint32_t cs0 = __builtin_amdgcn_perm(sv[e], cv[e], kPermLo);
-        const uint32_t cs1 = __builtin_amdgcn_perm(sv[e], cv[e], kPermHi);
+        const uint32_t cs0 = __builtin_amdgcn_perm(pc[e], cs[e], sel_lo);    // (c_2e, s_2e)
+        const uint32_t cs1 = __builtin_amdgcn_perm(pc[e], cs[e], sel_hi);    // (c_2e+1, s_2e+1)
         r[e] = pack_bf2(dot2_bf16(uw0, cs0), dot2_bf16(uw1, cs1));
     }
     return r;

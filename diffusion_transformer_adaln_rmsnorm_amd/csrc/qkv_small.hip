@@ -142,16 +142,15 @@ __global__ __launch_bounds__(kSmThreads) void k_qkv_small(const uint16_t* __rest
     const int j0 = (q % 6) * 8;                     // frequency index of this chunk (q < 12)
     const bool epi = t < 16 * 16;
     const bool need_cs = epi && kind < 2 && q < 12;
-    u32x4 cv = {0u, 0u, 0u, 0u}, sv = cv, nwv = cv;
+    u32x4 csv = {0u, 0u, 0u, 0u}, nwv = csv;
     if (need_cs) {
         // position: clamp(pos[row], 0, S - 1), or the row (identity); rows past M read position 0
         const __amdgpu_buffer_rsrc_t rpos = make_rsrc(pos, pos ? (uint32_t)(M * 8) : 0u);
         const int64_t p = pos != nullptr ? buf_ld_i64(rpos, (uint32_t)(row * 8)) : (int64_t)row;
         const int64_t pc = p < 0 ? 0 : (p > S - 1 ? S - 1 : p);
         const __amdgpu_buffer_rsrc_t rcs = make_rsrc(cs, (uint32_t)(S * kRopeCols * 2));
-        const uint32_t off = (uint32_t)((pc * kRopeCols + j0) * 2);
-        cv = buf_ld16(rcs, off);
-        sv = buf_ld16(rcs, off + kNFreq * 2);
+        // this lane's half: the cos chunk (q < 6) or the sin chunk (6 <= q < 12)
+        csv = buf_ld16(rcs, (uint32_t)((pc * kRopeCols + (q < 6 ? j0 : kNFreq + j0)) * 2));
     }
     if (epi && kind < 2) nwv = ld16((kind == 0 ? qw : kw) + d0);
     lds_barrier();
@@ -176,7 +175,7 @@ __global__ __launch_bounds__(kSmThreads) void k_qkv_small(const uint16_t* __rest
             nwlo[e] = nwv[e] & 0xFFFFu;
             nwhi[e] = nwv[e] & 0xFFFF0000u;
         }
-        o = qk_norm_rope(vp, nwlo, nwhi, qk_eps, q, cv, sv);
+        o = qk_norm_rope(vp, nwlo, nwhi, qk_eps, q, csv);
     }
     // destination-major pack: out[dst, m, hl, kind, d], destination dst holding heads
     // [dst hpd, (dst + 1) hpd)
