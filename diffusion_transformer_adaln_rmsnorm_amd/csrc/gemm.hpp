@@ -559,14 +559,15 @@ __device__ __forceinline__ void stage_tile_bf16(const Acc& acc, uint8_t* smem, c
 #pragma unroll
         for (int j = 0; j < Acc::NB; ++j) cscale[j] = cs[j * 16 + col_in];
     }
-    // row scales of block row i + 1 are loaded while block row i converts
+    // row scales of block row i + 1 are loaded while block row i converts: the lane's four rows
+    // are consecutive, one 16-byte load through a descriptor over the tile's rows (rows past M
+    // read 0; their accumulators are 0 and never stored)
+    const __amdgpu_buffer_rsrc_t rrs =
+        make_rsrc(rowscale + (rowscale ? m0 : 0), (uint32_t)((M - m0 < kBM ? M - m0 : kBM) * 4));
     auto load_rs = [&](int i, float (&rs)[4]) {
+        const u32x4 v = buf_ld16(rrs, (uint32_t)((wm * 128 + i * 16 + row_in) * 4));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int64_t gm = m0 + wm * 128 + i * 16 + row_in + r;
-            gm = gm < M ? gm : M - 1;
-            rs[r] = rowscale[gm];
-        }
+        for (int r = 0; r < 4; ++r) rs[r] = __uint_as_float(v[r]);
     };
     float rs[4], rs_nx[4];
     if (rowscale) load_rs(0, rs);

@@ -17,6 +17,7 @@
 #include "gated.hpp"
 #include "gemm.hpp"
 #include "kernels.hpp"
+#include "qk_epi.hpp"
 
 namespace dit {
 
@@ -59,10 +60,7 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
             amax = fmaxf(amax, fabsf(bf_lo(yv[k])));
             amax = fmaxf(amax, fabsf(bf_hi(yv[k])));
         }
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        amax = fmaxf(amax, __shfl_xor(amax, 4));
-        amax = fmaxf(amax, __shfl_xor(amax, 8));
+        amax = row16_max(amax);           // the row's 16 lanes are one DPP row
         buf_st16(ry, o1 + it * kPassB, yv);
         if ((t & 15) == 0 && row < (int)tile_rows)
             atomicMax(reinterpret_cast<unsigned int*>(y_amax + m0 + row), __float_as_uint(amax));

@@ -55,6 +55,16 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Maximum over the 16 lanes of a DPP row, left in every lane of it (x >= 0: the moves' fill
+// value 0 never wins).
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<kDppXor1>(x));
+    x = fmaxf(x, dpp_f<kDppXor2>(x));
+    x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp_f<kDppMirror>(x));
+    return x;
+}
+
 // Q/K output of one (row, head) for the 16 lanes of a DPP row: vp holds this lane's 8 dims
 // (chunk q) of the head as bf16; nwlo / nwhi its 8 norm weights as bf16 pairs with the high /
 // low half zeroed; cs this lane's 16 bytes of the row's cos/sin: the cos of frequencies
