@@ -125,8 +125,20 @@ def _table(t: torch.Tensor, name: str) -> Table:
     return Table(t.data_ptr(), t.shape[0], t.stride(0))
 
 
+_EMPTY = {}   # device -> a small buffer whose address stands in for zero-size tensors
+
+
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """The data pointer of t.  torch gives a zero-size tensor a null pointer, which the C ABI
+    refuses even where the size makes the call a no-op (M = 0), so such a tensor passes the
+    address of a small, never-touched buffer on its device instead (256-byte aligned)."""
+    if t is None:
+        return None
+    if t.numel() == 0:
+        if t.device not in _EMPTY:
+            _EMPTY[t.device] = torch.empty(256, dtype=torch.uint8, device=t.device)
+        return ctypes.c_void_p(_EMPTY[t.device].data_ptr())
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _check(fn, st):

@@ -276,7 +276,7 @@ def test_pre_attn_config0_full():
     check_pre(d, ws, out)
 
 
-@pytest.mark.parametrize("M", [1, 2, 3, 255, 256, 257])
+@pytest.mark.parametrize("M", [1, 2, 3, 16, 17, 255, 256, 257])
 def test_pre_attn_small_M_random_positions(M):
     _say(f"pre_attn small M={M}, random positions with clamps, rows=2 wide tables")
     d = synth.pre_attn_inputs(M, seed=100 + M, rows=2, S=64, positions="random", n_bad_positions=min(8, M),
@@ -284,6 +284,72 @@ def test_pre_attn_small_M_random_positions(M):
     ws = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
     _, out = run_pre(d, workspace=ws)
     check_pre(d, ws, out)
+
+
+def test_every_entry_point_treats_M_zero_as_a_no_op():
+    """M = 0 (zero-row views whose data pointers are those of real buffers): every entry point
+    returns without an error and writes nothing -- the buffers behind the views keep their
+    sentinel bytes.  The fp8 MLP's range starts at M = 1 (its page's limits) and is refused."""
+    dit = _dit()
+    _say("M = 0 through every entry point")
+    d = synth.pre_attn_inputs(2, seed=5, rows=2, S=4, positions="random", n_bad_positions=0,
+                              weight=_shared_weight())
+    t = synth.to_torch("pre_attn", d)
+    z = lambda a: a[:0]   # noqa: E731
+    sent = lambda shape, dt: torch.full(shape, 0x5A, dtype=torch.uint8, device="cuda").view(dt)  # noqa: E731
+    out_b = sent((1, 2, 56, 3, 256), torch.uint8)            # room for two bf16 rows
+    out_bf = out_b.view(torch.bfloat16)[:, :0]
+    out_e = sent((1, 2, 56, 3, 128), torch.uint8)
+    ws = sent((2, H * 2), torch.uint8)
+    ws_bf = ws.view(torch.bfloat16)[:0]
+    before = [b.clone() for b in (out_b, out_e, ws)]
+    common = (z(t["x"]), t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], z(t["adaln_index"]))
+    rope = dict(rope_positions=z(t["rope_positions"]), qk_eps=t["qk_eps"])
+    dit.dit_pre_attn_bf16(*common, t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
+                          ulysses_degree=1, out=out_bf, eps=t["eps"], workspace=ws_bf, **rope)
+    dit.dit_pre_attn_bf16_static_ws(*common, t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"],
+                                    t["rope_cos_sin"], ulysses_degree=2, out=out_b.view(torch.bfloat16)[:, :0]
+                                    .reshape(2, 0, 28, 3, 128), eps=t["eps"], **rope)
+    dit.dit_pre_attn_e4m3(*common, t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
+                          ulysses_degree=1, out=out_e[:, :0], q_descale=1.0, k_descale=1.0, v_descale=1.0,
+                          eps=t["eps"], workspace=ws_bf, **rope)
+    dit.dit_norm_adaln_bf16(*common, workspace=ws_bf, eps=t["eps"])
+    dit.dit_qkv_rope_pack_bf16(ws_bf, t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
+                               ulysses_degree=4, out=out_bf.reshape(4, 0, 14, 3, 128), **rope)
+    dit.dit_qkv_rope_pack_e4m3(ws_bf, t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
+                               ulysses_degree=1, out=out_e[:, :0], q_descale=1.0, k_descale=1.0, v_descale=1.0,
+                               **rope)
+    wq = torch.zeros((synth.QKV_ROWS, H // 2), dtype=torch.uint8, device="cuda")
+    wqs = torch.zeros((dit.dit_mx_scale_bytes(synth.QKV_ROWS, H),), dtype=torch.uint8, device="cuda")
+    mx_sc = sent((1024,), torch.uint8)
+    before.append(mx_sc.clone())
+    dit.dit_pre_attn_mxfp4(*common, wq, wqs, t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
+                           ulysses_degree=1, out=out_bf, eps=t["eps"], ws_codes=ws[:0, : H // 2],
+                           ws_scales=mx_sc[:0], **rope)
+    # out-projections and the quantiser
+    to = synth.to_torch("out_proj", synth.out_proj_inputs(2, seed=6))
+    res = sent((2, H * 2), torch.uint8)
+    res_bf = res.view(torch.bfloat16)[:0]
+    ac = sent((2, synth.ATTN_WIDTH // 2), torch.uint8)
+    before += [res.clone(), ac.clone()]
+    dit.dit_out_proj_gated_bf16(z(to["attn_out"]), to["o_weight"], to["gate"], z(to["gate_index"]), res_bf,
+                                out=res_bf)
+    wo = torch.zeros((H, synth.ATTN_WIDTH // 2), dtype=torch.uint8, device="cuda")
+    wos = torch.zeros((dit.dit_mx_scale_bytes(H, synth.ATTN_WIDTH),), dtype=torch.uint8, device="cuda")
+    dit.dit_out_proj_gated_mxfp4(z(to["attn_out"]), wo, wos, to["gate"], z(to["gate_index"]), res_bf, out=res_bf,
+                                 act_codes=ac[:0], act_scales=mx_sc[:0])
+    dit.dit_mx_quant_fp4(z(to["attn_out"]), codes=ac[:0], scales=mx_sc[:0])
+    torch.cuda.synchronize()
+    for b0, b1 in zip(before, [out_b, out_e, ws, mx_sc, res, ac]):
+        assert torch.equal(b0, b1), "an M = 0 call wrote to its buffers"
+    with pytest.raises(dit.DitError) as err:
+        dit.dit_mlp_fp8(z(t["x"]), t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], z(t["adaln_index"]),
+                        t["adaln_scale"], z(t["x"]),
+                        torch.zeros((synth.FC1_ROWS, H), dtype=torch.float8_e4m3fn, device="cuda"),
+                        torch.ones((synth.FC1_ROWS,), dtype=torch.float32, device="cuda"),
+                        torch.zeros((H, synth.INTER), dtype=torch.float8_e4m3fn, device="cuda"),
+                        torch.ones((H,), dtype=torch.float32, device="cuda"))
+    assert err.value.status == 2, err.value.status          # DIT_ERR_SHAPE: M below the range
 
 
 @pytest.mark.parametrize("P", [2, 4, 8])
