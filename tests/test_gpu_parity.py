@@ -352,6 +352,59 @@ def test_every_entry_point_treats_M_zero_as_a_no_op():
     assert err.value.status == 2, err.value.status          # DIT_ERR_SHAPE: M below the range
 
 
+def test_large_M_tiles_equal_their_repeated_4096_row_block():
+    """Byte offsets far past 2^32: the pre-attention at M = 2^20 (out 45 GB) and the
+    out-projection at M = 2^19 (out 5.6 GB), with inputs built by repeating a 4096-row block.
+    Every 256-row tile then holds the same rows as a tile of the M = 4096 run, so sampled
+    tiles (the first, those holding the 2^32- and 2^33-byte offsets of out, one in the middle
+    and the last) must equal that run bit for bit; the M = 4096 runs themselves are held to the
+    oracle (configs 1 and 3 tests)."""
+    B = 4096
+    d = synth.pre_attn_inputs(B, seed=21, rows=2, S=B, positions="random", weight=_shared_weight())
+    t = synth.to_torch("pre_attn", d)
+    ws0 = torch.empty((B, H), dtype=torch.bfloat16, device="cuda")
+    out0 = torch.empty((1, B, 56, 3, 128), dtype=torch.bfloat16, device="cuda")
+    args = (t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"])
+    rest = (t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"])
+    _dit().dit_pre_attn_bf16(t["x"], *args, t["adaln_index"], *rest, ulysses_degree=1, out=out0, eps=t["eps"],
+                             qk_eps=t["qk_eps"], rope_positions=t["rope_positions"], workspace=ws0)
+    M = 1 << 20
+    reps = M // B
+    _say(f"pre_attn M={M} from a repeated {B}-row block (out {M * 56 * 3 * 128 * 2 / 2**30:.0f} GiB)")
+    xb = t["x"].repeat(reps, 1)
+    wsb = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    outb = torch.empty((1, M, 56, 3, 128), dtype=torch.bfloat16, device="cuda")
+    _dit().dit_pre_attn_bf16(xb, *args, t["adaln_index"].repeat(reps), *rest, ulysses_degree=1, out=outb,
+                             eps=t["eps"], qk_eps=t["qk_eps"], rope_positions=t["rope_positions"].repeat(reps),
+                             workspace=wsb)
+    torch.cuda.synchronize()
+    row_bytes = 56 * 3 * 128 * 2
+    tiles = sorted({0, (1 << 32) // row_bytes // 256, (1 << 33) // row_bytes // 256, M // 512, M // 256 - 1})
+    for ti in tiles:
+        r0, b0 = ti * 256, (ti * 256) % B
+        assert torch.equal(outb[0, r0:r0 + 256].view(torch.int16), out0[0, b0:b0 + 256].view(torch.int16)), ti
+        assert torch.equal(wsb[r0:r0 + 256].view(torch.int16), ws0[b0:b0 + 256].view(torch.int16)), ti
+    del xb, wsb, outb
+    torch.cuda.empty_cache()
+
+    o = synth.out_proj_inputs(B, seed=22)
+    to = synth.to_torch("out_proj", o)
+    out0 = _dit().dit_out_proj_gated_bf16(to["attn_out"], to["o_weight"], to["gate"], to["gate_index"],
+                                          to["residual"])
+    M = 1 << 19
+    reps = M // B
+    _say(f"out_proj M={M} from a repeated {B}-row block")
+    outb = _dit().dit_out_proj_gated_bf16(to["attn_out"].repeat(reps, 1), to["o_weight"], to["gate"],
+                                          to["gate_index"].repeat(reps), to["residual"].repeat(reps, 1))
+    torch.cuda.synchronize()
+    tiles = sorted({0, (1 << 32) // (H * 2) // 256, M // 512, M // 256 - 1})
+    for ti in tiles:
+        r0, b0 = ti * 256, (ti * 256) % B
+        assert torch.equal(outb[r0:r0 + 256].view(torch.int16), out0[b0:b0 + 256].view(torch.int16)), ti
+    del outb
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("P", [2, 4, 8])
 def test_pre_attn_ulysses_pack_is_the_degree_one_output_repacked(P):
     """P destinations: the same values as P = 1, bit for bit, in the destination-major layout
