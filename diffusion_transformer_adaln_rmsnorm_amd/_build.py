@@ -12,7 +12,8 @@ LIB = os.path.join(PKG, "libdit.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.cpp", "norm_adaln.hip", "pre_attn.hip", "out_proj.hip", "mlp.hip", "mx.hip", "noalloc.hip", "qkv_small.hip"]
+SOURCES = ["api.cpp", "norm_adaln.hip", "pre_attn.hip", "out_proj.hip", "mlp.hip", "mx.hip", "noalloc.hip", "qkv_small.hip",
+           "queue.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I" + os.path.join(ROOT, "include")]

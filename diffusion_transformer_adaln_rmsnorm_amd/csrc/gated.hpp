@@ -31,7 +31,7 @@ struct GatedResidual {
     // index[m] of this thread's rows, checked against [0, gate_rows) at full width and kept
     // as a 32-bit row or -1 (rows past M read index 0: their stores are dropped)
     __device__ __forceinline__ void load_index(const Idx* index, int64_t m0, int64_t M, int64_t gate_rows) {
-        const int rsub = threadIdx.x >> 5;
+        const int rsub = opaque_tid() >> 5;
         const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
         const __amdgpu_buffer_rsrc_t ri = make_rsrc(index + m0, (uint32_t)(tile_rows * sizeof(Idx)));
 #pragma unroll
@@ -51,7 +51,7 @@ struct GatedResidual {
     // are staged, so their latency hides behind the staging; FC2's row and column scales leave
     // no registers for that, and it requests them after)
     __device__ __forceinline__ void load_residual(int64_t m0, int64_t M, int n0, const uint16_t* residual) {
-        const int t = threadIdx.x;
+        const int t = opaque_tid();
         const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
         const __amdgpu_buffer_rsrc_t rres = make_rsrc(residual + m0 * kHidden, (uint32_t)(tile_rows * kHidden * 2));
         const uint32_t o1 = (uint32_t)(((t >> 5) * kHidden + n0 + (t & 31) * 8) * 2);
@@ -69,7 +69,7 @@ struct GatedResidual {
     // With the residual chunks requested: out = bf16(r + bf16(g * o)).
     __device__ __forceinline__ void finish(const uint8_t* smem, int64_t m0, int64_t M, int n0, const uint16_t* gate,
                                            int64_t gate_rows, int64_t gate_ld, uint16_t* out) const {
-        const int t = threadIdx.x;
+        const int t = opaque_tid();
         const int c8 = (t & 31) * 8;
         const int rsub = t >> 5;
         const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;

@@ -69,15 +69,8 @@ enum class Mma { kBf16, kE4m3, kMxFp4 };
 // row l % 32 and block l / 32 of a 32 x 64 operand from lane l; register I of the four holds
 // the 32-row block I, byte q the stage's k-step q.
 
-// Workgroup id -> (m tile, n tile).  Workgroups are dispatched round-robin over the 8 XCDs,
-// so id % 8 names the XCD: each XCD gets one contiguous range of the logical order, and the
-// logical order walks groups of 4 m-tiles across all n-tiles (m fastest), so the ~32 tiles
-// an XCD runs at once share 4 A panels and 8 B panels in its L2.
-__device__ __forceinline__ void tile_coords(int bid, int mt, int nt, int& tm, int& tn) {
-    const int G = mt * nt;
-    const int xcd = bid & 7, idx = bid >> 3;
-    const int per = G >> 3, rem = G & 7;
-    const int L = xcd * per + (xcd < rem ? xcd : rem) + idx;
+// Logical tile order -> (m tile, n tile): groups of 4 m-tiles across all n-tiles, m fastest.
+__device__ __forceinline__ void logical_coords(int L, int mt, int nt, int& tm, int& tn) {
     constexpr int GM = 4;
     const int group = L / (GM * nt);
     const int first_m = group * GM;
@@ -87,7 +80,65 @@ __device__ __forceinline__ void tile_coords(int bid, int mt, int nt, int& tm, in
     tn = in / gsize;
 }
 
+// Workgroup id -> (m tile, n tile) for a launch of one workgroup per tile.  Workgroups are
+// dispatched round-robin over the 8 XCDs, so id % 8 names the XCD: each XCD gets one contiguous
+// range of the logical order, and the ~32 tiles an XCD runs at once share 4 A panels and 8 B
+// panels in its L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_range(int xcd, int G, int& lo, int& cnt) {
+    const int per = G / kXcds, rem = G % kXcds;
+    lo = xcd * per + (xcd < rem ? xcd : rem);
+    cnt = per + (xcd < rem ? 1 : 0);
+}
+__device__ __forceinline__ void tile_coords(int bid, int mt, int nt, int& tm, int& tn) {
+    int lo, cnt;
+    xcd_range(bid % kXcds, mt * nt, lo, cnt);
+    logical_coords(lo + bid / kXcds, mt, nt, tm, tn);
+}
+
+// Persistent launches: one workgroup per CU, which runs tile after tile.  Workgroup b runs on
+// XCD b % 8 (the dispatcher's round robin), and the workgroups of an XCD claim the tiles of the
+// same contiguous range of the logical order as above one at a time, from a counter of that
+// XCD: a tile keeps its place in the order (and the L2 window with it), and the CUs of an XCD
+// balance their work among themselves.  The counters (one per XCD, zero when the launch
+// starts) are claimed by one lane with a global atomic add; the index reaches the other waves
+// through an LDS word just past the staged epilogue tile, which no main loop or epilogue holds
+// at the two points it is used: after the main loop (claim) and after the epilogue's closing
+// barrier (read).
+struct TileQueue {
+    uint32_t* ctr;     // this XCD's counter
+    int lo, cnt;       // this XCD's range of the logical order
+    __device__ __forceinline__ TileQueue(uint32_t* counters, int mt, int nt) {
+        const int xcd = blockIdx.x % kXcds;
+        ctr = counters + xcd;
+        xcd_range(xcd, mt * nt, lo, cnt);
+    }
+    static __device__ __forceinline__ uint32_t* slot(uint8_t* smem) {
+        return reinterpret_cast<uint32_t*>(smem + kEpiBytes);
+    }
+    // thread 0 claims the next index (the caller's LDS use must leave the slot free)
+    __device__ __forceinline__ void claim(uint8_t* smem) const {
+        if (threadIdx.x == 0) *slot(smem) = atomicAdd(ctr, 1u);
+    }
+    // the index claimed last, after a barrier that follows claim()
+    __device__ __forceinline__ int claimed(uint8_t* smem) const {
+        return __builtin_amdgcn_readfirstlane((int)*slot(smem));
+    }
+};
+static_assert(kSmemBytes >= kEpiBytes + 4, "tile queue slot");
+
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// threadIdx.x through an empty volatile asm.  The persistent kernels run the same main loop and
+// epilogue tile after tile; per-lane setup computed from a plain threadIdx.x would be hoisted out
+// of that loop and kept live across it, and the registers it holds pushed the epilogues into
+// spilling.  A volatile asm is never moved out of the loop, so what derives from its value is
+// recomputed per tile, where it is used.
+__device__ __forceinline__ int opaque_tid() {
+    int t = (int)threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
 
 // Raw buffer descriptor over [base, base + bytes): loads at offsets >= bytes return zeros and
 // stores there are dropped (the check covers the per-lane offset, not the scalar one).
@@ -145,11 +196,16 @@ struct AccMx {
 //         lanes of a group hit 16 distinct bank groups (contiguous chunks 2 g, 2 g + 1 would
 //         put two lane groups of a read on the same banks).
 // swz has period 16 rows, so one offset serves every block of a wave (blocks are immediates).
+// A and B rows of a lane differ only by the wave's row bases, so the B offsets are the A offsets
+// plus a wave-uniform difference (bdelta, a scalar added to the B slot's base).
 constexpr int kBlk = 16 * kRowB;                // bytes between 16-row blocks
 struct FragAddr {
-    uint32_t a[2], b[2];
+    uint32_t a[2];
+    int bdelta;
     __device__ __forceinline__ void init() {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int tid = opaque_tid();
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int wm = wave / kWN, wn = wave % kWN;
         const int r = lane % 16, g = lane / 16;
         const int sw = swz(r);
@@ -157,8 +213,8 @@ struct FragAddr {
         for (int q = 0; q < 2; ++q) {
             const int c = 4 * q + g;
             a[q] = (uint32_t)((wm * 128 + r) * kRowB + ((c ^ sw) << 4));
-            b[q] = (uint32_t)((wn * kWaveN + r) * kRowB + ((c ^ sw) << 4));
         }
+        bdelta = (wn * kWaveN - wm * 128) * kRowB;
     }
 };
 
@@ -166,9 +222,12 @@ struct FragAddr {
 // 2 q + l / 32 (32 E2M1 values).  The 16 lanes of a read quarter sit on 16 consecutive rows of
 // one chunk, so the swizzle keeps them on 16 distinct bank groups.
 struct FragAddrMx {
-    uint32_t a[4], b[4];
+    uint32_t a[4];
+    int bdelta;
     __device__ __forceinline__ void init() {
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const int tid = opaque_tid();
+        const int lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int wm = wave / kWN, wn = wave % kWN;
         const int r = lane % 32, h = lane / 32;
         const int sw = swz(r);
@@ -176,8 +235,8 @@ struct FragAddrMx {
         for (int q = 0; q < 4; ++q) {
             const int c = 2 * q + h;
             a[q] = (uint32_t)((wm * 128 + r) * kRowB + ((c ^ sw) << 4));
-            b[q] = (uint32_t)((wn * kWaveN + r) * kRowB + ((c ^ sw) << 4));
         }
+        bdelta = (wn * kWaveN - wm * 128) * kRowB;
     }
 };
 
@@ -224,7 +283,7 @@ struct PPFrags<Mma::kBf16> {
 #pragma unroll
             for (int i = 0; i < MB; ++i) a[ks][i] = lds_bf16x8(st.a, fa.a[ks] + i * kBlk);
 #pragma unroll
-            for (int j = 0; j < NB; ++j) b[ks][j] = lds_bf16x8(st.b, fa.b[ks] + j * kBlk);
+            for (int j = 0; j < NB; ++j) b[ks][j] = lds_bf16x8(st.b + fa.bdelta, fa.a[ks] + j * kBlk);
         }
     }
     __device__ __forceinline__ void mma(Acc& acc) const {
@@ -245,7 +304,7 @@ struct PPFrags<Mma::kE4m3> {
 #pragma unroll
         for (int i = 0; i < MB; ++i) a[i] = lds_i32x8(st.a, fa.a[0] + i * kBlk, fa.a[1] + i * kBlk);
 #pragma unroll
-        for (int j = 0; j < NB; ++j) b[j] = lds_i32x8(st.b, fa.b[0] + j * kBlk, fa.b[1] + j * kBlk);
+        for (int j = 0; j < NB; ++j) b[j] = lds_i32x8(st.b + fa.bdelta, fa.a[0] + j * kBlk, fa.a[1] + j * kBlk);
     }
     __device__ __forceinline__ void mma(Acc& acc) const {
 #pragma unroll
@@ -270,7 +329,8 @@ struct PPFrags<Mma::kMxFp4> {
 #pragma unroll
             for (int i = 0; i < MB; ++i) a[q][i] = __builtin_bit_cast(i32x4, lds_ld16(st.a, fa.a[q] + i * 2 * kBlk));
 #pragma unroll
-            for (int j = 0; j < NB; ++j) b[q][j] = __builtin_bit_cast(i32x4, lds_ld16(st.b, fa.b[q] + j * 2 * kBlk));
+            for (int j = 0; j < NB; ++j)
+                b[q][j] = __builtin_bit_cast(i32x4, lds_ld16(st.b + fa.bdelta, fa.a[q] + j * 2 * kBlk));
         }
     }
     __device__ __forceinline__ void mma(AccMx& acc) const {
@@ -428,8 +488,9 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     constexpr bool kMx = kKind == Mma::kMxFp4;
     constexpr int kFills = 2 * kPPAPieces;          // fill loads per wave and memory phase
     constexpr int kScl = kMx ? 2 : 0;               // scale loads per wave, after its MFMAs
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wave
+    const int tid = opaque_tid();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const bool g0 = wave < 4;
     PPFill sf;
     const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
@@ -542,7 +603,8 @@ __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t 
 // Must follow a barrier that ends all LDS reads of the main loop.
 __device__ __forceinline__ void stage_tile_bf16(const Acc& acc, uint8_t* smem, const float* rowscale, int64_t m0,
                                                 int64_t M, const float* colscale_lo, const float* colscale_hi) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = opaque_tid();
+    const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / kWN, wn = wave % kWN;
     const int col_in = lane % 16, row_in = (lane / 16) * 4;
     const int odd = lane & 1;
@@ -603,7 +665,8 @@ __device__ __forceinline__ void stage_tile_bf16(const Acc& acc, uint8_t* smem, c
 // r and r + 1 (r even) of a block again hold rows R and R + 1 of one column, so the lane-pair
 // swap is the same.
 __device__ __forceinline__ void stage_tile_bf16(const AccMx& acc, uint8_t* smem) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int tid = opaque_tid();
+    const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave / kWN, wn = wave % kWN;
     const int col_in = lane % 32, row_in = (lane / 32) * 4;
     const int odd = lane & 1;

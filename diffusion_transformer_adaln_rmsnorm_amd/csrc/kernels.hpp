@@ -7,6 +7,10 @@
 
 namespace dit {
 
+// A zeroed set of per-XCD tile counters for one persistent GEMM launch on `stream` (a small
+// kernel that zeroes it is enqueued first), and the persistent grid of the current device.
+hipError_t tile_queue(hipStream_t stream, uint32_t** counters, int* grid);
+
 hipError_t launch_norm_adaln_bf16(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,
                                   int64_t ld_scale, const uint16_t* shift, int64_t ld_shift, int64_t rows,
                                   const int64_t* idx, float eps, uint16_t* ws, hipStream_t stream);

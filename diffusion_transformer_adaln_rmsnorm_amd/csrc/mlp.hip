@@ -23,21 +23,16 @@ namespace dit {
 
 using namespace gemm;
 
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
-void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale, int64_t M,
-                  const uint8_t* __restrict__ W1, const float* __restrict__ w1s, uint16_t* __restrict__ y,
-                  float* __restrict__ y_amax, int mt, int nt) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    int tm, tn;
-    tile_coords(blockIdx.x, mt, nt, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM;
-    const int j0 = tn * 128;
-    Acc acc;
-    mainloop<Mma::kE4m3>(a_q, kHidden, m0, M, W1, kHidden, j0, kInter + j0, kHidden / kRowB, smem, acc);
+// FC1 epilogue of one tile (rows m0.., gate columns j0.. and up columns kInter + j0..):
+// h = bf16((acc * a_scale[row]) * w1s[col]) staged in LDS, then y = bf16(bf16(silu(h_gate)) *
+// h_up) stored and the row maxima of |y| folded into y_amax.
+__device__ __forceinline__ void fc1_epilogue(const Acc& acc, uint8_t* smem, int64_t m0, int64_t M, int j0,
+                                             const float* __restrict__ a_scale, const float* __restrict__ w1s,
+                                             uint16_t* __restrict__ y, float* __restrict__ y_amax) {
     stage_tile_bf16(acc, smem, a_scale, m0, M, w1s + j0, w1s + kInter + j0);
     lds_barrier();
 
-    const int t = threadIdx.x;
+    const int t = opaque_tid();
     const int c8 = (t & 15) * 8;
     const int rsub = t >> 4;            // 0..kThreads/16-1
     constexpr int kRowsPerPass = kThreads / 16;
@@ -64,6 +59,27 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
         buf_st16(ry, o1 + it * kPassB, yv);
         if ((t & 15) == 0 && row < (int)tile_rows)
             atomicMax(reinterpret_cast<unsigned int*>(y_amax + m0 + row), __float_as_uint(amax));
+    }
+}
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_scale, int64_t M,
+                  const uint8_t* __restrict__ W1, const float* __restrict__ w1s, uint16_t* __restrict__ y,
+                  float* __restrict__ y_amax, int mt, int nt, uint32_t* tq_ctr) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    const TileQueue tq(tq_ctr, mt, nt);
+    tq.claim(smem);
+    __syncthreads();
+    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+        int tm, tn;
+        logical_coords(tq.lo + k, mt, nt, tm, tn);
+        const int64_t m0 = (int64_t)tm * kBM;
+        const int j0 = tn * 128;
+        Acc acc;
+        mainloop<Mma::kE4m3>(a_q, kHidden, m0, M, W1, kHidden, j0, kInter + j0, kHidden / kRowB, smem, acc);
+        tq.claim(smem);
+        fc1_epilogue(acc, smem, m0, M, j0, a_scale, w1s, y, y_amax);
+        __syncthreads();
     }
 }
 
@@ -105,27 +121,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_scale, int64_t M,
                  const uint8_t* __restrict__ W2, const float* __restrict__ w2s, const uint16_t* __restrict__ gate,
                  int64_t gate_rows, int64_t gate_ld, const int64_t* __restrict__ idx, const uint16_t* residual,
-                 uint16_t* out, int mt, int nt) {
+                 uint16_t* out, int mt, int nt, uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    int tm, tn;
-    tile_coords(blockIdx.x, mt, nt, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM;
-    const int n0 = tn * kBN;
-    Acc acc;
-    mainloop<Mma::kE4m3>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc);
-    GatedResidual<int64_t> gr;
-    gr.load_index(idx, m0, M, gate_rows);
-    stage_tile_bf16(acc, smem, y_scale, m0, M, w2s + n0, w2s + n0 + 128);
-    lds_barrier();
-    gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);
+    const TileQueue tq(tq_ctr, mt, nt);
+    tq.claim(smem);
+    __syncthreads();
+    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+        int tm, tn;
+        logical_coords(tq.lo + k, mt, nt, tm, tn);
+        const int64_t m0 = (int64_t)tm * kBM;
+        const int n0 = tn * kBN;
+        Acc acc;
+        mainloop<Mma::kE4m3>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc);
+        tq.claim(smem);
+        GatedResidual<int64_t> gr;
+        gr.load_index(idx, m0, M, gate_rows);
+        stage_tile_bf16(acc, smem, y_scale, m0, M, w2s + n0, w2s + n0 + 128);
+        lds_barrier();
+        gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);
+        __syncthreads();
+    }
 }
 
 hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M, const uint8_t* W1,
                              const float* w1s, uint16_t* y, float* y_amax, hipStream_t stream) {
     const int mt = (int)((M + kBM - 1) / kBM);
     const int nt = kInter / 128;
-    hipLaunchKernelGGL(k_fc1_swiglu, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, a_q, a_scale, M, W1, w1s,
-                       y, y_amax, mt, nt);
+    uint32_t* q = nullptr;
+    int grid = 0;
+    const hipError_t e = tile_queue(stream, &q, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_fc1_swiglu, dim3((unsigned)grid), dim3(kThreads), 0, stream, a_q, a_scale, M, W1, w1s, y,
+                       y_amax, mt, nt, q);
     return hipGetLastError();
 }
 
@@ -140,8 +167,12 @@ hipError_t launch_fc2_gated(const uint8_t* y_q, const float* y_scale, int64_t M,
                             const int64_t* idx, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
     const int mt = (int)((M + kBM - 1) / kBM);
     const int nt = kHidden / kBN;
-    hipLaunchKernelGGL(k_fc2_gated, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, y_q, y_scale, M, W2, w2s,
-                       gate, gate_rows, gate_ld, idx, residual, out, mt, nt);
+    uint32_t* q = nullptr;
+    int grid = 0;
+    const hipError_t e = tile_queue(stream, &q, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_fc2_gated, dim3((unsigned)grid), dim3(kThreads), 0, stream, y_q, y_scale, M, W2, w2s, gate,
+                       gate_rows, gate_ld, idx, residual, out, mt, nt, q);
     return hipGetLastError();
 }
 

@@ -61,27 +61,34 @@ void k_out_proj_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __rest
                       int64_t M, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
                       uint32_t w_sbytes, const uint16_t* __restrict__ gate, int64_t gate_rows, int64_t gate_ld,
                       const int32_t* __restrict__ gate_index, const uint16_t* residual, uint16_t* out, int mt,
-                      int nt) {
+                      int nt, uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    int tm, tn;
-    tile_coords(blockIdx.x, mt, nt, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM;
-    const int n0 = tn * kBN;
-    AccMx acc;
     MxScales mxs;
     mxs.a = a_scales;
     mxs.a_bytes = a_sbytes;
     mxs.b = w_scales;
     mxs.b_bytes = w_sbytes;
     constexpr int kRowBytes = kAttnWidth / 2;
-    mainloop<Mma::kMxFp4>(a_codes, kRowBytes, m0, M, w_codes, kRowBytes, n0, n0 + 128, kRowBytes / kRowB, smem, acc,
-                          mxs);
-    GatedResidual<int32_t> gr;
-    gr.load_index(gate_index, m0, M, gate_rows);
-    gr.load_residual(m0, M, n0, residual);
-    stage_tile_bf16(acc, smem);
-    lds_barrier();
-    gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
+    const TileQueue tq(tq_ctr, mt, nt);
+    tq.claim(smem);
+    __syncthreads();
+    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+        int tm, tn;
+        logical_coords(tq.lo + k, mt, nt, tm, tn);
+        const int64_t m0 = (int64_t)tm * kBM;
+        const int n0 = tn * kBN;
+        AccMx acc;
+        mainloop<Mma::kMxFp4>(a_codes, kRowBytes, m0, M, w_codes, kRowBytes, n0, n0 + 128, kRowBytes / kRowB, smem,
+                              acc, mxs);
+        tq.claim(smem);
+        GatedResidual<int32_t> gr;
+        gr.load_index(gate_index, m0, M, gate_rows);
+        gr.load_residual(m0, M, n0, residual);
+        stage_tile_bf16(acc, smem);
+        lds_barrier();
+        gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
+        __syncthreads();
+    }
 }
 
 int64_t mx_scale_bytes(int64_t rows, int64_t K) { return (rows + 127) / 128 * 128 * (K / 32); }
@@ -103,8 +110,12 @@ hipError_t launch_out_proj_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales
     const int nt = kHidden / kBN;
     const uint32_t a_sb = (uint32_t)mx_scale_bytes(M, kAttnWidth);
     const uint32_t w_sb = (uint32_t)mx_scale_bytes(kHidden, kAttnWidth);
-    hipLaunchKernelGGL(k_out_proj_mxfp4, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, a_codes, a_scales, a_sb,
-                       M, w_codes, w_scales, w_sb, gate, gate_rows, gate_ld, gate_index, residual, out, mt, nt);
+    uint32_t* q = nullptr;
+    int grid = 0;
+    const hipError_t e = tile_queue(stream, &q, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_out_proj_mxfp4, dim3((unsigned)grid), dim3(kThreads), 0, stream, a_codes, a_scales, a_sb, M,
+                       w_codes, w_scales, w_sb, gate, gate_rows, gate_ld, gate_index, residual, out, mt, nt, q);
     return hipGetLastError();
 }
 

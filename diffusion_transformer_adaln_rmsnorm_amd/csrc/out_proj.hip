@@ -20,22 +20,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves
 void k_out_proj_gemm(const uint16_t* __restrict__ attn, int64_t M, const uint16_t* __restrict__ Wo,
                      const uint16_t* __restrict__ gate, int64_t gate_rows, int64_t gate_ld,
                      const int32_t* __restrict__ gate_index, const uint16_t* residual, uint16_t* out, int mt,
-                     int nt) {
+                     int nt, uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    int tm, tn;
-    tile_coords(blockIdx.x, mt, nt, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM;
-    const int n0 = tn * kBN;
-    Acc acc;
-    mainloop<Mma::kBf16>(reinterpret_cast<const uint8_t*>(attn), kAttnWidth * 2, m0, M,
-                    reinterpret_cast<const uint8_t*>(Wo), kAttnWidth * 2, n0, n0 + 128, kAttnWidth * 2 / kRowB, smem,
-                    acc);
-    GatedResidual<int32_t> gr;
-    gr.load_index(gate_index, m0, M, gate_rows);
-    gr.load_residual(m0, M, n0, residual);
-    stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
-    lds_barrier();
-    gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
+    const TileQueue tq(tq_ctr, mt, nt);
+    tq.claim(smem);
+    __syncthreads();
+    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+        int tm, tn;
+        logical_coords(tq.lo + k, mt, nt, tm, tn);
+        const int64_t m0 = (int64_t)tm * kBM;
+        const int n0 = tn * kBN;
+        Acc acc;
+        mainloop<Mma::kBf16>(reinterpret_cast<const uint8_t*>(attn), kAttnWidth * 2, m0, M,
+                             reinterpret_cast<const uint8_t*>(Wo), kAttnWidth * 2, n0, n0 + 128,
+                             kAttnWidth * 2 / kRowB, smem, acc);
+        tq.claim(smem);
+        GatedResidual<int32_t> gr;
+        gr.load_index(gate_index, m0, M, gate_rows);
+        gr.load_residual(m0, M, n0, residual);
+        stage_tile_bf16(acc, smem, nullptr, m0, M, nullptr, nullptr);
+        lds_barrier();
+        gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
+        __syncthreads();
+    }
 }
 
 hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t* Wo, const uint16_t* gate,
@@ -43,8 +50,12 @@ hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t*
                                 const uint16_t* residual, uint16_t* out, hipStream_t stream) {
     const int mt = (int)((M + kBM - 1) / kBM);
     const int nt = kHidden / kBN;
-    hipLaunchKernelGGL(k_out_proj_gemm, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, attn, M, Wo, gate,
-                       gate_rows, gate_ld, gate_index, residual, out, mt, nt);
+    uint32_t* q = nullptr;
+    int grid = 0;
+    const hipError_t e = tile_queue(stream, &q, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_out_proj_gemm, dim3((unsigned)grid), dim3(kThreads), 0, stream, attn, M, Wo, gate, gate_rows,
+                       gate_ld, gate_index, residual, out, mt, nt, q);
     return hipGetLastError();
 }
 

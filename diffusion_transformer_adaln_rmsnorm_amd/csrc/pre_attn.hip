@@ -58,7 +58,7 @@ __device__ __forceinline__ void qkv_epilogue(AccT& acc, uint8_t* smem, int64_t m
                                              const uint16_t* __restrict__ cs, int64_t S,
                                              const int64_t* __restrict__ pos, float qk_eps, int hpd, float dq,
                                              float dk, float dv, void* __restrict__ out) {
-    const int t = threadIdx.x;
+    const int t = opaque_tid();
     const int li = t & 15;              // lane within the (row, head) group
     // 8-dim chunk of the head held by this lane (partner chunk q +/- 6 sits at lane li ^ 8)
     const int q = chunk_of_lane(li);
@@ -158,21 +158,30 @@ __device__ __forceinline__ void qkv_epilogue(AccT& acc, uint8_t* smem, int64_t m
 
 // kE4m3: out holds e4m3 codes (one byte per element) of the bf16 results divided by the
 // descale of their kind (dq, dk, dv); else bf16 values (the descales are unused).
+// Persistent: tiles are claimed from the queue tq (see TileQueue).
 template <bool kE4m3>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __restrict__ W,
                 const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
                 const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
-                int hpd, float dq, float dk, float dv, void* __restrict__ out, int mt, int nt) {
+                int hpd, float dq, float dk, float dv, void* __restrict__ out, int mt, int nt, uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    int tm, tn;
-    tile_coords(blockIdx.x, mt, nt, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM;
-    const int n0 = tn * kBN;
-    Acc acc;
-    mainloop<Mma::kBf16>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M, reinterpret_cast<const uint8_t*>(W),
-                    kHidden * 2, n0, n0 + 128, kHidden * 2 / kRowB, smem, acc);
-    qkv_epilogue<kE4m3>(acc, smem, m0, M, n0, qw, kw, cs, S, pos, qk_eps, hpd, dq, dk, dv, out);
+    const TileQueue tq(tq_ctr, mt, nt);
+    tq.claim(smem);
+    __syncthreads();
+    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+        int tm, tn;
+        logical_coords(tq.lo + k, mt, nt, tm, tn);
+        const int64_t m0 = (int64_t)tm * kBM;
+        const int n0 = tn * kBN;
+        Acc acc;
+        mainloop<Mma::kBf16>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M,
+                             reinterpret_cast<const uint8_t*>(W), kHidden * 2, n0, n0 + 128, kHidden * 2 / kRowB,
+                             smem, acc);
+        tq.claim(smem);
+        qkv_epilogue<kE4m3>(acc, smem, m0, M, n0, qw, kw, cs, S, pos, qk_eps, hpd, dq, dk, dv, out);
+        __syncthreads();
+    }
 }
 
 // The same tile on MXFP4 operands: the workspace's and the weight's E2M1 codes ([M, 2688],
@@ -182,22 +191,29 @@ void k_qkv_gemm_mxfp4(const uint8_t* __restrict__ ws_codes, const uint8_t* __res
                       int64_t M, const uint8_t* __restrict__ w_codes, const uint8_t* __restrict__ w_scales,
                       uint32_t w_sbytes, const uint16_t* __restrict__ qw, const uint16_t* __restrict__ kw,
                       const uint16_t* __restrict__ cs, int64_t S, const int64_t* __restrict__ pos, float qk_eps,
-                      int hpd, void* __restrict__ out, int mt, int nt) {
+                      int hpd, void* __restrict__ out, int mt, int nt, uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-    int tm, tn;
-    tile_coords(blockIdx.x, mt, nt, tm, tn);
-    const int64_t m0 = (int64_t)tm * kBM;
-    const int n0 = tn * kBN;
-    AccMx acc;
     MxScales mxs;
     mxs.a = ws_scales;
     mxs.a_bytes = ws_sbytes;
     mxs.b = w_scales;
     mxs.b_bytes = w_sbytes;
     constexpr int kRowBytes = kHidden / 2;
-    mainloop<Mma::kMxFp4>(ws_codes, kRowBytes, m0, M, w_codes, kRowBytes, n0, n0 + 128, kRowBytes / kRowB, smem, acc,
-                          mxs);
-    qkv_epilogue<false>(acc, smem, m0, M, n0, qw, kw, cs, S, pos, qk_eps, hpd, 1.0f, 1.0f, 1.0f, out);
+    const TileQueue tq(tq_ctr, mt, nt);
+    tq.claim(smem);
+    __syncthreads();
+    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+        int tm, tn;
+        logical_coords(tq.lo + k, mt, nt, tm, tn);
+        const int64_t m0 = (int64_t)tm * kBM;
+        const int n0 = tn * kBN;
+        AccMx acc;
+        mainloop<Mma::kMxFp4>(ws_codes, kRowBytes, m0, M, w_codes, kRowBytes, n0, n0 + 128, kRowBytes / kRowB, smem,
+                              acc, mxs);
+        tq.claim(smem);
+        qkv_epilogue<false>(acc, smem, m0, M, n0, qw, kw, cs, S, pos, qk_eps, hpd, 1.0f, 1.0f, 1.0f, out);
+        __syncthreads();
+    }
 }
 
 hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, const uint16_t* qw,
@@ -207,8 +223,12 @@ hipError_t launch_qkv_gemm(const uint16_t* ws, int64_t M, const uint16_t* W, con
     if (M <= 16) return launch_qkv_small(ws, M, W, qw, kw, cs, S, pos, qk_eps, P, out, stream);
     const int mt = (int)((M + kBM - 1) / kBM);
     const int nt = kQkvRows / kBN;
-    hipLaunchKernelGGL(k_qkv_gemm<false>, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs,
-                       S, pos, qk_eps, kHeads / P, 1.0f, 1.0f, 1.0f, out, mt, nt);
+    uint32_t* q = nullptr;
+    int grid = 0;
+    const hipError_t e = tile_queue(stream, &q, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_qkv_gemm<false>, dim3((unsigned)grid), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs, S,
+                       pos, qk_eps, kHeads / P, 1.0f, 1.0f, 1.0f, out, mt, nt, q);
     return hipGetLastError();
 }
 
@@ -220,8 +240,12 @@ hipError_t launch_qkv_gemm_mxfp4(const uint8_t* ws_codes, const uint8_t* ws_scal
     const int nt = kQkvRows / kBN;
     const uint32_t a_sb = (uint32_t)mx_scale_bytes(M, kHidden);
     const uint32_t w_sb = (uint32_t)mx_scale_bytes(kQkvRows, kHidden);
-    hipLaunchKernelGGL(k_qkv_gemm_mxfp4, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws_codes, ws_scales, a_sb,
-                       M, w_codes, w_scales, w_sb, qw, kw, cs, S, pos, qk_eps, kHeads / P, out, mt, nt);
+    uint32_t* q = nullptr;
+    int grid = 0;
+    const hipError_t e = tile_queue(stream, &q, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_qkv_gemm_mxfp4, dim3((unsigned)grid), dim3(kThreads), 0, stream, ws_codes, ws_scales, a_sb, M,
+                       w_codes, w_scales, w_sb, qw, kw, cs, S, pos, qk_eps, kHeads / P, out, mt, nt, q);
     return hipGetLastError();
 }
 
@@ -230,8 +254,12 @@ hipError_t launch_qkv_gemm_e4m3(const uint16_t* ws, int64_t M, const uint16_t* W
                                 float qk_eps, int P, float dq, float dk, float dv, uint8_t* out, hipStream_t stream) {
     const int mt = (int)((M + kBM - 1) / kBM);
     const int nt = kQkvRows / kBN;
-    hipLaunchKernelGGL(k_qkv_gemm<true>, dim3((unsigned)(mt * nt)), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs,
-                       S, pos, qk_eps, kHeads / P, dq, dk, dv, out, mt, nt);
+    uint32_t* q = nullptr;
+    int grid = 0;
+    const hipError_t e = tile_queue(stream, &q, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_qkv_gemm<true>, dim3((unsigned)grid), dim3(kThreads), 0, stream, ws, M, W, qw, kw, cs, S, pos,
+                       qk_eps, kHeads / P, dq, dk, dv, out, mt, nt, q);
     return hipGetLastError();
 }
 
