@@ -405,6 +405,84 @@ def test_large_M_tiles_equal_their_repeated_4096_row_block():
     torch.cuda.empty_cache()
 
 
+def test_persistent_gemms_on_two_streams_at_once():
+    """Each persistent GEMM launch takes its own set of tile counters: a pre-attention and an
+    out-projection enqueued on two streams without a sync between them (so that they may run
+    at the same time) give the same bits as the two run one after the other."""
+    dit = _dit()
+    d = synth.pre_attn_inputs(4096, seed=31, rows=2, S=4096, positions="random", weight=_shared_weight())
+    o = synth.out_proj_inputs(4096, seed=32)
+    t, to = synth.to_torch("pre_attn", d), synth.to_torch("out_proj", o)
+    outs = [torch.empty((1, 4096, 56, 3, 128), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    ws = [torch.empty((4096, H), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    po = [torch.empty((4096, H), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+
+    def pre(i):
+        dit.dit_pre_attn_bf16(t["x"], t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], t["adaln_index"],
+                              t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
+                              ulysses_degree=1, out=outs[i], eps=t["eps"], qk_eps=t["qk_eps"],
+                              rope_positions=t["rope_positions"], workspace=ws[i])
+
+    def oproj(i):
+        dit.dit_out_proj_gated_bf16(to["attn_out"], to["o_weight"], to["gate"], to["gate_index"], to["residual"],
+                                    out=po[i])
+
+    pre(0)
+    oproj(0)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        for b in outs[1:] + po[1:]:
+            b.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            pre(1)
+        with torch.cuda.stream(s2):
+            oproj(1)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[1].view(torch.int16), outs[0].view(torch.int16)), rep
+        assert torch.equal(po[1].view(torch.int16), po[0].view(torch.int16)), rep
+
+
+def test_persistent_gemm_replayed_from_a_captured_graph():
+    """The pre-attention (norm, counter zeroing, persistent QKV GEMM) captured in a HIP graph:
+    every replay, with eager work and synchronisations between replays, equals the eager run."""
+    dit = _dit()
+    d = synth.pre_attn_inputs(2048, seed=33, rows=2, S=2048, positions="random", weight=_shared_weight())
+    t = synth.to_torch("pre_attn", d)
+    out = torch.empty((1, 2048, 56, 3, 128), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty((2048, H), dtype=torch.bfloat16, device="cuda")
+
+    def pre():
+        dit.dit_pre_attn_bf16(t["x"], t["x_norm_weight"], t["adaln_scale"], t["adaln_shift"], t["adaln_index"],
+                              t["qkv_weight"], t["q_norm_weight"], t["k_norm_weight"], t["rope_cos_sin"],
+                              ulysses_degree=1, out=out, eps=t["eps"], qk_eps=t["qk_eps"],
+                              rope_positions=t["rope_positions"], workspace=ws)
+
+    pre()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        pre()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        pre()
+    for rep in range(4):
+        out.zero_()
+        ws.zero_()
+        pre() if rep == 2 else None             # eager work between replays
+        torch.cuda.synchronize()
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
+
+
 @pytest.mark.parametrize("P", [2, 4, 8])
 def test_pre_attn_ulysses_pack_is_the_degree_one_output_repacked(P):
     """P destinations: the same values as P = 1, bit for bit, in the destination-major layout
