@@ -104,14 +104,27 @@ __device__ __forceinline__ void tile_coords(int bid, int mt, int nt, int& tm, in
 // starts) are claimed by one lane with a global atomic add; the index reaches the other waves
 // through an LDS word just past the staged epilogue tile, which no main loop or epilogue holds
 // at the two points it is used: after the main loop (claim) and after the epilogue's closing
-// barrier (read).
+// barrier (read).  A counter set is kTileQueueWords words: the kXcds tile counters and a count
+// of finished workgroups.  The workgroup that finishes last puts the set back to zero for its
+// next launch (finish()): every other workgroup has made its last claim before it counted
+// itself finished.
+constexpr int kTileQueueWords = 16;
 struct TileQueue {
+    uint32_t* set;     // the launch's counter set
     uint32_t* ctr;     // this XCD's counter
     int lo, cnt;       // this XCD's range of the logical order
     __device__ __forceinline__ TileQueue(uint32_t* counters, int mt, int nt) {
         const int xcd = blockIdx.x % kXcds;
+        set = counters;
         ctr = counters + xcd;
         xcd_range(xcd, mt * nt, lo, cnt);
+    }
+    // after the workgroup's last claim: count it finished; the last one zeroes the set
+    __device__ __forceinline__ void finish() const {
+        if (threadIdx.x == 0 && atomicAdd(set + kXcds, 1u) == gridDim.x - 1) {
+#pragma unroll
+            for (int i = 0; i <= kXcds; ++i) __hip_atomic_store(set + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
     static __device__ __forceinline__ uint32_t* slot(uint8_t* smem) {
         return reinterpret_cast<uint32_t*>(smem + kEpiBytes);

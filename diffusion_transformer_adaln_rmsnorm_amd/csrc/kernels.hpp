@@ -7,8 +7,8 @@
 
 namespace dit {
 
-// A zeroed set of per-XCD tile counters for one persistent GEMM launch on `stream` (a small
-// kernel that zeroes it is enqueued first), and the persistent grid of the current device.
+// A zero set of per-XCD tile counters for one persistent GEMM launch on `stream` (the launch's
+// last workgroup leaves it zero again), and the persistent grid of the current device.
 hipError_t tile_queue(hipStream_t stream, uint32_t** counters, int* grid);
 
 hipError_t launch_norm_adaln_bf16(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,

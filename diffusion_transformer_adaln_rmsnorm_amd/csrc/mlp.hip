@@ -81,6 +81,7 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
         fc1_epilogue(acc, smem, m0, M, j0, a_scale, w1s, y, y_amax);
         __syncthreads();
     }
+    tq.finish();
 }
 
 // y quantisation: one wavefront per row; 14336 = 1792 chunks of 8, 28 per lane.
@@ -141,6 +142,7 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
         gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);
         __syncthreads();
     }
+    tq.finish();
 }
 
 hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M, const uint8_t* W1,

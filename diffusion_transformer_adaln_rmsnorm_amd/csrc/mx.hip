@@ -89,6 +89,7 @@ void k_out_proj_mxfp4(const uint8_t* __restrict__ a_codes, const uint8_t* __rest
         gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
         __syncthreads();
     }
+    tq.finish();
 }
 
 int64_t mx_scale_bytes(int64_t rows, int64_t K) { return (rows + 127) / 128 * 128 * (K / 32); }

@@ -43,6 +43,7 @@ void k_out_proj_gemm(const uint16_t* __restrict__ attn, int64_t M, const uint16_
         gr.finish(smem, m0, M, n0, gate, gate_rows, gate_ld, out);
         __syncthreads();
     }
+    tq.finish();
 }
 
 hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t* Wo, const uint16_t* gate,

@@ -1,11 +1,12 @@
 // Tile-queue counters of the persistent GEMM launches.
 //
-// Each persistent launch takes one set of per-XCD counters from a static device pool (a slot
-// per launch, in rotation) and enqueues a one-workgroup kernel that zeroes it, ahead of the GEMM
-// on the same stream.  A kernel, not a memset, so the pair can be captured in a HIP graph.
-// Launches that overlap in time get different slots as long as fewer than kQueueSlots of them
-// are in flight at once; the one case that shares a slot is two replays of the same captured
-// graph running at the same time (the slot is fixed at capture).
+// Each persistent launch takes one counter set from a static device pool (a set per launch,
+// in rotation).  A set starts at zero (the pool is zero when the module loads) and the last
+// workgroup of the launch that used it puts it back to zero when it finishes, so no kernel or
+// memset has to clear it and the launch can be captured in a HIP graph as it is.  Launches that
+// overlap in time get different sets as long as fewer than kQueueSlots of them are in flight
+// at once; the one case that shares a set is two replays of the same captured graph running at
+// the same time (the set is fixed at capture).
 //
 // The pool is a file-scope __device__ array: each GPU the library runs on holds its own copy.
 // Host code never names it in a kernel argument (there the name is a host-side stand-in, not a
@@ -25,11 +26,7 @@ namespace {
 constexpr int kQueueSlots = 4096;
 constexpr int kMaxDevices = 64;
 
-__device__ __align__(256) uint32_t g_tile_queues[kQueueSlots * gemm::kXcds];
-
-__global__ void k_zero_queue(uint32_t* q) {
-    if (threadIdx.x < gemm::kXcds) q[threadIdx.x] = 0u;
-}
+__device__ __align__(256) uint32_t g_tile_queues[kQueueSlots * gemm::kTileQueueWords];
 
 std::mutex g_mu;
 uint32_t* g_pool[kMaxDevices];     // device address of the pool on each device, once looked up
@@ -66,10 +63,10 @@ hipError_t tile_queue(hipStream_t stream, uint32_t** counters, int* grid) {
     uint32_t* pool = nullptr;
     hipError_t e = device_state(&pool, grid);
     if (e != hipSuccess) return e;
+    (void)stream;
     const uint64_t slot = g_seq.fetch_add(1, std::memory_order_relaxed) % kQueueSlots;
-    *counters = pool + slot * gemm::kXcds;
-    hipLaunchKernelGGL(k_zero_queue, dim3(1), dim3(64), 0, stream, *counters);
-    return hipGetLastError();
+    *counters = pool + slot * gemm::kTileQueueWords;
+    return hipSuccess;
 }
 
 }  // namespace dit

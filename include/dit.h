@@ -25,10 +25,10 @@
  *  - Calls that share output or workspace buffers must not overlap in time.
  *  - Every GEMM launch is persistent: one workgroup per CU claims tiles from per-XCD
  *    counters.  The counters come from a static per-GPU pool of 4096 sets, taken in rotation,
- *    and a one-workgroup kernel zeroes the set ahead of the GEMM on the same stream. The
- *    kernel counts below leave that zeroing kernel out.  Calls in flight at the same time get
- *    distinct sets while fewer than 4096 are in flight.  The one exception is two replays of a
- *    single captured HIP graph: they reuse the set fixed at capture and must not overlap.
+ *    and the launch's last workgroup leaves its set at zero for the set's next use.  Calls in
+ *    flight at the same time get distinct sets while fewer than 4096 are in flight.  The one
+ *    exception is two replays of a single captured HIP graph: they reuse the set fixed at
+ *    capture and must not overlap.
  *  - Launch failures reported by the HIP runtime return DIT_ERR_LAUNCH.
  */
 #ifndef DIT_H

@@ -444,6 +444,26 @@ def test_persistent_gemms_on_two_streams_at_once():
         assert torch.equal(po[1].view(torch.int16), po[0].view(torch.int16)), rep
 
 
+def test_counter_sets_are_left_at_zero_for_their_next_use():
+    """The tile counters come from a pool of 4096 sets in rotation, and the last workgroup of
+    each launch puts its set back to zero: 4200 out-projection launches (every set used twice
+    over, some three times) all give the bits of the first."""
+    dit = _dit()
+    o = synth.out_proj_inputs(300, seed=34)
+    to = synth.to_torch("out_proj", o)
+    outs = [torch.empty((300, H), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    dit.dit_out_proj_gated_bf16(to["attn_out"], to["o_weight"], to["gate"], to["gate_index"], to["residual"],
+                                out=outs[0])
+    torch.cuda.synchronize()
+    for i in range(4200):
+        dit.dit_out_proj_gated_bf16(to["attn_out"], to["o_weight"], to["gate"], to["gate_index"], to["residual"],
+                                    out=outs[1])
+        if i % 700 == 699:
+            torch.cuda.synchronize()
+            assert torch.equal(outs[1].view(torch.int16), outs[0].view(torch.int16)), i
+            outs[1].zero_()
+
+
 def test_persistent_gemm_replayed_from_a_captured_graph():
     """The pre-attention (norm, counter zeroing, persistent QKV GEMM) captured in a HIP graph:
     every replay, with eager work and synchronisations between replays, equals the eager run."""
