@@ -46,15 +46,25 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 // round a float to the nearest bf16 value, returned as float
 __device__ __forceinline__ float rbf(float f) { return bf2f(f2bf(f)); }
 
+// a.lo b.lo + a.hi b.hi + c for two packed bf16 pairs (v_dot2_f32_bf16, FP32 result).  The bf16
+// products are exact, but the sum is not always the correctly rounded one: measured against
+// exact sums of random terms it is one FP32 ulp off in about 1 case in 2000 with c = 0 (terms of
+// very different size) and in about 1 in 20 with a general c, and products below 2^-126 are
+// flushed to zero.  Where the exact sum is an FP32 value (1 + s for a bf16 s of magnitude at
+// least 2^-16, say) it is exact.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c = 0.0f) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 // a / s rounded to nearest, given y = RN(1 / s) (one division per row instead of one per
 // element): q0 = RN(a y), the remainder a - q0 s by fma, and one fma correction (Markstein's
-// final step for a correctly rounded reciprocal).
-// A zero remainder means q0 is exact and is returned as is, which also keeps the sign of a
-// zero a (the correction would turn -0 into +0).
+// final step for a correctly rounded reciprocal).  For s > 0 the quotient has a's sign, which
+// is put back on the result: the correction alone would turn the quotient of a = -0 into +0
+// (everywhere else the sign is already a's, as the correction is below an ulp of q0).
 __device__ __forceinline__ float div_by(float a, float s, float y) {
     const float q0 = a * y;
     const float r = fmaf(-q0, s, a);
-    return r == 0.0f ? q0 : fmaf(r, y, q0);
+    return __builtin_copysignf(fmaf(r, y, q0), a);
 }
 
 // fl32(a / s) for a positive per-row scale s: div_by with y = RN(1 / s) when s is a normal

@@ -8,9 +8,9 @@
 // OCP MXFP4: block 32 along K with one E8M0 (power-of-two) scale, so no global scale.
 //  - k_mx_quant_fp4: one thread per 32-value block.  E = floor(log2(amax)) - 2 + 127 clamped to
 //    [0, 254] (0 for an all-zero block), code = E2M1 nearest to v 2^(127 - E), ties to the even
-//    significand, saturating at 6, the sign kept (mx.hpp: the magnitude by the hardware's
-//    round-to-nearest-even fp4 conversion of the exact scaled value).  Scales go to the MX scale
-//    layout (gemm.hpp); the scales of padding rows up to the next multiple of 128 are written as 0.
+//    significand, saturating at 6, the sign kept (mx.hpp: the hardware's scaled bf16 -> fp4
+//    conversion).  Scales go to the MX scale layout (gemm.hpp); the scales of padding rows up to
+//    the next multiple of 128 are written as 0.
 //  - k_out_proj_mxfp4: the GEMM core on E2M1 codes (128 bytes = 256 values per stage), scales
 //    through LDS, then bf16(o) staged and the shared gated-residual epilogue.
 #include "common.hpp"
@@ -38,17 +38,13 @@ __global__ __launch_bounds__(256) void k_mx_quant_fp4(const uint16_t* __restrict
         u32x4 w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) w[q] = ld16(v + 8 * q);
-        float amax = 0.f;
+        uint32_t amax = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(w[q][e])), fabsf(bf_hi(w[q][e]))));
+        for (int q = 0; q < 4; ++q) amax = max(amax, amax_bits8(w[q]));
         E = mx_scale_byte(amax);
-        const float inv = mx_inv_scale(E);
         u32x4 out;
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            out[q] = e2m1_pack4(w[q][0], w[q][1], inv) | (e2m1_pack4(w[q][2], w[q][3], inv) << 16);
+        for (int q = 0; q < 4; ++q) out[q] = e2m1_pack8(w[q], E);
         st16(codes + r * (K / 2) + b * 16, out);
     }
     scales[mx_scale_offset(r, b, K)] = (uint8_t)E;

@@ -5,35 +5,46 @@
 
 namespace dit {
 
-// floor(log2(a)) of a positive finite float (normal or subnormal)
-__device__ __forceinline__ int ilog2f(float a) {
-    const uint32_t b = __float_as_uint(a);
-    const int ex = (int)(b >> 23);
-    return ex != 0 ? ex - 127 : (31 - __builtin_clz(b & 0x7FFFFFu)) - 149;
+// Largest magnitude among the 8 bf16 values of v, as bf16 bits with the sign cleared: for
+// finite values the order of |v| is the unsigned order of those bits (two 16-bit maxima per
+// instruction).
+__device__ __forceinline__ uint32_t amax_bits8(const u32x4& v) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m = __builtin_bit_cast(u16x2, v[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int e = 1; e < 4; ++e) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[e] & 0x7FFF7FFFu));
+    return m.x > m.y ? m.x : m.y;
 }
 
-// E8M0 scale byte of a block with maximum magnitude amax: floor(log2(amax)) - 2 + 127, clamped
-// to [0, 254]; 0 for an all-zero block
-__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
-    if (!(amax > 0.f)) return 0u;
-    const int e = ilog2f(amax) - 2 + 127;
-    return (uint32_t)(e < 0 ? 0 : (e > 254 ? 254 : e));
+// E8M0 scale byte of a block whose largest magnitude has bf16 bits amax: floor(log2(amax)) - 2 +
+// 127 clamped to [0, 254], 0 for an all-zero block.  For a finite bf16 that is its exponent
+// field minus 2, clamped at 0 (zero and subnormal maxima give 0; at most 252).
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t amax) {
+    const uint32_t ex = amax >> 7;
+    return ex > 2u ? ex - 2u : 0u;
 }
 
-// 2^(127 - E) as a normal float (E <= 252 for any finite bf16 amax)
-__device__ __forceinline__ float mx_inv_scale(uint32_t E) { return __uint_as_float((254u - E) << 23); }
+// Two E2M1 codes (one byte, the low half's code in the low nibble) of the bf16 pair w for scale
+// 2^(E - 127) given as the float s, written into byte kByte of old: v_cvt_scalef32_pk_fp4_bf16
+// divides by s (exactly: a power of two) and rounds to the nearest E2M1 value, ties to the even
+// significand, saturating at 6 and keeping the sign (so -0 and small negative values give code 8).
+// The pair arrives as a scalar: handed an element of a vector directly, the compiler has been seen
+// to pass the vector's first element for every byte.
+template <int kByte>
+__device__ __forceinline__ uint32_t e2m1_pair(uint32_t old, uint32_t w, float s) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(old, __builtin_bit_cast(bf16x2, w), s, kByte);
+}
 
-// four E2M1 codes of two packed bf16 pairs, element 2j in the low nibble of byte j.  The
-// magnitudes |v| 2^(127 - E) (exact in FP32 wherever they can round to a nonzero code) go
-// through v_cvt_scalef32_pk_fp4_f32 with a unit scale: round to nearest, ties to the even
-// significand, saturating at 6.  The sign bits are taken from the bf16 values themselves, so
-// -0 and negative values that round to 0 keep their sign.
-__device__ __forceinline__ uint32_t e2m1_pack4(uint32_t w0, uint32_t w1, float inv) {
-    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, fabsf(bf_lo(w0) * inv), fabsf(bf_hi(w0) * inv), 1.0f, 0);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, fabsf(bf_lo(w1) * inv), fabsf(bf_hi(w1) * inv), 1.0f, 1);
-    // bf16 sign bits 15 and 31 of each word -> bit 3 of nibbles 0, 1 (w0) and 2, 3 (w1)
-    const uint32_t sgn = ((w0 >> 12) & 0x8u) | ((w0 >> 24) & 0x80u) | ((w1 >> 4) & 0x800u) | ((w1 >> 16) & 0x8000u);
-    return (r & 0xFFFFu) | sgn;
+// The 8 E2M1 codes of the 8 bf16 values of v in a block with scale byte E, element 2j in the low
+// nibble of byte j (the nearest E2M1 value to v 2^(127 - E), as e2m1_pair rounds).  The scale
+// 2^(E - 127) is a float: subnormal for E = 0.
+__device__ __forceinline__ uint32_t e2m1_pack8(const u32x4& v, uint32_t E) {
+    const float s = __uint_as_float(E != 0u ? E << 23 : 0x00400000u);
+    const uint32_t w0 = v[0], w1 = v[1], w2 = v[2], w3 = v[3];
+    uint32_t q = e2m1_pair<0>(0u, w0, s);
+    q = e2m1_pair<1>(q, w1, s);
+    q = e2m1_pair<2>(q, w2, s);
+    return e2m1_pair<3>(q, w3, s);
 }
 
 // byte offset of the scale of row r, block b (values 32 b ..) of a [*, K] matrix in the MX scale

@@ -26,20 +26,43 @@ constexpr int kMaxPerLane = (kChunks + 63) / 64;  // 11
 
 __device__ __forceinline__ bool chunk_ok(int j, int lane) { return j * 64 + lane < kChunks; }
 
-// Loads the row into registers and returns r = 1 / sqrt(mean(x^2) + eps) (FP32 sum).  The
-// non-temporal loads keep x (read once) from displacing the tables and the workspace in the
-// caches: 10% faster on a cold M = 32760 pass.
-__device__ __forceinline__ float load_row_rms(const uint16_t* xr, int lane, float eps,
-                                              u32x4 (&xv)[kMaxPerLane]) {
+// The row's loads, issued in two groups so that every load not waiting on the index is in
+// flight before the guard: at small M each row is a chain of memory latencies (index -> table
+// rows), not a stream.  x is read once, so its loads are non-temporal and keep it from
+// displacing the tables and the workspace in the caches (10% faster on a cold M = 32760 pass).
+struct RowRegs {
+    u32x4 x[kMaxPerLane], w[kMaxPerLane], sc[kMaxPerLane], sh[kMaxPerLane];
+};
+
+__device__ __forceinline__ void load_x_w(const uint16_t* xr, const uint16_t* xw, int lane, RowRegs& rg) {
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (chunk_ok(j, lane)) {
+            rg.x[j] = ld16_nt(xr + (j * 64 + lane) * 8);
+            rg.w[j] = ld16(xw + (j * 64 + lane) * 8);
+        }
+    }
+}
+
+__device__ __forceinline__ void load_tables(const uint16_t* scr, const uint16_t* shr, int lane, RowRegs& rg) {
+#pragma unroll
+    for (int j = 0; j < kMaxPerLane; ++j) {
+        if (chunk_ok(j, lane)) {
+            rg.sc[j] = ld16(scr + (j * 64 + lane) * 8);
+            rg.sh[j] = ld16(shr + (j * 64 + lane) * 8);
+        }
+    }
+}
+
+// r = 1 / sqrt(mean(x^2) + eps) of the row held in registers: an FP32 sum, two squares (exact
+// bf16 products) per v_dot2 on the packed values
+__device__ __forceinline__ float row_rms(const RowRegs& rg, int lane, float eps) {
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (chunk_ok(j, lane)) {
-            xv[j] = ld16_nt(xr + (j * 64 + lane) * 8);   // x is read once: streaming load
-            float f[8];
-            unpack8(xv[j], f);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
+            for (int e = 0; e < 4; ++e) ss = dot2_bf16(rg.x[j][e], rg.x[j][e], ss);
         }
     }
     ss = wave_sum(ss);
@@ -49,8 +72,9 @@ __device__ __forceinline__ float load_row_rms(const uint16_t* xr, int lane, floa
 // a = bf16(shift + n * bf16(1 + scale)),  n = bf16((x * r) * w), for one 8-wide chunk, in FP32
 // in the formula block's order: x * r and its product with w each rounded to FP32, then RNE to
 // bf16.  1 + scale is exact in FP32 unless |scale| < 2^-16, where both roundings give 1;
-// n * bf16(1 + scale) is a product of two bf16 values, exact in FP32, so the fma rounds
-// shift + n s1 once to FP32 before the RNE to bf16.  r is the FP32 reciprocal root.
+// n * bf16(1 + scale) is a product of two bf16
+// values, exact in FP32, so the fma rounds shift + n s1 once to FP32 before the RNE to bf16.  r
+// is the FP32 reciprocal root.
 __device__ __forceinline__ void modulate_chunk(const u32x4& xv, const u32x4& wv, const u32x4& scv,
                                                const u32x4& shv, float r, uint32_t (&out)[4]) {
     float x[8], w[8], sc[8], sh[8];
@@ -79,18 +103,9 @@ __global__ __launch_bounds__(256) void k_norm_adaln_bf16(const uint16_t* __restr
     const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
     uint16_t* wr = ws + m * kHidden;
-    // Every load that does not depend on the index is issued before the guard: at small M the
-    // kernel is a chain of memory latencies (index -> table rows, x), not a stream.
     const int64_t i = idx[m];
-    u32x4 xv[kMaxPerLane], wv[kMaxPerLane];
-    const uint16_t* xr = x + m * kHidden;
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-        if (chunk_ok(j, lane)) {
-            xv[j] = ld16_nt(xr + (j * 64 + lane) * 8);
-            wv[j] = ld16(xw + (j * 64 + lane) * 8);
-        }
-    }
+    RowRegs rg;
+    load_x_w(x + m * kHidden, xw, lane, rg);
     if (!(i >= 0 && i < rows)) {               // full-width int64 guard
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -98,35 +113,14 @@ __global__ __launch_bounds__(256) void k_norm_adaln_bf16(const uint16_t* __restr
             if (chunk_ok(j, lane)) st16(wr + (j * 64 + lane) * 8, z);
         return;
     }
-    const uint16_t* scr = scale + i * ld_scale;
-    const uint16_t* shr = shift + i * ld_shift;
-    u32x4 scv[kMaxPerLane], shv[kMaxPerLane];
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-        if (chunk_ok(j, lane)) {
-            scv[j] = ld16(scr + (j * 64 + lane) * 8);
-            shv[j] = ld16(shr + (j * 64 + lane) * 8);
-        }
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-        if (chunk_ok(j, lane)) {
-            float f[8];
-            unpack8(xv[j], f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(f[e], f[e], ss);
-        }
-    }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)kHidden + eps);
+    load_tables(scale + i * ld_scale, shift + i * ld_shift, lane, rg);
+    const float r = row_rms(rg, lane, eps);
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (!chunk_ok(j, lane)) continue;
-        const int c = (j * 64 + lane) * 8;
         uint32_t a[4];
-        modulate_chunk(xv[j], wv[j], scv[j], shv[j], r, a);
-        st16(wr + c, u32x4{a[0], a[1], a[2], a[3]});
+        modulate_chunk(rg.x[j], rg.w[j], rg.sc[j], rg.sh[j], r, a);
+        st16(wr + (j * 64 + lane) * 8, u32x4{a[0], a[1], a[2], a[3]});
     }
 }
 
@@ -145,28 +139,33 @@ __global__ __launch_bounds__(256) void k_norm_adaln_mxfp4(const uint16_t* __rest
     const int lane = threadIdx.x & 63;
     const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= R_pad) return;
+    // scale byte of chunk j's block (b = 16 j + lane / 4) in the MX scale layout: a per-row and a
+    // per-lane part plus j * 2048 (b / 8 = 2 j + lane / 32, while b % 2 and (b % 8) / 2 depend on
+    // the lane only), mx_scale_offset taken apart for this row length
+    static_assert(kHidden % 256 == 0, "whole 256-column scale stages");
+    const int64_t rr = m % 128;
+    uint8_t* const srow = scales + (m / 128) * (kHidden / 256) * 1024 + 16 * (rr % 32) + 4 * (rr / 32) +
+                          (lane / 32) * 1024 + 512 * ((lane / 4) % 2) + (lane / 8) % 4;
     if (m >= M) {
 #pragma unroll
         for (int j = 0; j < kMaxPerLane; ++j)
-            if (chunk_ok(j, lane) && (lane & 3) == 0) scales[mx_scale_offset(m, (j * 64 + lane) / 4, kHidden)] = 0;
+            if (chunk_ok(j, lane) && (lane & 3) == 0) srow[j * 2048] = 0;
         return;
     }
     const int64_t i = idx[m];
-    const bool valid = i >= 0 && i < rows;            // full-width int64 guard
+    RowRegs rg;
+    load_x_w(x + m * kHidden, xw, lane, rg);
     u32x4 av[kMaxPerLane];
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) av[j] = u32x4{0u, 0u, 0u, 0u};
-    if (valid) {
-        u32x4 xv[kMaxPerLane];
-        const float r = load_row_rms(x + m * kHidden, lane, eps, xv);
-        const uint16_t* scr = scale + i * ld_scale;
-        const uint16_t* shr = shift + i * ld_shift;
+    if (i >= 0 && i < rows) {                         // full-width int64 guard
+        load_tables(scale + i * ld_scale, shift + i * ld_shift, lane, rg);
+        const float r = row_rms(rg, lane, eps);
 #pragma unroll
         for (int j = 0; j < kMaxPerLane; ++j) {
             if (!chunk_ok(j, lane)) continue;
-            const int c = (j * 64 + lane) * 8;
             uint32_t a[4];
-            modulate_chunk(xv[j], ld16(xw + c), ld16(scr + c), ld16(shr + c), r, a);
+            modulate_chunk(rg.x[j], rg.w[j], rg.sc[j], rg.sh[j], r, a);
             av[j] = u32x4{a[0], a[1], a[2], a[3]};
         }
     }
@@ -174,18 +173,13 @@ __global__ __launch_bounds__(256) void k_norm_adaln_mxfp4(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (!chunk_ok(j, lane)) continue;             // whole quads drop out together
-        float amax = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf_lo(av[j][e])), fabsf(bf_hi(av[j][e]))));
+        uint32_t amax = amax_bits8(av[j]);
         // quad_perm(1,0,3,2) then (2,3,0,1): the maximum over the block's four lanes
-        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0xB1, 0xF, 0xF, true)));
-        amax = fmaxf(amax, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(amax), 0x4E, 0xF, 0xF, true)));
+        amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, true));
+        amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0x4E, 0xF, 0xF, true));
         const uint32_t E = mx_scale_byte(amax);
-        const float inv = mx_inv_scale(E);
-        const int c = j * 64 + lane;
-        *reinterpret_cast<uint32_t*>(cr + c * 4) =
-            e2m1_pack4(av[j][0], av[j][1], inv) | (e2m1_pack4(av[j][2], av[j][3], inv) << 16);
-        if ((lane & 3) == 0) scales[mx_scale_offset(m, c / 4, kHidden)] = (uint8_t)E;
+        *reinterpret_cast<uint32_t*>(cr + (j * 64 + lane) * 4) = e2m1_pack8(av[j], E);
+        if ((lane & 3) == 0) srow[j * 2048] = (uint8_t)E;
     }
 }
 
@@ -203,8 +197,10 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
     if (m >= M) return;
     uint8_t* qr = a_q + m * kHidden;
     const int64_t i = idx[m];
+    RowRegs rg;
+    load_x_w(x + m * kHidden, xw, lane, rg);
     if (lane == 0) y_amax[m] = 0.f;
-    if (!(i >= 0 && i < rows)) {
+    if (!(i >= 0 && i < rows)) {               // full-width int64 guard
         const uint2 z = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < kMaxPerLane; ++j)
@@ -212,18 +208,15 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
         if (lane == 0) a_scale[m] = 0.f;
         return;
     }
-    u32x4 xv[kMaxPerLane];
-    const float r = load_row_rms(x + m * kHidden, lane, eps, xv);
-    const uint16_t* scr = scale + i * ld_scale;
-    const uint16_t* shr = shift + i * ld_shift;
+    load_tables(scale + i * ld_scale, shift + i * ld_shift, lane, rg);
+    const float r = row_rms(rg, lane, eps);
     u32x4 av[kMaxPerLane];
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (!chunk_ok(j, lane)) continue;
-        const int c = (j * 64 + lane) * 8;
         uint32_t ap[4];
-        modulate_chunk(xv[j], ld16(xw + c), ld16(scr + c), ld16(shr + c), r, ap);
+        modulate_chunk(rg.x[j], rg.w[j], rg.sc[j], rg.sh[j], r, ap);
         av[j] = u32x4{ap[0], ap[1], ap[2], ap[3]};
         float a[8];
         unpack8(av[j], a);
@@ -232,24 +225,37 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
     }
     amax = wave_max(amax);
     const float s = amax / 448.0f;             // IEEE division: RN(amax / 448)
-    const float inv = 1.0f / s;                // RN(1 / s); unused when s == 0
-    const bool s_normal = s >= 1.17549435e-38f;    // FLT_MIN
     if (lane == 0) a_scale[m] = s;
+    uint8_t* const ql = qr + lane * 8;
+    if (s == 0.f) {
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-        if (!chunk_ok(j, lane)) continue;
-        float a[8];
-        unpack8(av[j], a);
-        uint2 q;
-        if (s == 0.f) {
-            q = make_uint2(0u, 0u);
-        } else {
-            q.x = f2e4m3x2(div_row(a[0], s, inv, s_normal), div_row(a[1], s, inv, s_normal)) |
-                  (f2e4m3x2(div_row(a[2], s, inv, s_normal), div_row(a[3], s, inv, s_normal)) << 16);
-            q.y = f2e4m3x2(div_row(a[4], s, inv, s_normal), div_row(a[5], s, inv, s_normal)) |
-                  (f2e4m3x2(div_row(a[6], s, inv, s_normal), div_row(a[7], s, inv, s_normal)) << 16);
+        for (int j = 0; j < kMaxPerLane; ++j)
+            if (chunk_ok(j, lane)) *reinterpret_cast<uint2*>(ql + j * 512) = make_uint2(0u, 0u);
+    } else if (s >= 1.17549435e-38f) {         // FLT_MIN: RN(1 / s) is finite, div_by applies
+        const float inv = 1.0f / s;            // RN(1 / s)
+#pragma unroll
+        for (int j = 0; j < kMaxPerLane; ++j) {
+            if (!chunk_ok(j, lane)) continue;
+            float a[8];
+            unpack8(av[j], a);
+            uint2 q;
+            q.x = f2e4m3x2(div_by(a[0], s, inv), div_by(a[1], s, inv)) |
+                  (f2e4m3x2(div_by(a[2], s, inv), div_by(a[3], s, inv)) << 16);
+            q.y = f2e4m3x2(div_by(a[4], s, inv), div_by(a[5], s, inv)) |
+                  (f2e4m3x2(div_by(a[6], s, inv), div_by(a[7], s, inv)) << 16);
+            *reinterpret_cast<uint2*>(ql + j * 512) = q;
         }
-        *reinterpret_cast<uint2*>(qr + (j * 64 + lane) * 8) = q;
+    } else {                                   // subnormal s: IEEE division
+#pragma unroll
+        for (int j = 0; j < kMaxPerLane; ++j) {
+            if (!chunk_ok(j, lane)) continue;
+            float a[8];
+            unpack8(av[j], a);
+            uint2 q;
+            q.x = f2e4m3x2(a[0] / s, a[1] / s) | (f2e4m3x2(a[2] / s, a[3] / s) << 16);
+            q.y = f2e4m3x2(a[4] / s, a[5] / s) | (f2e4m3x2(a[6] / s, a[7] / s) << 16);
+            *reinterpret_cast<uint2*>(ql + j * 512) = q;
+        }
     }
 }
 

@@ -40,11 +40,6 @@ constexpr uint32_t kPermLo = 0x05040100u;
 constexpr uint32_t kPermHi = 0x07060302u;
 constexpr uint32_t kPermLoSwap = 0x01000504u;
 constexpr uint32_t kPermHiSwap = 0x03020706u;
-// a.lo b.lo + a.hi b.hi (+ c) for two packed bf16 pairs (v_dot2_f32_bf16, fp32 result; the
-// bf16 products are exact)
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c = 0.0f) {
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
-}
 
 // Sum over the 16 lanes of a DPP row, left in every lane of it.
 __device__ __forceinline__ float row16_sum(float x) {
@@ -75,7 +70,7 @@ __device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const u32x4& nwlo
                                               int q, const u32x4& cs) {
     // per-head RMSNorm in fp32 on the packed bf16 values: the squares and v w are exact
     // bf16 products (v_dot2; a zero half picks one product), the sum of squares carries fp32
-    // rounding only, and u = bf16((v w) r2); two partial sums halve the dependent chain
+    // rounding (v_dot2's) only, and u = bf16((v w) r2); two partial sums halve the dependent chain
     const float s0 = dot2_bf16(vp[1], vp[1], dot2_bf16(vp[0], vp[0]));
     const float s1 = dot2_bf16(vp[3], vp[3], dot2_bf16(vp[2], vp[2]));
     const float ss = row16_sum(s0 + s1);   // the 16 lanes of a (row, head) are one DPP row
@@ -101,7 +96,8 @@ __device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const u32x4& nwlo
     }
     if (q >= 12) return up;
     // o = u c + w s per element as one v_dot2 of the bf16 pairs (u, w) and (c, s): the two
-    // products are exact in fp32 and their sum is rounded once, as the fma form u c + (w s) is.
+    // products are exact in fp32 and their sum is rounded to fp32 (within one ulp of the
+    // correctly rounded sum that the fma form u c + (w s) gives, equal to it nearly always).
     // (c, s) pairs: cos from this lane (q < 6) or from the partner, through the selector.
     const uint32_t sel_lo = q < 6 ? kPermLo : kPermLoSwap, sel_hi = q < 6 ? kPermHi : kPermHiSwap;
     u32x4 r;

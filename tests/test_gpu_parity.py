@@ -790,6 +790,64 @@ def test_mx_quant_fp4_matches_the_oracle_bit_for_bit(R, K):
     assert np.all(pad == 0), "padding rows' scales"
 
 
+def test_mx_quant_fp4_every_finite_bf16_value_at_every_scale():
+    # For each scale byte E = 0 .. 252 (252 is the largest a finite bf16 maximum gives), blocks
+    # led by 2^(E - 125), whose exponent field E + 2 sets the block scale to E, and filled with
+    # every finite bf16 value of both signs with an exponent field up to E + 2: each finite value
+    # quantised at every scale its block can have, about 8.6 million values in all.
+    blocks, want_E = [], []
+    mags = np.arange(0x7F80, dtype=np.uint16)                         # finite magnitudes
+    for E in range(253):
+        vals = mags[(mags >> 7) <= E + 2]
+        vals = np.concatenate([vals, vals | 0x8000])
+        n = -(-vals.size // 31)
+        b = np.zeros((n, 32), np.uint16)
+        b[:, 0] = (E + 2) << 7
+        b[:, 1:].reshape(-1)[:vals.size] = vals
+        blocks.append(b)
+        want_E.append(np.full(n, E, np.uint8))
+    blocks, want_E = np.concatenate(blocks), np.concatenate(want_E)
+    K = 7168
+    per_row = K // 32
+    R = -(-blocks.shape[0] // per_row)
+    x = np.zeros((R * per_row, 32), np.uint16)
+    x[:blocks.shape[0]] = blocks
+    x = x.reshape(R, K)
+    _say(f"mx quant, every finite bf16 value at every scale: R={R} K={K}")
+    codes, scales = _dit().dit_mx_quant_fp4(_bf16_cuda(x))
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.mx_quant_fp4(x)
+    assert np.array_equal(s_ref.reshape(-1)[:want_E.size], want_E), "oracle scale bytes"
+    rm, pad = mx_scales_rowmajor(scales, R, K)
+    assert np.array_equal(rm, s_ref), "scales"
+    assert np.array_equal(codes.cpu().numpy(), c_ref), "codes"
+
+
+def test_norm_adaln_one_plus_scale_for_every_finite_bf16_scale():
+    # x = 1, w = 1 and shift = 0 make n = bf16(r) = 1 exactly (r = 1 / sqrt(1 + eps) rounds to the
+    # bf16 1), so the workspace is a = bf16(1 + scale) itself: every finite bf16 scale, bit for bit
+    pat = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    pat = pat[((pat >> 7) & 0xFF) != 0xFF]
+    rows = -(-pat.size // H)
+    sc = np.zeros((rows, H), np.uint16)
+    sc.reshape(-1)[:pat.size] = pat
+    zeros = np.zeros((rows, H), np.uint16)
+    one_x = np.full((rows, H), 0x3F80, np.uint16)
+    one_w = np.full(H, 0x3F80, np.uint16)
+    idx = np.arange(rows, dtype=np.int64)
+    _say(f"norm_adaln, 1 + scale for {pat.size} scale values")
+    ws = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    _dit().dit_norm_adaln_bf16(_bf16_cuda(one_x), _bf16_cuda(one_w), _bf16_cuda(sc), _bf16_cuda(zeros),
+                               torch.from_numpy(idx).cuda(), workspace=ws, eps=1e-6)
+    torch.cuda.synchronize()
+    d = {"M": rows, "x": one_x, "x_norm_weight": one_w, "adaln_scale": synth.Table(sc.reshape(-1), 0, rows, H),
+         "adaln_shift": synth.Table(zeros.reshape(-1), 0, rows, H), "adaln_index": idx, "eps": 1e-6}
+    ref = oracle.norm_adaln(d)
+    want = synth.to_bf16_bits((1.0 + bf16_val(sc)).astype(np.float32))
+    assert np.array_equal(ref, want), "oracle: bf16(1 + scale)"
+    assert np.array_equal(synth.bits(ws), ref), "workspace"
+
+
 _MXW = {}
 
 
