@@ -69,6 +69,8 @@ def lib():
         L.oracle_norm_adaln.argtypes = [_i64, _i64, _p, _p, _p, _p, _i64, _i64, _p, _d, _p]
         L.oracle_qkv_mxfp4.restype = None
         L.oracle_qkv_mxfp4.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _d, _p]
+        L.oracle_mlp_fc2.restype = None
+        L.oracle_mlp_fc2.argtypes = [_i64, _i64, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p]
         L.oracle_mlp.restype = None
         L.oracle_mlp.argtypes = [_i64, _i64, _p, _p, _p, _p, _p, _i64, _i64, _p, _p, _p, _p, _p, _p, _d,
                                  _p, _p, _p, _p, _p, _p]
@@ -333,6 +335,32 @@ def pre_attn_mxfp4(d, w_codes, w_scales, rows_sel=None, threads=None):
     ws = norm_adaln(d, rows_sel, threads)
     c, s = mx_quant_fp4(ws, threads)
     return ws, c, s, qkv_mxfp4(c, s, w_codes, w_scales, d, rows_sel, threads)
+
+
+def mlp_fc2(y_q, y_scale, d, rows_sel=None, threads=None):
+    """The MLP's FC2 + gated residual stage alone, on given codes y_q [R, 14336] u8 and scales
+    y_scale [R] f32 of the rows rows_sel (already selected), with those rows' index and residual
+    from d: out [R, 5376] u16.  The reference for that stage on another path's own y_q."""
+    M = d["M"]
+    sel = np.arange(M, dtype=np.int64) if rows_sel is None else np.asarray(rows_sel, np.int64)
+    R = sel.size
+    yq = _c(y_q, np.uint8)
+    ys = _c(y_scale, np.float32)
+    assert yq.shape == (R, INTER) and ys.shape == (R,)
+    idx = _c(d["adaln_index"][sel], np.int64)
+    res = _c(d["residual"].reshape(M, HIDDEN)[sel], np.uint16)
+    g_b, g_o, rows, ld = _table(d["gate"])
+    W2 = _c(d["fc2_q"], np.uint8)
+    s2 = _c(d["fc2_scale"], np.float32)
+    out = np.zeros((R, HIDDEN), np.uint16)
+    L = lib()
+
+    def run(r0, r1):
+        L.oracle_mlp_fc2(r0, r1, _ptr(yq), _ptr(ys), _table_ptr(g_b, g_o), rows, ld, _ptr(idx), _ptr(res), _ptr(W2),
+                         _ptr(s2), _ptr(out))
+
+    _fan_out(run, R, threads)
+    return out
 
 
 def mlp(d, rows_sel=None, threads=None):

@@ -425,6 +425,40 @@ static void e4m3_tab_init(void) {
  * y_q[M][14336], y_s[M] and out[M][5376].  out may alias res or x only when each row is
  * processed before the next reads it (this routine reads the row first).
  */
+/* FC2 and the gated residual of one row from its codes y_q and scale s_y (the MLP page's formula
+   block, last two lines): o = bf16(acc * s_y * w2s[n]) with acc the exact code dot product,
+   out = bf16(res + bf16(g * o)), g = 0 for a guarded row.  yq is scratch for INTER values. */
+static void fc2_gated_row(const uint8_t* yq_codes, float sy, int valid, const uint16_t* gate_row,
+                          const uint8_t* W2q, const float* w2s, const uint16_t* res_row, double* yq,
+                          uint16_t* out_row) {
+    for (int k = 0; k < INTER; k++) yq[k] = oracle_e4m3_value(yq_codes[k]);
+    for (int n = 0; n < HID; n++) {
+        const uint8_t* wr = W2q + (int64_t)n * INTER;
+        double acc = 0.0;
+        for (int k = 0; k < INTER; k++) acc += yq[k] * e4m3_tab[wr[k]];
+        double o = bf(oracle_round_bf16(acc * (double)sy * (double)w2s[n]));
+        double g = valid ? bf(gate_row[n]) : 0.0;
+        double go = bf(oracle_round_bf16(g * o));
+        out_row[n] = oracle_round_bf16(bf(res_row[n]) + go);
+    }
+}
+
+/* The FC2 + gated residual stage alone, on given y_q [R, 14336] and s_y [R] (rows m0 .. m1 of
+   them, with their idx and res rows): the reference for that stage on another path's own y_q. */
+void oracle_mlp_fc2(int64_t m0, int64_t m1, const uint8_t* y_q, const float* y_s, const uint16_t* gate,
+                    int64_t rows, int64_t ld, const int64_t* idx, const uint16_t* res, const uint8_t* W2q,
+                    const float* w2s, uint16_t* out) {
+    double* yq = (double*)malloc(sizeof(double) * INTER);
+    e4m3_tab_init();
+    for (int64_t m = m0; m < m1; m++) {
+        int64_t i = idx[m];
+        int valid = i >= 0 && i < rows;
+        fc2_gated_row(y_q + m * INTER, y_s[m], valid, valid ? gate + i * ld : gate, W2q, w2s, res + m * HID, yq,
+                      out + m * HID);
+    }
+    free(yq);
+}
+
 void oracle_mlp(int64_t m0, int64_t m1, const uint16_t* x, const uint16_t* xw,
                 const uint16_t* scale, const uint16_t* shift, const uint16_t* gate, int64_t rows,
                 int64_t ld, const int64_t* idx, const uint16_t* res, const uint8_t* W1q,
@@ -434,12 +468,10 @@ void oracle_mlp(int64_t m0, int64_t m1, const uint16_t* x, const uint16_t* xw,
     double* aq = (double*)malloc(sizeof(double) * HID);
     double* yq = (double*)malloc(sizeof(double) * INTER);
     double* h = (double*)malloc(sizeof(double) * 2 * INTER);
-    double* resrow = (double*)malloc(sizeof(double) * HID);
     e4m3_tab_init();
     for (int64_t m = m0; m < m1; m++) {
         int64_t i = idx[m];
         int valid = norm_adaln_row(x + m * HID, xw, scale, shift, rows, ld, i, eps, a);
-        for (int k = 0; k < HID; k++) resrow[k] = bf(res[m * HID + k]);
         float sa = quant_row(a, HID, a_q + m * HID);
         a_s[m] = sa;
         for (int k = 0; k < HID; k++) aq[k] = oracle_e4m3_value(a_q[m * HID + k]);
@@ -459,21 +491,11 @@ void oracle_mlp(int64_t m0, int64_t m1, const uint16_t* x, const uint16_t* xw,
         }
         float sy = quant_row(yrow, INTER, y_q + m * INTER);
         y_s[m] = sy;
-        for (int k = 0; k < INTER; k++) yq[k] = oracle_e4m3_value(y_q[m * INTER + k]);
-        /* FC2 + gated residual */
-        for (int n = 0; n < HID; n++) {
-            const uint8_t* wr = W2q + (int64_t)n * INTER;
-            double acc = 0.0;
-            for (int k = 0; k < INTER; k++) acc += yq[k] * e4m3_tab[wr[k]];
-            double o = bf(oracle_round_bf16(acc * (double)sy * (double)w2s[n]));
-            double g = valid ? bf(gate[i * ld + n]) : 0.0;
-            double go = bf(oracle_round_bf16(g * o));
-            out[m * HID + n] = oracle_round_bf16(resrow[n] + go);
-        }
+        fc2_gated_row(y_q + m * INTER, sy, valid, valid ? gate + i * ld : gate, W2q, w2s, res + m * HID, yq,
+                      out + m * HID);
     }
     free(a);
     free(aq);
     free(yq);
     free(h);
-    free(resrow);
 }

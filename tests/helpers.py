@@ -71,6 +71,43 @@ def bf16_tolerance_ok(got_bits, ref_bits, max_rel_l2=2e-3, elem=1e-2):
     return bool(rel_l2 <= max_rel_l2 and ok_elem), float(rel_l2), float(err.max() if err.size else 0.0)
 
 
+def gated_tolerance_ok(got_bits, ref_bits, res_bits, gate_vals, max_rel_l2=2e-3, elem=1e-2):
+    """The bar for gated-residual bf16 outputs out = bf16(res + bf16(g*o)).
+
+    The plain bar holds per element: relative L2 error <= max_rel_l2 and |err| <= elem (1 + |ref|).
+    Where the residual cancels the gated term, out is small while the error of the gated term
+    keeps its own size.  Carried from o meeting the plain bar (|do| <= elem (1 + |o|)) through
+    the two roundings, such an element may instead meet
+        |err| <= elem (|g| + |ref - res| + ulp(ref)) + ulp(ref) + ulp(ref - res),
+    with |ref - res| standing for |g*o| (within an ulp), for at most 4 + 1e-5 of the elements.
+    Returns (ok, rel_l2, max_err, n_carried, worst err / carried bound).
+    """
+    err, rel_l2, plain, carried = _gated_terms(got_bits, ref_bits, res_bits, gate_vals, elem)
+    n_far = int(np.sum(~plain))
+    worst = float((err[~plain] / carried[~plain]).max()) if n_far else 0.0
+    ok = rel_l2 <= max_rel_l2 and np.all(plain | (err <= carried)) and n_far <= 4 + 1e-5 * err.size
+    return bool(ok), float(rel_l2), float(err.max() if err.size else 0.0), n_far, worst
+
+
+def _gated_terms(got_bits, ref_bits, res_bits, gate_vals, elem):
+    g = bf16_val(got_bits)
+    r = bf16_val(ref_bits)
+    res = bf16_val(res_bits)
+    gv = np.abs(np.asarray(gate_vals, np.float64))
+    err = np.abs(g - r)
+    rel_l2 = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+    plain = err <= elem * (1.0 + np.abs(r))
+    carried = elem * (gv + np.abs(r - res) + ulp_bf16(r)) + ulp_bf16(r) + ulp_bf16(r - res)
+    return err, rel_l2, plain, carried
+
+
+def gated_outside(got_bits, ref_bits, res_bits, gate_vals, elem=1e-2):
+    """Mask of the elements (shape of got_bits) outside both the plain and the carried bar of
+    gated_tolerance_ok."""
+    err, _, plain, carried = _gated_terms(got_bits, ref_bits, res_bits, gate_vals, elem)
+    return ~plain & (err > carried)
+
+
 def rope_elem_bound(out_ref_bits, cos_sin_bits):
     """Derived per-element bound for the RoPE-rotated q/k outputs [R, 56, 3, 128].
 

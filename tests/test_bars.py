@@ -7,7 +7,7 @@ import numpy as np
 
 import oracle
 import synth
-from tests.helpers import bf16_val, e4m3_half_step, qkv_check, rope_elem_bound, ulp_bf16
+from tests.helpers import bf16_val, e4m3_half_step, gated_tolerance_ok, qkv_check, rope_elem_bound, ulp_bf16
 
 M = 3
 
@@ -104,3 +104,60 @@ def test_e4m3_half_step():
     s = np.float64(0.5)
     # codes at 1.0 * s are spaced 2^-3 s apart, subnormal codes 2^-9 s
     assert e4m3_half_step(np.array([0.5, 0.75, 2.0 ** -8]), s).tolist() == [2.0 ** -5, 2.0 ** -5, 2.0 ** -11]
+
+
+def _gated(seed=5, n=4000):
+    g = np.random.default_rng(seed)
+    res = synth.to_bf16_bits(g.standard_normal(n).astype(np.float32))
+    gate = bf16_val(synth.to_bf16_bits((g.standard_normal(n) * 0.5).astype(np.float32)))
+    o = bf16_val(synth.to_bf16_bits(g.standard_normal(n).astype(np.float32)))
+    go = bf16_val(synth.to_bf16_bits((gate * o).astype(np.float32)))
+    ref = synth.to_bf16_bits((bf16_val(res) + go).astype(np.float32))
+    return res, gate, o, go, ref
+
+
+def test_gated_bar_accepts_the_reference_itself():
+    res, gate, _, _, ref = _gated()
+    ok, rel, mx, n_far, _ = gated_tolerance_ok(ref, ref, res, gate)
+    assert ok and rel == 0.0 and n_far == 0
+
+
+def _cancelling(k):
+    """_gated()'s elements with the first k made cancelling: g = 1, bf16(g o) = 3 and res = -3 +
+    1/16, so out = 1/16; got takes bf16(g o) one bf16 ulp up (o one ulp off), which moves out by
+    2^-6: far past 1e-2 (1 + |out|), within the carried bound."""
+    res, gate, _, go, _ = _gated()
+    res, gate, go = bf16_val(res).copy(), gate.copy(), go.copy()
+    gate[:k], go[:k], res[:k] = 1.0, 3.0, -3.0 + 0.0625
+    res_b = synth.to_bf16_bits(res.astype(np.float32))
+    ref = synth.to_bf16_bits((bf16_val(res_b) + go).astype(np.float32))
+    go_up = go.copy()
+    go_up[:k] += 2.0 ** -6
+    got = synth.to_bf16_bits((bf16_val(res_b) + go_up).astype(np.float32))
+    return got, ref, res_b, gate
+
+
+def test_gated_bar_covers_a_cancelling_residual():
+    got, ref, res, gate = _cancelling(1)
+    err = abs(bf16_val(got)[0] - bf16_val(ref)[0])
+    assert err > 1e-2 * (1 + abs(bf16_val(ref)[0]))
+    ok, _, _, n_far, worst = gated_tolerance_ok(got, ref, res, gate)
+    assert ok and n_far == 1 and worst <= 1.0
+
+
+def test_gated_bar_rejects_a_dropped_gate():
+    res, gate, o, _, ref = _gated()
+    wrong = synth.to_bf16_bits((bf16_val(res) + o).astype(np.float32))
+    assert not gated_tolerance_ok(wrong, ref, res, gate)[0]
+
+
+def test_gated_bar_rejects_another_rows_residual():
+    res, gate, _, go, ref = _gated()
+    wrong = synth.to_bf16_bits((np.roll(bf16_val(res), 1) + go).astype(np.float32))
+    assert not gated_tolerance_ok(wrong, ref, res, gate)[0]
+
+
+def test_gated_bar_caps_the_elements_past_the_plain_bar():
+    # 4000 elements allow 4 + 0.04 past the plain bar
+    assert gated_tolerance_ok(*_cancelling(4))[0]
+    assert not gated_tolerance_ok(*_cancelling(5))[0]

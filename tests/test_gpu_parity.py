@@ -6,12 +6,19 @@ Bars (bf16 pre-attention, out-projection and fp8 MLP):
     |a_gpu - a_ref| <= ulp(a_ref) + 2 ulp(a_ref - shift), at most 1e-4 of elements differing
     (n's own rounding may land on the other neighbour; shift can cancel n*s1);
   - every bf16 output: relative L2 error <= 2e-3 and |err| <= 1e-2 * (1 + |ref|) per element.
+    A gated-residual output (out-projection, MLP) whose residual cancels the gated term may
+    instead meet that bar carried from o, helpers.gated_tolerance_ok, for at most 4 + 1e-5 of
+    the elements.  The MLP's out must meet these bars everywhere against the oracle's FC2 stage
+    fed the GPU's own y_q and s_y; against the full oracle, elements outside them may only lie in
+    rows whose s_y is not the oracle's (the whole row of y requantised).
     A RoPE-rotated q/k element may instead meet the derived bound of
     helpers.rope_elem_bound (an FP32-accumulated v may round to the other bf16 neighbour, and
     the rotation can carry that ulp of a large u into a small output), but at most
     4 + 4e-6 of the rotated elements may need it;
   - e4m3 activation codes within one code step and per-token activation scales within 1 bf16
-    ulp of the oracle's;
+    ulp of the oracle's; where the AdaLN shift cancels n*s1, a code may instead lie within the
+    workspace bar carried through the division (that distance over s_a plus both half code
+    steps), for at most 4 + 1e-5 of the codes;
   - the bf16 intermediate y: the same 1e-2 * (1 + |ref|) bar, relaxed to 4 ulp(ref) for at most
     1e-4 of its elements (y is three roundings past an FP32-accumulated GEMM);
   - the y quantisation: s_y == RN(amax|y_gpu|/448) and y_q == e4m3(y_gpu/s_y) on the GPU's own
@@ -23,8 +30,8 @@ Bars (bf16 pre-attention, out-projection and fp8 MLP):
   - rows with a guarded index: workspace/codes exactly zero, outputs zero (pre-attention) or
     equal to the residual (out-projection, MLP).
 At the full workload sizes the oracle runs on a sampled row set (rows are independent, so
-this is exact parity on those rows): the first 64 rows, the whole last 256-row tile, every
-guarded row, every clamped-position row and 256 seeded random rows.
+this is exact parity on those rows): the first 256 rows, the whole last 256-row tile, every
+guarded row, every clamped-position row and 512 seeded random rows.
 """
 from __future__ import annotations
 
@@ -36,7 +43,7 @@ import torch
 
 import oracle
 import synth
-from tests.helpers import (bf16_tolerance_ok, bf16_val, e4m3_half_step, e4m3_val, ordered_e4m3, qkv_check,
+from tests.helpers import (bf16_val, gated_outside, gated_tolerance_ok, e4m3_half_step, e4m3_val, ordered_e4m3, qkv_check,
                            torch_e4m3, ulp_bf16, ulp_diff_bf16, workspace_ok)
 
 pytestmark = pytest.mark.gpu
@@ -62,8 +69,8 @@ def _dit():
     return dit
 
 
-def sample_rows(M, d=None, n_random=256, seed=0):
-    rows = set(range(min(M, 64)))
+def sample_rows(M, d=None, n_random=512, seed=0):
+    rows = set(range(min(M, 256)))
     rows |= set(range(((M - 1) // 256) * 256, M))
     if d is not None:
         idx = d.get("adaln_index")
@@ -176,9 +183,12 @@ def check_out_proj(d, out_gpu, rows=None):
     gi = d["gate_index"][rows]
     bad = (gi < 0) | (gi >= d["gate"].rows)
     assert np.array_equal(got[bad], d["residual"].reshape(M, H)[rows][bad]), "guarded rows must equal residual"
-    ok, rel, mx = bf16_tolerance_ok(got, ref)
-    _say(f"out_proj M={M} rows={rows.size} relL2={rel:.2e} max|err|={mx:.3e} mismatch={np.mean(got != ref):.2e}")
-    assert ok, (rel, mx)
+    res = d["residual"].reshape(M, H)[rows]
+    g = np.where(bad[:, None], 0.0, bf16_val(d["gate"].dense())[np.where(bad, 0, gi)])
+    ok, rel, mx, n_far, worst = gated_tolerance_ok(got, ref, res, g)
+    _say(f"out_proj M={M} rows={rows.size} relL2={rel:.2e} max|err|={mx:.3e} mismatch={np.mean(got != ref):.2e} "
+         f"past the plain bar={n_far} (worst {worst:.2f} of the carried bound)")
+    assert ok, (rel, mx, n_far, worst)
 
 
 def run_mlp(d, alias=None):
@@ -240,10 +250,28 @@ def check_mlp(d, out_gpu, ws, rows=None):
     y_q = synth.bits(ws["workspace_y_q"])[rows]
     y_s = ws["workspace_y_scale"].cpu().numpy()[rows]
     out = synth.bits(out_gpu)[rows]
-    da = np.abs(ordered_e4m3(a_q) - ordered_e4m3(ref["a_q"]))
-    assert da.max() <= 1, f"a_q off by {da.max()} code steps"
     assert np.all(np.abs(a_s.astype(np.float64) - ref["a_scale"]) <= ulp_bf16(np.maximum(ref["a_scale"], 2.0 ** -126))), \
         "a_scale beyond 1 bf16 ulp"
+    # a_q: one code step, except where the AdaLN shift cancels n*s1.  There the GPU's a may sit
+    # the workspace bar's ulp(a) + 2 ulp(a - shift) from the oracle's a (n one bf16 ulp off, from
+    # the FP32 sum of squares), which a / s_a carries into many code steps of a small quotient;
+    # such codes must lie within that distance plus both half code steps in value.
+    da = np.abs(ordered_e4m3(a_q) - ordered_e4m3(ref["a_q"]))
+    idx = d["adaln_index"][rows]
+    bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
+    if np.any(da > 1):
+        dn = {k: d[k] for k in ("M", "x", "x_norm_weight", "adaln_scale", "adaln_shift", "adaln_index", "eps")}
+        a_r = bf16_val(oracle.norm_adaln(dn, rows_sel=rows))
+        shift = bf16_val(d["adaln_shift"].dense())[np.where(bad, 0, idx)]
+        s = a_s[:, None].astype(np.float64)
+        bound_a = ulp_bf16(a_r) + 2.0 * ulp_bf16(a_r - shift)
+        bound = bound_a + e4m3_half_step(np.abs(a_r) + bound_a, s) + e4m3_half_step(a_r, s)
+        dv = np.abs(e4m3_val(a_q) - e4m3_val(ref["a_q"])) * s
+        far = da > 1
+        assert np.all(dv[far] <= bound[far] * (1 + 1e-9)), "a_q beyond the carried workspace bar"
+        assert far.sum() <= 4 + 1e-5 * da.size, f"{far.sum()} a_q codes beyond one step"
+        _say(f"  a_q: {far.sum()} codes beyond one step (max {da.max()}), all within the carried workspace bar "
+             f"(worst {float((dv[far] / bound[far]).max()):.2f} of it)")
     # y: 1e-2 (1 + |ref|), or 4 ulp(ref) for at most 1e-4 of the elements
     yg, yr = bf16_val(y), bf16_val(ref["y"])
     erry = np.abs(yg - yr)
@@ -253,16 +281,29 @@ def check_mlp(d, out_gpu, ws, rows=None):
     assert rely <= 2e-3 and np.all(plain | (erry <= 4.0 * ulp_bf16(yr))), ("y", rely, float(erry.max()))
     assert n_relaxed <= 4 + 1e-4 * erry.size, f"{n_relaxed} y elements past the plain bar"
     check_y_quant(y, y_q, y_s, ref, f"mlp M={M}")
-    idx = d["adaln_index"][rows]
-    bad = (idx < 0) | (idx >= d["adaln_scale"].rows)
     assert np.all(a_q[bad] == 0) and np.all(a_s[bad] == 0) and np.all(y_s[bad] == 0)
     res = d["residual"].reshape(M, H)[rows]
     assert np.array_equal(out[bad], res[bad]), "guarded rows must equal the residual"
-    ok, rel, mx = bf16_tolerance_ok(out, ref["out"])
+    g = np.where(bad[:, None], 0.0, bf16_val(d["gate"].dense())[np.where(bad, 0, idx)])
+    # out against the FC2 stage of the oracle fed the GPU's own y_q and s_y: the plain bar (or
+    # the carried one where the residual cancels), everywhere
+    stage = oracle.mlp_fc2(y_q, y_s, d, rows_sel=rows)
+    ok_s, rel_s, mx_s, n_far_s, worst_s = gated_tolerance_ok(out, stage, res, g)
+    assert ok_s, ("out against the FC2 stage on the GPU's own y_q", rel_s, mx_s, n_far_s, worst_s)
+    # against the full oracle: relative L2, and the same bars except in rows whose s_y is not the
+    # oracle's (an amax one ulp off requantises the whole row of y, which moves o by more than its
+    # plain bar; the stage check above covers those rows), at most 4 + 1e-5 of the elements
+    ok, rel, mx, n_far, worst = gated_tolerance_ok(out, ref["out"], res, g)
+    outside = gated_outside(out, ref["out"], res, g)
+    requant = (y_s != ref["y_scale"])[:, None]
+    assert rel <= 2e-3, ("out relL2", rel)
+    assert not np.any(outside & ~requant), "out outside the bar in a row whose s_y is the oracle's"
+    assert n_far <= 4 + 1e-5 * out.size, f"{n_far} out elements past the plain bar"
     _say(f"mlp M={M} rows={rows.size} a_q mismatch={np.mean(a_q != ref['a_q']):.2e} "
          f"a_s exact={np.mean(a_s == ref['a_scale']):.3f} y relL2={rely:.2e} y max|err|={erry.max():.3e} "
-         f"y past plain bar={n_relaxed} out relL2={rel:.2e} max|err|={mx:.3e} guarded={bad.sum()}")
-    assert ok, (rel, mx)
+         f"y past plain bar={n_relaxed} out relL2={rel:.2e} max|err|={mx:.3e} out past the plain bar={n_far} "
+         f"({int(outside.sum())} outside the carried bound, all in rows with a requantised y; against the FC2 "
+         f"stage on the GPU's y_q: relL2={rel_s:.2e}, past the plain bar {n_far_s}) guarded={bad.sum()}")
     return ref
 
 
@@ -713,7 +754,7 @@ def test_pre_attn_config2_sampled_and_deterministic():
     ws1, out1 = synth.bits(ws), synth.bits(out)
     _, out2 = run_pre(d, workspace=ws)
     assert np.array_equal(out1, synth.bits(out2)) and np.array_equal(ws1, synth.bits(ws)), "not deterministic"
-    check_pre(d, ws, out, sample_rows(d["M"], d, n_random=192))
+    check_pre(d, ws, out, sample_rows(d["M"], d))
 
 
 # ---------------------------------------------------------------- out-projection
@@ -741,7 +782,7 @@ def test_out_proj_config3_sampled():
     o1 = synth.bits(out)
     out2 = run_out_proj(d)
     assert np.array_equal(o1, synth.bits(out2)), "not deterministic"
-    check_out_proj(d, out, sample_rows(d["M"], d, n_random=256))
+    check_out_proj(d, out, sample_rows(d["M"], d))
 
 
 # ---------------------------------------------------------------- MXFP4 W4A4 out-projection
@@ -891,9 +932,12 @@ def check_out_proj_mx(d, out_gpu, ac, asc, rows):
     gi = d["gate_index"][rows]
     bad = (gi < 0) | (gi >= d["gate"].rows)
     assert np.array_equal(got[bad], d["residual"].reshape(M, H)[rows][bad]), "guarded rows must equal residual"
-    ok, rel, mx = bf16_tolerance_ok(got, ref)
-    _say(f"out_proj mxfp4 M={M} rows={rows.size} relL2={rel:.2e} max|err|={mx:.3e} mismatch={np.mean(got != ref):.2e}")
-    assert ok, (rel, mx)
+    res = d["residual"].reshape(M, H)[rows]
+    g = np.where(bad[:, None], 0.0, bf16_val(d["gate"].dense())[np.where(bad, 0, gi)])
+    ok, rel, mx, n_far, worst = gated_tolerance_ok(got, ref, res, g)
+    _say(f"out_proj mxfp4 M={M} rows={rows.size} relL2={rel:.2e} max|err|={mx:.3e} mismatch={np.mean(got != ref):.2e} "
+         f"past the plain bar={n_far}")
+    assert ok, (rel, mx, n_far, worst)
 
 
 @pytest.mark.parametrize("M", [1, 300])
@@ -1099,7 +1143,7 @@ def test_mlp_subnormal_scales_and_visible_eps():
 
 def test_mlp_maximum_M():
     """M = 149796, the largest M the MLP page allows: 586 m-tiles, the last one ragged
-    (36 rows).  Sampled rows (the first 64, the last m-tile, every guarded row, 32 random)
+    (36 rows).  Sampled rows (the first 256, the last m-tile, every guarded row, 32 random)
     against the oracle."""
     M = 149796
     _say(f"fp8 MLP at the maximum M={M}")
@@ -1116,4 +1160,4 @@ def test_mlp_config4_sampled_and_deterministic():
     y1 = synth.bits(ws["workspace_y_q"])
     out2, ws2 = run_mlp(d)
     assert np.array_equal(o1, synth.bits(out2)) and np.array_equal(y1, synth.bits(ws2["workspace_y_q"]))
-    check_mlp(d, out, ws, sample_rows(d["M"], d, n_random=96))
+    check_mlp(d, out, ws, sample_rows(d["M"], d))

@@ -509,6 +509,36 @@ def test_mlp_fc2_gated_residual_closed_forms():
             assert is_nearest_bf16(o["out"][m], res[m] + ob).all()
 
 
+def test_mlp_fc2_stage_on_given_codes_closed_forms():
+    # the FC2 + gated residual stage alone, on random codes and scales (not the oracle's own):
+    # with the one-hot W2 and unit scales, o = bf16(y_q[k(n)] s_y) and out = bf16(res + bf16(g o))
+    M = 4
+    d = _mlp_one_hot(M)
+    gates = np.array([0.0, 1.0], np.float32)
+    wide_bits = d["adaln_scale"].base.copy().reshape(2, 6 * H)
+    wide_bits[:, 5 * H:] = synth.to_bf16_bits(np.repeat(gates[:, None], H, 1))
+    base = wide_bits.reshape(-1)
+    d["gate"] = synth.Table(base, 5 * H, 2, 6 * H)
+    d["adaln_index"][:] = [0, 1, -1, 1]
+    g = np.random.default_rng(3)
+    y_q = g.integers(0, 256, (M, synth.INTER)).astype(np.uint8)
+    y_q[(y_q & 0x7F) == 0x7F] = 0x38                                   # no NaN codes
+    y_s = (g.random(M) * 0.1 + 0.01).astype(np.float32)
+    out = oracle.mlp_fc2(y_q, y_s, d)
+    res = bf16_val(d["residual"].reshape(M, H))
+    kk = (np.arange(H) * 11 + 5) % synth.INTER
+    for m in range(M):
+        oo = e4m3_val(y_q[m][kk]) * float(y_s[m])
+        ob = bf16_val(synth.to_bf16_bits(oo.astype(np.float32)))
+        if d["adaln_index"][m] != 1:                                   # gate 0, or a guarded row
+            assert np.array_equal(out[m], d["residual"].reshape(M, H)[m])
+        else:
+            assert is_nearest_bf16(out[m], res[m] + ob).all()
+    # on the full oracle's own codes it reproduces the full oracle's out
+    o = oracle.mlp(d)
+    assert np.array_equal(oracle.mlp_fc2(o["y_q"], o["y_scale"], d), o["out"])
+
+
 # ---------------------------------------------------------------- cross-check with brute force
 
 @pytest.mark.parametrize("M", [1, 2])
