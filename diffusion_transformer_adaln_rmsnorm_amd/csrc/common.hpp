@@ -56,6 +56,41 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c = 0.0
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// r_i = a_i.lo b_i.lo + a_i.hi b_i.hi for four independent bf16 pairs, by the three-operand
+// v_dot2_f32_bf16 with an inline zero addend.  For dot2_bf16 the compiler emits the accumulating
+// two-operand form, which takes a freshly zeroed register per use; this form takes none.  A
+// VALU instruction may read a three-operand v_dot2's result only 3 wait states after it is
+// written: the compiler pads its own uses (s_nop 2) but sees nothing inside an asm block, so
+// the block ends with those wait states.
+__device__ __forceinline__ void dot2x4_zero(uint32_t a0, uint32_t b0, uint32_t a1, uint32_t b1, uint32_t a2,
+                                            uint32_t b2, uint32_t a3, uint32_t b3, float (&r)[4]) {
+    asm("v_dot2_f32_bf16 %0, %4, %5, 0\n\t"
+        "v_dot2_f32_bf16 %1, %6, %7, 0\n\t"
+        "v_dot2_f32_bf16 %2, %8, %9, 0\n\t"
+        "v_dot2_f32_bf16 %3, %10, %11, 0\n\t"
+        "s_nop 2"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3));
+}
+
+// 1 + s for the eight bf16 values of four packed words s0 .. s3: per value one three-operand
+// v_dot2 of its word with a unit weight on its half, plus the inline addend 1.0 (r[2i] from the
+// low half of s_i, r[2i + 1] from the high half).  The weights sit in SGPRs; the block ends with
+// the wait states of dot2x4_zero.  Exact wherever 1 + s is an FP32 value.
+__device__ __forceinline__ void one_plus_x8(uint32_t s0, uint32_t s1, uint32_t s2, uint32_t s3, float (&r)[8]) {
+    asm("v_dot2_f32_bf16 %0, %8, %12, 1.0\n\t"
+        "v_dot2_f32_bf16 %1, %8, %13, 1.0\n\t"
+        "v_dot2_f32_bf16 %2, %9, %12, 1.0\n\t"
+        "v_dot2_f32_bf16 %3, %9, %13, 1.0\n\t"
+        "v_dot2_f32_bf16 %4, %10, %12, 1.0\n\t"
+        "v_dot2_f32_bf16 %5, %10, %13, 1.0\n\t"
+        "v_dot2_f32_bf16 %6, %11, %12, 1.0\n\t"
+        "v_dot2_f32_bf16 %7, %11, %13, 1.0\n\t"
+        "s_nop 2"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7])
+        : "v"(s0), "v"(s1), "v"(s2), "v"(s3), "s"(0x00003F80u), "s"(0x3F800000u));
+}
+
 // a / s rounded to nearest, given y = RN(1 / s) (one division per row instead of one per
 // element): q0 = RN(a y), the remainder a - q0 s by fma, and one fma correction (Markstein's
 // final step for a correctly rounded reciprocal).  For s > 0 the quotient has a's sign, which

@@ -71,22 +71,22 @@ __device__ __forceinline__ float row_rms(const RowRegs& rg, int lane, float eps)
 
 // a = bf16(shift + n * bf16(1 + scale)),  n = bf16((x * r) * w), for one 8-wide chunk, in FP32
 // in the formula block's order: x * r and its product with w each rounded to FP32, then RNE to
-// bf16.  1 + scale is exact in FP32 unless |scale| < 2^-16, where both roundings give 1;
-// n * bf16(1 + scale) is a product of two bf16
+// bf16.  1 + scale is exact in FP32 unless |scale| < 2^-16, where every rounding of it gives
+// the bf16 1 (one_plus_x8 takes it on the packed scale); n * bf16(1 + scale) is a product of two bf16
 // values, exact in FP32, so the fma rounds shift + n s1 once to FP32 before the RNE to bf16.  r
 // is the FP32 reciprocal root.
 __device__ __forceinline__ void modulate_chunk(const u32x4& xv, const u32x4& wv, const u32x4& scv,
                                                const u32x4& shv, float r, uint32_t (&out)[4]) {
-    float x[8], w[8], sc[8], sh[8];
+    float x[8], w[8], sc1[8], sh[8];
     unpack8(xv, x);
     unpack8(wv, w);
-    unpack8(scv, sc);
+    one_plus_x8(scv[0], scv[1], scv[2], scv[3], sc1);
     unpack8(shv, sh);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         // two elements per packed bf16 conversion
         const uint32_t n = pack_bf2((x[2 * k] * r) * w[2 * k], (x[2 * k + 1] * r) * w[2 * k + 1]);
-        const uint32_t s1 = pack_bf2(1.0f + sc[2 * k], 1.0f + sc[2 * k + 1]);
+        const uint32_t s1 = pack_bf2(sc1[2 * k], sc1[2 * k + 1]);
         out[k] = pack_bf2(fmaf(bf_lo(n), bf_lo(s1), sh[2 * k]), fmaf(bf_hi(n), bf_hi(s1), sh[2 * k + 1]));
     }
 }

@@ -71,18 +71,17 @@ __device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const u32x4& nwlo
     // per-head RMSNorm in fp32 on the packed bf16 values: the squares and v w are exact
     // bf16 products (v_dot2; a zero half picks one product), the sum of squares carries fp32
     // rounding (v_dot2's) only, and u = bf16((v w) r2); two partial sums halve the dependent chain
-    const float s0 = dot2_bf16(vp[1], vp[1], dot2_bf16(vp[0], vp[0]));
-    const float s1 = dot2_bf16(vp[3], vp[3], dot2_bf16(vp[2], vp[2]));
-    const float ss = row16_sum(s0 + s1);   // the 16 lanes of a (row, head) are one DPP row
+    float sq[4];
+    dot2x4_zero(vp[0], vp[0], vp[1], vp[1], vp[2], vp[2], vp[3], vp[3], sq);
+    const float ss = row16_sum((sq[0] + sq[1]) + (sq[2] + sq[3]));   // a (row, head)'s 16 lanes are one DPP row
     // v_rsq_f32 directly: its argument is at least qk_eps, a normal float, where the library
     // rsqrtf adds only a denormal-range rescaling around the same instruction
     const float r2 = __builtin_amdgcn_rsqf(ss * (1.0f / kHeadDim) + qk_eps);
-    float u[8];
+    float u[8], vw[8];
+    dot2x4_zero(vp[0], nwlo[0], vp[0], nwhi[0], vp[1], nwlo[1], vp[1], nwhi[1], *reinterpret_cast<float(*)[4]>(vw));
+    dot2x4_zero(vp[2], nwlo[2], vp[2], nwhi[2], vp[3], nwlo[3], vp[3], nwhi[3], *reinterpret_cast<float(*)[4]>(vw + 4));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        u[2 * e] = dot2_bf16(vp[e], nwlo[e]) * r2;
-        u[2 * e + 1] = dot2_bf16(vp[e], nwhi[e]) * r2;
-    }
+    for (int e = 0; e < 8; ++e) u[e] = vw[e] * r2;
     const u32x4 up = pack8(u);          // the bf16 u, packed
     // RoPE partner chunk q + 6 (q < 6) or q - 6 (6 <= q < 12), 8 lanes away; its sign flipped
     // for the first half, so both halves take o = u c + w s:
@@ -100,16 +99,18 @@ __device__ __forceinline__ u32x4 qk_norm_rope(const u32x4& vp, const u32x4& nwlo
     // correctly rounded sum that the fma form u c + (w s) gives, equal to it nearly always).
     // (c, s) pairs: cos from this lane (q < 6) or from the partner, through the selector.
     const uint32_t sel_lo = q < 6 ? kPermLo : kPermLoSwap, sel_hi = q < 6 ? kPermHi : kPermHiSwap;
-    u32x4 r;
+    uint32_t uw[8], cw[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const uint32_t uw0 = __builtin_amdgcn_perm(pv[e], up[e], kPermLo);   // (u_2e, w_2e)
-        const uint32_t uw1 = __builtin_amdgcn_perm(pv[e], up[e], kPermHi);   // (u_2e+1, w_2e+1)
-        const uint32_t cs0 = __builtin_amdgcn_perm(pc[e], cs[e], sel_lo);    // (c_2e, s_2e)
-        const uint32_t cs1 = __builtin_amdgcn_perm(pc[e], cs[e], sel_hi);    // (c_2e+1, s_2e+1)
-        r[e] = pack_bf2(dot2_bf16(uw0, cs0), dot2_bf16(uw1, cs1));
+        uw[2 * e] = __builtin_amdgcn_perm(pv[e], up[e], kPermLo);       // (u_2e, w_2e)
+        uw[2 * e + 1] = __builtin_amdgcn_perm(pv[e], up[e], kPermHi);   // (u_2e+1, w_2e+1)
+        cw[2 * e] = __builtin_amdgcn_perm(pc[e], cs[e], sel_lo);        // (c_2e, s_2e)
+        cw[2 * e + 1] = __builtin_amdgcn_perm(pc[e], cs[e], sel_hi);    // (c_2e+1, s_2e+1)
     }
-    return r;
+    float o[8];
+    dot2x4_zero(uw[0], cw[0], uw[1], cw[1], uw[2], cw[2], uw[3], cw[3], *reinterpret_cast<float(*)[4]>(o));
+    dot2x4_zero(uw[4], cw[4], uw[5], cw[5], uw[6], cw[6], uw[7], cw[7], *reinterpret_cast<float(*)[4]>(o + 4));
+    return pack8(o);
 }
 
 // 8-dim chunk of a head held by lane li of its DPP row (the partner chunk q +/- 6 sits at
