@@ -71,10 +71,10 @@ __device__ __forceinline__ float row_rms(const RowRegs& rg, int lane, float eps)
 
 // a = bf16(shift + n * bf16(1 + scale)),  n = bf16((x * r) * w), for one 8-wide chunk, in FP32
 // in the formula block's order: x * r and its product with w each rounded to FP32, then RNE to
-// bf16.  1 + scale is exact in FP32 unless |scale| < 2^-16, where every rounding of it gives
-// the bf16 1 (one_plus_x8 takes it on the packed scale); n * bf16(1 + scale) is a product of two bf16
-// values, exact in FP32, so the fma rounds shift + n s1 once to FP32 before the RNE to bf16.  r
-// is the FP32 reciprocal root.
+// bf16.  1 + scale is exact in FP32 unless |scale| < 2^-16, where every rounding of it gives the
+// bf16 1 (one_plus_x8 takes it on the packed scale).  n * bf16(1 + scale) is a product of two
+// bf16 values, exact in FP32, so the fma rounds shift + n s1 once to FP32 before the RNE to bf16.
+// r is the FP32 reciprocal root.
 __device__ __forceinline__ void modulate_chunk(const u32x4& xv, const u32x4& wv, const u32x4& scv,
                                                const u32x4& shv, float r, uint32_t (&out)[4]) {
     float x[8], w[8], sc1[8], sh[8];
