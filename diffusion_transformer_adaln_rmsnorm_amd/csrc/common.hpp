@@ -141,6 +141,17 @@ __device__ __forceinline__ uint32_t f2e4m3x2(float a, float b) {
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// Largest magnitude among the 8 bf16 values of v, as bf16 bits with the sign cleared: for
+// finite values the order of |v| is the unsigned order of those bits (two 16-bit maxima per
+// instruction).  As float bits (<< 16) it is that magnitude in FP32.
+__device__ __forceinline__ uint32_t amax_bits8(const u32x4& v) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    u16x2 m = __builtin_bit_cast(u16x2, v[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int e = 1; e < 4; ++e) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[e] & 0x7FFF7FFFu));
+    return m.x > m.y ? m.x : m.y;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);

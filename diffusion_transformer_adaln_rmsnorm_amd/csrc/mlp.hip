@@ -46,19 +46,18 @@ __device__ __forceinline__ void fc1_epilogue(const Acc& acc, uint8_t* smem, int6
         const int row = it * kRowsPerPass + rsub;
         const u32x4 hg = epi_ld(smem, row, c8), hu = epi_ld(smem, row, 128 + c8);
         u32x4 yv;
-        float amax = 0.f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             // two columns at a time: bf16(silu(h_gate)), then y = bf16(that * h_up)
             const uint32_t sl = pack_bf2(silu_fast(bf_lo(hg[k])), silu_fast(bf_hi(hg[k])));
             yv[k] = pack_bf2(bf_lo(sl) * bf_lo(hu[k]), bf_hi(sl) * bf_hi(hu[k]));
-            amax = fmaxf(amax, fabsf(bf_lo(yv[k])));
-            amax = fmaxf(amax, fabsf(bf_hi(yv[k])));
         }
-        amax = row16_max(amax);           // the row's 16 lanes are one DPP row
+        // max |y| of the row's 128 columns on the bf16 bits (the row's 16 lanes are one DPP
+        // row); as float bits it is the FP32 value, whose unsigned order the atomic max keeps
+        const uint32_t amax = row16_max_u32(amax_bits8(yv)) << 16;
         buf_st16(ry, o1 + it * kPassB, yv);
         if ((t & 15) == 0 && row < (int)tile_rows)
-            atomicMax(reinterpret_cast<unsigned int*>(y_amax + m0 + row), __float_as_uint(amax));
+            atomicMax(reinterpret_cast<unsigned int*>(y_amax + m0 + row), amax);
     }
 }
 

@@ -5,17 +5,6 @@
 
 namespace dit {
 
-// Largest magnitude among the 8 bf16 values of v, as bf16 bits with the sign cleared: for
-// finite values the order of |v| is the unsigned order of those bits (two 16-bit maxima per
-// instruction).
-__device__ __forceinline__ uint32_t amax_bits8(const u32x4& v) {
-    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-    u16x2 m = __builtin_bit_cast(u16x2, v[0] & 0x7FFF7FFFu);
-#pragma unroll
-    for (int e = 1; e < 4; ++e) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, v[e] & 0x7FFF7FFFu));
-    return m.x > m.y ? m.x : m.y;
-}
-
 // E8M0 scale byte of a block whose largest magnitude has bf16 bits amax: floor(log2(amax)) - 2 +
 // 127 clamped to [0, 254], 0 for an all-zero block.  For a finite bf16 that is its exponent
 // field minus 2, clamped at 0 (zero and subnormal maxima give 0; at most 252).

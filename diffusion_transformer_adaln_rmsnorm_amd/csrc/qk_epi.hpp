@@ -50,13 +50,12 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// Maximum over the 16 lanes of a DPP row, left in every lane of it (x >= 0: the moves' fill
-// value 0 never wins).
-__device__ __forceinline__ float row16_max(float x) {
-    x = fmaxf(x, dpp_f<kDppXor1>(x));
-    x = fmaxf(x, dpp_f<kDppXor2>(x));
-    x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
-    x = fmaxf(x, dpp_f<kDppMirror>(x));
+// Unsigned maximum over the 16 lanes of a DPP row, left in every lane of it
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
+    x = max(x, dpp_u<kDppXor1>(x));
+    x = max(x, dpp_u<kDppXor2>(x));
+    x = max(x, dpp_u<kDppHalfMirror>(x));
+    x = max(x, dpp_u<kDppMirror>(x));
     return x;
 }
 
