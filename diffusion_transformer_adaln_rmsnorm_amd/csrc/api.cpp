@@ -304,10 +304,9 @@ dit_status dit_mlp_fp8(const void* x, int64_t M, const void* x_norm_weight, dit_
     st = launched(dit::launch_norm_adaln_fp8q(
         xs, M, static_cast<const uint16_t*>(x_norm_weight), static_cast<const uint16_t*>(adaln_scale.ptr),
         adaln_scale.row_stride, static_cast<const uint16_t*>(adaln_shift.ptr), adaln_shift.row_stride,
-        adaln_scale.rows, adaln_index, eps, ws_a_q, ws_a_scale, ws_y_scale, s));
+        adaln_scale.rows, adaln_index, eps, ws_a_q, ws_a_scale, s));
     if (st != DIT_OK) return st;
-    st = launched(dit::launch_fc1_swiglu(ws_a_q, ws_a_scale, M, fc1_q, fc1_scale, static_cast<uint16_t*>(ws_y),
-                                         ws_y_scale, s));
+    st = launched(dit::launch_fc1_swiglu(ws_a_q, ws_a_scale, M, fc1_q, fc1_scale, static_cast<uint16_t*>(ws_y), s));
     if (st != DIT_OK) return st;
     st = launched(dit::launch_quant_rows(static_cast<const uint16_t*>(ws_y), M, ws_y_scale, ws_y_q, s));
     if (st != DIT_OK) return st;

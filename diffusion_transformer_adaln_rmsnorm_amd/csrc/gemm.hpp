@@ -492,7 +492,13 @@ struct PPFill {
     }
 };
 
-template <Mma kKind>
+// kInterleaveB: B local rows 32 w + [0, 16) are global rows nb0 + 16 w + [0, 16) and 32 w + [16,
+// 32) are nb1 + 16 w + [0, 16) (w = 0..7), so each wave's 16-column blocks alternate between the
+// two halves and a lane holds matching columns of both in adjacent blocks.  kOpenTail: return
+// after this wave's last in-loop barrier, without the closing barrier pair and drain; the caller
+// then owes G0 one barrier (the one that ends G1's last compute phase) and every wave a drain of
+// its loads before the LDS is reused (the dead loads past the end still write zeros into slots).
+template <Mma kKind, bool kInterleaveB = false, bool kOpenTail = false>
 __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                             const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
                                             int ktiles, uint8_t* smem, typename KindTypes<kKind>::AccT& acc,
@@ -515,7 +521,13 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         const int row = 32 * wave + j * kRowsPerPiece + lane / kSlots;
         sf.va[j] = (uint32_t)(row * lda) + (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
         const int64_t r0 = 32 * wave + j * kRowsPerPiece;                // piece's first row (uniform)
-        sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
+        if constexpr (kInterleaveB) {
+            static_assert(kPPAPieces == 4 && kRowsPerPiece == 8, "two pieces per 16-row half");
+            const int64_t g = j < 2 ? 16 * wave + 8 * j : (nb1 - nb0) + 16 * wave + 8 * (j - 2);
+            sf.sb[j] = (uint32_t)(g * ldb);
+        } else {
+            sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
+        }
         if (j < kVPat) {
             const int brow = (int)r0 + lane / kSlots;
             sf.vb[j] = (uint32_t)((lane / kSlots) * ldb) + (uint32_t)(((lane % kSlots) ^ swz(brow)) << 4);
@@ -589,21 +601,23 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         pp_barrier<kPPAPieces + kScl>();             // A(kt+1) (G0: and B(kt+1)) landed
         sb_read = sb_read == 2 ? 0 : sb_read + 1;
     }
-    if (g0) pp_barrier<63>();        // G1's last compute phase
-    // drain every load (the dead ones too: they write zeros into the slots the caller reuses)
-    __syncthreads();
+    if constexpr (!kOpenTail) {
+        if (g0) pp_barrier<63>();    // G1's last compute phase
+        // drain every load (the dead ones too: they write zeros into the slots the caller reuses)
+        __syncthreads();
+    }
 }
 
 // Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
 // [0,128) are global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a
 // plain tile; for MXFP4 both multiples of 128).  Ends with all loads drained and a barrier, so
 // the caller may reuse the LDS (kSmemBytes).
-template <Mma kKind>
+template <Mma kKind, bool kInterleaveB = false, bool kOpenTail = false>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
                                          int ktiles, uint8_t* smem, typename KindTypes<kKind>::AccT& acc,
                                          const MxScales& mxs = MxScales{}) {
-    mainloop_pp<kKind>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs);
+    mainloop_pp<kKind, kInterleaveB, kOpenTail>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs);
 }
 
 

@@ -17,7 +17,7 @@ hipError_t launch_norm_adaln_bf16(const uint16_t* x, int64_t M, const uint16_t* 
 
 hipError_t launch_norm_adaln_fp8q(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,
                                   int64_t ld_scale, const uint16_t* shift, int64_t ld_shift, int64_t rows,
-                                  const int64_t* idx, float eps, uint8_t* a_q, float* a_scale, float* y_amax,
+                                  const int64_t* idx, float eps, uint8_t* a_q, float* a_scale,
                                   hipStream_t stream);
 
 // P: Ulysses destination count (1, 2, 4 or 8); out is [P, M, 56 / P, 3, 128]
@@ -57,10 +57,9 @@ hipError_t launch_out_proj_mxfp4(const uint8_t* a_codes, const uint8_t* a_scales
                                  hipStream_t stream);
 
 hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M, const uint8_t* W1,
-                             const float* w1s, uint16_t* y, float* y_amax, hipStream_t stream);
+                             const float* w1s, uint16_t* y, hipStream_t stream);
 
-hipError_t launch_quant_rows(const uint16_t* y, int64_t M, float* y_scale_inout, uint8_t* y_q,
-                             hipStream_t stream);
+hipError_t launch_quant_rows(const uint16_t* y, int64_t M, float* y_scale, uint8_t* y_q, hipStream_t stream);
 
 hipError_t launch_fc2_gated(const uint8_t* y_q, const float* y_scale, int64_t M, const uint8_t* W2,
                             const float* w2s, const uint16_t* gate, int64_t gate_rows, int64_t gate_ld,

@@ -184,14 +184,13 @@ __global__ __launch_bounds__(256) void k_norm_adaln_mxfp4(const uint16_t* __rest
 }
 
 // MLP kernel A: the same row steps, then s_a = RN(amax|a| / 448) and a_q = e4m3(a / s_a).
-// Also clears y_amax[m], the per-row |y| maximum that the FC1 epilogue accumulates.
 __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restrict__ x, int64_t M,
                                                          const uint16_t* __restrict__ xw,
                                                          const uint16_t* __restrict__ scale, int64_t ld_scale,
                                                          const uint16_t* __restrict__ shift, int64_t ld_shift,
                                                          int64_t rows, const int64_t* __restrict__ idx,
                                                          float eps, uint8_t* __restrict__ a_q,
-                                                         float* __restrict__ a_scale, float* __restrict__ y_amax) {
+                                                         float* __restrict__ a_scale) {
     const int lane = threadIdx.x & 63;
     const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (m >= M) return;
@@ -199,7 +198,6 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
     const int64_t i = idx[m];
     RowRegs rg;
     load_x_w(x + m * kHidden, xw, lane, rg);
-    if (lane == 0) y_amax[m] = 0.f;
     if (!(i >= 0 && i < rows)) {               // full-width int64 guard
         const uint2 z = {0u, 0u};
 #pragma unroll
@@ -279,11 +277,10 @@ hipError_t launch_norm_adaln_mxfp4(const uint16_t* x, int64_t M, const uint16_t*
 
 hipError_t launch_norm_adaln_fp8q(const uint16_t* x, int64_t M, const uint16_t* xw, const uint16_t* scale,
                                   int64_t ld_scale, const uint16_t* shift, int64_t ld_shift, int64_t rows,
-                                  const int64_t* idx, float eps, uint8_t* a_q, float* a_scale, float* y_amax,
-                                  hipStream_t stream) {
+                                  const int64_t* idx, float eps, uint8_t* a_q, float* a_scale, hipStream_t stream) {
     const int64_t blocks = (M + 3) / 4;
     hipLaunchKernelGGL(k_norm_adaln_fp8q, dim3((unsigned)blocks), dim3(256), 0, stream, x, M, xw, scale, ld_scale,
-                       shift, ld_shift, rows, idx, eps, a_q, a_scale, y_amax);
+                       shift, ld_shift, rows, idx, eps, a_q, a_scale);
     return hipGetLastError();
 }
 

@@ -50,15 +50,6 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
-// Unsigned maximum over the 16 lanes of a DPP row, left in every lane of it
-__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
-    x = max(x, dpp_u<kDppXor1>(x));
-    x = max(x, dpp_u<kDppXor2>(x));
-    x = max(x, dpp_u<kDppHalfMirror>(x));
-    x = max(x, dpp_u<kDppMirror>(x));
-    return x;
-}
-
 // Q/K output of one (row, head) for the 16 lanes of a DPP row: vp holds this lane's 8 dims
 // (chunk q) of the head as bf16; nwlo / nwhi its 8 norm weights as bf16 pairs with the high /
 // low half zeroed; cs this lane's 16 bytes of the row's cos/sin: the cos of frequencies
