@@ -73,6 +73,26 @@ __device__ __forceinline__ void dot2x4_zero(uint32_t a0, uint32_t b0, uint32_t a
         : "v"(a0), "v"(b0), "v"(a1), "v"(b1), "v"(a2), "v"(b2), "v"(a3), "v"(b3));
 }
 
+// RoPE of four pairs by eight three-operand v_dot2 with an inline zero addend: with
+// ua_e = (u_e, w_e), ub_e = (w_e, u_e) and cs_e = (c_e, s_e) (bf16 pairs),
+//   o_e = u_e c_e - w_e s_e (neg_hi negates the high half of cs_e),  o_(4+e) = w_e c_e + u_e s_e,
+// each product exact and the sum rounded once; the block ends with the wait states of dot2x4_zero.
+__device__ __forceinline__ void rope_dot2x8(const uint32_t (&ua)[4], const uint32_t (&ub)[4], const uint32_t (&cs)[4],
+                                            float (&o)[8]) {
+    asm("v_dot2_f32_bf16 %0, %8, %16, 0 neg_hi:[0,1,0]\n\t"
+        "v_dot2_f32_bf16 %1, %9, %17, 0 neg_hi:[0,1,0]\n\t"
+        "v_dot2_f32_bf16 %2, %10, %18, 0 neg_hi:[0,1,0]\n\t"
+        "v_dot2_f32_bf16 %3, %11, %19, 0 neg_hi:[0,1,0]\n\t"
+        "v_dot2_f32_bf16 %4, %12, %16, 0\n\t"
+        "v_dot2_f32_bf16 %5, %13, %17, 0\n\t"
+        "v_dot2_f32_bf16 %6, %14, %18, 0\n\t"
+        "v_dot2_f32_bf16 %7, %15, %19, 0\n\t"
+        "s_nop 2"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+        : "v"(ua[0]), "v"(ua[1]), "v"(ua[2]), "v"(ua[3]), "v"(ub[0]), "v"(ub[1]), "v"(ub[2]), "v"(ub[3]),
+          "v"(cs[0]), "v"(cs[1]), "v"(cs[2]), "v"(cs[3]));
+}
+
 // 1 + s for the eight bf16 values of four packed words s0 .. s3: per value one three-operand
 // v_dot2 of its word with a unit weight on its half, plus the inline addend 1.0 (r[2i] from the
 // low half of s_i, r[2i + 1] from the high half).  The weights sit in SGPRs; the block ends with

@@ -4,7 +4,7 @@
 // [M, K], weights [N, K]), FP32 accumulation.
 //
 // Workgroup: 8 waves, two per SIMD, and one 256 x 256 output tile; each wave owns a 128 x 64
-// wave tile (128 FP32 accumulators per lane, so a wave fits in 256 registers):
+// wave tile, or 64 x 128 (128 FP32 accumulators per lane, so a wave fits in 256 registers):
 //   bf16:  8 x 4 blocks of 16 x 16, v_mfma_f32_16x16x32_bf16, two k-steps per stage;
 //   e4m3:  8 x 4 blocks of 16 x 16, v_mfma_f32_16x16x128_f8f6f4 (the scaled builtin with zero
 //          scale operands, which the compiler emits as the unscaled instruction), one k-step per
@@ -187,12 +187,19 @@ struct Stage {
     const uint8_t* b;
 };
 
-// Accumulators of one wave: 8 x 4 blocks of 16 x 16.  Lane l, register r of a block holds
-// row 4 (l / 16) + r and column l % 16.
-struct Acc {
-    static constexpr int MB = 8, NB = 4;
+// Accumulators of one wave: MB x NB blocks of 16 x 16.  Lane l, register r of a block holds
+// row 4 (l / 16) + r and column l % 16.  Acc: a 128 x 64 wave tile (two waves across m, four
+// across n); AccW: 64 x 128 (four across m, two across n), so that one wave holds whole
+// 128-column blocks of its rows.  Waves 0-3 hold tile rows 0-127 in both.
+template <int kMB, int kNB>
+struct AccN {
+    static constexpr int MB = kMB, NB = kNB;
+    static constexpr int kRows = 16 * kMB;              // rows of the wave tile
+    static constexpr int kWavesN = kBN / (16 * kNB);    // waves across n
     f32x4 v[MB][NB];
 };
+using Acc = AccN<8, 4>;
+using AccW = AccN<4, 8>;
 // MXFP4: 4 x 2 blocks of 32 x 32.  Lane l, register r of a block holds row
 // 8 (r / 4) + 4 (l / 32) + r % 4 and column l % 32.
 struct AccMx {
@@ -212,24 +219,26 @@ struct AccMx {
 // A and B rows of a lane differ only by the wave's row bases, so the B offsets are the A offsets
 // plus a wave-uniform difference (bdelta, a scalar added to the B slot's base).
 constexpr int kBlk = 16 * kRowB;                // bytes between 16-row blocks
-struct FragAddr {
+template <class AccT>
+struct FragAddrN {
     uint32_t a[2];
     int bdelta;
     __device__ __forceinline__ void init() {
         const int tid = opaque_tid();
         const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int wm = wave / kWN, wn = wave % kWN;
+        const int wm = wave / AccT::kWavesN, wn = wave % AccT::kWavesN;
         const int r = lane % 16, g = lane / 16;
-        const int sw = swz(r);
+        const int sw = swz(r);      // wave row bases are multiples of 16
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int c = 4 * q + g;
-            a[q] = (uint32_t)((wm * 128 + r) * kRowB + ((c ^ sw) << 4));
+            a[q] = (uint32_t)((wm * AccT::kRows + r) * kRowB + ((c ^ sw) << 4));
         }
-        bdelta = (wn * kWaveN - wm * 128) * kRowB;
+        bdelta = (wn * 16 * AccT::NB - wm * AccT::kRows) * kRowB;
     }
 };
+using FragAddr = FragAddrN<Acc>;
 
 // MXFP4 (32x32x64): lane l reads row l % 32 of each 32-row block and, for k-step q, chunk
 // 2 q + l / 32 (32 E2M1 values).  The 16 lanes of a read quarter sit on 16 consecutive rows of
@@ -284,13 +293,13 @@ __device__ __forceinline__ f32x16 mfma_mxfp4(const i32x4& a, const i32x4& b, con
 
 // Every fragment of one stage in registers (24 16-byte reads, 96 registers; MXFP4 adds its 24
 // bytes of scales, which the main loop loads from global memory).
-template <Mma kKind>
+template <Mma kKind, class AccT>
 struct PPFrags;
-template <>
-struct PPFrags<Mma::kBf16> {
-    static constexpr int MB = Acc::MB, NB = Acc::NB;
+template <class AccT>
+struct PPFrags<Mma::kBf16, AccT> {
+    static constexpr int MB = AccT::MB, NB = AccT::NB;
     bf16x8 a[2][MB], b[2][NB];
-    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
+    __device__ __forceinline__ void read(const Stage& st, const FragAddrN<AccT>& fa) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -299,7 +308,7 @@ struct PPFrags<Mma::kBf16> {
             for (int j = 0; j < NB; ++j) b[ks][j] = lds_bf16x8(st.b + fa.bdelta, fa.a[ks] + j * kBlk);
         }
     }
-    __device__ __forceinline__ void mma(Acc& acc) const {
+    __device__ __forceinline__ void mma(AccT& acc) const {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -309,17 +318,17 @@ struct PPFrags<Mma::kBf16> {
                     acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][i], b[ks][j], acc.v[i][j], 0, 0, 0);
     }
 };
-template <>
-struct PPFrags<Mma::kE4m3> {
-    static constexpr int MB = Acc::MB, NB = Acc::NB;
+template <class AccT>
+struct PPFrags<Mma::kE4m3, AccT> {
+    static constexpr int MB = AccT::MB, NB = AccT::NB;
     i32x8 a[MB], b[NB];
-    __device__ __forceinline__ void read(const Stage& st, const FragAddr& fa) {
+    __device__ __forceinline__ void read(const Stage& st, const FragAddrN<AccT>& fa) {
 #pragma unroll
         for (int i = 0; i < MB; ++i) a[i] = lds_i32x8(st.a, fa.a[0] + i * kBlk, fa.a[1] + i * kBlk);
 #pragma unroll
         for (int j = 0; j < NB; ++j) b[j] = lds_i32x8(st.b + fa.bdelta, fa.a[0] + j * kBlk, fa.a[1] + j * kBlk);
     }
-    __device__ __forceinline__ void mma(Acc& acc) const {
+    __device__ __forceinline__ void mma(AccT& acc) const {
 #pragma unroll
         for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -331,7 +340,7 @@ struct PPFrags<Mma::kE4m3> {
 // (32 values, block 2 q + l / 32) of its row.  Scale byte q of the lane's A record I belongs
 // to block row I, k-step q (B: record J).
 template <>
-struct PPFrags<Mma::kMxFp4> {
+struct PPFrags<Mma::kMxFp4, AccMx> {
     static constexpr int MB = AccMx::MB, NB = AccMx::NB;
     i32x4 a[4][MB], b[4][NB];
     u32x4 sa;      // this lane's E8M0 scale records of the stage (loaded by the main loop)
@@ -364,11 +373,12 @@ struct PPFrags<Mma::kMxFp4> {
 // accumulator, placed after the opening barrier and after the MFMAs, orders them: volatile asm
 // statements keep their program order, and the MFMAs consume the first one's outputs and feed the
 // second one's inputs.
-__device__ __forceinline__ void pin_acc(Acc& acc) {
+template <int kMB, int kNB>
+__device__ __forceinline__ void pin_acc(AccN<kMB, kNB>& acc) {
 #pragma unroll
-    for (int i = 0; i < Acc::MB; ++i)
+    for (int i = 0; i < kMB; ++i)
 #pragma unroll
-        for (int j = 0; j < Acc::NB; ++j) asm volatile("" : "+v"(acc.v[i][j]));
+        for (int j = 0; j < kNB; ++j) asm volatile("" : "+v"(acc.v[i][j]));
 }
 __device__ __forceinline__ void pin_acc(AccMx& acc) {
 #pragma unroll
@@ -377,16 +387,26 @@ __device__ __forceinline__ void pin_acc(AccMx& acc) {
         for (int j = 0; j < AccMx::NB; ++j) asm volatile("" : "+v"(acc.w[i][j]));
 }
 
-// Accumulator and fragment-address types of an operand kind.
-template <Mma kKind>
+// Fragment-address type of an operand kind and accumulator layout.
+template <Mma kKind, class AccT>
 struct KindTypes {
-    using AccT = Acc;
-    using FragAddrT = FragAddr;
+    using FragAddrT = FragAddrN<AccT>;
 };
 template <>
-struct KindTypes<Mma::kMxFp4> {
-    using AccT = AccMx;
+struct KindTypes<Mma::kMxFp4, AccMx> {
     using FragAddrT = FragAddrMx;
+};
+
+// B row order of a tile.  BRowsDefault: the local rows [0, 128) are global rows nb0.. and
+// [128, 256) are nb1.. (or interleaved by 16, kInterleaveB).  A map with kMapped set instead
+// names, for each local row L of the B slot, its global row nb0 + row(L) (row(L) in [0, 256),
+// nb1 = nb0 + 128), so the columns of the wave tiles can follow another order.  The fills keep
+// their form (per lane: the row within the 8-row piece, by piece parity; per piece: a uniform
+// base), so the map must satisfy, for every wave w and k < 8,
+//   row(32 w + 8 p + k) - row(32 w + 8 p)  the same for pieces p and p + 2.
+struct BRowsDefault {
+    static constexpr bool kMapped = false;
+    __device__ __forceinline__ int row(int L) const { return L; }
 };
 
 // Phase-ending barrier: wait for vmcnt(kVm) and lgkmcnt(0), then a bare s_barrier.  These
@@ -498,11 +518,12 @@ struct PPFill {
 // after this wave's last in-loop barrier, without the closing barrier pair and drain; the caller
 // then owes G0 one barrier (the one that ends G1's last compute phase) and every wave a drain of
 // its loads before the LDS is reused (the dead loads past the end still write zeros into slots).
-template <Mma kKind, bool kInterleaveB = false, bool kOpenTail = false>
+// AccT: the wave tile (Acc or AccW; AccMx for MXFP4).  bmap: the B row order (BRowsDefault).
+template <Mma kKind, bool kInterleaveB, bool kOpenTail, class AccT, class BMap>
 __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                             const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                            int ktiles, uint8_t* smem, typename KindTypes<kKind>::AccT& acc,
-                                            const MxScales& mxs) {
+                                            int ktiles, uint8_t* smem, AccT& acc, const MxScales& mxs,
+                                            const BMap& bmap) {
     static_assert(kWaves == 8 && kRowB == 128, "ping-pong layout");
     constexpr bool kMx = kKind == Mma::kMxFp4;
     constexpr int kFills = 2 * kPPAPieces;          // fill loads per wave and memory phase
@@ -511,6 +532,8 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const bool g0 = wave < 4;
+    constexpr bool kMapped = BMap::kMapped;
+    static_assert(!(kMapped && (kInterleaveB || kMx)), "one B row order");
     PPFill sf;
     const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
     sf.ra = make_rsrc(A + m0 * lda, (uint32_t)(arows * lda));
@@ -521,7 +544,9 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         const int row = 32 * wave + j * kRowsPerPiece + lane / kSlots;
         sf.va[j] = (uint32_t)(row * lda) + (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
         const int64_t r0 = 32 * wave + j * kRowsPerPiece;                // piece's first row (uniform)
-        if constexpr (kInterleaveB) {
+        if constexpr (kMapped) {
+            sf.sb[j] = (uint32_t)(bmap.row((int)r0) * ldb);
+        } else if constexpr (kInterleaveB) {
             static_assert(kPPAPieces == 4 && kRowsPerPiece == 8, "two pieces per 16-row half");
             const int64_t g = j < 2 ? 16 * wave + 8 * j : (nb1 - nb0) + 16 * wave + 8 * (j - 2);
             sf.sb[j] = (uint32_t)(g * ldb);
@@ -530,7 +555,8 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         }
         if (j < kVPat) {
             const int brow = (int)r0 + lane / kSlots;
-            sf.vb[j] = (uint32_t)((lane / kSlots) * ldb) + (uint32_t)(((lane % kSlots) ^ swz(brow)) << 4);
+            const int in_piece = kMapped ? bmap.row(brow) - bmap.row((int)r0) : lane / kSlots;
+            sf.vb[j] = (uint32_t)(in_piece * ldb) + (uint32_t)(((lane % kSlots) ^ swz(brow)) << 4);
         }
     }
     sf.lds_rows = (uint32_t)(32 * wave * kRowB);
@@ -547,7 +573,7 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         sf.vsa = (uint32_t)(lane * 16);
         sf.vsb = (uint32_t)(lane * 16 + (wn % 2) * 8);
     }
-    typename KindTypes<kKind>::FragAddrT fa;
+    typename KindTypes<kKind, AccT>::FragAddrT fa;
     fa.init();
     if constexpr (kMx) {
 #pragma unroll
@@ -556,12 +582,12 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
             for (int j = 0; j < AccMx::NB; ++j) acc.w[i][j] = 0.f;
     } else {
 #pragma unroll
-        for (int i = 0; i < Acc::MB; ++i)
+        for (int i = 0; i < AccT::MB; ++i)
 #pragma unroll
-            for (int j = 0; j < Acc::NB; ++j) acc.v[i][j] = 0.f;
+            for (int j = 0; j < AccT::NB; ++j) acc.v[i][j] = 0.f;
     }
 
-    PPFrags<kKind> fr;
+    PPFrags<kKind, AccT> fr;
     // prologue: this wave's rows of A(0), B(0) (and the scales of stage 0), then B(1).  A(0)
     // and B(0) must land before the first reads; B(1) before this wave's first wait that
     // covers it (G1: the end of its first memory phase; G0: the end of its first compute phase)
@@ -610,14 +636,15 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
 
 // Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
 // [0,128) are global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a
-// plain tile; for MXFP4 both multiples of 128).  Ends with all loads drained and a barrier, so
-// the caller may reuse the LDS (kSmemBytes).
-template <Mma kKind, bool kInterleaveB = false, bool kOpenTail = false>
+// plain tile; for MXFP4 both multiples of 128), unless bmap orders them.  Ends with all loads
+// drained and a barrier, so the caller may reuse the LDS (kSmemBytes), unless kOpenTail.
+template <Mma kKind, bool kInterleaveB = false, bool kOpenTail = false, class AccT, class BMap = BRowsDefault>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
-                                         int ktiles, uint8_t* smem, typename KindTypes<kKind>::AccT& acc,
-                                         const MxScales& mxs = MxScales{}) {
-    mainloop_pp<kKind, kInterleaveB, kOpenTail>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs);
+                                         int ktiles, uint8_t* smem, AccT& acc, const MxScales& mxs = MxScales{},
+                                         const BMap& bmap = BMap{}) {
+    mainloop_pp<kKind, kInterleaveB, kOpenTail, AccT, BMap>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc,
+                                                             mxs, bmap);
 }
 
 
