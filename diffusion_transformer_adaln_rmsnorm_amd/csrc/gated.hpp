@@ -100,5 +100,110 @@ struct GatedResidual {
     }
 };
 
+// The same gated residual straight from the accumulators: 64 x 128 wave tiles (AccW) with the
+// B rows in Cols8BRows order, so wave (wm, h) holds rows 64 wm + 16 i + 4 (l / 16) + r
+// (i, r < 4) of the tile and, for each, the 8 columns n0 + 128 h + 8 (l % 16) .. + 7 (block j:
+// column + j).  kScaled: o = bf16((acc s_row) s_col) with the row scales rowscale[m] and the
+// column scales colscale[n] (FC2), else o = bf16(acc).  Then out = bf16(r + bf16(g o)) with
+// the staged epilogue's arithmetic, 16 bytes per row and lane for r, g and out.  The 16 lanes of
+// a DPP row share their 16 rows: lane l % 16 = c loads the index of row (c / 4, c % 4) and hands
+// the checked gate row to the others (ds_bpermute).  No LDS and no barrier, so G0 can run it
+// while G1 finishes its last compute phase.  Each lane reads its residual chunk before it
+// writes the same chunk of out, so out may be the residual buffer.
+template <typename Idx, bool kScaled>
+__device__ __forceinline__ void gated_epilogue_regs(const AccW& acc, int64_t m0, int64_t M, int n0,
+                                                    const float* __restrict__ rowscale,
+                                                    const float* __restrict__ colscale, const Idx* __restrict__ index,
+                                                    const uint16_t* __restrict__ gate, int64_t gate_rows,
+                                                    int64_t gate_ld, const uint16_t* residual, uint16_t* out) {
+    const int t = opaque_tid();
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave / AccW::kWavesN, h = wave % AccW::kWavesN;
+    const int c = lane & 15, rq = lane >> 4;
+    const int rbase = wm * AccW::kRows + 4 * rq;          // + 16 i + r: this lane's rows
+    const int col0 = n0 + 128 * h + 8 * c;                // this lane's 8 columns
+    const int64_t tile_rows = M - m0 < kBM ? M - m0 : kBM;
+    // residual, out and the row indices through descriptors over the tile's rows: rows past M
+    // read zeros (index 0) and their stores are dropped
+    const uint32_t bytes = (uint32_t)(tile_rows * kHidden * 2);
+    const __amdgpu_buffer_rsrc_t rres = make_rsrc(residual + m0 * kHidden, bytes);
+    const __amdgpu_buffer_rsrc_t rout = make_rsrc(out + m0 * kHidden, bytes);
+    const uint32_t vo = (uint32_t)((rbase * kHidden + col0) * 2);   // row (i, r) adds (16 i + r) kHidden 2
+    int32_t gi_own;
+    {
+        const __amdgpu_buffer_rsrc_t ri = make_rsrc(index + m0, (uint32_t)(tile_rows * sizeof(Idx)));
+        const uint32_t off = (uint32_t)((rbase + 16 * (c >> 2) + (c & 3)) * sizeof(Idx));
+        int64_t iv;
+        if constexpr (sizeof(Idx) == 8) {
+            iv = buf_ld_i64(ri, off);
+        } else {
+            iv = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (int)off, 0, 0);
+        }
+        gi_own = (iv >= 0 && iv < gate_rows) ? (int32_t)iv : -1;
+    }
+    // one 4-row block's residual and gate chunks (requested a block ahead)
+    auto load_block = [&](int i, u32x4 (&rr)[4], u32x4 (&gg)[4]) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            rr[r] = buf_ld16(rres, vo + (uint32_t)((16 * i + r) * kHidden * 2));
+            const int gi = __builtin_amdgcn_ds_bpermute(4 * (16 * rq + 4 * i + r), gi_own);
+            gg[r] = u32x4{0u, 0u, 0u, 0u};
+            if (gi >= 0) gg[r] = ld16(gate + (int64_t)gi * gate_ld + col0);
+        }
+    };
+    u32x4 rr_nx[4], gg_nx[4];
+    load_block(0, rr_nx, gg_nx);
+    // o as bf16, packed: op[i][r][k] = columns 2 k, 2 k + 1 of row (i, r)
+    u32x4 op[AccW::MB][4];
+    if constexpr (kScaled) {
+        float cs[8];    // (the column scales need only 4-byte alignment: one load each)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[e] = colscale[col0 + e];
+        const __amdgpu_buffer_rsrc_t rrs = make_rsrc(rowscale + m0, (uint32_t)(tile_rows * 4));
+#pragma unroll
+        for (int i = 0; i < AccW::MB; ++i) {
+            const u32x4 rsv = buf_ld16(rrs, (uint32_t)((rbase + 16 * i) * 4));
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float rs = __uint_as_float(rsv[r]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    op[i][r][k] = pack_bf2((acc.v[i][2 * k][r] * rs) * cs[2 * k],
+                                           (acc.v[i][2 * k + 1][r] * rs) * cs[2 * k + 1]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < AccW::MB; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) op[i][r][k] = pack_bf2(acc.v[i][2 * k][r], acc.v[i][2 * k + 1][r]);
+    }
+#pragma unroll
+    for (int i = 0; i < AccW::MB; ++i) {
+        u32x4 rr[4], gg[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            rr[r] = rr_nx[r];
+            gg[r] = gg_nx[r];
+        }
+        if (i + 1 < AccW::MB) load_block(i + 1, rr_nx, gg_nx);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            u32x4 res;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // as in finish(): g o rounded to bf16, then r + that, one rounding of the exact sum
+                const uint32_t ov = op[i][r][k];
+                const uint32_t go = pack_bf2(bf_lo(gg[r][k]) * bf_lo(ov), bf_hi(gg[r][k]) * bf_hi(ov));
+                res[k] = pack_bf2(bf_lo(rr[r][k]) + bf_lo(go), bf_hi(rr[r][k]) + bf_hi(go));
+            }
+            buf_st16(rout, vo + (uint32_t)((16 * i + r) * kHidden * 2), res);
+        }
+    }
+}
+
 }  // namespace gemm
 }  // namespace dit

@@ -408,6 +408,32 @@ struct BRowsDefault {
     static constexpr bool kMapped = false;
     __device__ __forceinline__ int row(int L) const { return L; }
 };
+// Compile-time check of a row map given as a constexpr function of L: a permutation of [0, 256)
+// with the fill form above.
+template <class RowFn>
+constexpr bool brow_map_ok(RowFn row) {
+    bool seen[256] = {};
+    for (int L = 0; L < 256; ++L) {
+        const int g = row(L);
+        if (g < 0 || g >= 256 || seen[g]) return false;
+        seen[g] = true;
+    }
+    for (int L0 = 0; L0 < 256; L0 += 32)
+        for (int p = 0; p < 2; ++p)
+            for (int k = 0; k < 8; ++k)
+                if (row(L0 + 8 * p + k) - row(L0 + 8 * p) != row(L0 + 8 * (p + 2) + k) - row(L0 + 8 * (p + 2)))
+                    return false;
+    return true;
+}
+// The map that gives each lane of a 64 x 128 wave tile (AccW) 8 contiguous columns: local row
+// L = 128 h + 16 j + c is row 128 h + 8 c + j, so lane column c of block j holds column 8 c + j of
+// its 128-column half.
+__host__ __device__ constexpr int cols8_brow(int L) { return 128 * (L >> 7) + 8 * (L & 15) + ((L >> 4) & 7); }
+struct Cols8BRows {
+    static constexpr bool kMapped = true;
+    __device__ __forceinline__ int row(int L) const { return cols8_brow(L); }
+};
+static_assert(brow_map_ok([](int L) { return cols8_brow(L); }), "8-column B row order");
 
 // Phase-ending barrier: wait for vmcnt(kVm) and lgkmcnt(0), then a bare s_barrier.  These
 // waits are all the hand-over needs, so younger fill loads stay in flight across it (the

@@ -160,15 +160,20 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
         logical_coords(tq.lo + k, mt, nt, tm, tn);
         const int64_t m0 = (int64_t)tm * kBM;
         const int n0 = tn * kBN;
-        Acc acc;
-        mainloop<Mma::kE4m3>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc);
-        tq.claim(smem);
-        GatedResidual<int64_t> gr;
-        gr.load_index(idx, m0, M, gate_rows);
-        stage_tile_bf16(acc, smem, y_scale, m0, M, w2s + n0, w2s + n0 + 128);
-        lds_barrier();
-        gr.run(smem, m0, M, n0, gate, gate_rows, gate_ld, residual, out);
-        __syncthreads();
+        AccW acc;
+        mainloop<Mma::kE4m3, false, true>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc,
+                                          MxScales{}, Cols8BRows{});
+        if (opaque_tid() < kThreads / 2) {          // G0: its epilogue overlaps G1's last compute phase
+            __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): G0's dead fills landed (claim word rows)
+            gated_epilogue_regs<int64_t, true>(acc, m0, M, n0, y_scale, w2s, idx, gate, gate_rows, gate_ld, residual,
+                                               out);
+            pp_barrier<63>();   // the barrier that ends G1's last compute phase
+            tq.claim(smem);
+        } else {
+            gated_epilogue_regs<int64_t, true>(acc, m0, M, n0, y_scale, w2s, idx, gate, gate_rows, gate_ld, residual,
+                                               out);
+        }
+        __syncthreads();        // every wave's loads drained before the next fills; the claim visible
     }
     tq.finish();
 }

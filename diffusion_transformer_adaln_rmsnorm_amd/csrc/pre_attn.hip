@@ -59,22 +59,9 @@ struct QkvBRows {
 // The order is a permutation of the tile's 256 rows, and it keeps the fills' form: within each
 // 8-row fill piece the rows step from the piece's first row the same way in pieces p and p + 2
 // of a wave (by 4 for rotated dims, by 8 for pass-through and V dims).
-constexpr bool qkv_brows_ok(bool rope) {
-    bool seen[256] = {};
-    for (int L = 0; L < 256; ++L) {
-        const int g = qkv_brow(L, rope);
-        if (g < 0 || g >= 256 || seen[g]) return false;
-        seen[g] = true;
-    }
-    for (int L0 = 0; L0 < 256; L0 += 32)
-        for (int p = 0; p < 2; ++p)
-            for (int k = 0; k < 8; ++k)
-                if (qkv_brow(L0 + 8 * p + k, rope) - qkv_brow(L0 + 8 * p, rope) !=
-                    qkv_brow(L0 + 8 * (p + 2) + k, rope) - qkv_brow(L0 + 8 * (p + 2), rope))
-                    return false;
-    return true;
-}
-static_assert(qkv_brows_ok(true) && qkv_brows_ok(false), "QKV B row order");
+static_assert(brow_map_ok([](int L) { return qkv_brow(L, true); }) &&
+                  brow_map_ok([](int L) { return qkv_brow(L, false); }),
+              "QKV B row order");
 
 // e4m3 output mode ("minimax_h3_nvfp4_pre_attention", Parameters: out_mode "e4m3" with
 // per-tensor q/k/v dequantization scales): 4 bf16 values (two packed pairs) become
