@@ -137,6 +137,27 @@ struct TileQueue {
     __device__ __forceinline__ int claimed(uint8_t* smem) const {
         return __builtin_amdgcn_readfirstlane((int)*slot(smem));
     }
+    // The claim of persistent_tiles: thread 0 marks the slot empty once the tile's main loop no
+    // longer writes it (mark_empty) and, past a barrier, claims into it (claim_wait); the waves
+    // wait on the slot itself, not on a barrier, for the claimed index (wait_claimed).  A counter
+    // never reaches kEmpty (it grows by at most one per claim past its range's length).
+    static constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+    __device__ __forceinline__ void mark_empty(uint8_t* smem) const {
+        if (threadIdx.x == 0) *slot(smem) = kEmpty;
+    }
+    __device__ __forceinline__ int wait_claimed(uint8_t* smem) const {
+        volatile uint32_t* w = slot(smem);
+        uint32_t v = *w;
+        while (v == kEmpty) {           // thread 0 of this workgroup writes it once its atomic returns
+            __builtin_amdgcn_s_sleep(1);
+            v = *w;
+        }
+        return __builtin_amdgcn_readfirstlane((int)v);
+    }
+    __device__ __forceinline__ int claim_wait(uint8_t* smem) const {
+        if (threadIdx.x == 0) *(volatile uint32_t*)slot(smem) = atomicAdd(ctr, 1u);
+        return wait_claimed(smem);
+    }
 };
 static_assert(kSmemBytes >= kEpiBytes + 4, "tile queue slot");
 
@@ -538,18 +559,66 @@ struct PPFill {
     }
 };
 
+// The operands of one tile's main loop: A rows m0.. of its M rows (rows past M read as zero),
+// B local rows [0, 128) from global row nb0 and [128, 256) from nb1 (nb1 = nb0 + 128 for a plain
+// tile; for MXFP4 both multiples of 128), unless kInterleaveB or a row map orders them; ktiles
+// stages of kRowB bytes per row.
+struct TileOps {
+    const uint8_t* A;
+    int64_t lda, m0, M;
+    const uint8_t* B;
+    int64_t ldb, nb0, nb1;
+    int ktiles;
+};
+
+// The fill descriptors and per-lane offsets of wave `wave`'s 32 rows of A and B (lane `lane`).
+template <bool kInterleaveB, class BMap>
+__device__ __forceinline__ void fill_setup(PPFill& sf, const TileOps& t, int wave, int lane, const BMap& bmap) {
+    constexpr bool kMapped = BMap::kMapped;
+    static_assert(!(kMapped && kInterleaveB), "one B row order");
+    const int64_t arows = t.M - t.m0 < kBM ? t.M - t.m0 : kBM;
+    sf.ra = make_rsrc(t.A + t.m0 * t.lda, (uint32_t)(arows * t.lda));
+    sf.rb = make_rsrc(t.B + t.nb0 * t.ldb, (uint32_t)((t.nb1 - t.nb0 + 128) * t.ldb));
+    sf.rnull = make_rsrc(t.B, 0u);
+#pragma unroll
+    for (int j = 0; j < kPPAPieces; ++j) {
+        const int row = 32 * wave + j * kRowsPerPiece + lane / kSlots;
+        sf.va[j] = (uint32_t)(row * t.lda) + (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
+        const int64_t r0 = 32 * wave + j * kRowsPerPiece;                // piece's first row (uniform)
+        if constexpr (kMapped) {
+            sf.sb[j] = (uint32_t)(bmap.row((int)r0) * t.ldb);
+        } else if constexpr (kInterleaveB) {
+            static_assert(kPPAPieces == 4 && kRowsPerPiece == 8, "two pieces per 16-row half");
+            const int64_t g = j < 2 ? 16 * wave + 8 * j : (t.nb1 - t.nb0) + 16 * wave + 8 * (j - 2);
+            sf.sb[j] = (uint32_t)(g * t.ldb);
+        } else {
+            sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (t.nb1 - t.nb0 - 128)) * t.ldb);
+        }
+        if (j < kVPat) {
+            const int brow = (int)r0 + lane / kSlots;
+            const int in_piece = kMapped ? bmap.row(brow) - bmap.row((int)r0) : lane / kSlots;
+            sf.vb[j] = (uint32_t)(in_piece * t.ldb) + (uint32_t)(((lane % kSlots) ^ swz(brow)) << 4);
+        }
+    }
+    sf.lds_rows = (uint32_t)(32 * wave * kRowB);
+}
+
 // kInterleaveB: B local rows 32 w + [0, 16) are global rows nb0 + 16 w + [0, 16) and 32 w + [16,
 // 32) are nb1 + 16 w + [0, 16) (w = 0..7), so each wave's 16-column blocks alternate between the
-// two halves and a lane holds matching columns of both in adjacent blocks.  kOpenTail: return
-// after this wave's last in-loop barrier, without the closing barrier pair and drain; the caller
-// then owes G0 one barrier (the one that ends G1's last compute phase) and every wave a drain of
-// its loads before the LDS is reused (the dead loads past the end still write zeros into slots).
+// two halves and a lane holds matching columns of both in adjacent blocks.  kPersist: the tile is
+// one of a persistent workgroup's run (persistent_tiles).  Then, when `prefilled`, its prologue
+// fills (A(0), B(0), B(1), all 256 rows) were issued by G0 during the previous tile's boundary
+// and have landed behind a barrier; each group waits for every load of its last phase that issues
+// any (the dead ones past the end included) before that phase's barrier, so that once G0 has left
+// the loop no fill of the tile is in flight; and the loop returns after each wave's last in-loop
+// barrier, without the closing barrier: the caller then owes G0 one barrier (the one that ends
+// G1's last compute phase).
 // AccT: the wave tile (Acc or AccW; AccMx for MXFP4).  bmap: the B row order (BRowsDefault).
-template <Mma kKind, bool kInterleaveB, bool kOpenTail, class AccT, class BMap>
+template <Mma kKind, bool kInterleaveB, bool kPersist, class AccT, class BMap>
 __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                             const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
                                             int ktiles, uint8_t* smem, AccT& acc, const MxScales& mxs,
-                                            const BMap& bmap) {
+                                            const BMap& bmap, bool prefilled = false) {
     static_assert(kWaves == 8 && kRowB == 128, "ping-pong layout");
     constexpr bool kMx = kKind == Mma::kMxFp4;
     constexpr int kFills = 2 * kPPAPieces;          // fill loads per wave and memory phase
@@ -558,34 +627,10 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform per wave
     const bool g0 = wave < 4;
-    constexpr bool kMapped = BMap::kMapped;
-    static_assert(!(kMapped && (kInterleaveB || kMx)), "one B row order");
+    static_assert(!(BMap::kMapped && kMx), "one B row order");
+    static_assert(!(kPersist && kMx), "persistent runs take register epilogues (no MXFP4 scales)");
     PPFill sf;
-    const int64_t arows = M - m0 < kBM ? M - m0 : kBM;
-    sf.ra = make_rsrc(A + m0 * lda, (uint32_t)(arows * lda));
-    sf.rb = make_rsrc(B + nb0 * ldb, (uint32_t)((nb1 - nb0 + 128) * ldb));
-    sf.rnull = make_rsrc(B, 0u);
-#pragma unroll
-    for (int j = 0; j < kPPAPieces; ++j) {
-        const int row = 32 * wave + j * kRowsPerPiece + lane / kSlots;
-        sf.va[j] = (uint32_t)(row * lda) + (uint32_t)(((lane % kSlots) ^ swz(row)) << 4);
-        const int64_t r0 = 32 * wave + j * kRowsPerPiece;                // piece's first row (uniform)
-        if constexpr (kMapped) {
-            sf.sb[j] = (uint32_t)(bmap.row((int)r0) * ldb);
-        } else if constexpr (kInterleaveB) {
-            static_assert(kPPAPieces == 4 && kRowsPerPiece == 8, "two pieces per 16-row half");
-            const int64_t g = j < 2 ? 16 * wave + 8 * j : (nb1 - nb0) + 16 * wave + 8 * (j - 2);
-            sf.sb[j] = (uint32_t)(g * ldb);
-        } else {
-            sf.sb[j] = (uint32_t)((r0 < 128 ? r0 : r0 + (nb1 - nb0 - 128)) * ldb);
-        }
-        if (j < kVPat) {
-            const int brow = (int)r0 + lane / kSlots;
-            const int in_piece = kMapped ? bmap.row(brow) - bmap.row((int)r0) : lane / kSlots;
-            sf.vb[j] = (uint32_t)(in_piece * ldb) + (uint32_t)(((lane % kSlots) ^ swz(brow)) << 4);
-        }
-    }
-    sf.lds_rows = (uint32_t)(32 * wave * kRowB);
+    fill_setup<kInterleaveB>(sf, TileOps{A, lda, m0, M, B, ldb, nb0, nb1, ktiles}, wave, lane, bmap);
     if constexpr (kMx) {
         // A: the 128-row group of this wave's rows (the last m tile's second group may lie past
         // the array: zero records, scales read as 0); B: the group of this wave's 64 columns
@@ -614,14 +659,16 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
     }
 
     PPFrags<kKind, AccT> fr;
-    // prologue: this wave's rows of A(0), B(0) (and the scales of stage 0), then B(1).  A(0)
-    // and B(0) must land before the first reads; B(1) before this wave's first wait that
-    // covers it (G1: the end of its first memory phase; G0: the end of its first compute phase)
-    sf.a_rows(smem, 0, 0, true);
-    sf.b_rows(smem, 0, 0, true);
-    if constexpr (kMx) sf.scales(fr.sa, fr.sb, 0, true);
-    sf.b_rows(smem, 1, 1, ktiles > 1);
-    pp_barrier<kPPAPieces + kScl>();
+    if (!(kPersist && prefilled)) {
+        // prologue: this wave's rows of A(0), B(0) (and the scales of stage 0), then B(1).  A(0)
+        // and B(0) must land before the first reads; B(1) before this wave's first wait that
+        // covers it (G1: the end of its first memory phase; G0: the end of its first compute phase)
+        sf.a_rows(smem, 0, 0, true);
+        sf.b_rows(smem, 0, 0, true);
+        if constexpr (kMx) sf.scales(fr.sa, fr.sb, 0, true);
+        sf.b_rows(smem, 1, 1, ktiles > 1);
+        pp_barrier<kPPAPieces + kScl>();
+    }
     if (!g0) pp_barrier<63>();       // G1 starts one phase behind
     int sb_read = 0;                 // B slot of stage kt (kt % 3)
     // Not unrolled or peeled: in a peeled copy the scheduler reordered the MFMAs of the two
@@ -639,8 +686,10 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         __builtin_amdgcn_sched_barrier(0);
         if (g0) {
             pp_barrier<kMx ? kFills : 63>();         // MXFP4: the scales of stage kt landed
-        } else {
+        } else if (!kPersist || kt + 1 < ktiles) {
             pp_barrier<kFills>();                    // B(kt+1) (and the scales of kt) landed
+        } else {
+            pp_barrier<0>();                         // the last one: its dead fills landed too
         }
         // compute phase: MFMAs only, then the next stage's scales into the registers they used
         __builtin_amdgcn_sched_barrier(0);
@@ -650,29 +699,100 @@ __device__ __forceinline__ void mainloop_pp(const uint8_t* __restrict__ A, int64
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (kMx) sf.scales(fr.sa, fr.sb, kt + 1, kt + 1 < ktiles);
         __builtin_amdgcn_sched_barrier(0);
-        pp_barrier<kPPAPieces + kScl>();             // A(kt+1) (G0: and B(kt+1)) landed
+        if (!kPersist || kt + 1 < ktiles || !g0) {
+            pp_barrier<kPPAPieces + kScl>();         // A(kt+1) (G0: and B(kt+1)) landed
+        } else {
+            pp_barrier<0>();                         // G0's last: its dead fills landed too
+        }
         sb_read = sb_read == 2 ? 0 : sb_read + 1;
     }
-    if constexpr (!kOpenTail) {
+    if constexpr (!kPersist) {
         if (g0) pp_barrier<63>();    // G1's last compute phase
         // drain every load (the dead ones too: they write zeros into the slots the caller reuses)
         __syncthreads();
     }
 }
 
-// Main loop over `ktiles` stages of K.  A rows m0.. (rows past M read as zero), B local rows
-// [0,128) are global rows nb0.., local rows [128,256) are nb1.. (nb1 = nb0 + 128 for a
-// plain tile; for MXFP4 both multiples of 128), unless bmap orders them.  Ends with all loads
-// drained and a barrier, so the caller may reuse the LDS (kSmemBytes), unless kOpenTail.
-template <Mma kKind, bool kInterleaveB = false, bool kOpenTail = false, class AccT, class BMap = BRowsDefault>
+// Main loop over `ktiles` stages of K for one tile (TileOps).  Ends with all loads drained and a
+// barrier, so the caller may reuse the LDS (kSmemBytes).
+template <Mma kKind, bool kInterleaveB = false, class AccT, class BMap = BRowsDefault>
 __device__ __forceinline__ void mainloop(const uint8_t* __restrict__ A, int64_t lda, int64_t m0, int64_t M,
                                          const uint8_t* __restrict__ B, int64_t ldb, int64_t nb0, int64_t nb1,
                                          int ktiles, uint8_t* smem, AccT& acc, const MxScales& mxs = MxScales{},
                                          const BMap& bmap = BMap{}) {
-    mainloop_pp<kKind, kInterleaveB, kOpenTail, AccT, BMap>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc,
-                                                             mxs, bmap);
+    mainloop_pp<kKind, kInterleaveB, false, AccT, BMap>(A, lda, m0, M, B, ldb, nb0, nb1, ktiles, smem, acc, mxs,
+                                                         bmap);
 }
 
+// G0 wave w issues a tile's prologue fills for its own rows and for those of wave w + 4 (G1):
+// A(0) and B(0) first (16 loads), then B(1) (8 loads; through the null descriptor for a one-stage
+// tile).
+template <bool kInterleaveB, class BMap>
+__device__ __forceinline__ void prefill(const TileOps& t, uint8_t* smem, const BMap& bmap) {
+    const int tid = opaque_tid();
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    PPFill f0, f1;
+    fill_setup<kInterleaveB>(f0, t, wave, lane, bmap);
+    fill_setup<kInterleaveB>(f1, t, wave + 4, lane, bmap);
+    f0.a_rows(smem, 0, 0, true);
+    f1.a_rows(smem, 0, 0, true);
+    f0.b_rows(smem, 0, 0, true);
+    f1.b_rows(smem, 0, 0, true);
+    f0.b_rows(smem, 1, 1, t.ktiles > 1);
+    f1.b_rows(smem, 1, 1, t.ktiles > 1);
+}
+
+// A persistent workgroup's run over the tiles it claims from tq, for the kernels whose epilogue
+// works from the accumulators (no LDS).  tile(k, TileOps&, BMap&) names the operands of claimed
+// tile k; epi(acc, TileOps) writes the tile out.  At each tile boundary G0 runs its epilogue while
+// G1 finishes its last compute phase; past the barrier that ends that phase, G1 runs its epilogue
+// while G0 claims the next tile.  kPrefill: G0 then also issues the next tile's prologue fills for
+// all 256 rows, so their latency hides behind G1's epilogue instead of following it, and the next
+// main loop starts with its first memory phase.  That pays where the clock has headroom (the e4m3
+// GEMMs: MLP -0.85%); the bf16 GEMMs run at the power limit, where a shorter idle gap only lowers
+// the clock (QKV and out-projection +0.2-0.3%, within noise), and load their own prologue.  The
+// barrier after both epilogues drains every load.
+template <Mma kKind, bool kInterleaveB, bool kPrefill, class AccT, class BMap, class TileFn, class EpiFn>
+__device__ __forceinline__ void persistent_tiles(const TileQueue& tq, uint8_t* smem, TileFn tile, EpiFn epi) {
+    tq.claim(smem);
+    __syncthreads();
+    const bool g0 = __builtin_amdgcn_readfirstlane(opaque_tid() >> 6) < 4;
+    bool prefilled = false;
+    int k = tq.claimed(smem);
+    while (k < tq.cnt) {
+        TileOps t;
+        BMap bm;
+        tile(k, t, bm);
+        AccT acc;
+        mainloop_pp<kKind, kInterleaveB, true, AccT, BMap>(t.A, t.lda, t.m0, t.M, t.B, t.ldb, t.nb0, t.nb1,
+                                                            t.ktiles, smem, acc, MxScales{}, bm, prefilled);
+        int kn;
+        if (g0) {
+            // no fill is in flight (the main loop's last barriers waited for them all, the dead
+            // ones that write the claim word's rows included), so the slot keeps what is written
+            tq.mark_empty(smem);
+            epi(acc, t);
+            pp_barrier<63>();   // the barrier that ends G1's last compute phase
+            kn = tq.claim_wait(smem);
+            if (kPrefill && kn < tq.cnt) {
+                TileOps tn;
+                BMap bmn;
+                tile(kn, tn, bmn);
+                prefill<kInterleaveB>(tn, smem, bmn);
+            }
+        } else {
+            epi(acc, t);
+            kn = tq.wait_claimed(smem);
+        }
+        // every wave's loads drained (the next tile's prologue fills landed) and every read of the
+        // claim word done before the next tile's first fill of its row
+        __syncthreads();
+        k = kn;
+        prefilled = kPrefill;
+    }
+    tq.finish();
+}
 
 // Epilogue phase 1: tile[row][col] = bf16((acc * rowscale[row]) * colscale[col]) into LDS
 // (row pitch kEpiPitch), the products in fp32 as printed, then RNE to bf16.

@@ -82,29 +82,14 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
                   int nt, uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     const TileQueue tq(tq_ctr, mt, nt);
-    tq.claim(smem);
-    __syncthreads();
-    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+    auto tile = [&](int k, TileOps& t, BRowsDefault&) {
         int tm, tn;
         logical_coords(tq.lo + k, mt, nt, tm, tn);
-        const int64_t m0 = (int64_t)tm * kBM;
         const int j0 = tn * 128;
-        Acc acc;
-        mainloop<Mma::kE4m3, true, true>(a_q, kHidden, m0, M, W1, kHidden, j0, kInter + j0, kHidden / kRowB, smem,
-                                         acc);
-        if (opaque_tid() < kThreads / 2) {          // G0: its epilogue overlaps G1's last compute phase
-            // G0's dead fills past the end land first (they write the slot rows that hold the
-            // claim word); the epilogue's own loads and stores need no wait before the barrier
-            __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
-            fc1_epilogue_regs(acc, m0, M, j0, a_scale, w1s, y);
-            pp_barrier<63>();   // the barrier that ends G1's last compute phase
-            tq.claim(smem);
-        } else {
-            fc1_epilogue_regs(acc, m0, M, j0, a_scale, w1s, y);
-        }
-        __syncthreads();        // every wave's loads drained before the next fills; the claim visible
-    }
-    tq.finish();
+        t = TileOps{a_q, kHidden, (int64_t)tm * kBM, M, W1, kHidden, j0, kInter + j0, kHidden / kRowB};
+    };
+    auto epi = [&](const Acc& acc, const TileOps& t) { fc1_epilogue_regs(acc, t.m0, M, (int)t.nb0, a_scale, w1s, y); };
+    persistent_tiles<Mma::kE4m3, true, true, Acc, BRowsDefault>(tq, smem, tile, epi);
 }
 
 // y quantisation: one wavefront per row; 14336 = 1792 chunks of 8, 28 per lane.  The row is
@@ -153,29 +138,17 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
                  uint16_t* out, int mt, int nt, uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     const TileQueue tq(tq_ctr, mt, nt);
-    tq.claim(smem);
-    __syncthreads();
-    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+    auto tile = [&](int k, TileOps& t, Cols8BRows&) {
         int tm, tn;
         logical_coords(tq.lo + k, mt, nt, tm, tn);
-        const int64_t m0 = (int64_t)tm * kBM;
         const int n0 = tn * kBN;
-        AccW acc;
-        mainloop<Mma::kE4m3, false, true>(y_q, kInter, m0, M, W2, kInter, n0, n0 + 128, kInter / kRowB, smem, acc,
-                                          MxScales{}, Cols8BRows{});
-        if (opaque_tid() < kThreads / 2) {          // G0: its epilogue overlaps G1's last compute phase
-            __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): G0's dead fills landed (claim word rows)
-            gated_epilogue_regs<int64_t, true>(acc, m0, M, n0, y_scale, w2s, idx, gate, gate_rows, gate_ld, residual,
-                                               out);
-            pp_barrier<63>();   // the barrier that ends G1's last compute phase
-            tq.claim(smem);
-        } else {
-            gated_epilogue_regs<int64_t, true>(acc, m0, M, n0, y_scale, w2s, idx, gate, gate_rows, gate_ld, residual,
-                                               out);
-        }
-        __syncthreads();        // every wave's loads drained before the next fills; the claim visible
-    }
-    tq.finish();
+        t = TileOps{y_q, kInter, (int64_t)tm * kBM, M, W2, kInter, n0, n0 + 128, kInter / kRowB};
+    };
+    auto epi = [&](const AccW& acc, const TileOps& t) {
+        gated_epilogue_regs<int64_t, true>(acc, t.m0, M, (int)t.nb0, y_scale, w2s, idx, gate, gate_rows, gate_ld,
+                                           residual, out);
+    };
+    persistent_tiles<Mma::kE4m3, false, true, AccW, Cols8BRows>(tq, smem, tile, epi);
 }
 
 hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M, const uint8_t* W1,

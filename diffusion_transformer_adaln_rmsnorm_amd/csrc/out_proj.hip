@@ -23,32 +23,18 @@ void k_out_proj_gemm(const uint16_t* __restrict__ attn, int64_t M, const uint16_
                      int nt, uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     const TileQueue tq(tq_ctr, mt, nt);
-    tq.claim(smem);
-    __syncthreads();
-    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+    auto tile = [&](int k, TileOps& t, Cols8BRows&) {
         int tm, tn;
         logical_coords(tq.lo + k, mt, nt, tm, tn);
-        const int64_t m0 = (int64_t)tm * kBM;
         const int n0 = tn * kBN;
-        AccW acc;
-        mainloop<Mma::kBf16, false, true>(reinterpret_cast<const uint8_t*>(attn), kAttnWidth * 2, m0, M,
-                                          reinterpret_cast<const uint8_t*>(Wo), kAttnWidth * 2, n0, n0 + 128,
-                                          kAttnWidth * 2 / kRowB, smem, acc, MxScales{}, Cols8BRows{});
-        if (opaque_tid() < kThreads / 2) {          // G0: its epilogue overlaps G1's last compute phase
-            // G0's dead fills past the end land first (they write the slot rows that hold the
-            // claim word); the epilogue's own loads and stores need no wait before the barrier
-            __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
-            gated_epilogue_regs<int32_t, false>(acc, m0, M, n0, nullptr, nullptr, gate_index, gate, gate_rows,
-                                                gate_ld, residual, out);
-            pp_barrier<63>();   // the barrier that ends G1's last compute phase
-            tq.claim(smem);
-        } else {
-            gated_epilogue_regs<int32_t, false>(acc, m0, M, n0, nullptr, nullptr, gate_index, gate, gate_rows,
-                                                gate_ld, residual, out);
-        }
-        __syncthreads();        // every wave's loads drained before the next fills; the claim visible
-    }
-    tq.finish();
+        t = TileOps{reinterpret_cast<const uint8_t*>(attn), kAttnWidth * 2, (int64_t)tm * kBM, M,
+                    reinterpret_cast<const uint8_t*>(Wo), kAttnWidth * 2, n0, n0 + 128, kAttnWidth * 2 / kRowB};
+    };
+    auto epi = [&](const AccW& acc, const TileOps& t) {
+        gated_epilogue_regs<int32_t, false>(acc, t.m0, M, (int)t.nb0, nullptr, nullptr, gate_index, gate, gate_rows,
+                                            gate_ld, residual, out);
+    };
+    persistent_tiles<Mma::kBf16, false, false, AccW, Cols8BRows>(tq, smem, tile, epi);
 }
 
 hipError_t launch_out_proj_gemm(const uint16_t* attn, int64_t M, const uint16_t* Wo, const uint16_t* gate,

@@ -353,31 +353,18 @@ void k_qkv_gemm(const uint16_t* __restrict__ ws, int64_t M, const uint16_t* __re
                 int hpd, float dq, float dk, float dv, void* __restrict__ out, int mt, int nt, uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     const TileQueue tq(tq_ctr, mt, nt);
-    tq.claim(smem);
-    __syncthreads();
-    for (int k = tq.claimed(smem); k < tq.cnt; k = tq.claimed(smem)) {
+    auto tile = [&](int k, TileOps& t, QkvBRows& bm) {
         int tm, tn;
         logical_coords(tq.lo + k, mt, nt, tm, tn);
-        const int64_t m0 = (int64_t)tm * kBM;
         const int n0 = tn * kBN;
-        AccW acc;
-        mainloop<Mma::kBf16, false, true>(reinterpret_cast<const uint8_t*>(ws), kHidden * 2, m0, M,
-                                          reinterpret_cast<const uint8_t*>(W), kHidden * 2, n0, n0 + 128,
-                                          kHidden * 2 / kRowB, smem, acc, MxScales{},
-                                          QkvBRows{n0 < 2 * kAttnWidth});
-        if (opaque_tid() < kThreads / 2) {          // G0: its epilogue overlaps G1's last compute phase
-            // G0's dead fills past the end land first (they write the slot rows that hold the
-            // claim word); the epilogue's own loads and stores need no wait before the barrier
-            __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
-            qkv_epilogue_regs<kE4m3>(acc, m0, M, n0, qw, kw, cs, S, pos, qk_eps, hpd, dq, dk, dv, out);
-            pp_barrier<63>();   // the barrier that ends G1's last compute phase
-            tq.claim(smem);
-        } else {
-            qkv_epilogue_regs<kE4m3>(acc, m0, M, n0, qw, kw, cs, S, pos, qk_eps, hpd, dq, dk, dv, out);
-        }
-        __syncthreads();        // every wave's loads drained before the next fills; the claim visible
-    }
-    tq.finish();
+        t = TileOps{reinterpret_cast<const uint8_t*>(ws), kHidden * 2, (int64_t)tm * kBM, M,
+                    reinterpret_cast<const uint8_t*>(W), kHidden * 2, n0, n0 + 128, kHidden * 2 / kRowB};
+        bm = QkvBRows{n0 < 2 * kAttnWidth};
+    };
+    auto epi = [&](const AccW& acc, const TileOps& t) {
+        qkv_epilogue_regs<kE4m3>(acc, t.m0, M, (int)t.nb0, qw, kw, cs, S, pos, qk_eps, hpd, dq, dk, dv, out);
+    };
+    persistent_tiles<Mma::kBf16, false, false, AccW, QkvBRows>(tq, smem, tile, epi);
 }
 
 // The same tile on MXFP4 operands: the workspace's and the weight's E2M1 codes ([M, 2688],
