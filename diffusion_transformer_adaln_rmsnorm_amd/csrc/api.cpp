@@ -308,6 +308,11 @@ dit_status dit_mlp_fp8(const void* x, int64_t M, const void* x_norm_weight, dit_
     if (st != DIT_OK) return st;
     st = launched(dit::launch_fc1_swiglu(ws_a_q, ws_a_scale, M, fc1_q, fc1_scale, static_cast<uint16_t*>(ws_y), s));
     if (st != DIT_OK) return st;
+    if (dit::fc2_fused_fits(M))
+        return launched(dit::launch_fc2_fused(static_cast<const uint16_t*>(ws_y), ws_y_scale, ws_y_q, M, fc2_q,
+                                              fc2_scale, static_cast<const uint16_t*>(gate.ptr), gate.rows,
+                                              gate.row_stride, adaln_index, static_cast<const uint16_t*>(residual),
+                                              static_cast<uint16_t*>(out), s));
     st = launched(dit::launch_quant_rows(static_cast<const uint16_t*>(ws_y), M, ws_y_scale, ws_y_q, s));
     if (st != DIT_OK) return st;
     return launched(dit::launch_fc2_gated(ws_y_q, ws_y_scale, M, fc2_q, fc2_scale,

@@ -85,6 +85,10 @@ __device__ __forceinline__ void logical_coords(int L, int mt, int nt, int& tm, i
 // range of the logical order, and the ~32 tiles an XCD runs at once share 4 A panels and 8 B
 // panels in its L2.
 constexpr int kXcds = 8;
+// The XCD this wave runs on (the XCC_ID hardware register, 0..7).
+__device__ __forceinline__ int hw_xcd() {
+    return (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & (kXcds - 1));
+}
 __device__ __forceinline__ void xcd_range(int xcd, int G, int& lo, int& cnt) {
     const int per = G / kXcds, rem = G % kXcds;
     lo = xcd * per + (xcd < rem ? xcd : rem);
@@ -104,26 +108,33 @@ __device__ __forceinline__ void tile_coords(int bid, int mt, int nt, int& tm, in
 // starts) are claimed by one lane with a global atomic add; the index reaches the other waves
 // through an LDS word just past the staged epilogue tile, which no main loop or epilogue holds
 // at the two points it is used: after the main loop (claim) and after the epilogue's closing
-// barrier (read).  A counter set is kTileQueueWords words: the kXcds tile counters and a count
-// of finished workgroups.  The workgroup that finishes last puts the set back to zero for its
-// next launch (finish()): every other workgroup has made its last claim before it counted
-// itself finished.
-constexpr int kTileQueueWords = 16;
+// barrier (read).  A counter set is kTileQueueWords words: the kXcds tile counters, a count of
+// finished workgroups and, from kReadyBase, the ready counters of a launch that hands work
+// between its workgroups (the fused FC2).  The workgroup that finishes last puts the set back to
+// zero for its next launch (finish()): every other workgroup has made its last claim, and read
+// its last ready counter, before it counted itself finished.
+constexpr int kReadyBase = 16;
+constexpr int kMaxReady = 144;
+constexpr int kTileQueueWords = kReadyBase + kMaxReady;
 struct TileQueue {
     uint32_t* set;     // the launch's counter set
     uint32_t* ctr;     // this XCD's counter
+    int xcd;           // the XCD whose range this workgroup works on
     int lo, cnt;       // this XCD's range of the logical order
-    __device__ __forceinline__ TileQueue(uint32_t* counters, int mt, int nt) {
-        const int xcd = blockIdx.x % kXcds;
+    __device__ __forceinline__ TileQueue(uint32_t* counters, int mt, int nt, int x = -1) {
+        xcd = x >= 0 ? x : (int)(blockIdx.x % kXcds);
         set = counters;
         ctr = counters + xcd;
         xcd_range(xcd, mt * nt, lo, cnt);
     }
-    // after the workgroup's last claim: count it finished; the last one zeroes the set
-    __device__ __forceinline__ void finish() const {
+    // after the workgroup's last claim: count it finished; the last one zeroes the set (the tile
+    // counters, the finished count and the first nready ready counters)
+    __device__ __forceinline__ void finish(int nready = 0) const {
         if (threadIdx.x == 0 && atomicAdd(set + kXcds, 1u) == gridDim.x - 1) {
 #pragma unroll
             for (int i = 0; i <= kXcds; ++i) __hip_atomic_store(set + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            for (int i = 0; i < nready; ++i)
+                __hip_atomic_store(set + kReadyBase + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     static __device__ __forceinline__ uint32_t* slot(uint8_t* smem) {
@@ -787,6 +798,7 @@ __device__ __forceinline__ void persistent_tiles(const TileQueue& tq, uint8_t* s
         }
         // every wave's loads drained (the next tile's prologue fills landed) and every read of the
         // claim word done before the next tile's first fill of its row
+        __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
         __syncthreads();
         k = kn;
         prefilled = kPrefill;

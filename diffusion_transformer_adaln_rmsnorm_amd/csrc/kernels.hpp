@@ -61,6 +61,13 @@ hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M
 
 hipError_t launch_quant_rows(const uint16_t* y, int64_t M, float* y_scale, uint8_t* y_q, hipStream_t stream);
 
+// FC2 with the y quantisation in the same launch (y -> y_q, y_scale, then the gated FC2), for the
+// M that fc2_fused_fits accepts (the m tiles split into whole groups per XCD).
+bool fc2_fused_fits(int64_t M);
+hipError_t launch_fc2_fused(const uint16_t* y, float* y_scale, uint8_t* y_q, int64_t M, const uint8_t* W2,
+                            const float* w2s, const uint16_t* gate, int64_t gate_rows, int64_t gate_ld,
+                            const int64_t* idx, const uint16_t* residual, uint16_t* out, hipStream_t stream);
+
 hipError_t launch_fc2_gated(const uint8_t* y_q, const float* y_scale, int64_t M, const uint8_t* W2,
                             const float* w2s, const uint16_t* gate, int64_t gate_rows, int64_t gate_ld,
                             const int64_t* idx, const uint16_t* residual, uint16_t* out, hipStream_t stream);

@@ -9,9 +9,11 @@
 //
 // FC1 tile: 256 rows x (128 gate columns j0.. and the 128 up columns 14336+j0..), so the
 // SwiGLU pair of every column is in the same tile; its epilogue writes y straight from the
-// accumulators.  The quantisation kernel then reads each row of y once, takes its maximum |y|
-// for s_y and writes y_q; FC2 consumes y_q.  Stream order separates the three launches, so no
-// tile-ready flags are needed.
+// accumulators.  The y quantisation then reads each row of y once, takes its maximum |y| for s_y
+// and writes y_q, and FC2 consumes y_q: where the m tiles split into whole groups per XCD, FC2
+// quantises y itself, a group ahead of its GEMM tiles, behind ready counters
+// (k_fc2_gated_fused); otherwise a launch of its own does it, and stream order separates the
+// three launches.
 #include "common.hpp"
 #include "gated.hpp"
 #include "gemm.hpp"
@@ -92,19 +94,18 @@ void k_fc1_swiglu(const uint8_t* __restrict__ a_q, const float* __restrict__ a_s
     persistent_tiles<Mma::kE4m3, true, true, Acc, BRowsDefault>(tq, smem, tile, epi);
 }
 
-// y quantisation: one wavefront per row; 14336 = 1792 chunks of 8, 28 per lane.  The row is
+// y quantisation of row m by one wavefront: 14336 = 1792 chunks of 8, 28 per lane.  The row is
 // read once into registers: its maximum |y| (on the bf16 bits, as in the MX quantiser), then
-// s_y = RN(amax / 448) and the codes.
-__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ y, int64_t M,
-                                                    float* __restrict__ y_scale, uint8_t* __restrict__ y_q) {
-    const int lane = threadIdx.x & 63;
-    const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (m >= M) return;
+// s_y = RN(amax / 448) and the codes.  kNt: y is read with the non-temporal cache policy (inside
+// FC2, so that the stream does not evict the GEMM tiles' operands from L2).
+template <bool kNt = false>
+__device__ __forceinline__ void quant_y_row(const uint16_t* __restrict__ y, int64_t m, float* __restrict__ y_scale,
+                                            uint8_t* __restrict__ y_q, int lane) {
     constexpr int kPerLane = kInter / 8 / 64;    // 28
     const uint16_t* yr = y + m * kInter;
     u32x4 yv[kPerLane];
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) yv[j] = ld16(yr + (j * 64 + lane) * 8);
+    for (int j = 0; j < kPerLane; ++j) yv[j] = kNt ? ld16_nt(yr + (j * 64 + lane) * 8) : ld16(yr + (j * 64 + lane) * 8);
     uint32_t am = 0;
 #pragma unroll
     for (int j = 0; j < kPerLane; ++j) am = max(am, amax_bits8(yv[j]));
@@ -131,6 +132,14 @@ __global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__
     if (lane == 0) y_scale[m] = s;
 }
 
+// y quantisation as a launch of its own: one wavefront per row.
+__global__ __launch_bounds__(256) void k_quant_rows(const uint16_t* __restrict__ y, int64_t M,
+                                                    float* __restrict__ y_scale, uint8_t* __restrict__ y_q) {
+    const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (m >= M) return;
+    quant_y_row(y, m, y_scale, y_q, threadIdx.x & 63);
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
 void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_scale, int64_t M,
                  const uint8_t* __restrict__ W2, const float* __restrict__ w2s, const uint16_t* __restrict__ gate,
@@ -149,6 +158,175 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
                                            residual, out);
     };
     persistent_tiles<Mma::kE4m3, false, true, AccW, Cols8BRows>(tq, smem, tile, epi);
+}
+
+// FC2 with the y quantisation in the same launch, as the MLP page's FC2 quantises y for its own
+// tiles and publishes tile-ready flags (description under its formula block).  Used when the m
+// tiles split into the XCDs' ranges as whole groups of kQGroupTiles m tiles (mt a multiple of
+// 4 x 8), so that every row of a group is quantised and consumed on one XCD.  Each XCD's queue
+// interleaves quant units (32 rows of y -> y_q and s_y, 4 rows per wave) with its GEMM tiles: the
+// 32 units of its first group, then each group's 84 tiles in four chunks of 21, each chunk
+// followed by 8 of the next group's units, so that a group's units run one group ahead, beside
+// GEMM tiles, and the y stream overlaps the MFMA work.
+//
+// Hand-over: a unit's waves wait for their stores, then its workgroup adds one to the group's
+// ready counter; a GEMM tile of the group (or G0, before it issues the tile's prologue fills)
+// waits until the counter holds all 32 units.  Producer and consumer run on the same XCD (the
+// range is chosen by the hardware XCD id), so the codes and scales are in the L2 they both use;
+// no CU has read those rows' codes or scales earlier in the launch (each L1 starts empty), so no
+// L1 holds stale copies.  Every unit a tile waits for was claimed earlier by a running
+// workgroup and waits for nothing itself, so the wait ends.
+constexpr int kQGroupTiles = 4;                               // m tiles per group (the logical order's)
+constexpr int kQUnitRows = kWaves * 4;                        // rows of y per quant unit
+constexpr int kQUnits = kQGroupTiles * kBM / kQUnitRows;      // units per group: 32
+constexpr int kQNt = kHidden / kBN;                           // FC2's n tiles: 21
+constexpr int kQGroupN = kQGroupTiles * kQNt;                 // GEMM tiles per group: 84
+constexpr int kQChunks = 4;
+constexpr int kQChunkTiles = kQGroupN / kQChunks;             // 21
+constexpr int kQChunkUnits = kQUnits / kQChunks;              // 8
+constexpr int kQChunk = kQChunkTiles + kQChunkUnits;          // 29
+constexpr int kQSpan = kQGroupN + kQUnits;                    // items per group: 116
+static_assert(kQGroupN % kQChunks == 0 && kQUnits % kQChunks == 0, "chunks");
+
+// Item i of an XCD's queue (ng groups): a unit (group g, unit idx) or a GEMM tile (group g, tile
+// idx of the group, in the logical order).
+struct QItem {
+    bool unit;
+    int g, idx;
+};
+__host__ __device__ constexpr QItem q_item(int i, int ng) {
+    if (i < kQUnits) return QItem{true, 0, i};
+    i -= kQUnits;
+    if (i < kQSpan * (ng - 1)) {
+        const int g = i / kQSpan, r = i - g * kQSpan, c = r / kQChunk, p = r - c * kQChunk;
+        return p < kQChunkTiles ? QItem{false, g, kQChunkTiles * c + p}
+                                : QItem{true, g + 1, kQChunkUnits * c + (p - kQChunkTiles)};
+    }
+    return QItem{false, ng - 1, i - kQSpan * (ng - 1)};
+}
+// Every tile and unit of ng groups appears once, and a group's units all precede its first tile.
+constexpr bool q_order_ok(int ng) {
+    int units_seen[32] = {}, tiles_seen[32] = {};
+    bool tile_seen[32 * kQGroupN] = {}, unit_seen[32 * kQUnits] = {};
+    for (int i = 0; i < kQSpan * ng; ++i) {
+        const QItem it = q_item(i, ng);
+        if (it.g < 0 || it.g >= ng) return false;
+        if (it.unit) {
+            if (it.idx < 0 || it.idx >= kQUnits || unit_seen[it.g * kQUnits + it.idx]) return false;
+            if (tiles_seen[it.g] != 0) return false;
+            unit_seen[it.g * kQUnits + it.idx] = true;
+            ++units_seen[it.g];
+        } else {
+            if (it.idx < 0 || it.idx >= kQGroupN || tile_seen[it.g * kQGroupN + it.idx]) return false;
+            if (units_seen[it.g] != kQUnits) return false;
+            tile_seen[it.g * kQGroupN + it.idx] = true;
+            ++tiles_seen[it.g];
+        }
+    }
+    for (int g = 0; g < ng; ++g)
+        if (units_seen[g] != kQUnits || tiles_seen[g] != kQGroupN) return false;
+    return true;
+}
+static_assert(q_order_ok(1) && q_order_ok(2) && q_order_ok(4) && q_order_ok(7) && q_order_ok(18), "quant unit order");
+static_assert(kMaxReady >= kXcds * 18, "ready counters for the largest fused launch");
+
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kWaves / 4, kWaves / 4)))
+void k_fc2_gated_fused(const uint16_t* __restrict__ y, float* __restrict__ y_scale, uint8_t* __restrict__ y_q,
+                       int64_t M, const uint8_t* __restrict__ W2, const float* __restrict__ w2s,
+                       const uint16_t* __restrict__ gate, int64_t gate_rows, int64_t gate_ld,
+                       const int64_t* __restrict__ idx, const uint16_t* residual, uint16_t* out, int mt,
+                       uint32_t* tq_ctr) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+    const int ng = mt / (kQGroupTiles * kXcds);                    // groups per XCD
+    const TileQueue tq(tq_ctr, kXcds * kQSpan * ng, 1, hw_xcd());  // kQSpan ng items per XCD
+    const int gx = tq.xcd * ng;                                    // this XCD's first group
+    uint32_t* const ready = tq.set + kReadyBase;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const bool g0 = wave < 4;
+    auto tile = [&](const QItem& it, TileOps& to) {
+        int tm, tn;
+        logical_coords((gx + it.g) * kQGroupN + it.idx, mt, kQNt, tm, tn);
+        const int n0 = tn * kBN;
+        to = TileOps{y_q, kInter, (int64_t)tm * kBM, M, W2, kInter, n0, n0 + 128, kInter / kRowB};
+    };
+    // until every unit of group g has been counted (read at L2: the load skips the L1)
+    auto wait_ready = [&](int g) {
+        const uint32_t* r = ready + gx + g;
+        while (__hip_atomic_load(r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)kQUnits)
+            __builtin_amdgcn_s_sleep(2);
+    };
+    tq.claim(smem);
+    __syncthreads();
+    int k = tq.claimed(smem);
+    bool prefilled = false;
+    while (k < tq.cnt) {
+        const QItem it = q_item(k, ng);
+        if (it.unit) {
+            const int64_t r0 = (int64_t)(gx + it.g) * (kQGroupTiles * kBM) + it.idx * kQUnitRows + 4 * wave;
+            for (int q = 0; q < 4; ++q)
+                if (r0 + q < M) quant_y_row<true>(y, r0 + q, y_scale, y_q, threadIdx.x & 63);
+            __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): this wave's codes and scale are in L2
+            __syncthreads();
+            if (threadIdx.x == 0) atomicAdd(ready + gx + it.g, 1u);
+            tq.claim(smem);
+            __syncthreads();
+            k = tq.claimed(smem);
+            prefilled = false;
+            continue;
+        }
+        TileOps to;
+        tile(it, to);
+        if (!prefilled) wait_ready(it.g);
+        AccW acc;
+        mainloop_pp<Mma::kE4m3, false, true, AccW, Cols8BRows>(to.A, to.lda, to.m0, to.M, to.B, to.ldb, to.nb0,
+                                                               to.nb1, to.ktiles, smem, acc, MxScales{},
+                                                               Cols8BRows{}, prefilled);
+        int kn;
+        if (g0) {
+            tq.mark_empty(smem);
+            gated_epilogue_regs<int64_t, true>(acc, to.m0, M, (int)to.nb0, y_scale, w2s, idx, gate, gate_rows, gate_ld,
+                                               residual, out);
+            pp_barrier<63>();   // the barrier that ends G1's last compute phase
+            kn = tq.claim_wait(smem);
+            if (kn < tq.cnt) {
+                const QItem nx = q_item(kn, ng);
+                if (!nx.unit) {
+                    wait_ready(nx.g);
+                    TileOps tn;
+                    tile(nx, tn);
+                    prefill<false>(tn, smem, Cols8BRows{});
+                }
+            }
+        } else {
+            gated_epilogue_regs<int64_t, true>(acc, to.m0, M, (int)to.nb0, y_scale, w2s, idx, gate, gate_rows, gate_ld,
+                                               residual, out);
+            kn = tq.wait_claimed(smem);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0): the prologue fills landed
+        __syncthreads();
+        prefilled = kn < tq.cnt && !q_item(kn, ng).unit;
+        k = kn;
+    }
+    tq.finish(kXcds * ng);
+}
+
+bool fc2_fused_fits(int64_t M) {
+    const int64_t mt = (M + kBM - 1) / kBM;
+    return mt % (kQGroupTiles * kXcds) == 0 && mt / kQGroupTiles <= kMaxReady;
+}
+
+hipError_t launch_fc2_fused(const uint16_t* y, float* y_scale, uint8_t* y_q, int64_t M, const uint8_t* W2,
+                            const float* w2s, const uint16_t* gate, int64_t gate_rows, int64_t gate_ld,
+                            const int64_t* idx, const uint16_t* residual, uint16_t* out, hipStream_t stream) {
+    if (!fc2_fused_fits(M)) return hipErrorInvalidValue;
+    const int mt = (int)((M + kBM - 1) / kBM);
+    uint32_t* q = nullptr;
+    int grid = 0;
+    const hipError_t e = tile_queue(stream, &q, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_fc2_gated_fused, dim3((unsigned)grid), dim3(kThreads), 0, stream, y, y_scale, y_q, M, W2, w2s,
+                       gate, gate_rows, gate_ld, idx, residual, out, mt, q);
+    return hipGetLastError();
 }
 
 hipError_t launch_fc1_swiglu(const uint8_t* a_q, const float* a_scale, int64_t M, const uint8_t* W1,

@@ -252,8 +252,10 @@ dit_status dit_mlp_fp8(const void* x, int64_t M, const void* x_norm_weight,
 
 /*
  * Number of int32 tile-ready flags dit_mlp_fp8 needs for M rows (the counterpart of the
- * page's minimax_h3_mlp_fc2_flags_sm120).  This implementation orders FC1, the y quant and
- * FC2 by stream order and needs none: it returns 0 for every M, and ws_flags is ignored.
+ * page's minimax_h3_mlp_fc2_flags_sm120).  This implementation needs none from the caller: it
+ * returns 0 for every M, and ws_flags is ignored.  (Where FC2 quantises y in its own launch, its
+ * ready counters live in the library's per-GPU tile-queue pool, zeroed by each launch that uses
+ * them.)
  */
 int64_t dit_mlp_fp8_flags_elems(int64_t M);
 

@@ -1152,6 +1152,23 @@ def test_mlp_maximum_M():
     check_mlp(d, out, ws, sample_rows(M, d, n_random=32))
 
 
+@pytest.mark.parametrize("M", [8192, 16300])
+def test_mlp_y_quant_inside_fc2(M):
+    """M whose m tiles split into whole groups of four per XCD (32 and 64 m tiles), where FC2
+    quantises y in its own launch: one group per XCD (all units before the tiles), and two
+    groups per XCD (the second group's units among the first group's tiles) with a ragged last
+    m tile (172 rows).  Sampled rows against the oracle (codes, scales, y and out), and a
+    second run bit-identical."""
+    _say(f"fp8 MLP, y quantised inside FC2, M={M}")
+    d = synth.mlp_inputs(M, seed=950 + M % 97, weights=_mlp_weights(), bad_index_frac=0.001)
+    out, ws = run_mlp(d)
+    out2, ws2 = run_mlp(d)
+    assert np.array_equal(synth.bits(out), synth.bits(out2)), "out not deterministic"
+    for k in ("workspace_y_q", "workspace_y_scale"):
+        assert torch.equal(ws[k].view(torch.uint8), ws2[k].view(torch.uint8)), f"{k} not deterministic"
+    check_mlp(d, out, ws, sample_rows(M, d, n_random=96))
+
+
 def test_mlp_config4_sampled_and_deterministic():
     _say("config 4: fp8 MLP M=32760")
     kind, d = synth.config(4)
