@@ -30,18 +30,21 @@ __device__ __forceinline__ bool chunk_ok(int j, int lane) { return j * 64 + lane
 // flight before the guard: at small M each row is a chain of memory latencies (index -> table
 // rows), not a stream.  x is read once, so its loads are non-temporal and keep it from
 // displacing the tables and the workspace in the caches (10% faster on a cold M = 32760 pass).
+// The norm weight, the same for every row, is staged once per workgroup in LDS (stage_weight)
+// and read from there chunk by chunk: held in registers beside the row's x, scale and shift it
+// took 44 more of them and kept the kernels at 2 waves per SIMD (3 now: bf16 norm -8%).
 struct RowRegs {
-    u32x4 x[kMaxPerLane], w[kMaxPerLane], sc[kMaxPerLane], sh[kMaxPerLane];
+    u32x4 x[kMaxPerLane], sc[kMaxPerLane], sh[kMaxPerLane];
 };
 
-__device__ __forceinline__ void load_x_w(const uint16_t* xr, const uint16_t* xw, int lane, RowRegs& rg) {
+__device__ __forceinline__ void stage_weight(const uint16_t* xw, u32x4* wl) {
+    for (int c = threadIdx.x; c < kChunks; c += 256) wl[c] = ld16(xw + c * 8);
+}
+
+__device__ __forceinline__ void load_x(const uint16_t* xr, int lane, RowRegs& rg) {
 #pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) {
-        if (chunk_ok(j, lane)) {
-            rg.x[j] = ld16_nt(xr + (j * 64 + lane) * 8);
-            rg.w[j] = ld16(xw + (j * 64 + lane) * 8);
-        }
-    }
+    for (int j = 0; j < kMaxPerLane; ++j)
+        if (chunk_ok(j, lane)) rg.x[j] = ld16_nt(xr + (j * 64 + lane) * 8);
 }
 
 __device__ __forceinline__ void load_tables(const uint16_t* scr, const uint16_t* shr, int lane, RowRegs& rg) {
@@ -99,27 +102,32 @@ __global__ __launch_bounds__(256) void k_norm_adaln_bf16(const uint16_t* __restr
                                                          const uint16_t* __restrict__ shift, int64_t ld_shift,
                                                          int64_t rows, const int64_t* __restrict__ idx,
                                                          float eps, uint16_t* __restrict__ ws) {
+    __shared__ __attribute__((aligned(16))) u32x4 wl[kChunks];
     const int lane = threadIdx.x & 63;
     const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (m >= M) return;
-    uint16_t* wr = ws + m * kHidden;
-    const int64_t i = idx[m];
+    const bool live = m < M;
+    stage_weight(xw, wl);
+    const int64_t i = live ? idx[m] : -1;
+    const bool ok = i >= 0 && i < rows;        // full-width int64 guard
     RowRegs rg;
-    load_x_w(x + m * kHidden, xw, lane, rg);
-    if (!(i >= 0 && i < rows)) {               // full-width int64 guard
+    if (live) load_x(x + m * kHidden, lane, rg);
+    if (ok) load_tables(scale + i * ld_scale, shift + i * ld_shift, lane, rg);
+    __syncthreads();                           // the weight staged (every wave, before any exit)
+    if (!live) return;
+    uint16_t* wr = ws + m * kHidden;
+    if (!ok) {
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < kMaxPerLane; ++j)
             if (chunk_ok(j, lane)) st16(wr + (j * 64 + lane) * 8, z);
         return;
     }
-    load_tables(scale + i * ld_scale, shift + i * ld_shift, lane, rg);
     const float r = row_rms(rg, lane, eps);
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (!chunk_ok(j, lane)) continue;
         uint32_t a[4];
-        modulate_chunk(rg.x[j], rg.w[j], rg.sc[j], rg.sh[j], r, a);
+        modulate_chunk(rg.x[j], wl[j * 64 + lane], rg.sc[j], rg.sh[j], r, a);
         st16(wr + (j * 64 + lane) * 8, u32x4{a[0], a[1], a[2], a[3]});
     }
 }
@@ -136,8 +144,17 @@ __global__ __launch_bounds__(256) void k_norm_adaln_mxfp4(const uint16_t* __rest
                                                           int64_t rows, const int64_t* __restrict__ idx, float eps,
                                                           int64_t R_pad, uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
+    __shared__ __attribute__((aligned(16))) u32x4 wl[kChunks];
     const int lane = threadIdx.x & 63;
     const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    stage_weight(xw, wl);
+    const bool live = m < M;
+    const int64_t i = live ? idx[m] : -1;
+    const bool ok = i >= 0 && i < rows;               // full-width int64 guard
+    RowRegs rg;
+    if (live) load_x(x + m * kHidden, lane, rg);
+    if (ok) load_tables(scale + i * ld_scale, shift + i * ld_shift, lane, rg);
+    __syncthreads();                                  // the weight staged (every wave, before any exit)
     if (m >= R_pad) return;
     // scale byte of chunk j's block (b = 16 j + lane / 4) in the MX scale layout: a per-row and a
     // per-lane part plus j * 2048 (b / 8 = 2 j + lane / 32, while b % 2 and (b % 8) / 2 depend on
@@ -146,39 +163,31 @@ __global__ __launch_bounds__(256) void k_norm_adaln_mxfp4(const uint16_t* __rest
     const int64_t rr = m % 128;
     uint8_t* const srow = scales + (m / 128) * (kHidden / 256) * 1024 + 16 * (rr % 32) + 4 * (rr / 32) +
                           (lane / 32) * 1024 + 512 * ((lane / 4) % 2) + (lane / 8) % 4;
-    if (m >= M) {
+    if (!live) {
 #pragma unroll
         for (int j = 0; j < kMaxPerLane; ++j)
             if (chunk_ok(j, lane) && (lane & 3) == 0) srow[j * 2048] = 0;
         return;
     }
-    const int64_t i = idx[m];
-    RowRegs rg;
-    load_x_w(x + m * kHidden, xw, lane, rg);
-    u32x4 av[kMaxPerLane];
-#pragma unroll
-    for (int j = 0; j < kMaxPerLane; ++j) av[j] = u32x4{0u, 0u, 0u, 0u};
-    if (i >= 0 && i < rows) {                         // full-width int64 guard
-        load_tables(scale + i * ld_scale, shift + i * ld_shift, lane, rg);
-        const float r = row_rms(rg, lane, eps);
-#pragma unroll
-        for (int j = 0; j < kMaxPerLane; ++j) {
-            if (!chunk_ok(j, lane)) continue;
-            uint32_t a[4];
-            modulate_chunk(rg.x[j], rg.w[j], rg.sc[j], rg.sh[j], r, a);
-            av[j] = u32x4{a[0], a[1], a[2], a[3]};
-        }
-    }
+    // each chunk is quantised as soon as it is modulated (its 32-value block is one quad's
+    // chunks), so the modulated row is never held whole; guarded rows quantise a = 0
+    const float r = ok ? row_rms(rg, lane, eps) : 0.f;
     uint8_t* cr = codes + m * (kHidden / 2);
 #pragma unroll
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (!chunk_ok(j, lane)) continue;             // whole quads drop out together
-        uint32_t amax = amax_bits8(av[j]);
+        u32x4 av = {0u, 0u, 0u, 0u};
+        if (ok) {
+            uint32_t a[4];
+            modulate_chunk(rg.x[j], wl[j * 64 + lane], rg.sc[j], rg.sh[j], r, a);
+            av = u32x4{a[0], a[1], a[2], a[3]};
+        }
+        uint32_t amax = amax_bits8(av);
         // quad_perm(1,0,3,2) then (2,3,0,1): the maximum over the block's four lanes
         amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, true));
         amax = max(amax, (uint32_t)__builtin_amdgcn_mov_dpp((int)amax, 0x4E, 0xF, 0xF, true));
         const uint32_t E = mx_scale_byte(amax);
-        *reinterpret_cast<uint32_t*>(cr + (j * 64 + lane) * 4) = e2m1_pack8(av[j], E);
+        *reinterpret_cast<uint32_t*>(cr + (j * 64 + lane) * 4) = e2m1_pack8(av, E);
         if ((lane & 3) == 0) srow[j * 2048] = (uint8_t)E;
     }
 }
@@ -191,14 +200,20 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
                                                          int64_t rows, const int64_t* __restrict__ idx,
                                                          float eps, uint8_t* __restrict__ a_q,
                                                          float* __restrict__ a_scale) {
+    __shared__ __attribute__((aligned(16))) u32x4 wl[kChunks];
     const int lane = threadIdx.x & 63;
     const int64_t m = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (m >= M) return;
-    uint8_t* qr = a_q + m * kHidden;
-    const int64_t i = idx[m];
+    const bool live = m < M;
+    stage_weight(xw, wl);
+    const int64_t i = live ? idx[m] : -1;
+    const bool ok = i >= 0 && i < rows;        // full-width int64 guard
     RowRegs rg;
-    load_x_w(x + m * kHidden, xw, lane, rg);
-    if (!(i >= 0 && i < rows)) {               // full-width int64 guard
+    if (live) load_x(x + m * kHidden, lane, rg);
+    if (ok) load_tables(scale + i * ld_scale, shift + i * ld_shift, lane, rg);
+    __syncthreads();                           // the weight staged (every wave, before any exit)
+    if (!live) return;
+    uint8_t* qr = a_q + m * kHidden;
+    if (!ok) {
         const uint2 z = {0u, 0u};
 #pragma unroll
         for (int j = 0; j < kMaxPerLane; ++j)
@@ -206,7 +221,6 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
         if (lane == 0) a_scale[m] = 0.f;
         return;
     }
-    load_tables(scale + i * ld_scale, shift + i * ld_shift, lane, rg);
     const float r = row_rms(rg, lane, eps);
     u32x4 av[kMaxPerLane];
     float amax = 0.f;
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(256) void k_norm_adaln_fp8q(const uint16_t* __restr
     for (int j = 0; j < kMaxPerLane; ++j) {
         if (!chunk_ok(j, lane)) continue;
         uint32_t ap[4];
-        modulate_chunk(rg.x[j], rg.w[j], rg.sc[j], rg.sh[j], r, ap);
+        modulate_chunk(rg.x[j], wl[j * 64 + lane], rg.sc[j], rg.sh[j], r, ap);
         av[j] = u32x4{ap[0], ap[1], ap[2], ap[3]};
         float a[8];
         unpack8(av[j], a);
