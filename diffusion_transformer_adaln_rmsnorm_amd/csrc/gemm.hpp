@@ -85,10 +85,6 @@ __device__ __forceinline__ void logical_coords(int L, int mt, int nt, int& tm, i
 // range of the logical order, and the ~32 tiles an XCD runs at once share 4 A panels and 8 B
 // panels in its L2.
 constexpr int kXcds = 8;
-// The XCD this wave runs on (the XCC_ID hardware register, 0..7).
-__device__ __forceinline__ int hw_xcd() {
-    return (int)(__builtin_amdgcn_s_getreg((20 << 0) | (0 << 6) | (3 << 11)) & (kXcds - 1));
-}
 __device__ __forceinline__ void xcd_range(int xcd, int G, int& lo, int& cnt) {
     const int per = G / kXcds, rem = G % kXcds;
     lo = xcd * per + (xcd < rem ? xcd : rem);
@@ -119,10 +115,10 @@ constexpr int kTileQueueWords = kReadyBase + kMaxReady;
 struct TileQueue {
     uint32_t* set;     // the launch's counter set
     uint32_t* ctr;     // this XCD's counter
-    int xcd;           // the XCD whose range this workgroup works on
+    int xcd;           // the XCD (range) this workgroup works on: blockIdx.x % kXcds
     int lo, cnt;       // this XCD's range of the logical order
-    __device__ __forceinline__ TileQueue(uint32_t* counters, int mt, int nt, int x = -1) {
-        xcd = x >= 0 ? x : (int)(blockIdx.x % kXcds);
+    __device__ __forceinline__ TileQueue(uint32_t* counters, int mt, int nt) {
+        xcd = (int)(blockIdx.x % kXcds);
         set = counters;
         ctr = counters + xcd;
         xcd_range(xcd, mt * nt, lo, cnt);

@@ -171,11 +171,13 @@ void k_fc2_gated(const uint8_t* __restrict__ y_q, const float* __restrict__ y_sc
 //
 // Hand-over: a unit's waves wait for their stores, then its workgroup adds one to the group's
 // ready counter; a GEMM tile of the group (or G0, before it issues the tile's prologue fills)
-// waits until the counter holds all 32 units.  Producer and consumer run on the same XCD (the
-// range is chosen by the hardware XCD id), so the codes and scales are in the L2 they both use;
-// no CU has read those rows' codes or scales earlier in the launch (each L1 starts empty), so no
-// L1 holds stale copies.  Every unit a tile waits for was claimed earlier by a running
-// workgroup and waits for nothing itself, so the wait ends.
+// waits until the counter holds all 32 units.  Producer and consumer work on the same range, so
+// they run on the same XCD: the dispatcher deals workgroups to the XCDs round robin, and workgroup
+// b takes range b % 8, so every workgroup of a range sits on XCD b % (XCDs of the device), which
+// holds for a device of 8, 4, 2 or 1 XCDs.  The codes and scales are therefore in the L2 both
+// use, and no CU has read those rows' codes or scales earlier in the launch (each L1 starts
+// empty), so no L1 holds stale copies.  Every unit a tile waits for was claimed earlier by a
+// running workgroup and waits for nothing itself, so the wait ends.
 constexpr int kQGroupTiles = 4;                               // m tiles per group (the logical order's)
 constexpr int kQUnitRows = kWaves * 4;                        // rows of y per quant unit
 constexpr int kQUnits = kQGroupTiles * kBM / kQUnitRows;      // units per group: 32
@@ -238,8 +240,8 @@ void k_fc2_gated_fused(const uint16_t* __restrict__ y, float* __restrict__ y_sca
                        uint32_t* tq_ctr) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
     const int ng = mt / (kQGroupTiles * kXcds);                    // groups per XCD
-    const TileQueue tq(tq_ctr, kXcds * kQSpan * ng, 1, hw_xcd());  // kQSpan ng items per XCD
-    const int gx = tq.xcd * ng;                                    // this XCD's first group
+    const TileQueue tq(tq_ctr, kXcds * kQSpan * ng, 1);            // kQSpan ng items per range
+    const int gx = tq.xcd * ng;                                    // this range's first group
     uint32_t* const ready = tq.set + kReadyBase;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const bool g0 = wave < 4;
