@@ -190,5 +190,9 @@ __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cas
 __device__ __forceinline__ u32x4 ld16_nt(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+// Streaming (non-temporal) 16-byte store for outputs the writer never reads back.
+__device__ __forceinline__ void st16_nt(void* p, const u32x4& v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 
 }  // namespace dit

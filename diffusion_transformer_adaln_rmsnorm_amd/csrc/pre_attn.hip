@@ -237,8 +237,8 @@ __device__ __forceinline__ void qkv_epilogue_regs(const AccW& acc, int64_t m0, i
                 __builtin_amdgcn_raw_buffer_store_b32(e4m3_codes4(res[2], res[3], ds, ds_inv), rout, (int)(vo1 + roff),
                                                       0, 0);
             } else {
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{res[0], res[1]}, rout, (int)(vo0 + roff), 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{res[2], res[3]}, rout, (int)(vo1 + roff), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{res[0], res[1]}, rout, (int)(vo0 + roff), 0, kStoreNt);
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{res[2], res[3]}, rout, (int)(vo1 + roff), 0, kStoreNt);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -337,7 +337,7 @@ __device__ __forceinline__ void qkv_epilogue_staged(AccMx& acc, uint8_t* smem, i
         if (hpd == kHeads) {
             buf_st16(rout, e1, o);
         } else if (m < M) {
-            st16(out8 + eP * 2, o);
+            st16_nt(out8 + eP * 2, o);
         }
     }
 }
