@@ -197,12 +197,12 @@ __device__ __forceinline__ int64_t buf_ld_i64(__amdgpu_buffer_rsrc_t r, uint32_t
     return (int64_t)(((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0]);
 }
 // The GEMM epilogues' output stores carry the non-temporal cache policy (the nt bit of the
-// buffer instruction's cache-policy operand): a launch writes each output once and never reads it,
-// and streaming it keeps the stores from evicting the operand panels that the workgroups of an XCD
-// share in L2 (MXFP4 pre-attention -6%, whose short tiles store 4x as often per flop as the bf16
-// ones; out-projection -0.3%; bf16 QKV unchanged).  FC1's y is read back at once by FC2 and keeps
-// the default policy, and so do the e4m3 output mode's 4- and 8-byte stores: streamed, their
-// partial lines reached HBM as separate writes (WRITE_SIZE +26%, time +0.4%).
+// buffer instruction's cache-policy operand): a launch writes each output once and never reads it.
+// Measured: MXFP4 pre-attention -6% (its short tiles store 4x as often per flop as the bf16 ones),
+// out-projection -0.3%, bf16 QKV unchanged; the L2-miss reads (FETCH_SIZE) stay the same, so the
+// gain is on the write path.  FC1's y is read back at once by FC2 and keeps the default policy,
+// and so do the e4m3 output mode's 4- and 8-byte stores: streamed, their partial lines reached
+// HBM as separate writes (WRITE_SIZE +26%, time +0.4%).
 constexpr int kStoreNt = 2;
 __device__ __forceinline__ void buf_st16(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, kStoreNt);
